@@ -1,0 +1,538 @@
+// C ABI of the exact layer-0 cached block step (declared in include/lacache.h).
+//
+// Host side only: argument validation (all before any launch), the work
+// decomposition computed from the host block table (no device->host sync),
+// the RoPE table, and the kernel launches on the caller's stream.  The block
+// table of each launch travels inside the kernel arguments; batches larger
+// than lc::kMaxInline samples are launched in slices.
+
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "lacache.h"
+
+struct lacache_ctx {
+  lacache_config cfg;
+  int device;
+  float2 *rope;
+  unsigned *flags;
+  int split_keys;
+  std::string last_error;
+  // Diagnostics: event pairs bracketing each launch while profiling is on.
+  bool profiling = false;
+  struct Mark { int kernel; hipEvent_t start, stop; };
+  std::vector<Mark> marks;
+  std::vector<hipEvent_t> free_events;
+  double prof_ms[LACACHE_KERNEL_COUNT] = {};
+  int64_t prof_n[LACACHE_KERNEL_COUNT] = {};
+};
+
+namespace {
+
+using lc::kMaxInline;
+
+lacache_status fail(const lacache_ctx *ctx, lacache_status st, const char *fmt, ...)
+    __attribute__((format(printf, 3, 4)));
+
+lacache_status fail(const lacache_ctx *ctx, lacache_status st, const char *fmt, ...) {
+  if (ctx) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    const_cast<lacache_ctx *>(ctx)->last_error = buf;
+  }
+  return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+lacache_status check_device(lacache_ctx *ctx) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ctx, LACACHE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev != ctx->device)
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "context was created on device %d but device %d is current",
+                ctx->device, dev);
+  return LACACHE_OK;
+}
+
+// Block-table checks shared by every call.  n_rows < 0: no row bound.
+lacache_status check_table(lacache_ctx *ctx, const lacache_seq *seqs, int32_t batch, int64_t n_rows) {
+  if (!seqs) return fail(ctx, LACACHE_ERR_INVALID_ARG, "seqs is NULL");
+  if (batch < 1) return fail(ctx, LACACHE_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  std::vector<std::pair<int64_t, int64_t>> ranges;
+  ranges.reserve(batch);
+  for (int i = 0; i < batch; ++i) {
+    const lacache_seq &s = seqs[i];
+    if (s.seq_offset < 0 || s.seq_len < 1)
+      return fail(ctx, LACACHE_ERR_INVALID_ARG, "sample %d: seq_offset %d / seq_len %d invalid", i, s.seq_offset,
+                  s.seq_len);
+    if (s.seq_len > ctx->cfg.max_seq_len)
+      return fail(ctx, LACACHE_ERR_INVALID_ARG, "sample %d: seq_len %d exceeds max_seq_len %d", i, s.seq_len,
+                  ctx->cfg.max_seq_len);
+    if (!(0 <= s.block_start && s.block_start < s.block_end && s.block_end <= s.seq_len))
+      return fail(ctx, LACACHE_ERR_INVALID_ARG, "sample %d: block [%d, %d) not inside [0, %d) or empty", i,
+                  s.block_start, s.block_end, s.seq_len);
+    if (s.block_end - s.block_start > 128)
+      return fail(ctx, LACACHE_ERR_UNSUPPORTED, "sample %d: block of %d tokens (at most 128 supported)", i,
+                  s.block_end - s.block_start);
+    const int64_t end = (int64_t)s.seq_offset + s.seq_len;
+    if (n_rows >= 0 && end > n_rows)
+      return fail(ctx, LACACHE_ERR_INVALID_ARG, "sample %d: rows [%d, %lld) exceed the %lld rows of the buffers", i,
+                  s.seq_offset, (long long)end, (long long)n_rows);
+    ranges.emplace_back(s.seq_offset, end);
+  }
+  std::sort(ranges.begin(), ranges.end());
+  for (size_t i = 1; i < ranges.size(); ++i)
+    if (ranges[i].first < ranges[i - 1].second)
+      return fail(ctx, LACACHE_ERR_INVALID_ARG, "row ranges of two samples overlap at row %lld",
+                  (long long)ranges[i].first);
+  return LACACHE_OK;
+}
+
+int nchunks(const lacache_ctx *ctx, int len) { return (len + ctx->split_keys - 1) / ctx->split_keys; }
+
+int64_t partial_rows(const lacache_ctx *ctx, const lacache_seq *seqs, int32_t batch) {
+  int64_t p = 0;
+  for (int i = 0; i < batch; ++i) p += (int64_t)nchunks(ctx, seqs[i].seq_len) * (seqs[i].block_end - seqs[i].block_start);
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace layout for type-A partials: part_ml [P, H] float2, part_o [P, H, d_h] float.
+size_t partial_bytes(const lacache_ctx *ctx, int64_t P) {
+  const size_t H = ctx->cfg.n_heads, d = ctx->cfg.head_dim;
+  return align256((size_t)P * H * sizeof(float2)) + align256((size_t)P * H * d * sizeof(float));
+}
+
+lc::SeqArgs slice_args(const lacache_seq *seqs, int s0, int ns) {
+  lc::SeqArgs sa;
+  std::memset(&sa, 0, sizeof(sa));
+  sa.n = ns;
+  for (int i = 0; i < ns; ++i) {
+    sa.off[i] = seqs[s0 + i].seq_offset;
+    sa.len[i] = seqs[s0 + i].seq_len;
+    sa.bs[i] = seqs[s0 + i].block_start;
+    sa.be[i] = seqs[s0 + i].block_end;
+  }
+  return sa;
+}
+
+hipEvent_t take_event(lacache_ctx *ctx) {
+  if (!ctx->free_events.empty()) {
+    hipEvent_t e = ctx->free_events.back();
+    ctx->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (returning hipError_t), bracketed by events when profiling.
+template <typename F> hipError_t timed(lacache_ctx *ctx, int kernel, hipStream_t s, F &&launch) {
+  if (!ctx->profiling) return launch();
+  hipEvent_t a = take_event(ctx), b = take_event(ctx);
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  if (e == hipSuccess) ctx->marks.push_back({kernel, a, b});
+  return e;
+}
+
+lc::DType dtype_of(const lacache_ctx *ctx) { return ctx->cfg.dtype == LACACHE_BF16 ? lc::kBF16 : lc::kF32; }
+
+float scale_log2(const lacache_ctx *ctx) {
+  const double s = ctx->cfg.sm_scale > 0 ? (double)ctx->cfg.sm_scale : 1.0 / std::sqrt((double)ctx->cfg.head_dim);
+  return (float)(s * 1.4426950408889634);
+}
+
+lacache_status hip_fail(lacache_ctx *ctx, const char *what, hipError_t e) {
+  return fail(ctx, LACACHE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+lacache_status check_cache(lacache_ctx *ctx, const lacache_cache *c, bool facache) {
+  if (!c) return fail(ctx, LACACHE_ERR_INVALID_ARG, "cache is NULL");
+  const void *ptrs[7] = {c->h, c->q, c->k, c->v, c->m, c->l, c->o_acc};
+  const char *names[7] = {"h", "q", "k", "v", "m", "l", "o_acc"};
+  for (int i = 0; i < (facache ? 7 : 4); ++i) {
+    if (!ptrs[i]) return fail(ctx, LACACHE_ERR_INVALID_ARG, "cache.%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(ctx, LACACHE_ERR_INVALID_ARG, "cache.%s is not 16-byte aligned", names[i]);
+  }
+  if (c->n_rows < 1) return fail(ctx, LACACHE_ERR_INVALID_ARG, "cache.n_rows must be >= 1");
+  return LACACHE_OK;
+}
+
+lacache_status check_weights(lacache_ctx *ctx, const lacache_weights *w) {
+  if (!w || !w->embed || !w->gamma || !w->w_qkv) return fail(ctx, LACACHE_ERR_INVALID_ARG, "weights or a weight pointer is NULL");
+  if (!aligned16(w->embed) || !aligned16(w->gamma) || !aligned16(w->w_qkv))
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  return LACACHE_OK;
+}
+
+lc::QkvArgs qkv_args(lacache_ctx *ctx, const lacache_weights *w, const lacache_cache *c, const int32_t *ids, int mode) {
+  lc::QkvArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.ids = ids;
+  a.E = w->embed;
+  a.gamma = w->gamma;
+  a.W = w->w_qkv;
+  a.h = c->h;
+  a.q = c->q;
+  a.k = c->k;
+  a.v = c->v;
+  a.rope = ctx->rope;
+  a.flags = ctx->flags;
+  a.mode = mode;
+  a.vocab = ctx->cfg.vocab;
+  a.D = ctx->cfg.d_model;
+  a.H = ctx->cfg.n_heads;
+  a.Hkv = ctx->cfg.n_kv_heads;
+  a.dh = ctx->cfg.head_dim;
+  a.eps = ctx->cfg.rms_eps;
+  return a;
+}
+
+int features(const lacache_ctx *ctx) {
+  return (ctx->cfg.n_heads + 2 * ctx->cfg.n_kv_heads) * ctx->cfg.head_dim;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lacache_status_string(lacache_status s) {
+  switch (s) {
+    case LACACHE_OK: return "ok";
+    case LACACHE_ERR_INVALID_ARG: return "invalid argument";
+    case LACACHE_ERR_UNSUPPORTED: return "unsupported";
+    case LACACHE_ERR_WORKSPACE: return "workspace missing or too small";
+    case LACACHE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *lacache_last_error(const lacache_ctx *ctx) { return ctx ? ctx->last_error.c_str() : "NULL context"; }
+
+lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
+  if (!out) return LACACHE_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!cfg) return LACACHE_ERR_INVALID_ARG;
+  const lacache_config &c = *cfg;
+  if (c.head_dim != 64 && c.head_dim != 128) return LACACHE_ERR_UNSUPPORTED;
+  if (c.d_model < 256 || c.d_model % 256 != 0) return LACACHE_ERR_UNSUPPORTED;
+  if (c.n_heads < 1 || c.n_kv_heads < 1 || c.n_heads % c.n_kv_heads != 0) return LACACHE_ERR_INVALID_ARG;
+  if (c.vocab < 1 || c.max_seq_len < 1 || c.max_seq_len > (1 << 20)) return LACACHE_ERR_INVALID_ARG;
+  if (!(c.rope_theta > 0) || !(c.rms_eps >= 0) || !std::isfinite(c.sm_scale)) return LACACHE_ERR_INVALID_ARG;
+  if (c.dtype != LACACHE_F32 && c.dtype != LACACHE_BF16) return LACACHE_ERR_INVALID_ARG;
+
+  lacache_ctx *ctx = new lacache_ctx();
+  ctx->cfg = c;
+  ctx->rope = nullptr;
+  ctx->flags = nullptr;
+  ctx->split_keys = 256;
+  if (const char *env = std::getenv("LACACHE_SPLIT_KEYS")) {
+    const int v = std::atoi(env);
+    if (v >= 32 && v % 32 == 0) ctx->split_keys = v;
+  }
+  hipError_t e = hipGetDevice(&ctx->device);
+  // RoPE angles in double on the host: position * theta^(-2i/d_h), stored as fp32 (cos, sin).
+  const int half = c.head_dim / 2;
+  std::vector<float2> tab((size_t)c.max_seq_len * half);
+  for (int p = 0; p < c.max_seq_len; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / (double)c.head_dim);
+      tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  if (e == hipSuccess) e = hipMalloc(&ctx->rope, tab.size() * sizeof(float2));
+  if (e == hipSuccess) e = hipMemcpy(ctx->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMalloc(&ctx->flags, 256);
+  if (e == hipSuccess) e = hipMemset(ctx->flags, 0, 256);
+  if (e == hipSuccess) e = lc::setup_kernel_attributes();
+  if (e != hipSuccess) {
+    if (ctx->rope) (void)hipFree(ctx->rope);
+    if (ctx->flags) (void)hipFree(ctx->flags);
+    delete ctx;
+    return LACACHE_ERR_HIP;
+  }
+  *out = ctx;
+  return LACACHE_OK;
+}
+
+lacache_status lacache_destroy(lacache_ctx *ctx) {
+  if (!ctx) return LACACHE_OK;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(ctx->device);
+  (void)hipDeviceSynchronize();
+  (void)hipFree(ctx->rope);
+  (void)hipFree(ctx->flags);
+  for (auto &mk : ctx->marks) {
+    (void)hipEventDestroy(mk.start);
+    (void)hipEventDestroy(mk.stop);
+  }
+  for (auto e : ctx->free_events) (void)hipEventDestroy(e);
+  if (prev >= 0) (void)hipSetDevice(prev);
+  delete ctx;
+  return LACACHE_OK;
+}
+
+lacache_status lacache_workspace_size(const lacache_ctx *cctx, int32_t op, const lacache_seq *seqs, int32_t batch,
+                                      size_t *bytes) {
+  lacache_ctx *ctx = const_cast<lacache_ctx *>(cctx);
+  if (!ctx || !bytes) return LACACHE_ERR_INVALID_ARG;
+  *bytes = 0;
+  lacache_status st = check_table(ctx, seqs, batch, -1);
+  if (st != LACACHE_OK) return st;
+  switch (op) {
+    case LACACHE_OP_PREFILL: *bytes = 0; return LACACHE_OK;
+    case LACACHE_OP_BLOCK_STEP:
+    case LACACHE_OP_DUALCACHE_ATTN: *bytes = partial_bytes(ctx, partial_rows(ctx, seqs, batch)); return LACACHE_OK;
+  }
+  return fail(ctx, LACACHE_ERR_INVALID_ARG, "unknown op %d", op);
+}
+
+lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w, const int32_t *ids,
+                                     const lacache_seq *seqs, int32_t batch, const lacache_cache *cache, void *out,
+                                     float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if ((st = check_weights(ctx, w)) != LACACHE_OK) return st;
+  if ((st = check_cache(ctx, cache, true)) != LACACHE_OK) return st;
+  if (!ids) return fail(ctx, LACACHE_ERR_INVALID_ARG, "ids is NULL");
+  if (!out || !aligned16(out)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
+  if ((st = check_table(ctx, seqs, batch, cache->n_rows)) != LACACHE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const lc::DType dt = dtype_of(ctx);
+  const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads;
+
+  for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
+    const int ns = std::min(kMaxInline, batch - s0);
+    lc::SeqArgs sa = slice_args(seqs, s0, ns);
+    for (int i = 0; i < ns; ++i) {
+      sa.pre[0][i + 1] = sa.pre[0][i] + sa.len[i];
+      sa.pre[1][i + 1] = sa.pre[1][i] + (sa.len[i] + lc::kRowsR - 1) / lc::kRowsR;
+    }
+    lc::QkvArgs qa = qkv_args(ctx, w, cache, ids, 1);
+    qa.M = sa.pre[0][ns];
+    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV, s, [&] { return lc::launch_qkv(dt, sa, qa, features(ctx), s); });
+    if (e != hipSuccess) return hip_fail(ctx, "prefill qkv launch", e);
+
+    lc::AttnArgs aa;
+    std::memset(&aa, 0, sizeof(aa));
+    aa.q = cache->q;
+    aa.k = cache->k;
+    aa.v = cache->v;
+    aa.out = out;
+    aa.lse = lse;
+    aa.m_w = cache->m;
+    aa.l_w = cache->l;
+    aa.o_w = cache->o_acc;
+    aa.H = H;
+    aa.Hkv = ctx->cfg.n_kv_heads;
+    aa.split_keys = ctx->split_keys;
+    aa.scale_log2 = scale_log2(ctx);
+    e = timed(ctx, LACACHE_KERNEL_REFRESH_ATTN, s,
+              [&] { return lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s); });
+    if (e != hipSuccess) return hip_fail(ctx, "refresh attention launch", e);
+  }
+  return LACACHE_OK;
+}
+
+namespace {
+
+// Type-A items (block rows x key chunks) and partial rows of each sample.
+void plan_block_rows(const lacache_ctx *ctx, lc::SeqArgs &sa) {
+  for (int i = 0; i < sa.n; ++i) {
+    const int B = sa.be[i] - sa.bs[i];
+    const int nch = nchunks(ctx, sa.len[i]);
+    sa.pre[0][i + 1] = sa.pre[0][i] + B;
+    sa.pre[1][i + 1] = sa.pre[1][i] + nch * ((B + lc::kRowsA - 1) / lc::kRowsA);
+    sa.pre[3][i + 1] = sa.pre[3][i] + nch * B;
+  }
+}
+
+}  // namespace
+
+lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, const int32_t *block_ids,
+                                  const lacache_seq *seqs, int32_t batch, const lacache_cache *cache, void *out,
+                                  float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if ((st = check_weights(ctx, w)) != LACACHE_OK) return st;
+  if ((st = check_cache(ctx, cache, true)) != LACACHE_OK) return st;
+  if (!block_ids) return fail(ctx, LACACHE_ERR_INVALID_ARG, "block_ids is NULL");
+  if (!out || !aligned16(out)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
+  if ((st = check_table(ctx, seqs, batch, cache->n_rows)) != LACACHE_OK) return st;
+  const int64_t P = partial_rows(ctx, seqs, batch);
+  const size_t need = partial_bytes(ctx, P);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
+                workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const lc::DType dt = dtype_of(ctx);
+  const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads;
+  float2 *part_ml = static_cast<float2 *>(workspace);
+  float *part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)P * H * sizeof(float2)));
+
+  int row_base = 0, part_base = 0;
+  for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
+    const int ns = std::min(kMaxInline, batch - s0);
+    lc::SeqArgs sa = slice_args(seqs, s0, ns);
+    plan_block_rows(ctx, sa);
+    for (int i = 0; i < ns; ++i)
+      sa.pre[2][i + 1] = sa.pre[2][i] + (sa.len[i] - (sa.be[i] - sa.bs[i]) + lc::kRowsB - 1) / lc::kRowsB;
+    const int M = sa.pre[0][ns];
+
+    lc::QkvArgs qa = qkv_args(ctx, w, cache, block_ids, 0);
+    qa.M = M;
+    qa.ids_base = row_base;
+    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV, s, [&] { return lc::launch_qkv(dt, sa, qa, features(ctx), s); });
+    if (e != hipSuccess) return hip_fail(ctx, "block-step qkv launch", e);
+
+    lc::AttnArgs aa;
+    std::memset(&aa, 0, sizeof(aa));
+    aa.q = cache->q;
+    aa.k = cache->k;
+    aa.v = cache->v;
+    aa.out = out;
+    aa.lse = lse;
+    aa.m_c = cache->m;
+    aa.l_c = cache->l;
+    aa.o_c = cache->o_acc;
+    aa.part_ml = part_ml;
+    aa.part_o = part_o;
+    aa.qmode = 0;
+    aa.omode = 0;
+    aa.row_base = row_base;
+    aa.part_base = part_base;
+    aa.H = H;
+    aa.Hkv = ctx->cfg.n_kv_heads;
+    aa.split_keys = ctx->split_keys;
+    aa.scale_log2 = scale_log2(ctx);
+    aa.nA = sa.pre[1][ns] * H;
+    e = timed(ctx, LACACHE_KERNEL_STEP_ATTN, s, [&] {
+      return lc::launch_step_attn(dt, dh, sa, aa, (sa.pre[1][ns] + sa.pre[2][ns]) * H, s);
+    });
+    if (e != hipSuccess) return hip_fail(ctx, "block-step attention launch", e);
+    e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&] { return lc::launch_merge(dt, dh, sa, aa, M, s); });
+    if (e != hipSuccess) return hip_fail(ctx, "block-step merge launch", e);
+    row_base += M;
+    part_base += sa.pre[3][ns];
+  }
+  return LACACHE_OK;
+}
+
+lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *q_block, const void *k, const void *v,
+                                      int64_t n_rows, const lacache_seq *seqs, int32_t batch, void *out_block,
+                                      float *lse_block, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if (!q_block || !k || !v || !out_block)
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "q_block, k, v and out_block must not be NULL");
+  if (!aligned16(q_block) || !aligned16(k) || !aligned16(v) || !aligned16(out_block))
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "q_block, k, v and out_block must be 16-byte aligned");
+  if (n_rows < 1) return fail(ctx, LACACHE_ERR_INVALID_ARG, "n_rows must be >= 1");
+  if ((st = check_table(ctx, seqs, batch, n_rows)) != LACACHE_OK) return st;
+  const int64_t P = partial_rows(ctx, seqs, batch);
+  const size_t need = partial_bytes(ctx, P);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
+                workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const lc::DType dt = dtype_of(ctx);
+  const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads;
+  float2 *part_ml = static_cast<float2 *>(workspace);
+  float *part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)P * H * sizeof(float2)));
+
+  int row_base = 0, part_base = 0;
+  for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
+    const int ns = std::min(kMaxInline, batch - s0);
+    lc::SeqArgs sa = slice_args(seqs, s0, ns);
+    plan_block_rows(ctx, sa);
+    const int M = sa.pre[0][ns];
+    lc::AttnArgs aa;
+    std::memset(&aa, 0, sizeof(aa));
+    aa.q = q_block;
+    aa.k = k;
+    aa.v = v;
+    aa.out = out_block;
+    aa.lse = lse_block;
+    aa.part_ml = part_ml;
+    aa.part_o = part_o;
+    aa.qmode = 1;
+    aa.omode = 1;
+    aa.row_base = row_base;
+    aa.part_base = part_base;
+    aa.H = H;
+    aa.Hkv = ctx->cfg.n_kv_heads;
+    aa.split_keys = ctx->split_keys;
+    aa.scale_log2 = scale_log2(ctx);
+    aa.nA = sa.pre[1][ns] * H;
+    hipError_t e = timed(ctx, LACACHE_KERNEL_DUAL_ATTN, s, [&] { return lc::launch_block_attn(dt, dh, sa, aa, aa.nA, s); });
+    if (e != hipSuccess) return hip_fail(ctx, "dualcache attention launch", e);
+    e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&] { return lc::launch_merge(dt, dh, sa, aa, M, s); });
+    if (e != hipSuccess) return hip_fail(ctx, "dualcache merge launch", e);
+    row_base += M;
+    part_base += sa.pre[3][ns];
+  }
+  return LACACHE_OK;
+}
+
+lacache_status lacache_read_device_status(lacache_ctx *ctx, void *stream, uint32_t *flags) {
+  if (!ctx || !flags) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(flags, ctx->flags, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(ctx->flags, 0, sizeof(uint32_t));
+  if (e != hipSuccess) return hip_fail(ctx, "read device status", e);
+  return LACACHE_OK;
+}
+
+lacache_status lacache_profile_enable(lacache_ctx *ctx, int enable) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  ctx->profiling = enable != 0;
+  return LACACHE_OK;
+}
+
+lacache_status lacache_profile_read(lacache_ctx *ctx, int32_t kernel, double *total_ms, int64_t *launches) {
+  if (!ctx || !total_ms || !launches) return LACACHE_ERR_INVALID_ARG;
+  if (kernel < 0 || kernel >= LACACHE_KERNEL_COUNT)
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "unknown kernel class %d", kernel);
+  for (auto &mk : ctx->marks) {
+    hipError_t e = hipEventSynchronize(mk.stop);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, mk.start, mk.stop);
+    if (e != hipSuccess) return hip_fail(ctx, "profile events", e);
+    ctx->prof_ms[mk.kernel] += ms;
+    ctx->prof_n[mk.kernel] += 1;
+    ctx->free_events.push_back(mk.start);
+    ctx->free_events.push_back(mk.stop);
+  }
+  ctx->marks.clear();
+  *total_ms = ctx->prof_ms[kernel];
+  *launches = ctx->prof_n[kernel];
+  ctx->prof_ms[kernel] = 0;
+  ctx->prof_n[kernel] = 0;
+  return LACACHE_OK;
+}
+
+}  // extern "C"

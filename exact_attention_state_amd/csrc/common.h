@@ -1,0 +1,155 @@
+// Device-side helpers shared by the gfx950 kernels: element types, 16-byte
+// loads, bf16 conversion, the 16x16 MFMA fragment abstraction, wave
+// reductions, and the per-launch block table passed by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lc {
+
+typedef uint16_t bf16_t;                                      // bf16 storage
+typedef _Float16 f16_t;                                       // fp16 storage
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kF16Max = 65504.0f;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Samples per launch whose block-table rows travel inside the kernel
+// arguments (no host->device copy per call).  Larger batches are launched in
+// slices of this many samples.
+constexpr int kMaxInline = 64;
+
+// Block table of one launch.  pre[j][i] are non-decreasing prefix sums over
+// samples (meaning fixed by each launcher); pre[j][n] is the total.
+struct SeqArgs {
+  int n;
+  int off[kMaxInline];
+  int len[kMaxInline];
+  int bs[kMaxInline];
+  int be[kMaxInline];
+  int pre[4][kMaxInline + 1];
+};
+
+// Largest b < n with pre[b] <= item (samples with no items are skipped).
+__device__ __forceinline__ int find_sample(const int *pre, int n, int item) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= item) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf2f(v); }
+template <> __device__ __forceinline__ float to_f32<f16_t>(f16_t v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f2bf(v); }
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float v) { return (f16_t)v; }
+
+// ---------------------------------------------------------------------------
+// 8 consecutive elements along the contraction index: the per-lane operand
+// of one 16x16 MFMA step of 32 (bf16 / fp16: one v_mfma_f32_16x16x32_bf16 /
+// _f16; fp32: eight v_mfma_f32_16x16x4_f32).  For both, lane l supplies row/col l%16 and
+// its lane group g = l/16 supplies 8 contraction elements; the hardware pairs
+// A's and B's elements of the same lane group and slot, so any assignment of
+// contraction indices to (group, slot) is valid as long as A and B share it.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> { bf16x8_t v; };
+template <> struct Frag<f16_t> { f16x8_t v; };
+template <> struct Frag<float> { float v[8]; };
+
+template <typename T> __device__ __forceinline__ void frag_zero(Frag<T> &f);
+template <> __device__ __forceinline__ void frag_zero<bf16_t>(Frag<bf16_t> &f) {
+  f.v = bf16x8_t{};
+}
+template <> __device__ __forceinline__ void frag_zero<f16_t>(Frag<f16_t> &f) {
+  f.v = f16x8_t{};
+}
+template <> __device__ __forceinline__ void frag_zero<float>(Frag<float> &f) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.v[i] = 0.f;
+}
+
+// Load 8 consecutive elements (16 B for bf16, 32 B for fp32) from global or LDS.
+template <typename T> __device__ __forceinline__ void frag_load(Frag<T> &f, const T *p);
+template <> __device__ __forceinline__ void frag_load<bf16_t>(Frag<bf16_t> &f, const bf16_t *p) {
+  uint4 u = *reinterpret_cast<const uint4 *>(p);
+  f.v = __builtin_bit_cast(bf16x8_t, u);
+}
+template <> __device__ __forceinline__ void frag_load<f16_t>(Frag<f16_t> &f, const f16_t *p) {
+  uint4 u = *reinterpret_cast<const uint4 *>(p);
+  f.v = __builtin_bit_cast(f16x8_t, u);
+}
+template <> __device__ __forceinline__ void frag_load<float>(Frag<float> &f, const float *p) {
+  float4 a = reinterpret_cast<const float4 *>(p)[0];
+  float4 b = reinterpret_cast<const float4 *>(p)[1];
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// Element access as fp32 (for prologue arithmetic on loaded values).
+template <typename T> __device__ __forceinline__ float frag_get(const Frag<T> &f, int i);
+template <> __device__ __forceinline__ float frag_get<bf16_t>(const Frag<bf16_t> &f, int i) {
+  return (float)f.v[i];
+}
+template <> __device__ __forceinline__ float frag_get<f16_t>(const Frag<f16_t> &f, int i) {
+  return (float)f.v[i];
+}
+template <> __device__ __forceinline__ float frag_get<float>(const Frag<float> &f, int i) {
+  return f.v[i];
+}
+template <typename T> __device__ __forceinline__ void frag_set(Frag<T> &f, int i, float x);
+template <> __device__ __forceinline__ void frag_set<bf16_t>(Frag<bf16_t> &f, int i, float x) {
+  f.v[i] = (__bf16)x;
+}
+template <> __device__ __forceinline__ void frag_set<f16_t>(Frag<f16_t> &f, int i, float x) {
+  f.v[i] = (_Float16)x;
+}
+template <> __device__ __forceinline__ void frag_set<float>(Frag<float> &f, int i, float x) {
+  f.v[i] = x;
+}
+
+// acc += A * B over one contraction step of 32.
+__device__ __forceinline__ void mma16(f32x4_t &acc, const Frag<bf16_t> &a, const Frag<bf16_t> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4_t &acc, const Frag<f16_t> &a, const Frag<f16_t> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4_t &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+}
+
+// Reductions across the four lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace lc

@@ -1,0 +1,70 @@
+// Internal interface between the C-ABI front end (api.hip) and the kernel
+// launchers (qkv.hip, attn.hip).  Plain pointers and sizes only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace lc {
+
+enum DType { kF32 = 0, kBF16 = 1 };
+
+// Fused embedding gather + RMSNorm + QKV projection + RoPE + cache write.
+struct QkvArgs {
+  const int *ids;          // mode 0: [tokens of launch] block ids; mode 1: flat ids by row
+  const void *E;           // [vocab, D]
+  const void *gamma;       // [D]
+  const void *W;           // [F, D]
+  void *h;                 // EmbedCache [rows, D]
+  void *q, *k, *v;         // RoPECache
+  const float2 *rope;      // [max_pos, dh/2] (cos, sin)
+  unsigned *flags;         // device status word
+  int mode;                // 0: block step, 1: prefill
+  int M;                   // tokens in this launch
+  int ids_base;            // mode 0: index of the launch's first token in `ids`
+  int vocab, D, H, Hkv, dh;
+  float eps;
+};
+
+// Attention kernels: block-row split partials (type A), invariant rows from
+// FACache (type B), the refresh, and the merge of partials.
+struct AttnArgs {
+  const void *q;           // qmode 0: q cache [rows, H, dh]; qmode 1: q_block [M, H, dh]
+  const void *k, *v;       // [rows, Hkv, dh]
+  void *out;               // omode 0: [rows, H, dh]; omode 1: out_block [M, H, dh]
+  float *lse;              // matching rows, [.., H], or null
+  const float *m_c, *l_c, *o_c;   // FACache read (block step)
+  float *m_w, *l_w, *o_w;         // FACache write (refresh)
+  float2 *part_ml;         // [P, H] (max in log2 units, normaliser)
+  float *part_o;           // [P, H, dh]
+  int qmode, omode;
+  int row_base;            // index of the slice's first block row in q_block/out_block
+  int part_base;           // index of the slice's first partial row
+  int H, Hkv;
+  int split_keys;          // keys per type-A chunk (multiple of 32)
+  int nA;                  // type-A workgroups (items * H); the rest are type B
+  float scale_log2;        // sm_scale * log2(e)
+};
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipStream_t s);
+hipError_t launch_step_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
+                            hipStream_t s);
+hipError_t launch_block_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
+                             hipStream_t s);
+hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int M, hipStream_t s);
+hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
+                               hipStream_t s);
+hipError_t setup_kernel_attributes();
+
+// Work decomposition shared by the planner and the kernels.
+constexpr int kRowsA = 32;     // block rows per type-A item
+constexpr int kRowsB = 64;     // invariant rows per type-B item
+constexpr int kRowsR = 64;     // rows per refresh item
+constexpr int kQkvRows = 32;   // token rows per QKV tile
+constexpr int kQkvNB = 3;      // 16-feature column blocks per QKV tile
+constexpr int kQkvWaves = 8;   // waves splitting the contraction
+
+}  // namespace lc

@@ -1,0 +1,271 @@
+"""Thin Python binding of liblacache.so (include/lacache.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype,
+shape and contiguity and handed to the C ABI as raw pointers together with
+the current HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no Python or CPU fallback, and a missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblacache.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+F32, BF16 = 0, 1
+OP_PREFILL, OP_BLOCK_STEP, OP_DUALCACHE_ATTN = 0, 1, 2
+DEVFLAG_BAD_TOKEN_ID = 1
+DEVFLAG_CACHE_RANGE = 2
+
+EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "lacache_prefill_cache",
+            "lacache_block_step", "lacache_dualcache_attn", "lacache_read_device_status",
+            "lacache_profile_enable", "lacache_profile_read", "lacache_status_string", "lacache_last_error")
+KERNEL_QKV, KERNEL_STEP_ATTN, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_DUAL_ATTN = range(5)
+KERNEL_NAMES = ("qkv", "step_attn", "merge", "refresh_attn", "dual_attn")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("vocab", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("sm_scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("m", ctypes.c_void_p), ("l", ctypes.c_void_p), ("o_acc", ctypes.c_void_p),
+                ("n_rows", ctypes.c_int64)]
+
+
+class Seq(ctypes.Structure):
+    _fields_ = [("seq_offset", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("block_start", ctypes.c_int32), ("block_end", ctypes.c_int32)]
+
+
+class LaCacheError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load liblacache.so and declare its signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_attention_state_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    st = ctypes.c_int
+    sig = {
+        "lacache_create": (st, [ctypes.POINTER(Config), ctypes.POINTER(P)]),
+        "lacache_destroy": (st, [P]),
+        "lacache_workspace_size": (st, [P, I32, ctypes.POINTER(Seq), I32, ctypes.POINTER(SZ)]),
+        "lacache_prefill_cache": (st, [P, ctypes.POINTER(Weights), P, ctypes.POINTER(Seq), I32,
+                                       ctypes.POINTER(Cache), P, P, P, SZ, P]),
+        "lacache_block_step": (st, [P, ctypes.POINTER(Weights), P, ctypes.POINTER(Seq), I32,
+                                    ctypes.POINTER(Cache), P, P, P, SZ, P]),
+        "lacache_dualcache_attn": (st, [P, P, P, P, I64, ctypes.POINTER(Seq), I32, P, P, P, SZ, P]),
+        "lacache_read_device_status": (st, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
+        "lacache_profile_enable": (st, [P, ctypes.c_int]),
+        "lacache_profile_read": (st, [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
+        "lacache_status_string": (ctypes.c_char_p, [st]),
+        "lacache_last_error": (ctypes.c_char_p, [P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def _seqs(table):
+    arr = (Seq * len(table))()
+    for i, (off, n, bs, be) in enumerate(table):
+        arr[i] = Seq(int(off), int(n), int(bs), int(be))
+    return arr
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+# RoPECache element type: fp32 for fp32 parameters, fp16 for bf16 parameters.
+_CACHE_DTYPE = {F32: torch.float32, BF16: torch.float16}
+
+
+@dataclass
+class CacheTensors:
+    """Caller-owned device buffers of the caches, the output and the LSE."""
+
+    h: torch.Tensor
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    m: torch.Tensor
+    l: torch.Tensor
+    o_acc: torch.Tensor
+    out: torch.Tensor
+    lse: torch.Tensor
+
+    @property
+    def n_rows(self):
+        return self.h.shape[0]
+
+
+class Context:
+    """One lacache_ctx: layer-0 shape, RoPE table, device status word."""
+
+    def __init__(self, d_model, n_heads, n_kv_heads, head_dim, vocab, max_seq_len, rope_theta,
+                 rms_eps=1e-5, sm_scale=0.0, dtype="bf16"):
+        self.lib = load_library()
+        self.dtype_code = BF16 if dtype in ("bf16", BF16, torch.bfloat16) else F32
+        self.torch_dtype = _TORCH_DTYPE[self.dtype_code]
+        self.cache_dtype = _CACHE_DTYPE[self.dtype_code]
+        self.cfg = Config(d_model, n_heads, n_kv_heads, head_dim, vocab, max_seq_len, rope_theta, rms_eps,
+                          sm_scale, self.dtype_code)
+        h = ctypes.c_void_p()
+        st = self.lib.lacache_create(ctypes.byref(self.cfg), ctypes.byref(h))
+        if st != OK:
+            raise LaCacheError(st, "lacache_create: " + self.lib.lacache_status_string(st).decode())
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.lacache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------------
+    def _check(self, st, what):
+        if st != OK:
+            msg = self.lib.lacache_last_error(self.handle).decode()
+            raise LaCacheError(st, f"{what}: {msg}")
+
+    def alloc_cache(self, n_rows, device="cuda"):
+        """Allocate (uninitialised) cache, output and LSE buffers of n_rows rows."""
+        c = self.cfg
+        dt, ct = self.torch_dtype, self.cache_dtype
+        e = dict(device=device)
+        return CacheTensors(
+            h=torch.empty(n_rows, c.d_model, dtype=dt, **e),
+            q=torch.empty(n_rows, c.n_heads, c.head_dim, dtype=ct, **e),
+            k=torch.empty(n_rows, c.n_kv_heads, c.head_dim, dtype=ct, **e),
+            v=torch.empty(n_rows, c.n_kv_heads, c.head_dim, dtype=ct, **e),
+            m=torch.empty(n_rows, c.n_heads, dtype=torch.float32, **e),
+            l=torch.empty(n_rows, c.n_heads, dtype=torch.float32, **e),
+            o_acc=torch.empty(n_rows, c.n_heads, c.head_dim, dtype=torch.float32, **e),
+            out=torch.empty(n_rows, c.n_heads, c.head_dim, dtype=dt, **e),
+            lse=torch.empty(n_rows, c.n_heads, dtype=torch.float32, **e),
+        )
+
+    def workspace_size(self, op, table):
+        n = ctypes.c_size_t()
+        seqs = _seqs(table)
+        self._check(self.lib.lacache_workspace_size(self.handle, op, seqs, len(table), ctypes.byref(n)),
+                    "lacache_workspace_size")
+        return n.value
+
+    def alloc_workspace(self, op, table, device="cuda"):
+        n = self.workspace_size(op, table)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+    def _weights(self, embed, gamma, w_qkv):
+        for name, t in (("embed", embed), ("gamma", gamma), ("w_qkv", w_qkv)):
+            if t.dtype != self.torch_dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {self.torch_dtype} CUDA tensor")
+        return Weights(embed.data_ptr(), gamma.data_ptr(), w_qkv.data_ptr())
+
+    @staticmethod
+    def _cache(ct: CacheTensors):
+        return Cache(ct.h.data_ptr(), ct.q.data_ptr(), ct.k.data_ptr(), ct.v.data_ptr(), ct.m.data_ptr(),
+                     ct.l.data_ptr(), ct.o_acc.data_ptr(), ct.n_rows)
+
+    @staticmethod
+    def _ids(t):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("token ids must be a contiguous int32 CUDA tensor")
+        return t
+
+    def prefill_cache(self, weights, ids, table, ct: CacheTensors, workspace=None, stream=None, lse=True):
+        w = self._weights(*weights)
+        seqs = _seqs(table)
+        cache = self._cache(ct)
+        ws = workspace
+        st = self.lib.lacache_prefill_cache(self.handle, ctypes.byref(w), _ptr(self._ids(ids)), seqs, len(table),
+                                            ctypes.byref(cache), _ptr(ct.out), _ptr(ct.lse) if lse else None,
+                                            _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+        self._check(st, "lacache_prefill_cache")
+
+    def block_step(self, weights, block_ids, table, ct: CacheTensors, workspace, stream=None, lse=True):
+        w = self._weights(*weights)
+        seqs = _seqs(table)
+        cache = self._cache(ct)
+        st = self.lib.lacache_block_step(self.handle, ctypes.byref(w), _ptr(self._ids(block_ids)), seqs,
+                                         len(table), ctypes.byref(cache), _ptr(ct.out),
+                                         _ptr(ct.lse) if lse else None, _ptr(workspace),
+                                         0 if workspace is None else workspace.numel(), _stream(stream))
+        self._check(st, "lacache_block_step")
+
+    def dualcache_attn(self, q_block, k, v, table, out_block, lse_block=None, workspace=None, stream=None):
+        for name, t, dt in (("q_block", q_block, self.cache_dtype), ("k", k, self.cache_dtype),
+                            ("v", v, self.cache_dtype), ("out_block", out_block, self.torch_dtype)):
+            if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor")
+        seqs = _seqs(table)
+        st = self.lib.lacache_dualcache_attn(self.handle, _ptr(q_block), _ptr(k), _ptr(v), k.shape[0], seqs,
+                                             len(table), _ptr(out_block), _ptr(lse_block), _ptr(workspace),
+                                             0 if workspace is None else workspace.numel(), _stream(stream))
+        self._check(st, "lacache_dualcache_attn")
+
+    def profile(self, enable: bool):
+        """Bracket every launch with HIP events (diagnostics)."""
+        self._check(self.lib.lacache_profile_enable(self.handle, int(bool(enable))), "lacache_profile_enable")
+
+    def profile_read(self):
+        """{kernel name: (total ms, launches)} since the last read; synchronises the events."""
+        res = {}
+        for k, name in enumerate(KERNEL_NAMES):
+            ms, n = ctypes.c_double(), ctypes.c_int64()
+            self._check(self.lib.lacache_profile_read(self.handle, k, ctypes.byref(ms), ctypes.byref(n)),
+                        "lacache_profile_read")
+            res[name] = (ms.value, n.value)
+        return res
+
+    def read_device_status(self, stream=None):
+        flags = ctypes.c_uint32()
+        self._check(self.lib.lacache_read_device_status(self.handle, _stream(stream), ctypes.byref(flags)),
+                    "lacache_read_device_status")
+        return flags.value
+
+
+def context_for(wl, max_seq_len=None):
+    """Context for a synthetic workload (exact_attention_state_amd.synth.Workload)."""
+    return Context(wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.vocab,
+                   max_seq_len or max(wl.seq_lens), wl.rope_theta, wl.rms_eps, 0.0, wl.dtype)

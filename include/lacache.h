@@ -1,0 +1,248 @@
+/*
+ * lacache.h -- C ABI of the exact layer-0 cached block step (LaCache) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (LaCache, "Exact Caching and Precision-Adaptive Inference for
+ * Diffusion Large Language Models", arXiv 2607.16339):
+ *   - Section 3.3.1 (Notation): a sequence of N tokens; C is the current
+ *     block [block_start, block_end); U is every other token.
+ *   - Section 3.3.2, Eq. (1): EmbedCache H = Embed(x) and RoPECache
+ *     Q, K = RoPE(Norm(H) W_{Q,K}), V = Norm(H) W_V, recomputed for C only.
+ *   - Section 3.3.3, Eqs. (2)-(6): FACache, the online-softmax state
+ *     (m, l, O~) of every row of U over the keys of U; in later steps a row of
+ *     U starts from that state and streams only the keys of C.
+ *   - Algorithm 1 ("the first layer's Flash-Attention"): output O and the
+ *     log-sum-exp L of every row; the cache is written at the first step of a
+ *     block only.
+ * The block-row attention over [prefix | fresh block | suffix] keys is the
+ * inner step of Fast-dLLM's block-wise DualCache (DantinoX documentation,
+ * "Block-wise Generation" and "Building the Dual Cache Manually"); the flat,
+ * pre-allocated, token-major cache with a per-sample block table follows the
+ * Flash-dLLM article ("Flash-Cache", block table and flat cache layout).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every device buffer is owned by the caller and stays owned by the
+ *   caller.  The library keeps only the context (configuration, a device
+ *   RoPE table and a device status word, allocated by lacache_create).
+ *   Pointers marked "device" must be device memory aligned to 16 bytes;
+ *   pointers marked "host" are read before the call returns.
+ * Layouts (row-major, token-major, one flat buffer for the whole batch):
+ *   embed  [vocab, d_model]                   dtype
+ *   gamma  [d_model]                          dtype
+ *   w_qkv  [(H + 2 H_kv) d_h, d_model]        dtype; output features of the Q
+ *          heads, then K heads, then V heads, each head's d_h rows contiguous
+ *   h      [n_rows, d_model]                  dtype  (EmbedCache)
+ *   q      [n_rows, H, d_h]                   ctype  (RoPECache, after RoPE)
+ *   k, v   [n_rows, H_kv, d_h]                ctype  (RoPECache; v not rotated)
+ *   m, l   [n_rows, H]                        fp32   (FACache running max in
+ *          natural-log units of the scaled scores, and normaliser)
+ *   o_acc  [n_rows, H, d_h]                   fp32   (FACache unnormalised O~)
+ *   out    [n_rows, H, d_h]                   dtype
+ *   lse    [n_rows, H]                        fp32   (natural log)
+ *   dtype is fp32 or bf16 (lacache_config.dtype).  ctype, the RoPECache
+ *   element type, is fp32 for fp32 and IEEE fp16 for bf16: fp16 carries 3 more
+ *   mantissa bits than bf16 at the same size and MFMA rate (magnitudes above
+ *   65504 set LACACHE_DEVFLAG_CACHE_RANGE).  Sample b owns rows
+ *   seq_offset .. seq_offset + seq_len - 1; its token positions are
+ *   0 .. seq_len - 1 (layout [prompt | block 0 | ...]).  Keys never cross
+ *   samples.
+ * Streams.  `stream` is a hipStream_t (NULL: the default stream).  Every
+ *   compute call only enqueues kernels on it and returns; results are valid
+ *   once the stream has reached them.  No call synchronises the device,
+ *   except lacache_read_device_status.
+ * Errors.  Arguments are validated before anything is enqueued; on an error
+ *   nothing is launched, the status is returned and lacache_last_error(ctx)
+ *   describes it.  A failed launch returns LACACHE_ERR_HIP.  Token ids are
+ *   device data and cannot be checked on the host: an id outside
+ *   [0, vocab) is read as an all-zero embedding row and sets
+ *   LACACHE_DEVFLAG_BAD_TOKEN_ID in the context's device status word.
+ * Threads.  Calls on different contexts are independent.  One context may
+ *   be used from several threads if each call has its own workspace and
+ *   stream; lacache_last_error then reports whichever call failed last.
+ */
+#ifndef LACACHE_H
+#define LACACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef LACACHE_API
+#define LACACHE_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+  LACACHE_OK = 0,
+  LACACHE_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, bad block table */
+  LACACHE_ERR_UNSUPPORTED = 2,   /* valid request this build does not serve  */
+  LACACHE_ERR_WORKSPACE = 3,     /* workspace missing or too small           */
+  LACACHE_ERR_HIP = 4            /* a HIP runtime call or launch failed      */
+} lacache_status;
+
+typedef enum { LACACHE_F32 = 0, LACACHE_BF16 = 1 } lacache_dtype;
+
+/* Device status flags (lacache_read_device_status). */
+#define LACACHE_DEVFLAG_BAD_TOKEN_ID 1u
+#define LACACHE_DEVFLAG_CACHE_RANGE 2u   /* a q/k/v value exceeded the fp16 range */
+
+/* First-layer shape (Section 3.3.2).  Supported: head_dim 64 or 128,
+ * d_model a multiple of 256, n_heads a multiple of n_kv_heads,
+ * 1 <= max_seq_len <= 1<<20.  sm_scale <= 0 selects 1/sqrt(head_dim).
+ * rope_theta > 0: feature i of a head is paired with feature i + d_h/2 and
+ * rotated by position * rope_theta^(-2i/d_h).  rms_eps >= 0:
+ * Norm(x) = gamma * x / sqrt(mean(x^2) + rms_eps). */
+typedef struct {
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t vocab;
+  int32_t max_seq_len;
+  float rope_theta;
+  float rms_eps;
+  float sm_scale;
+  int32_t dtype;                  /* lacache_dtype */
+} lacache_config;
+
+/* Layer-0 parameters, device, layouts above. */
+typedef struct {
+  const void *embed;
+  const void *gamma;
+  const void *w_qkv;
+} lacache_weights;
+
+/* The caches (device), layouts above; n_rows = rows every buffer holds. */
+typedef struct {
+  void *h;
+  void *q;
+  void *k;
+  void *v;
+  float *m;
+  float *l;
+  float *o_acc;
+  int64_t n_rows;
+} lacache_cache;
+
+/* One row of the block table (host): sample rows
+ * [seq_offset, seq_offset + seq_len) and current block
+ * [block_start, block_end) in positions of the sample.  Rules:
+ * 0 <= block_start < block_end <= seq_len <= max_seq_len,
+ * block_end - block_start <= 128, row ranges of different samples disjoint
+ * and inside [0, n_rows). */
+typedef struct {
+  int32_t seq_offset;
+  int32_t seq_len;
+  int32_t block_start;
+  int32_t block_end;
+} lacache_seq;
+
+typedef struct lacache_ctx lacache_ctx;
+
+/* Operations, for lacache_workspace_size. */
+typedef enum {
+  LACACHE_OP_PREFILL = 0,
+  LACACHE_OP_BLOCK_STEP = 1,
+  LACACHE_OP_DUALCACHE_ATTN = 2
+} lacache_op;
+
+/* Creates a context on the current HIP device: validates the configuration,
+ * builds the RoPE cos/sin table (computed in double on the host, stored as
+ * fp32 [max_seq_len, head_dim/2] pairs) and a device status word.  The
+ * context must be used on that device only.  *out is NULL on failure. */
+LACACHE_API lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out);
+
+/* Frees the context's device memory (synchronises the device first).
+ * NULL is accepted. */
+LACACHE_API lacache_status lacache_destroy(lacache_ctx *ctx);
+
+/* Bytes of device workspace an operation needs for this block table
+ * (0 is possible).  seqs: host, `batch` rows. */
+LACACHE_API lacache_status lacache_workspace_size(const lacache_ctx *ctx, int32_t op,
+                                      const lacache_seq *seqs, int32_t batch,
+                                      size_t *bytes);
+
+/* Refresh at the first denoising step of a block (Section 3.3, "populated at
+ * the first denoising step of each SAR block"; Algorithm 1 with its first-step
+ * flag set): the full layer-0 forward of every row of every sample.
+ *   ids      device int32 [n_rows]: token id of every row (rows outside all
+ *            samples are not read).
+ * Writes h, q, k, v for every row of every sample; m, l, o_acc for every row
+ * of U (the state over the keys of U only); out and lse (lse may be NULL) for
+ * every row.  FACache rows of C are left unspecified. */
+LACACHE_API lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
+                                     const int32_t *ids, const lacache_seq *seqs,
+                                     int32_t batch, const lacache_cache *cache,
+                                     void *out, float *lse, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/* One cached inner step (Section 3.3.2 and 3.3.3; Figure 3 right):
+ *   block_ids device int32 [sum_b (block_end - block_start)]: the current
+ *            ids of every sample's block, concatenated in sample order.
+ * Writes h, q, k, v of the block rows only (EmbedCache / RoPECache update);
+ * block rows attend over all keys of their sample; every row of U is finished
+ * from its FACache state plus the block's keys.  Writes out and lse (may be
+ * NULL) for every row of every sample.  Reads, never writes, the FACache.
+ * The result equals a full recompute of layer 0 on the new ids, up to
+ * rounding, provided the caches were filled by lacache_prefill_cache for the
+ * same block table and only block ids changed since. */
+LACACHE_API lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w,
+                                  const int32_t *block_ids, const lacache_seq *seqs,
+                                  int32_t batch, const lacache_cache *cache,
+                                  void *out, float *lse, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* Block-query attention over [prefix | fresh block | suffix] keys: the
+ * attention of Fast-dLLM's DualCache inner step (decode_block), exact at
+ * layer 0.
+ *   q_block   device [sum_b B_b, H, d_h] ctype: the block rows' queries,
+ *             concatenated in sample order.
+ *   k, v      device [n_rows, H_kv, d_h] ctype: every sample's keys/values
+ *             at its rows (prefix, block and suffix), as in the cache.
+ *   n_rows    rows k and v hold.
+ *   out_block device [sum_b B_b, H, d_h] dtype; lse_block [sum_b B_b, H]
+ *             fp32 or NULL. */
+LACACHE_API lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *q_block,
+                                      const void *k, const void *v, int64_t n_rows,
+                                      const lacache_seq *seqs, int32_t batch,
+                                      void *out_block, float *lse_block,
+                                      void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+/* Reads and clears the device status word (LACACHE_DEVFLAG_*), after
+ * synchronising `stream`. */
+LACACHE_API lacache_status lacache_read_device_status(lacache_ctx *ctx, void *stream,
+                                          uint32_t *flags);
+
+/* Optional per-kernel timing (diagnostics, off by default).  While enabled,
+ * every kernel launch of this context is bracketed by two HIP events on the
+ * call's stream.  lacache_profile_read synchronises those events and returns,
+ * for one kernel class, the summed event time in milliseconds and the number
+ * of launches since the last read of that class (then resets that class). */
+typedef enum {
+  LACACHE_KERNEL_QKV = 0,          /* embed + RMSNorm + QKV + RoPE + cache write */
+  LACACHE_KERNEL_STEP_ATTN = 1,    /* block-row split partials + invariant rows  */
+  LACACHE_KERNEL_MERGE = 2,        /* merge of the block-row partials           */
+  LACACHE_KERNEL_REFRESH_ATTN = 3, /* refresh attention with FACache snapshot   */
+  LACACHE_KERNEL_DUAL_ATTN = 4,    /* DualCache block-query partials            */
+  LACACHE_KERNEL_COUNT = 5
+} lacache_kernel;
+
+LACACHE_API lacache_status lacache_profile_enable(lacache_ctx *ctx, int enable);
+LACACHE_API lacache_status lacache_profile_read(lacache_ctx *ctx, int32_t kernel, double *total_ms,
+                                                int64_t *launches);
+
+/* Static description of a status code. */
+LACACHE_API const char *lacache_status_string(lacache_status s);
+
+/* Description of the last failed call on this context ("" if none). */
+LACACHE_API const char *lacache_last_error(const lacache_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LACACHE_H */
