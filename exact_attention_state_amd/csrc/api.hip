@@ -231,7 +231,7 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   if (!cfg) return LACACHE_ERR_INVALID_ARG;
   const lacache_config &c = *cfg;
   if (c.head_dim != 64 && c.head_dim != 128) return LACACHE_ERR_UNSUPPORTED;
-  if (c.d_model < 256 || c.d_model % 256 != 0) return LACACHE_ERR_UNSUPPORTED;
+  if (c.d_model < 256 || c.d_model % 256 != 0 || c.d_model > lc::kQkvMaxD) return LACACHE_ERR_UNSUPPORTED;
   if (c.n_heads < 1 || c.n_kv_heads < 1 || c.n_heads % c.n_kv_heads != 0) return LACACHE_ERR_INVALID_ARG;
   if (c.vocab < 1 || c.max_seq_len < 1 || c.max_seq_len > (1 << 20)) return LACACHE_ERR_INVALID_ARG;
   if (!(c.rope_theta > 0) || !(c.rms_eps >= 0) || !std::isfinite(c.sm_scale)) return LACACHE_ERR_INVALID_ARG;

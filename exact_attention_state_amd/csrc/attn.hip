@@ -30,8 +30,78 @@
 
 namespace lc {
 
-template <typename T> struct VtPad { static constexpr int v = 8; };
-template <> struct VtPad<float> { static constexpr int v = 4; };
+// ---------------------------------------------------------------------------
+// V of up to MAXC keys staged in LDS, read back as the A operand of P*V (one
+// head-dim row, 8 consecutive keys per lane).
+//   16-bit types: V is kept row-major (key rows of DH + 16 elements; the pad
+//   puts 8 consecutive rows on disjoint bank groups) and written with 16-byte
+//   stores; the operand is read with ds_read_b64_tr_b16, which hands lane i
+//   of a 16-lane group element i%4 of the 8-byte chunks addressed by lanes
+//   4j + i/4 (j = 0..3).  Lane t of group g points at key 8g + t/4 (+4 for the
+//   second read), features 16*db + 4*(t%4): lane i then holds keys 8g..8g+7
+//   of feature 16*db + i.
+//   fp32: V is stored transposed, V^T[d][c], and read with plain loads.
+// ---------------------------------------------------------------------------
+template <typename T, int DH, int MAXC> struct VTile {
+  static constexpr bool kTr = sizeof(T) == 2;
+  static constexpr int kStride = kTr ? DH + 16 : MAXC + 4;     // elements per LDS row
+  static constexpr size_t kBytes = (size_t)(kTr ? MAXC : DH) * kStride * sizeof(T);
+};
+
+typedef __fp16 h4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) h4_t lds_h4_t;
+
+template <typename T, int DH, int MAXC>
+__device__ __forceinline__ void vtile_frag(Frag<T> &f, const T *buf, int c0, int db, int lane) {
+  using VT = VTile<T, DH, MAXC>;
+  const int g = lane >> 4, r16 = lane & 15;
+  if constexpr (VT::kTr) {
+    const T *p = buf + (size_t)(c0 + 8 * g + (r16 >> 2)) * VT::kStride + 16 * db + 4 * (r16 & 3);
+    const h4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4_t *)(p));
+    const h4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4_t *)(p + 4 * VT::kStride));
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef short s8_t __attribute__((ext_vector_type(8)));
+    const s4_t a = __builtin_bit_cast(s4_t, lo), b = __builtin_bit_cast(s4_t, hi);
+    const s8_t v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    f.v = __builtin_bit_cast(decltype(f.v), v);
+  } else {
+    frag_load(f, buf + (16 * db + r16) * VT::kStride + c0 + 8 * g);
+  }
+}
+
+// Stage MAXC keys starting at vbase; keys >= nvalid (>= 1) get a copy of key
+// nvalid-1 (finite values; their probabilities are zero).  NTHR threads
+// cooperate; consecutive threads take consecutive 16-byte pieces of one key
+// row.  Loads and stores are unconditional: any guard lets the compiler sink
+// each load next to its store and serialise the round trips.
+template <typename T, int DH, int MAXC, int NTHR>
+__device__ __forceinline__ void vtile_stage(T *buf, const T *vbase, size_t vstride, int nvalid, int t) {
+  using VT = VTile<T, DH, MAXC>;
+  constexpr int EPC = 16 / sizeof(T);            // elements per 16-byte piece
+  constexpr int CPK = DH / EPC;                  // pieces per key row
+  static_assert((MAXC * CPK) % NTHR == 0, "staging threads must tile the buffer");
+  constexpr int ITER = MAXC * CPK / NTHR;
+  uint4 u[ITER];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int idx = t + it * NTHR;
+    const int c = min(idx / CPK, nvalid - 1), ch = idx % CPK;
+    u[it] = *reinterpret_cast<const uint4 *>(vbase + (size_t)c * vstride + ch * EPC);
+  }
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int idx = t + it * NTHR;
+    const int c = idx / CPK, ch = idx % CPK;
+    if constexpr (VT::kTr) {
+      *reinterpret_cast<uint4 *>(buf + (size_t)c * VT::kStride + ch * EPC) = u[it];
+    } else {
+      const uint32_t wd[4] = {u[it].x, u[it].y, u[it].z, u[it].w};
+      uint32_t *v32 = reinterpret_cast<uint32_t *>(buf);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v32[(ch * 4 + j) * VT::kStride + c] = wd[j];
+    }
+  }
+}
 
 template <int MB, int DH> struct AttnState {
   float m[MB];                 // running max, log2 units (same in the 4 lane groups)
@@ -58,53 +128,55 @@ __device__ __forceinline__ void frag_load2(Frag<T> &f0, Frag<T> &f1, const T *p)
 
 // Query fragments of one row (lane%16 of each row block): head-dim slot
 // mapping shared with the key fragments: step kd = 2p + half covers features
-// 64p + 16g + 8*half + (0..7).
+// 64p + 16g + 8*half + (0..7).  Loads are unconditional (callers point rows
+// without a query at some valid row and drop their results): a guarded load
+// would make the compiler wait for it at the branch join.
 template <typename T, int MB, int DH>
-__device__ __forceinline__ void load_q(Frag<T> (&qf)[MB][DH / 32], const T *const (&qrow)[MB],
-                                       const bool (&qvalid)[MB], int g) {
+__device__ __forceinline__ void load_q(Frag<T> (&qf)[MB][DH / 32], const T *const (&qrow)[MB], int g) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int p = 0; p < DH / 64; ++p) {
-      if (qvalid[mb]) {
-        frag_load2(qf[mb][2 * p], qf[mb][2 * p + 1], qrow[mb] + 64 * p + 16 * g);
-      } else {
-        frag_zero(qf[mb][2 * p]);
-        frag_zero(qf[mb][2 * p + 1]);
-      }
-    }
+    for (int p = 0; p < DH / 64; ++p) frag_load2(qf[mb][2 * p], qf[mb][2 * p + 1], qrow[mb] + 64 * p + 16 * g);
 }
 
-// One step of up to 32 keys.  kbase points at key 0 of the step (head offset
-// applied), kstride = elements between consecutive keys.  vt = LDS V^T of the
-// step: vt[d * vts + c] for key c.  Keys c >= nvalid are masked; their V^T
-// entries must be finite (the stager writes zeros).
-template <typename T, int MB, int DH>
-__device__ __forceinline__ void attend_step(AttnState<MB, DH> &st, const Frag<T> (&qf)[MB][DH / 32],
-                                            const T *kbase, size_t kstride, int nvalid, const T *vt,
-                                            int vts, float scale_log2, int lane) {
+// Key fragments of one step of 32 keys (1 <= nvalid): key block kb (16 keys)
+// x head-dim steps.  The A-operand row r16 of key block kb holds key
+// 8*(r16/4) + 4*kb + r16%4, so that in the S^T result lane group g holds keys
+// 8g..8g+7 of the step (the B-operand slots of P^T in the P*V product).
+template <typename T, int DH> struct KStep {
+  Frag<T> f[2][DH / 32];
+};
+
+template <typename T, int DH>
+__device__ __forceinline__ void load_k_step(KStep<T, DH> &kf, const T *kbase, size_t kstride, int nvalid,
+                                            int lane) {
   const int g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    // Keys past nvalid read key nvalid-1 (their scores are masked later).
+    const int key = min(8 * (r16 >> 2) + 4 * kb + (r16 & 3), nvalid - 1);
+#pragma unroll
+    for (int p = 0; p < DH / 64; ++p)
+      frag_load2(kf.f[kb][2 * p], kf.f[kb][2 * p + 1], kbase + (size_t)key * kstride + 64 * p + 16 * g);
+  }
+}
+
+// One step of up to 32 keys with its key fragments already loaded; V of the
+// step is keys c0 .. c0+31 of the staged tile `vbuf`.  Keys >= nvalid are
+// masked; their staged V must be finite (the stager copies a valid key).
+template <typename T, int MB, int DH, int MAXC>
+__device__ __forceinline__ void attend_step_pre(AttnState<MB, DH> &st, const Frag<T> (&qf)[MB][DH / 32],
+                                                const KStep<T, DH> &kf, int nvalid, const T *vbuf, int c0,
+                                                float scale_log2, int lane) {
+  const int g = lane >> 4;
   f32x4_t s[2][MB];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int key = 8 * (r16 >> 2) + 4 * kb + (r16 & 3);
-    const bool kv = key < nvalid;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) s[kb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb) {
+      s[kb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < DH / 64; ++p) {
-      Frag<T> k0, k1;
-      if (kv) {
-        frag_load2(k0, k1, kbase + (size_t)key * kstride + 64 * p + 16 * g);
-      } else {
-        frag_zero(k0);
-        frag_zero(k1);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        mma16(s[kb][mb], k0, qf[mb][2 * p]);
-        mma16(s[kb][mb], k1, qf[mb][2 * p + 1]);
-      }
+      for (int kd = 0; kd < DH / 32; ++kd) mma16(s[kb][mb], kf.f[kb][kd], qf[mb][kd]);
     }
   }
   Frag<T> pf[MB];
@@ -135,47 +207,32 @@ __device__ __forceinline__ void attend_step(AttnState<MB, DH> &st, const Frag<T>
 #pragma unroll
   for (int db = 0; db < DH / 16; ++db) {
     Frag<T> vf;
-    frag_load(vf, vt + (16 * db + r16) * vts + 8 * g);
+    vtile_frag<T, DH, MAXC>(vf, vbuf, c0, db, lane);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) mma16(st.o[mb][db], vf, pf[mb]);
   }
 }
 
-// Stage V^T for `ncols` keys starting at vbase (zeros for keys >= nvalid):
-// vt[d * vts + c].  Threads [tid0, tid0 + nthr) cooperate; consecutive threads
-// read consecutive 16/32-byte chunks of one key row.
-template <typename T, int DH>
-__device__ __forceinline__ void stage_vt(T *vt, int vts, const T *vbase, size_t vstride, int nvalid,
-                                         int ncols, int t, int nthr) {
-  constexpr int CH = DH / 8;
-  for (int idx = t; idx < ncols * CH; idx += nthr) {
-    const int c = idx / CH, ch = idx % CH;
-    if constexpr (sizeof(T) == 2) {
-      // Raw 16-bit halves of one 16-byte load (8 features of key c).
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (c < nvalid) u = *reinterpret_cast<const uint4 *>(vbase + (size_t)c * vstride + ch * 8);
-      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        reinterpret_cast<uint16_t *>(vt)[(ch * 8 + j) * vts + c] = (uint16_t)((wd[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-    } else {
-      Frag<T> f;
-      if (c < nvalid) frag_load(f, vbase + (size_t)c * vstride + ch * 8); else frag_zero(f);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vt[(ch * 8 + j) * vts + c] = frag_get(f, j);
-    }
-  }
+template <typename T, int MB, int DH, int MAXC>
+__device__ __forceinline__ void attend_step(AttnState<MB, DH> &st, const Frag<T> (&qf)[MB][DH / 32],
+                                            const T *kbase, size_t kstride, int nvalid, const T *vbuf, int c0,
+                                            float scale_log2, int lane) {
+  KStep<T, DH> kf;
+  load_k_step<T, DH>(kf, kbase, kstride, nvalid, lane);
+  attend_step_pre<T, MB, DH, MAXC>(st, qf, kf, nvalid, vbuf, c0, scale_log2, lane);
 }
 
 // ---------------------------------------------------------------------------
-// Type A: block rows x key chunk -> partial state in the workspace.
+// Type A: 32 block rows x one key chunk -> partial state in the workspace.
+// Wave w takes row block w%2 and key half w/2 of every staged 128-key tile.
 // ---------------------------------------------------------------------------
+constexpr int kTileA = 128;     // keys staged in LDS per tile (type A, refresh)
+
 template <typename T, typename TO, int DH>
 __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int item, int h, char *smem) {
-  constexpr int MB = kRowsA / 16;
-  constexpr int VTS = 32 + VtPad<T>::v;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
+  const int rb = w & 1, kh = w >> 1;
 
   const int b = find_sample(sa.pre[1], sa.n, item);
   const int t = item - sa.pre[1][b];
@@ -184,88 +241,83 @@ __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int ite
   const int chunk = t / nrg, rg = t % nrg;
   const int key0 = chunk * a.split_keys;
   const int nkeys = min(a.split_keys, N - key0);
-  const int nsteps = (nkeys + 31) / 32;
   const int hk = h / (a.H / a.Hkv);
   const size_t kvstride = (size_t)a.Hkv * DH;
 
-  const T *q = static_cast<const T *>(a.q);
-  const T *qrow[MB];
-  bool qvalid[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int r = rg * kRowsA + mb * 16 + r16;
-    qvalid[mb] = r < B;
-    const int row = a.qmode == 0 ? sa.off[b] + sa.bs[b] + r : a.row_base + sa.pre[0][b] + r;
-    qrow[mb] = q + ((size_t)(qvalid[mb] ? row : 0) * a.H + h) * DH;
-  }
-  Frag<T> qf[MB][DH / 32];
-  load_q<T, MB, DH>(qf, qrow, qvalid, g);
+  const int r = rg * kRowsA + rb * 16 + r16;
+  const bool qvalid1 = r < B;
+  const int rq = min(r, B - 1);
+  const int qrow_i = a.qmode == 0 ? sa.off[b] + sa.bs[b] + rq : a.row_base + sa.pre[0][b] + rq;
+  const T *qrow[1] = {static_cast<const T *>(a.q) + ((size_t)qrow_i * a.H + h) * DH};
+  Frag<T> qf[1][DH / 32];
+  load_q<T, 1, DH>(qf, qrow, g);
 
-  AttnState<MB, DH> st;
+  AttnState<1, DH> st;
   state_init_empty(st);
-  T *vt = reinterpret_cast<T *>(smem) + w * (DH * VTS);
+  T *vbuf = reinterpret_cast<T *>(smem);
   const T *kbase0 = static_cast<const T *>(a.k) + ((size_t)(sa.off[b] + key0)) * kvstride + hk * DH;
   const T *vbase0 = static_cast<const T *>(a.v) + ((size_t)(sa.off[b] + key0)) * kvstride + hk * DH;
-  const int niter = (nsteps + 3) / 4;
-  for (int it = 0; it < niter; ++it) {
-    const int step = it * 4 + w;
-    const bool valid = step < nsteps;
-    const int nvalid = valid ? min(32, nkeys - step * 32) : 0;
+  for (int t0 = 0; t0 < nkeys; t0 += kTileA) {
+    const int nk = min(kTileA, nkeys - t0);
+    // This wave's two steps of the tile: keys [64*kh, 64*kh + 64).
+    KStep<T, DH> kf[2];
+    int nv[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int c0 = 64 * kh + 32 * s2;
+      nv[s2] = max(0, min(32, nk - c0));
+      // A step past the tile's end reads the tile's first keys (and is skipped).
+      load_k_step<T, DH>(kf[s2], kbase0 + (size_t)(t0 + (nv[s2] > 0 ? c0 : 0)) * kvstride, kvstride, max(nv[s2], 1),
+                         lane);
+    }
     __syncthreads();
-    if (valid) stage_vt<T, DH>(vt, VTS, vbase0 + (size_t)step * 32 * kvstride, kvstride, nvalid, 32, lane, 64);
+    vtile_stage<T, DH, kTileA, 256>(vbuf, vbase0 + (size_t)t0 * kvstride, kvstride, nk, tid);
     __syncthreads();
-    if (valid)
-      attend_step<T, MB, DH>(st, qf, kbase0 + (size_t)step * 32 * kvstride, kvstride, nvalid, vt, VTS,
-                             a.scale_log2, lane);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      if (nv[s2] > 0)
+        attend_step_pre<T, 1, DH, kTileA>(st, qf, kf[s2], nv[s2], vbuf, 64 * kh + 32 * s2, a.scale_log2, lane);
   }
   __syncthreads();
 
-  // Merge the 4 waves' states of each row in LDS.
-  float *s_m = reinterpret_cast<float *>(smem);              // [4][kRowsA]
-  float *s_l = s_m + 4 * kRowsA;                             // [4][kRowsA]
-  float *s_o = s_l + 4 * kRowsA;                             // [4][kRowsA][DH]
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int rr = mb * 16 + r16;
-    const float lt = group_sum(st.l[mb]);
+  // Merge the two key halves of each row block in LDS, then write the partial.
+  float *s_m = reinterpret_cast<float *>(smem);     // [2 row blocks][16]
+  float *s_l = s_m + 32;
+  float *s_o = s_l + 32;                            // [2][16][DH]
+  const float lt = group_sum(st.l[0]);
+  if (kh == 1) {
     if (g == 0) {
-      s_m[w * kRowsA + rr] = st.m[mb];
-      s_l[w * kRowsA + rr] = lt;
+      s_m[rb * 16 + r16] = st.m[0];
+      s_l[rb * 16 + r16] = lt;
     }
 #pragma unroll
     for (int db = 0; db < DH / 16; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[(w * kRowsA + rr) * DH + 16 * db + 4 * g + i] = st.o[mb][db][i];
+      *reinterpret_cast<f32x4_t *>(s_o + (rb * 16 + r16) * DH + 16 * db + 4 * g) = st.o[0][db];
   }
   __syncthreads();
-  const int pbase = a.part_base + sa.pre[3][b] + chunk * B;
-  for (int idx = tid; idx < kRowsA * DH; idx += blockDim.x) {
-    const int rr = idx / DH, d = idx % DH;
-    const int r = rg * kRowsA + rr;
-    if (r >= B) continue;
-    float mx = s_m[rr];
+  const size_t pbase = (size_t)(a.part_base + sa.pre[3][b]) + r;      // chunk c: pbase + c*B
+  if (kh == 0 && qvalid1) {
+    const float m1 = s_m[rb * 16 + r16], l1 = s_l[rb * 16 + r16];
+    const float mx = fmaxf(st.m[0], m1);
+    const float e0 = fast_exp2(st.m[0] - mx), e1 = fast_exp2(m1 - mx);
+    const size_t prow = (pbase + (size_t)chunk * B) * a.H + h;
+    float *po = a.part_o + prow * DH;
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) mx = fmaxf(mx, s_m[ww * kRowsA + rr]);
-    float lsum = 0.f, osum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float e = fast_exp2(s_m[ww * kRowsA + rr] - mx);
-      lsum = fmaf(e, s_l[ww * kRowsA + rr], lsum);
-      osum = fmaf(e, s_o[(ww * kRowsA + rr) * DH + d], osum);
+    for (int db = 0; db < DH / 16; ++db) {
+      const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(s_o + (rb * 16 + r16) * DH + 16 * db + 4 * g);
+      *reinterpret_cast<f32x4_t *>(po + 16 * db + 4 * g) = st.o[0][db] * e0 + o1 * e1;
     }
-    const size_t prow = (size_t)(pbase + r) * a.H + h;
-    a.part_o[prow * DH + d] = osum;
-    if (d == 0) a.part_ml[prow] = make_float2(mx, lsum);
+    if (g == 0) a.part_ml[prow] = make_float2(mx, lt * e0 + l1 * e1);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Type B: 64 invariant rows, state from FACache, stream the block's keys.
+// All global loads (queries, FACache, first key step, V^T) are issued before
+// the first wait.
 // ---------------------------------------------------------------------------
-template <typename T, typename TO, int DH>
+template <typename T, typename TO, int DH, int BMAX>
 __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, int h, char *smem) {
-  constexpr int MB = 1;
-  constexpr int VTS = 128 + VtPad<T>::v;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
 
@@ -277,37 +329,42 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
   const size_t kvstride = (size_t)a.Hkv * DH;
   const int off = sa.off[b];
 
-  T *vt = reinterpret_cast<T *>(smem);
-  stage_vt<T, DH>(vt, VTS, static_cast<const T *>(a.v) + (size_t)(off + bs) * kvstride + hk * DH, kvstride, B,
-                  (B + 31) & ~31, tid, blockDim.x);
-
+  // Rows past the last invariant row load the last one (results dropped).
   const int u = tile * kRowsB + w * 16 + r16;
   const bool uvalid = u < nU;
-  const int row = off + (u < bs ? u : u + B);
-  const T *q = static_cast<const T *>(a.q);
-  const T *qrow[MB] = {q + ((size_t)(uvalid ? row : off) * a.H + h) * DH};
-  const bool qvalid[MB] = {uvalid};
-  Frag<T> qf[MB][DH / 32];
-  load_q<T, MB, DH>(qf, qrow, qvalid, g);
+  const int uc = min(u, nU - 1);
+  const int row = off + (uc < bs ? uc : uc + B);
+  const T *qrow[1] = {static_cast<const T *>(a.q) + ((size_t)row * a.H + h) * DH};
+  Frag<T> qf[1][DH / 32];
+  load_q<T, 1, DH>(qf, qrow, g);
 
   // FACache state of this row (Algorithm 1: initialise with the cache).
-  AttnState<MB, DH> st;
-  const size_t crow = (size_t)(uvalid ? row : off) * a.H + h;
-  if (uvalid) {
-    st.m[0] = a.m_c[crow] * kLog2e;
-    st.l[0] = g == 0 ? a.l_c[crow] : 0.f;
+  AttnState<1, DH> st;
+  const size_t crow = (size_t)row * a.H + h;
+  st.m[0] = a.m_c[crow] * kLog2e;
+  const float lc = a.l_c[crow];
+  st.l[0] = g == 0 ? lc : 0.f;
 #pragma unroll
-    for (int db = 0; db < DH / 16; ++db)
-      st.o[0][db] = *reinterpret_cast<const f32x4_t *>(a.o_c + crow * DH + 16 * db + 4 * g);
-  } else {
-    state_init_empty(st);
-  }
+  for (int db = 0; db < DH / 16; ++db)
+    st.o[0][db] = *reinterpret_cast<const f32x4_t *>(a.o_c + crow * DH + 16 * db + 4 * g);
+  const T *kbase = static_cast<const T *>(a.k) + (size_t)(off + bs) * kvstride + hk * DH;
+  KStep<T, DH> kf[2];
+  load_k_step<T, DH>(kf[0], kbase, kvstride, min(32, B), lane);
+
+  T *vbuf = reinterpret_cast<T *>(smem);
+  vtile_stage<T, DH, BMAX, 256>(vbuf, static_cast<const T *>(a.v) + (size_t)(off + bs) * kvstride + hk * DH, kvstride,
+                                B, tid);
   __syncthreads();
 
-  const T *kbase = static_cast<const T *>(a.k) + (size_t)(off + bs) * kvstride + hk * DH;
-  for (int c0 = 0; c0 < B; c0 += 32)
-    attend_step<T, MB, DH>(st, qf, kbase + (size_t)c0 * kvstride, kvstride, min(32, B - c0), vt + c0, VTS,
-                           a.scale_log2, lane);
+  // Up to 4 steps (block <= 128 keys); the next step's keys load during this one.
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    if (c0 + 32 < B) load_k_step<T, DH>(kf[1], kbase + (size_t)(c0 + 32) * kvstride, kvstride, min(32, B - c0 - 32), lane);
+    attend_step_pre<T, 1, DH, BMAX>(st, qf, kf[0], min(32, B - c0), vbuf, c0, a.scale_log2, lane);
+    if (c0 + 32 < B) {
+      if (c0 + 64 < B) load_k_step<T, DH>(kf[0], kbase + (size_t)(c0 + 64) * kvstride, kvstride, min(32, B - c0 - 64), lane);
+      attend_step_pre<T, 1, DH, BMAX>(st, qf, kf[1], min(32, B - c0 - 32), vbuf, c0 + 32, a.scale_log2, lane);
+    }
+  }
 
   const float lt = group_sum(st.l[0]);
   if (uvalid) {
@@ -321,7 +378,8 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
   }
 }
 
-template <typename T, typename TO, int DH>
+// BMAX: staged block keys (32, 64 or 128 >= every block of the launch).
+template <typename T, typename TO, int DH, int BMAX>
 __global__ __launch_bounds__(256) void step_attn_kernel(const SeqArgs sa, const AttnArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int gid = blockIdx.x;
@@ -329,7 +387,7 @@ __global__ __launch_bounds__(256) void step_attn_kernel(const SeqArgs sa, const 
     block_rows_partial<T, TO, DH>(sa, a, gid / a.H, gid % a.H, smem);
   } else {
     const int j = gid - a.nA;
-    invariant_rows<T, TO, DH>(sa, a, j / a.H, j % a.H, smem);
+    invariant_rows<T, TO, DH, BMAX>(sa, a, j / a.H, j % a.H, smem);
   }
 }
 
@@ -341,7 +399,8 @@ __global__ __launch_bounds__(256) void block_attn_kernel(const SeqArgs sa, const
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the type-A partial states: one wave per (block row, head).
+// Merge of the type-A partial states: one wave per (block row, head).  Lane c
+// reads chunk c's (max, normaliser); the feature sums read all chunks at once.
 // ---------------------------------------------------------------------------
 template <typename T, typename TO, int DH>
 __global__ __launch_bounds__(256) void merge_kernel(const SeqArgs sa, const AttnArgs a, int M) {
@@ -353,27 +412,49 @@ __global__ __launch_bounds__(256) void merge_kernel(const SeqArgs sa, const Attn
   const int r = m - sa.pre[0][b];
   const int B = sa.be[b] - sa.bs[b];
   const int nch = (sa.len[b] + a.split_keys - 1) / a.split_keys;
-  const int pbase = a.part_base + sa.pre[3][b];
+  const size_t pb = (size_t)(a.part_base + sa.pre[3][b] + r) * a.H + h;   // chunk c at pb + c*B*H
+  const size_t cstride = (size_t)B * a.H;
 
   float mx = -INFINITY;
-  for (int c = lane; c < nch; c += 64) mx = fmaxf(mx, a.part_ml[(size_t)(pbase + c * B + r) * a.H + h].x);
+  for (int c = lane; c < nch; c += 64) mx = fmaxf(mx, a.part_ml[pb + c * cstride].x);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   float lsum = 0.f;
-  float acc[DH / 64] = {};
-  for (int c = 0; c < nch; ++c) {
-    const size_t prow = (size_t)(pbase + c * B + r) * a.H + h;
-    const float2 ml = a.part_ml[prow];
-    const float e = fast_exp2(ml.x - mx);
-    lsum = fmaf(e, ml.y, lsum);
+  for (int c = lane; c < nch; c += 64) {
+    const float2 ml = a.part_ml[pb + c * cstride];
+    lsum = fmaf(fast_exp2(ml.x - mx), ml.y, lsum);
+  }
 #pragma unroll
-    for (int j = 0; j < DH / 64; ++j) acc[j] = fmaf(e, a.part_o[prow * DH + lane + 64 * j], acc[j]);
+  for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+
+  constexpr int PER = DH / 64;
+  float acc[PER] = {};
+  for (int c0 = 0; c0 < nch; c0 += 8) {
+    float v[8][PER], e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = c0 + j;
+      e[j] = 0.f;
+      if (c < nch) {
+        const size_t prow = pb + c * cstride;
+        e[j] = fast_exp2(a.part_ml[prow].x - mx);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) v[j][k] = a.part_o[prow * DH + lane + 64 * k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) v[j][k] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] = fmaf(e[j], v[j][k], acc[k]);
   }
   const int orow = a.omode == 0 ? sa.off[b] + sa.bs[b] + r : a.row_base + m;
   const float inv = 1.0f / lsum;
   TO *out = static_cast<TO *>(a.out) + ((size_t)orow * a.H + h) * DH;
 #pragma unroll
-  for (int j = 0; j < DH / 64; ++j) out[lane + 64 * j] = from_f32<TO>(acc[j] * inv);
+  for (int k = 0; k < PER; ++k) out[lane + 64 * k] = from_f32<TO>(acc[k] * inv);
   if (a.lse && lane == 0) a.lse[(size_t)orow * a.H + h] = (mx + __log2f(lsum)) * kLn2;
 }
 
@@ -386,7 +467,6 @@ __global__ __launch_bounds__(256) void refresh_attn_kernel(const SeqArgs sa, con
   extern __shared__ __align__(16) char smem[];
   constexpr int MB = 1;
   constexpr int TK = 128;                     // keys staged per tile
-  constexpr int VTS = TK + VtPad<T>::v;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int item = blockIdx.x / a.H, h = blockIdx.x % a.H;
@@ -402,14 +482,13 @@ __global__ __launch_bounds__(256) void refresh_attn_kernel(const SeqArgs sa, con
   const bool tvalid = t < N;
   const bool in_u = tvalid && (t < bs || t >= be);
   const T *q = static_cast<const T *>(a.q);
-  const T *qrow[MB] = {q + ((size_t)(off + (tvalid ? t : 0)) * a.H + h) * DH};
-  const bool qvalid[MB] = {tvalid};
+  const T *qrow[MB] = {q + ((size_t)(off + min(t, N - 1)) * a.H + h) * DH};
   Frag<T> qf[MB][DH / 32];
-  load_q<T, MB, DH>(qf, qrow, qvalid, g);
+  load_q<T, MB, DH>(qf, qrow, g);
 
   AttnState<MB, DH> st;
   state_init_empty(st);
-  T *vt = reinterpret_cast<T *>(smem);
+  T *vbuf = reinterpret_cast<T *>(smem);
   const T *kb = static_cast<const T *>(a.k) + (size_t)off * kvstride + hk * DH;
   const T *vb = static_cast<const T *>(a.v) + (size_t)off * kvstride + hk * DH;
   const size_t crow = (size_t)(off + (tvalid ? t : 0)) * a.H + h;
@@ -435,11 +514,11 @@ __global__ __launch_bounds__(256) void refresh_attn_kernel(const SeqArgs sa, con
     for (int k0 = seg_lo[sgi]; k0 < seg_hi[sgi]; k0 += TK) {
       const int nk = min(TK, seg_hi[sgi] - k0);
       __syncthreads();
-      stage_vt<T, DH>(vt, VTS, vb + (size_t)k0 * kvstride, kvstride, nk, (nk + 31) & ~31, tid, blockDim.x);
+      vtile_stage<T, DH, TK, 256>(vbuf, vb + (size_t)k0 * kvstride, kvstride, nk, tid);
       __syncthreads();
       for (int c0 = 0; c0 < nk; c0 += 32)
-        attend_step<T, MB, DH>(st, qf, kb + (size_t)(k0 + c0) * kvstride, kvstride, min(32, nk - c0), vt + c0,
-                               VTS, a.scale_log2, lane);
+        attend_step<T, MB, DH, TK>(st, qf, kb + (size_t)(k0 + c0) * kvstride, kvstride, min(32, nk - c0), vbuf, c0,
+                                   a.scale_log2, lane);
     }
   }
   const float lt = group_sum(st.l[0]);
@@ -458,14 +537,12 @@ __global__ __launch_bounds__(256) void refresh_attn_kernel(const SeqArgs sa, con
 // Launchers
 // ---------------------------------------------------------------------------
 template <typename T, int DH> constexpr size_t step_smem() {
-  constexpr size_t vt_a = 4 * DH * (32 + VtPad<T>::v) * sizeof(T);
-  constexpr size_t merge_a = (2 * 4 * kRowsA + 4 * kRowsA * DH) * sizeof(float);
-  constexpr size_t vt_b = DH * (128 + VtPad<T>::v) * sizeof(T);
-  constexpr size_t m1 = vt_a > merge_a ? vt_a : merge_a;
-  return m1 > vt_b ? m1 : vt_b;
+  constexpr size_t vt = VTile<T, DH, 128>::kBytes;                  // type A tile, type B block keys
+  constexpr size_t merge_a = (64 + 32 * DH) * sizeof(float);
+  return vt > merge_a ? vt : merge_a;
 }
 template <typename T, int DH> constexpr size_t refresh_smem() {
-  return DH * (128 + VtPad<T>::v) * sizeof(T);
+  return VTile<T, DH, 128>::kBytes;
 }
 
 // Cache type T and output type TO: fp16 / bf16 for bf16 parameters, fp32 / fp32.
@@ -482,7 +559,14 @@ template <typename T, int DH> constexpr size_t refresh_smem() {
 
 hipError_t launch_step_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
-  LC_DISPATCH(dt, dh, (step_attn_kernel<T, TO, DH><<<n_blocks, 256, step_smem<T, DH>(), s>>>(sa, a)));
+  int bmax = 0;
+  for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
+  if (bmax <= 32)
+    LC_DISPATCH(dt, dh, (step_attn_kernel<T, TO, DH, 32><<<n_blocks, 256, step_smem<T, DH>(), s>>>(sa, a)));
+  else if (bmax <= 64)
+    LC_DISPATCH(dt, dh, (step_attn_kernel<T, TO, DH, 64><<<n_blocks, 256, step_smem<T, DH>(), s>>>(sa, a)));
+  else
+    LC_DISPATCH(dt, dh, (step_attn_kernel<T, TO, DH, 128><<<n_blocks, 256, step_smem<T, DH>(), s>>>(sa, a)));
   return hipGetLastError();
 }
 
@@ -512,10 +596,15 @@ hipError_t setup_kernel_attributes() {
   if (e == hipSuccess)                                                                           \
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(K), hipFuncAttributeMaxDynamicSharedMemorySize, \
                             (int)(BYTES));
-  LC_ATTR((step_attn_kernel<f16_t, bf16_t, 128>), (step_smem<f16_t, 128>()));
-  LC_ATTR((step_attn_kernel<f16_t, bf16_t, 64>), (step_smem<f16_t, 64>()));
-  LC_ATTR((step_attn_kernel<float, float, 128>), (step_smem<float, 128>()));
-  LC_ATTR((step_attn_kernel<float, float, 64>), (step_smem<float, 64>()));
+#define LC_ATTR_STEP(BM)                                                   \
+  LC_ATTR((step_attn_kernel<f16_t, bf16_t, 128, BM>), (step_smem<f16_t, 128>())); \
+  LC_ATTR((step_attn_kernel<f16_t, bf16_t, 64, BM>), (step_smem<f16_t, 64>()));   \
+  LC_ATTR((step_attn_kernel<float, float, 128, BM>), (step_smem<float, 128>()));  \
+  LC_ATTR((step_attn_kernel<float, float, 64, BM>), (step_smem<float, 64>()));
+  LC_ATTR_STEP(32)
+  LC_ATTR_STEP(64)
+  LC_ATTR_STEP(128)
+#undef LC_ATTR_STEP
   LC_ATTR((block_attn_kernel<f16_t, bf16_t, 128>), (step_smem<f16_t, 128>()));
   LC_ATTR((block_attn_kernel<f16_t, bf16_t, 64>), (step_smem<f16_t, 64>()));
   LC_ATTR((block_attn_kernel<float, float, 128>), (step_smem<float, 128>()));

@@ -66,5 +66,6 @@ constexpr int kRowsR = 64;     // rows per refresh item
 constexpr int kQkvRows = 32;   // token rows per QKV tile
 constexpr int kQkvNB = 3;      // 16-feature column blocks per QKV tile
 constexpr int kQkvWaves = 8;   // waves splitting the contraction
+constexpr int kQkvMaxD = 8192; // largest d_model (gamma is staged in LDS)
 
 }  // namespace lc

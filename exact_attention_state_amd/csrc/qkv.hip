@@ -25,13 +25,16 @@
 
 namespace lc {
 
-template <typename T, typename TC, int NB, int KW, bool SPLIT>
+// NG > 0: the wave's contraction range is exactly NG groups of U steps and
+// the pipeline is unrolled at compile time; NG == 0: runtime group count.
+template <typename T, typename TC, int NB, int KW, bool SPLIT, int U, int NG>
 __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, const QkvArgs a) {
   constexpr int MB = 2;                    // 16-row blocks per tile
   constexpr int BM = 16 * MB;
   __shared__ int s_id[BM], s_dst[BM], s_pos[BM];
   __shared__ float s_ssq[KW][BM];
   __shared__ f32x4_t s_red[KW][MB][NB][64];
+  __shared__ __align__(16) T s_gamma[kQkvMaxD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
@@ -69,82 +72,144 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
 
   const T *E = static_cast<const T *>(a.E);
   const T *W = static_cast<const T *>(a.W);
-  const T *gamma = static_cast<const T *>(a.gamma);
+  {
+    // RMSNorm gain: staged once per workgroup, read per step from LDS.
+    const uint4 *gsrc = static_cast<const uint4 *>(a.gamma);
+    uint4 *gdst = reinterpret_cast<uint4 *>(s_gamma);
+    for (int i = tid; i < D * (int)sizeof(T) / 16; i += blockDim.x) gdst[i] = gsrc[i];
+  }
+  __syncthreads();
 
+  // Rows without a valid token read row 0 and are zeroed in the epilogue;
+  // column blocks past the last feature read row 0 and are dropped there, so
+  // every load of the main loop is unconditional.
   const T *arow[MB];
-  bool avalid[MB];
-  int adst[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int id = s_id[mb * 16 + r16];
-    avalid[mb] = id >= 0;
-    adst[mb] = s_dst[mb * 16 + r16];
-    arow[mb] = E + (size_t)(avalid[mb] ? id : 0) * D;
+    arow[mb] = E + (size_t)(id >= 0 ? id : 0) * D;
   }
   const T *brow[NB];
-  bool bvalid[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int cb = cb0 + nb;
-    bvalid[nb] = cb < ncb;
+    const int cb = min(cb0 + nb, ncb - 1);
     const int hh = cb / cbh, p0 = (cb % cbh) * 8;
     const int wrow = hh * dh + (r16 < 8 ? p0 + r16 : dh / 2 + p0 + (r16 - 8));
-    brow[nb] = W + (size_t)(bvalid[nb] ? wrow : 0) * D;
+    brow[nb] = W + (size_t)wrow * D;
   }
-  const bool write_h = (blockIdx.x == 0) && (a.h != nullptr);
-  T *hout = static_cast<T *>(a.h);
 
   f32x4_t acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float ssq[MB] = {};
+  f32x4_t ssq[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) ssq[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Contraction range of this wave, in steps of 32, processed in groups of U
+  // steps (U divides the step count); the loads of group i+1 are in flight
+  // while group i is multiplied.
   const int kper = D / KW;
   const int kbeg = w * kper;
-#pragma unroll 4
-  for (int k = kbeg; k < kbeg + kper; k += 32) {
-    const int kk = k + 8 * g;
-    Frag<T> gm, af[MB], al[MB], bf[NB], raw[MB];
-    frag_load(gm, gamma + kk);
+  const int ngroups = kper / (32 * U);
+
+  struct Group {
+    Frag<T> w[U][NB], e[U][MB];
+  };
+  auto load_group = [&](Group &G, int grp) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if (bvalid[nb]) frag_load(bf[nb], brow[nb] + kk); else frag_zero(bf[nb]);
+    for (int u = 0; u < U; ++u) {
+      const int kk = kbeg + (grp * U + u) * 32 + 8 * g;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) frag_load(G.w[u][nb], brow[nb] + kk);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) frag_load(G.e[u][mb], arow[mb] + kk);
     }
+  };
+  auto compute_group = [&](const Group &G, int grp) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (avalid[mb]) frag_load(raw[mb], arow[mb] + kk); else frag_zero(raw[mb]);
+    for (int u = 0; u < U; ++u) {
+      Frag<T> gm;
+      frag_load(gm, s_gamma + kbeg + (grp * U + u) * 32 + 8 * g);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        // Sum of squares on the matrix core: E_rows * E_rows^T, whose diagonal
+        // is each row's sum of x^2 (exact products, fp32 accumulation).
+        mma16(ssq[mb], G.e[u][mb], G.e[u][mb]);
+        Frag<T> af, al;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float y = frag_get(G.e[u][mb], i) * frag_get(gm, i);
+          frag_set(af, i, y);
+          if constexpr (SPLIT) frag_set(al, i, y - frag_get(af, i));
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          mma16(acc[mb][nb], af, G.w[u][nb]);
+          if constexpr (SPLIT) mma16(acc[mb][nb], al, G.w[u][nb]);
+        }
+      }
     }
+  };
+
+  if constexpr (NG > 0) {
+    // Two groups in flight while a third is multiplied.
+    Group gbuf[3];
+    load_group(gbuf[0], 0);
+    if (NG > 1) load_group(gbuf[1], 1);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (write_h && adst[mb] >= 0) {
-        T *dstp = hout + (size_t)adst[mb] * D + kk;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dstp[i] = from_f32<T>(frag_get(raw[mb], i));
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = frag_get(raw[mb], i);
-        ssq[mb] = fmaf(x, x, ssq[mb]);
-        const float y = x * frag_get(gm, i);
-        frag_set(af[mb], i, y);
-        if constexpr (SPLIT) frag_set(al[mb], i, y - frag_get(af[mb], i));
+    for (int gi = 0; gi < NG; ++gi) {
+      // Keep the schedule as written: loads two groups ahead, then this
+      // group's MFMAs (without the fences the scheduler hoists loads of later
+      // groups and runs out of registers).
+      if (gi + 2 < NG) load_group(gbuf[(gi + 2) % 3], gi + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_group(gbuf[gi % 3], gi);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    Group ga, gb;
+    load_group(ga, 0);
+    for (int grp = 0; grp < ngroups; grp += 2) {
+      if (grp + 1 < ngroups) load_group(gb, grp + 1);
+      compute_group(ga, grp);
+      if (grp + 1 < ngroups) {
+        if (grp + 2 < ngroups) load_group(ga, grp + 2);
+        compute_group(gb, grp + 1);
       }
     }
+  }
+
+  // EmbedCache: copy this token tile's embedding rows to h, spread over the
+  // column tiles of the grid (16-byte pieces; rows with a bad id get zeros).
+  {
+    const int pieces = BM * (D / 8);
+    const int per = (pieces + gridDim.x - 1) / gridDim.x;
+    for (int t = tid; t < per; t += blockDim.x) {
+      const int c = blockIdx.x * per + t;
+      if (c >= pieces) break;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int dst = s_dst[row], id = s_id[row];
+      if (dst < 0) continue;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      constexpr int NV = sizeof(T) * 8 / 16;   // uint4 pieces per 8 elements
+      T *hp = static_cast<T *>(a.h) + (size_t)dst * D + col;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        mma16(acc[mb][nb], af[mb], bf[nb]);
-        if constexpr (SPLIT) mma16(acc[mb][nb], al[mb], bf[nb]);
+      for (int j = 0; j < NV; ++j) {
+        if (id >= 0) v = reinterpret_cast<const uint4 *>(E + (size_t)id * D + col)[j];
+        reinterpret_cast<uint4 *>(hp)[j] = v;
       }
+    }
   }
 
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const float s = group_sum(ssq[mb]);
-    if (g == 0) s_ssq[w][mb * 16 + r16] = s;
+    // Diagonal entry (r, r) of the 16x16 result sits in lane r + 16*(r/4), slot r%4.
+    if ((r16 >> 2) == g) {
+      const int i = r16 & 3;
+      s_ssq[w][mb * 16 + r16] = i == 0 ? ssq[mb][0] : i == 1 ? ssq[mb][1] : i == 2 ? ssq[mb][2] : ssq[mb][3];
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s_red[w][mb][nb][lane] = acc[mb][nb];
   }
@@ -170,7 +235,7 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
       float ss = 0.f;
 #pragma unroll
       for (int ww = 0; ww < KW; ++ww) ss += s_ssq[ww][row];
-      const float y = sum[i] * rsqrtf(ss * invD + a.eps);
+      const float y = s_id[row] >= 0 ? sum[i] * rsqrtf(ss * invD + a.eps) : 0.f;
       const float other = __shfl_xor(y, 8);
       float o = y;
       if (rot) {
@@ -200,10 +265,28 @@ hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipS
   const int ncb = F / 16;
   dim3 grid((ncb + kQkvNB - 1) / kQkvNB, (a.M + kQkvRows - 1) / kQkvRows);
   dim3 block(64 * kQkvWaves);
-  if (dt == kBF16)
-    qkv_fused_kernel<bf16_t, f16_t, kQkvNB, kQkvWaves, true><<<grid, block, 0, s>>>(sa, a);
-  else
-    qkv_fused_kernel<float, float, kQkvNB, kQkvWaves, false><<<grid, block, 0, s>>>(sa, a);
+  const int steps_per_wave = a.D / kQkvWaves / 32;
+#define LC_QKV(TP, TC, SPLIT, U, NG) \
+  qkv_fused_kernel<TP, TC, kQkvNB, kQkvWaves, SPLIT, U, NG><<<grid, block, 0, s>>>(sa, a)
+  if (dt == kBF16) {
+    switch (steps_per_wave) {
+      case 2: LC_QKV(bf16_t, f16_t, true, 2, 1); break;
+      case 4: LC_QKV(bf16_t, f16_t, true, 2, 2); break;
+      case 8: LC_QKV(bf16_t, f16_t, true, 2, 4); break;
+      case 16: LC_QKV(bf16_t, f16_t, true, 2, 8); break;
+      case 32: LC_QKV(bf16_t, f16_t, true, 2, 16); break;
+      default:
+        if (steps_per_wave % 2 == 0) LC_QKV(bf16_t, f16_t, true, 2, 0);
+        else LC_QKV(bf16_t, f16_t, true, 1, 0);
+    }
+  } else {
+    switch (steps_per_wave) {
+      case 1: LC_QKV(float, float, false, 1, 1); break;
+      case 2: LC_QKV(float, float, false, 1, 2); break;
+      default: LC_QKV(float, float, false, 1, 0);
+    }
+  }
+#undef LC_QKV
   return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ typedef enum { LACACHE_F32 = 0, LACACHE_BF16 = 1 } lacache_dtype;
 #define LACACHE_DEVFLAG_CACHE_RANGE 2u   /* a q/k/v value exceeded the fp16 range */
 
 /* First-layer shape (Section 3.3.2).  Supported: head_dim 64 or 128,
- * d_model a multiple of 256, n_heads a multiple of n_kv_heads,
+ * d_model a multiple of 256 up to 8192, n_heads a multiple of n_kv_heads,
  * 1 <= max_seq_len <= 1<<20.  sm_scale <= 0 selects 1/sqrt(head_dim).
  * rope_theta > 0: feature i of a head is paired with feature i + d_h/2 and
  * rotated by position * rope_theta^(-2i/d_h).  rms_eps >= 0:
