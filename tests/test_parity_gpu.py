@@ -126,3 +126,227 @@ def test_dualcache_attention_equals_block_rows_of_full_recompute():
     ref = oracle.full_recompute(dw.params, cfg_of(wl), dw.ids_host, dw.table)
     check_output(host(out_block), ref["out"][crow], wl.dtype, "dualcache out")
     check_lse(host(lse_block), ref["lse"][crow], wl.dtype, "dualcache lse")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: sampled outputs, each computed by the oracle one by one
+# ---------------------------------------------------------------------------
+
+def _sample_rows(rng, n, bs, be, k):
+    """Block rows, their neighbours, both ends, and random invariant rows."""
+    fixed = [0, max(bs - 1, 0), bs, (bs + be) // 2, be - 1, min(be, n - 1), n - 1]
+    rand = rng.choice(n, size=min(k, n), replace=False).tolist()
+    return sorted(set(int(r) for r in fixed + rand if 0 <= r < n))
+
+
+def _check_sampled(dw, rng, n_samples, heads, what, k_rows=12):
+    wl = dw.wl
+    cfg = cfg_of(wl)
+    out, lse = host(dw.ct.out), host(dw.ct.lse)
+    samples = rng.choice(len(dw.table), size=min(n_samples, len(dw.table)), replace=False)
+    worst = {}
+    for b in samples:
+        off, n, bs, be = dw.table[b]
+        rows = _sample_rows(rng, n, bs, be, k_rows)
+        ref = oracle.layer0_rows(dw.params, cfg, dw.ids_host[off:off + n], rows, heads)
+        got_o = out[off + np.asarray(rows)][:, heads]
+        got_l = lse[off + np.asarray(rows)][:, heads]
+        st = check_output(got_o, ref["out"], wl.dtype, f"{what} sample {b}")
+        check_lse(got_l, ref["lse"], wl.dtype, f"{what} sample {b}")
+        worst = {k: max(worst.get(k, 0.0), v) for k, v in st.items()}
+    return worst
+
+
+@pytest.mark.parametrize("name", ["batched16", "long4", "varlen32"])
+def test_full_size_configs_sampled(name):
+    """Refresh, step 1 and step 20 at full size; sampled rows/heads vs the oracle."""
+    wl = synth.WORKLOADS[name]
+    _say(f"[parity] {name}: batch {wl.batch} seq_lens {wl.seq_lens[:6]}... block {wl.block_size} "
+         f"T {wl.total_tokens} M {wl.block_tokens}")
+    rng = np.random.default_rng([11, len(name)])
+    heads = [0, 7, 31]
+    dw = DeviceWorkload(wl)
+    dw.prefill()
+    torch.cuda.synchronize()
+    _say(f"[parity] {name} refresh {_check_sampled(dw, rng, 3, heads, name + ' refresh')}")
+    for s in range(1, wl.steps + 1):
+        blk = dw.next_block_ids()
+        dw.block_step(blk)
+        if s in (1, wl.steps):
+            torch.cuda.synchronize()
+            _say(f"[parity] {name} step {s} {_check_sampled(dw, rng, 3, heads, f'{name} step {s}')}")
+
+
+def test_varlen32_dualcache_attention_sampled():
+    """DualCache block-query attention on the variable-length batch (block rows only)."""
+    wl = synth.WORKLOADS["varlen32"]
+    _say(f"[parity] varlen32 dualcache: batch {wl.batch}")
+    dw = DeviceWorkload(wl)
+    dw.prefill()
+    crow = np.concatenate([off + np.arange(bs, be) for (off, n, bs, be) in dw.table])
+    q_block = dw.ct.q.index_select(0, torch.from_numpy(crow).to("cuda")).contiguous()
+    out_block = torch.empty(q_block.shape, dtype=dw.ctx.torch_dtype, device="cuda")
+    lse_block = torch.empty(q_block.shape[:2], dtype=torch.float32, device="cuda")
+    ws = dw.ctx.alloc_workspace(lacache.OP_DUALCACHE_ATTN, dw.table)
+    dw.ctx.dualcache_attn(q_block, dw.ct.k, dw.ct.v, dw.table, out_block, lse_block, ws)
+    torch.cuda.synchronize()
+    # The block rows of the refresh output are the same quantity, computed by another kernel;
+    # the oracle pins both on sampled samples.
+    cfg = cfg_of(wl)
+    rng = np.random.default_rng(5)
+    heads = [1, 16, 30]
+    got_o, got_l = host(out_block), host(lse_block)
+    row0 = np.cumsum([0] + [be - bs for (_, _, bs, be) in dw.table])
+    for b in rng.choice(len(dw.table), size=4, replace=False):
+        off, n, bs, be = dw.table[b]
+        rows = list(range(bs, be))
+        ref = oracle.layer0_rows(dw.params, cfg, dw.ids_host[off:off + n], rows, heads)
+        sl = slice(row0[b], row0[b + 1])
+        check_output(got_o[sl][:, heads], ref["out"], wl.dtype, f"dualcache sample {b}")
+        check_lse(got_l[sl][:, heads], ref["lse"], wl.dtype, f"dualcache sample {b}")
+
+
+# ---------------------------------------------------------------------------
+# Bit-exact indexing, determinism and edge cases
+# ---------------------------------------------------------------------------
+
+def _small_batched(seed=31, dtype="bf16"):
+    return synth.custom("bitexact", dtype=dtype, d_model=512, n_heads=4, n_kv_heads=2, head_dim=128, vocab=900,
+                        prompt_lens=(33, 170, 64, 7), gen_len=64, block_size=16, block_idx=(1, 3, 0, 2), steps=2,
+                        seed=seed)
+
+
+def test_batched_equals_per_sample_bitwise():
+    """A sample's results do not depend on the other samples of the batch."""
+    wl = _small_batched()
+    _say(f"[bitexact] batched vs per-sample on {wl.name}")
+    dw = DeviceWorkload(wl)
+    dw.prefill()
+    blk = dw.next_block_ids()
+    dw.block_step(blk)
+    torch.cuda.synchronize()
+    full = {k: getattr(dw.ct, k).clone() for k in ("h", "q", "k", "v", "out", "lse", "m", "l", "o_acc")}
+    crow0 = 0
+    for b, (off, n, bs, be) in enumerate(dw.table):
+        B = be - bs
+        one = DeviceWorkload(wl, ctx=dw.ctx, n_rows=dw.n_rows)
+        one.table = [(off, n, bs, be)]
+        one.ids_host = synth.initial_ids(wl)
+        one.prefill()
+        one.ctx.block_step(one.weights, blk[crow0:crow0 + B].contiguous(), one.table, one.ct,
+                           one.ctx.alloc_workspace(lacache.OP_BLOCK_STEP, one.table))
+        torch.cuda.synchronize()
+        rows = slice(off, off + n)
+        for k in ("h", "q", "k", "v", "out", "lse"):
+            assert torch.equal(getattr(one.ct, k)[rows], full[k][rows]), f"sample {b}: {k} differs"
+        urows = torch.from_numpy(off + np.r_[0:bs, be:n]).to("cuda")
+        for k in ("m", "l", "o_acc"):
+            assert torch.equal(getattr(one.ct, k).index_select(0, urows), full[k].index_select(0, urows)), k
+        crow0 += B
+
+
+def test_repeated_step_is_bitwise_deterministic():
+    wl = _small_batched(seed=32)
+    dw = DeviceWorkload(wl)
+    dw.prefill()
+    blk = dw.next_block_ids()
+    dw.block_step(blk)
+    torch.cuda.synchronize()
+    first = (dw.ct.out.clone(), dw.ct.lse.clone(), dw.ct.q.clone())
+    for _ in range(3):
+        dw.block_step(blk)
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], dw.ct.out) and torch.equal(first[1], dw.ct.lse) and torch.equal(first[2], dw.ct.q)
+
+
+def test_rows_outside_the_block_table_are_untouched():
+    """Sentinel-filled rows that belong to no sample keep their bytes; a block step
+    rewrites only the block rows of the caches and never the FACache."""
+    wl = synth.custom("sentinel", dtype="bf16", d_model=512, n_heads=4, head_dim=128, vocab=500,
+                      prompt_lens=(40, 50), gen_len=32, block_size=16, block_idx=(1, 0), seed=33)
+    ctx = lacache.context_for(wl)
+    gap = 17
+    table = [(3, 72, 56, 72), (3 + 72 + gap, 82, 50, 66)]
+    n_rows = table[-1][0] + table[-1][1] + 9
+    dw = DeviceWorkload(wl, ctx=ctx, n_rows=n_rows)
+    dw.table = table
+    ids = np.zeros(n_rows, np.int32)
+    base = synth.initial_ids(wl)
+    ids[3:75] = base[:72]
+    ids[92:174] = base[72:154]
+    for t in dw.ct.__dict__.values():
+        if t.dtype in (torch.float32, torch.float16, torch.bfloat16):
+            t.fill_(-1024.0)
+    dw.ctx.prefill_cache(dw.weights, torch.from_numpy(ids).cuda(), table, dw.ct)
+    torch.cuda.synchronize()
+    outside = np.r_[0:3, 75:92, 174:n_rows]
+    for k in ("h", "q", "k", "v", "out", "lse", "m", "l", "o_acc"):
+        t = getattr(dw.ct, k).float().cpu().numpy()
+        assert (t[outside] == -1024.0).all(), f"{k}: rows outside the table were written"
+    snap = {k: getattr(dw.ct, k).clone() for k in ("h", "q", "k", "v", "m", "l", "o_acc")}
+    blk = torch.from_numpy(np.concatenate([ids[3 + 56:3 + 72], ids[92 + 50:92 + 66]])[::-1].copy()).cuda()
+    ws = dw.ctx.alloc_workspace(lacache.OP_BLOCK_STEP, table)
+    dw.ctx.block_step(dw.weights, blk, table, dw.ct, ws)
+    torch.cuda.synchronize()
+    blockrows = np.r_[3 + 56:3 + 72, 92 + 50:92 + 66]
+    keep = np.setdiff1d(np.arange(n_rows), blockrows)
+    for k in ("h", "q", "k", "v"):
+        a, b_ = getattr(dw.ct, k).float().cpu().numpy(), snap[k].float().cpu().numpy()
+        assert np.array_equal(a[keep], b_[keep]), f"{k}: non-block rows changed"
+    for k in ("m", "l", "o_acc"):
+        assert torch.equal(getattr(dw.ct, k), snap[k]), f"{k}: FACache was written by a block step"
+
+
+def test_block_covering_the_whole_sequence():
+    """No invariant rows (N = B): the step is plain attention over the block."""
+    wl = synth.custom("u_empty", dtype="bf16", d_model=512, n_heads=4, head_dim=128, vocab=300,
+                      prompt_lens=(0, 0), gen_len=32, block_size=32, block_idx=(0, 0), steps=1, seed=34)
+    _run_full(wl, 1)
+
+
+def test_out_of_range_token_id_reads_zero_row_and_sets_flag():
+    wl = synth.custom("bad_id", dtype="f32", d_model=256, n_heads=4, head_dim=64, vocab=100,
+                      prompt_lens=(20,), gen_len=16, block_size=16, block_idx=(0,), steps=1, embed_std=0.02, seed=35)
+    dw = DeviceWorkload(wl)
+    dw.prefill()
+    assert dw.ctx.read_device_status() == 0
+    blk = dw.next_block_ids()
+    bad = blk.clone()
+    bad[3] = wl.vocab + 5
+    dw.block_step(bad)
+    flags = dw.ctx.read_device_status()
+    assert flags & lacache.DEVFLAG_BAD_TOKEN_ID
+    assert dw.ctx.read_device_status() == 0          # reading clears the word
+    off, n, bs, be = dw.table[0]
+    assert torch.count_nonzero(dw.ct.h[off + bs + 3]) == 0
+    assert torch.count_nonzero(dw.ct.q[off + bs + 3]) == 0
+    assert torch.isfinite(dw.ct.out).all()
+
+
+def test_invalid_arguments_are_rejected_before_any_launch():
+    wl = synth.WORKLOADS["tiny"]
+    dw = DeviceWorkload(wl)
+    dw.prefill()
+    torch.cuda.synchronize()
+    before = dw.ct.out.clone()
+    blk = dw.next_block_ids()
+    bad_tables = [
+        [(0, 128, 80, 80)],          # empty block
+        [(0, 128, 90, 80)],          # block_end < block_start
+        [(0, 128, 80, 129)],         # block past the sequence
+        [(0, 129, 80, 96)],          # rows past n_rows / max_seq_len
+        [(-1, 128, 80, 96)],         # negative offset
+        [(0, 64, 0, 16), (32, 64, 32, 48)],   # overlapping samples
+        [(0, 128, 0, 129)],
+    ]
+    for t in bad_tables:
+        with pytest.raises(lacache.LaCacheError) as ei:
+            dw.ctx.block_step(dw.weights, blk, t, dw.ct, dw.ws)
+        assert ei.value.status in (lacache.ERR_INVALID_ARG, lacache.ERR_UNSUPPORTED), t
+    with pytest.raises(lacache.LaCacheError) as ei:
+        dw.ctx.block_step(dw.weights, blk, dw.table, dw.ct, None)
+    assert ei.value.status == lacache.ERR_WORKSPACE
+    with pytest.raises(lacache.LaCacheError) as ei:
+        dw.ctx.block_step(dw.weights, blk, [(0, 160, 0, 160)], dw.ct, dw.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(before, dw.ct.out), "a rejected call wrote the output"
