@@ -139,15 +139,17 @@ hipEvent_t take_event(lacache_ctx *ctx) {
   return e;
 }
 
-// Runs `launch` (returning hipError_t), bracketed by events when profiling.
+// Runs `launch(events)` (returning hipError_t); when profiling, the launch
+// carries a start/stop event pair stamped by the dispatch itself.
 template <typename F> hipError_t timed(lacache_ctx *ctx, int kernel, hipStream_t s, F &&launch) {
-  if (!ctx->profiling) return launch();
-  hipEvent_t a = take_event(ctx), b = take_event(ctx);
-  if (!a || !b) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(a, s);
-  if (e == hipSuccess) e = launch();
-  if (e == hipSuccess) e = hipEventRecord(b, s);
-  if (e == hipSuccess) ctx->marks.push_back({kernel, a, b});
+  (void)s;
+  if (!ctx->profiling) return launch(lc::LaunchEvents{});
+  lc::LaunchEvents ev;
+  ev.start = take_event(ctx);
+  ev.stop = take_event(ctx);
+  if (!ev.start || !ev.stop) return hipErrorOutOfMemory;
+  hipError_t e = launch(ev);
+  if (e == hipSuccess) ctx->marks.push_back({kernel, ev.start, ev.stop});
   return e;
 }
 
@@ -329,7 +331,7 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
     }
     lc::QkvArgs qa = qkv_args(ctx, w, cache, ids, 1);
     qa.M = sa.pre[0][ns];
-    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV, s, [&] { return lc::launch_qkv(dt, sa, qa, features(ctx), s); });
+    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv(dt, sa, qa, features(ctx), s, ev); });
     if (e != hipSuccess) return hip_fail(ctx, "prefill qkv launch", e);
 
     lc::AttnArgs aa;
@@ -347,7 +349,7 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
     aa.split_keys = ctx->split_keys;
     aa.scale_log2 = scale_log2(ctx);
     e = timed(ctx, LACACHE_KERNEL_REFRESH_ATTN, s,
-              [&] { return lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s); });
+              [&](const lc::LaunchEvents &ev) { return lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev); });
     if (e != hipSuccess) return hip_fail(ctx, "refresh attention launch", e);
   }
   return LACACHE_OK;
@@ -402,7 +404,7 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     lc::QkvArgs qa = qkv_args(ctx, w, cache, block_ids, 0);
     qa.M = M;
     qa.ids_base = row_base;
-    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV, s, [&] { return lc::launch_qkv(dt, sa, qa, features(ctx), s); });
+    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv(dt, sa, qa, features(ctx), s, ev); });
     if (e != hipSuccess) return hip_fail(ctx, "block-step qkv launch", e);
 
     lc::AttnArgs aa;
@@ -426,11 +428,11 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     aa.split_keys = ctx->split_keys;
     aa.scale_log2 = scale_log2(ctx);
     aa.nA = sa.pre[1][ns] * H;
-    e = timed(ctx, LACACHE_KERNEL_STEP_ATTN, s, [&] {
-      return lc::launch_step_attn(dt, dh, sa, aa, (sa.pre[1][ns] + sa.pre[2][ns]) * H, s);
+    e = timed(ctx, LACACHE_KERNEL_STEP_ATTN, s, [&](const lc::LaunchEvents &ev) {
+      return lc::launch_step_attn(dt, dh, sa, aa, (sa.pre[1][ns] + sa.pre[2][ns]) * H, s, ev);
     });
     if (e != hipSuccess) return hip_fail(ctx, "block-step attention launch", e);
-    e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&] { return lc::launch_merge(dt, dh, sa, aa, M, s); });
+    e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
     if (e != hipSuccess) return hip_fail(ctx, "block-step merge launch", e);
     row_base += M;
     part_base += sa.pre[3][ns];
@@ -485,9 +487,9 @@ lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *q_block, con
     aa.split_keys = ctx->split_keys;
     aa.scale_log2 = scale_log2(ctx);
     aa.nA = sa.pre[1][ns] * H;
-    hipError_t e = timed(ctx, LACACHE_KERNEL_DUAL_ATTN, s, [&] { return lc::launch_block_attn(dt, dh, sa, aa, aa.nA, s); });
+    hipError_t e = timed(ctx, LACACHE_KERNEL_DUAL_ATTN, s, [&](const lc::LaunchEvents &ev) { return lc::launch_block_attn(dt, dh, sa, aa, aa.nA, s, ev); });
     if (e != hipSuccess) return hip_fail(ctx, "dualcache attention launch", e);
-    e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&] { return lc::launch_merge(dt, dh, sa, aa, M, s); });
+    e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
     if (e != hipSuccess) return hip_fail(ctx, "dualcache merge launch", e);
     row_base += M;
     part_base += sa.pre[3][ns];

@@ -557,36 +557,39 @@ template <typename T, int DH> constexpr size_t refresh_smem() {
     }                                                                                    \
   } while (0)
 
-hipError_t launch_step_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s) {
+hipError_t launch_step_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
+                            const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
   int bmax = 0;
   for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
   if (bmax <= 32)
-    LC_DISPATCH(dt, dh, (step_attn_kernel<T, TO, DH, 32><<<n_blocks, 256, step_smem<T, DH>(), s>>>(sa, a)));
+    LC_DISPATCH(dt, dh, (lc_launch(step_attn_kernel<T, TO, DH, 32>, dim3(n_blocks), dim3(256), step_smem<T, DH>(), s, ev, sa, a)));
   else if (bmax <= 64)
-    LC_DISPATCH(dt, dh, (step_attn_kernel<T, TO, DH, 64><<<n_blocks, 256, step_smem<T, DH>(), s>>>(sa, a)));
+    LC_DISPATCH(dt, dh, (lc_launch(step_attn_kernel<T, TO, DH, 64>, dim3(n_blocks), dim3(256), step_smem<T, DH>(), s, ev, sa, a)));
   else
-    LC_DISPATCH(dt, dh, (step_attn_kernel<T, TO, DH, 128><<<n_blocks, 256, step_smem<T, DH>(), s>>>(sa, a)));
+    LC_DISPATCH(dt, dh, (lc_launch(step_attn_kernel<T, TO, DH, 128>, dim3(n_blocks), dim3(256), step_smem<T, DH>(), s, ev, sa, a)));
   return hipGetLastError();
 }
 
-hipError_t launch_block_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s) {
+hipError_t launch_block_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
+                             const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
-  LC_DISPATCH(dt, dh, (block_attn_kernel<T, TO, DH><<<n_blocks, 256, step_smem<T, DH>(), s>>>(sa, a)));
+  LC_DISPATCH(dt, dh, (lc_launch(block_attn_kernel<T, TO, DH>, dim3(n_blocks), dim3(256), step_smem<T, DH>(), s, ev, sa, a)));
   return hipGetLastError();
 }
 
-hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int M, hipStream_t s) {
+hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int M, hipStream_t s,
+                        const LaunchEvents &ev) {
   const int waves = M * a.H;
   if (waves <= 0) return hipSuccess;
-  LC_DISPATCH(dt, dh, (merge_kernel<T, TO, DH><<<(waves + 3) / 4, 256, 0, s>>>(sa, a, M)));
+  LC_DISPATCH(dt, dh, (lc_launch(merge_kernel<T, TO, DH>, dim3((waves + 3) / 4), dim3(256), 0, s, ev, sa, a, M)));
   return hipGetLastError();
 }
 
 hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
-                               hipStream_t s) {
+                               hipStream_t s, const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
-  LC_DISPATCH(dt, dh, (refresh_attn_kernel<T, TO, DH><<<n_blocks, 256, refresh_smem<T, DH>(), s>>>(sa, a)));
+  LC_DISPATCH(dt, dh, (lc_launch(refresh_attn_kernel<T, TO, DH>, dim3(n_blocks), dim3(256), refresh_smem<T, DH>(), s, ev, sa, a)));
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // launchers (qkv.hip, attn.hip).  Plain pointers and sizes only.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,15 +49,33 @@ struct AttnArgs {
   float scale_log2;        // sm_scale * log2(e)
 };
 
+// Optional timing events attached to a launch: when set, the kernel is
+// dispatched with hipExtLaunchKernelGGL, which stamps the events with the
+// dispatch's own start and end times.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Launch one kernel on stream s, with events if requested.
+template <typename... KArgs, typename... Args>
+inline void lc_launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned shmem, hipStream_t s,
+                      const LaunchEvents &ev, Args... args) {
+  if (ev.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
+
 // Launchers: return hipSuccess or the launch error.
-hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipStream_t s);
+hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_step_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
-                            hipStream_t s);
+                            hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_block_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
-                             hipStream_t s);
-hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int M, hipStream_t s);
+                             hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int M, hipStream_t s,
+                        const LaunchEvents &ev);
 hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
-                               hipStream_t s);
+                               hipStream_t s, const LaunchEvents &ev);
 hipError_t setup_kernel_attributes();
 
 // Work decomposition shared by the planner and the kernels.

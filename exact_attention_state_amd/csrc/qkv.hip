@@ -260,14 +260,14 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
   }
 }
 
-hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipStream_t s) {
+hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipStream_t s, const LaunchEvents &ev) {
   if (a.M <= 0) return hipSuccess;
   const int ncb = F / 16;
   dim3 grid((ncb + kQkvNB - 1) / kQkvNB, (a.M + kQkvRows - 1) / kQkvRows);
   dim3 block(64 * kQkvWaves);
   const int steps_per_wave = a.D / kQkvWaves / 32;
 #define LC_QKV(TP, TC, SPLIT, U, NG) \
-  qkv_fused_kernel<TP, TC, kQkvNB, kQkvWaves, SPLIT, U, NG><<<grid, block, 0, s>>>(sa, a)
+  lc_launch(qkv_fused_kernel<TP, TC, kQkvNB, kQkvWaves, SPLIT, U, NG>, grid, block, 0, s, ev, sa, a)
   if (dt == kBF16) {
     switch (steps_per_wave) {
       case 2: LC_QKV(bf16_t, f16_t, true, 2, 1); break;

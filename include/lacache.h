@@ -218,8 +218,8 @@ LACACHE_API lacache_status lacache_read_device_status(lacache_ctx *ctx, void *st
                                           uint32_t *flags);
 
 /* Optional per-kernel timing (diagnostics, off by default).  While enabled,
- * every kernel launch of this context is bracketed by two HIP events on the
- * call's stream.  lacache_profile_read synchronises those events and returns,
+ * every kernel launch of this context carries two HIP events that the
+ * dispatch itself stamps with its start and end (hipExtLaunchKernelGGL).  lacache_profile_read synchronises those events and returns,
  * for one kernel class, the summed event time in milliseconds and the number
  * of launches since the last read of that class (then resets that class). */
 typedef enum {
