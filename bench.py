@@ -58,8 +58,8 @@ def parse():
 
 KERNEL_SOURCES = {
     "qkv": ["exact_attention_state_amd/csrc/qkv.hip"],
-    "step_attn": ["exact_attention_state_amd/csrc/attn.hip"],
-    "merge": ["exact_attention_state_amd/csrc/attn.hip"],
+    "block_rows": ["exact_attention_state_amd/csrc/attn.hip"],
+    "invariant_rows": ["exact_attention_state_amd/csrc/attn.hip"],
 }
 COMMON_SOURCES = ["exact_attention_state_amd/csrc/common.h", "exact_attention_state_amd/csrc/internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llada8b_step.json")
@@ -99,26 +99,36 @@ def copy_calibration():
 
 
 def step_accounting(wl):
-    """Work and algorithmic HBM bytes of one block step of workload `wl`."""
-    s = 2 if wl.dtype == "bf16" else 4
+    """Work and algorithmic HBM bytes of one block step of workload `wl`, per kernel.
+
+    Algorithmic bytes are what the step must move at least: W_qkv, gamma, the
+    block rows' embedding rows and Q/K/V/h writes (qkv); Q of the block rows,
+    K and V of every key, O and LSE of the block rows (block_rows, whose merge
+    runs in the next kernel); Q and the FACache state (m, l, O~/l) of the
+    invariant rows, their O and LSE (invariant_rows).  The split-KV partials
+    are not counted: they are an artefact of the kernel split.
+    """
+    s = 2 if wl.dtype == "bf16" else 4          # parameter / output bytes
+    c = 2 if wl.dtype == "bf16" else 4          # cache (ctype) bytes
     D, H, Hk, d, F = wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.n_features
     M = sum(be - bs for (_, _, bs, be) in wl.table())
-    pairs_c = pairs_e = 0
-    attn_bytes = attn_flops = 0
+    pairs_c = pairs_e = pairs_a = pairs_b = 0
+    a_bytes = b_bytes = 0
     for (_, n, bs, be) in wl.table():
         B = be - bs
         U = n - B
-        pairs_c += H * (B * n + U * B)
+        pairs_a += H * B * n
+        pairs_b += H * U * B
         pairs_e += H * n * n
-        # block rows: Q_C, all K/V of the sample, O and LSE of the block rows
-        attn_bytes += B * H * d * s + 2 * n * Hk * d * s + B * H * d * s + B * H * 4
-        # invariant rows: Q_U, FACache (m, l, O~ fp32), O and LSE
-        attn_bytes += U * H * d * s + U * H * (2 + d) * 4 + U * H * d * s + U * H * 4
-    attn_flops = 4 * d * pairs_c
-    qkv_bytes = F * D * s + 2 * M * D * s + D * s + M * F * s + M * 4
-    qkv_flops = 2 * M * F * D
-    return dict(M=M, pairs_computed=pairs_c, pairs_equiv=pairs_e, qkv_bytes=qkv_bytes, qkv_flops=qkv_flops,
-                attn_bytes=attn_bytes, attn_flops=attn_flops)
+        a_bytes += B * H * d * c + 2 * n * Hk * d * c + B * H * d * s + B * H * 4
+        b_bytes += U * H * d * c + U * H * (2 * 4 + d * c) + U * H * d * s + U * H * 4
+    pairs_c = pairs_a + pairs_b
+    qkv_bytes = F * D * s + 2 * M * D * s + D * s + M * F * c + M * 4
+    kern = {"qkv": dict(bytes=qkv_bytes, flops=2 * M * F * D),
+            "block_rows": dict(bytes=a_bytes, flops=4 * d * pairs_a),
+            "invariant_rows": dict(bytes=b_bytes, flops=4 * d * pairs_b)}
+    return dict(M=M, pairs_computed=pairs_c, pairs_equiv=pairs_e, kernels=kern,
+                qkv_bytes=qkv_bytes, attn_bytes=a_bytes + b_bytes)
 
 
 def cpu_baseline(wl, budget_s):
@@ -302,10 +312,7 @@ def main():
     # Roofline of the dominant kernel.
     dom = max(kern, key=lambda k: kern[k]["ms_total"])
     t_dom = kern[dom]["us_avg"] * 1e-6
-    if dom == "qkv":
-        flops, nbytes = acc["qkv_flops"], acc["qkv_bytes"]
-    else:
-        flops, nbytes = acc["attn_flops"], acc["attn_bytes"]
+    flops, nbytes = acc["kernels"][dom]["flops"], acc["kernels"][dom]["bytes"]
     peak_flops = (MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS) * 1e12
     ridge = peak_flops / (HBM_PEAK_GBS * 1e9)
     if flops / nbytes < ridge:
@@ -348,6 +355,8 @@ def main():
         "us_per_step_graph": None if ms_graph is None else ms_graph * 1e3,
         "us_per_step_warm_eager": ms_warm * 1e3,
         "kernels_us_avg": {k: v["us_avg"] for k, v in kern.items()},
+        "kernels_hbm_frac": {k: acc["kernels"][k]["bytes"] / (v["us_avg"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+                             for k, v in kern.items() if k in acc["kernels"]},
         "kernel_source_sha256": {k: kernel_source_hash(k) for k in kern},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -23,9 +23,9 @@ struct lacache_ctx {
   int device;
   float2 *rope;
   unsigned *flags;
-  int split_keys;
+  int split_keys;          // keys per type-A chunk if fixed by LACACHE_SPLIT_KEYS, else 0 (per call)
   std::string last_error;
-  // Diagnostics: event pairs bracketing each launch while profiling is on.
+  // Diagnostics: event pairs stamped by each launch while profiling is on.
   bool profiling = false;
   struct Mark { int kernel; hipEvent_t start, stop; };
   std::vector<Mark> marks;
@@ -99,20 +99,55 @@ lacache_status check_table(lacache_ctx *ctx, const lacache_seq *seqs, int32_t ba
   return LACACHE_OK;
 }
 
-int nchunks(const lacache_ctx *ctx, int len) { return (len + ctx->split_keys - 1) / ctx->split_keys; }
+int nchunks(int split, int len) { return (len + split - 1) / split; }
 
-int64_t partial_rows(const lacache_ctx *ctx, const lacache_seq *seqs, int32_t batch) {
+// Keys per type-A chunk for a batch: one 128-key tile per workgroup while
+// that leaves at most ~4 workgroups per CU; longer chunks (and fewer partial
+// rows to merge) beyond that.  LACACHE_SPLIT_KEYS (a multiple of 32) fixes it.
+int split_keys(const lacache_ctx *ctx, const lacache_seq *seqs, int32_t batch) {
+  if (ctx->split_keys > 0) return ctx->split_keys;
+  auto items = [&](int split) {
+    int64_t n = 0;
+    for (int i = 0; i < batch; ++i) {
+      const int B = seqs[i].block_end - seqs[i].block_start;
+      n += (int64_t)nchunks(split, seqs[i].seq_len) * ((B + lc::kRowsA - 1) / lc::kRowsA);
+    }
+    return n * ctx->cfg.n_heads;
+  };
+  int max_len = 1;
+  for (int i = 0; i < batch; ++i) max_len = std::max(max_len, seqs[i].seq_len);
+  int split = 128;
+  while (split < max_len && items(2 * split) >= 1024) split *= 2;
+  return split;
+}
+
+int64_t partial_rows(int split, const lacache_seq *seqs, int32_t batch) {
   int64_t p = 0;
-  for (int i = 0; i < batch; ++i) p += (int64_t)nchunks(ctx, seqs[i].seq_len) * (seqs[i].block_end - seqs[i].block_start);
+  for (int i = 0; i < batch; ++i) p += (int64_t)nchunks(split, seqs[i].seq_len) * (seqs[i].block_end - seqs[i].block_start);
   return p;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace layout for type-A partials: part_ml [P, H] float2, part_o [P, H, d_h] float.
+size_t cache_elem_bytes(const lacache_ctx *ctx) { return ctx->cfg.dtype == LACACHE_BF16 ? 2 : 4; }
+
+// Workspace layout for type-A partials: part_ml [P, H] float2, part_o [P, H, d_h] in the cache type.
+struct Partials {
+  float2 *ml;
+  void *o;
+};
 size_t partial_bytes(const lacache_ctx *ctx, int64_t P) {
   const size_t H = ctx->cfg.n_heads, d = ctx->cfg.head_dim;
-  return align256((size_t)P * H * sizeof(float2)) + align256((size_t)P * H * d * sizeof(float));
+  return align256((size_t)P * H * sizeof(float2)) + align256((size_t)P * H * d * cache_elem_bytes(ctx));
+}
+Partials partial_layout(const lacache_ctx *ctx, void *ws, int64_t P) {
+  const size_t H = ctx->cfg.n_heads, d = ctx->cfg.head_dim;
+  char *p = static_cast<char *>(ws);
+  Partials r;
+  r.ml = reinterpret_cast<float2 *>(p);
+  p += align256((size_t)P * H * sizeof(float2));
+  r.o = p;
+  return r;
 }
 
 lc::SeqArgs slice_args(const lacache_seq *seqs, int s0, int ns) {
@@ -166,8 +201,8 @@ lacache_status hip_fail(lacache_ctx *ctx, const char *what, hipError_t e) {
 
 lacache_status check_cache(lacache_ctx *ctx, const lacache_cache *c, bool facache) {
   if (!c) return fail(ctx, LACACHE_ERR_INVALID_ARG, "cache is NULL");
-  const void *ptrs[7] = {c->h, c->q, c->k, c->v, c->m, c->l, c->o_acc};
-  const char *names[7] = {"h", "q", "k", "v", "m", "l", "o_acc"};
+  const void *ptrs[7] = {c->h, c->q, c->k, c->v, c->m, c->l, c->o};
+  const char *names[7] = {"h", "q", "k", "v", "m", "l", "o"};
   for (int i = 0; i < (facache ? 7 : 4); ++i) {
     if (!ptrs[i]) return fail(ctx, LACACHE_ERR_INVALID_ARG, "cache.%s is NULL", names[i]);
     if (!aligned16(ptrs[i])) return fail(ctx, LACACHE_ERR_INVALID_ARG, "cache.%s is not 16-byte aligned", names[i]);
@@ -243,7 +278,7 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   ctx->cfg = c;
   ctx->rope = nullptr;
   ctx->flags = nullptr;
-  ctx->split_keys = 256;
+  ctx->split_keys = 0;
   if (const char *env = std::getenv("LACACHE_SPLIT_KEYS")) {
     const int v = std::atoi(env);
     if (v >= 32 && v % 32 == 0) ctx->split_keys = v;
@@ -300,7 +335,9 @@ lacache_status lacache_workspace_size(const lacache_ctx *cctx, int32_t op, const
   switch (op) {
     case LACACHE_OP_PREFILL: *bytes = 0; return LACACHE_OK;
     case LACACHE_OP_BLOCK_STEP:
-    case LACACHE_OP_DUALCACHE_ATTN: *bytes = partial_bytes(ctx, partial_rows(ctx, seqs, batch)); return LACACHE_OK;
+    case LACACHE_OP_DUALCACHE_ATTN:
+      *bytes = partial_bytes(ctx, partial_rows(split_keys(ctx, seqs, batch), seqs, batch));
+      return LACACHE_OK;
   }
   return fail(ctx, LACACHE_ERR_INVALID_ARG, "unknown op %d", op);
 }
@@ -343,10 +380,9 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
     aa.lse = lse;
     aa.m_w = cache->m;
     aa.l_w = cache->l;
-    aa.o_w = cache->o_acc;
+    aa.o_w = cache->o;
     aa.H = H;
     aa.Hkv = ctx->cfg.n_kv_heads;
-    aa.split_keys = ctx->split_keys;
     aa.scale_log2 = scale_log2(ctx);
     e = timed(ctx, LACACHE_KERNEL_REFRESH_ATTN, s,
               [&](const lc::LaunchEvents &ev) { return lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev); });
@@ -358,10 +394,10 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
 namespace {
 
 // Type-A items (block rows x key chunks) and partial rows of each sample.
-void plan_block_rows(const lacache_ctx *ctx, lc::SeqArgs &sa) {
+void plan_block_rows(int split, lc::SeqArgs &sa) {
   for (int i = 0; i < sa.n; ++i) {
     const int B = sa.be[i] - sa.bs[i];
-    const int nch = nchunks(ctx, sa.len[i]);
+    const int nch = nchunks(split, sa.len[i]);
     sa.pre[0][i + 1] = sa.pre[0][i] + B;
     sa.pre[1][i + 1] = sa.pre[1][i] + nch * ((B + lc::kRowsA - 1) / lc::kRowsA);
     sa.pre[3][i + 1] = sa.pre[3][i] + nch * B;
@@ -381,7 +417,8 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
   if (!block_ids) return fail(ctx, LACACHE_ERR_INVALID_ARG, "block_ids is NULL");
   if (!out || !aligned16(out)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
   if ((st = check_table(ctx, seqs, batch, cache->n_rows)) != LACACHE_OK) return st;
-  const int64_t P = partial_rows(ctx, seqs, batch);
+  const int split = split_keys(ctx, seqs, batch);
+  const int64_t P = partial_rows(split, seqs, batch);
   const size_t need = partial_bytes(ctx, P);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
@@ -389,14 +426,13 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lc::DType dt = dtype_of(ctx);
   const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads;
-  float2 *part_ml = static_cast<float2 *>(workspace);
-  float *part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)P * H * sizeof(float2)));
+  const Partials part = partial_layout(ctx, workspace, P);
 
   int row_base = 0, part_base = 0;
   for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
     const int ns = std::min(kMaxInline, batch - s0);
     lc::SeqArgs sa = slice_args(seqs, s0, ns);
-    plan_block_rows(ctx, sa);
+    plan_block_rows(split, sa);
     for (int i = 0; i < ns; ++i)
       sa.pre[2][i + 1] = sa.pre[2][i] + (sa.len[i] - (sa.be[i] - sa.bs[i]) + lc::kRowsB - 1) / lc::kRowsB;
     const int M = sa.pre[0][ns];
@@ -416,24 +452,25 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     aa.lse = lse;
     aa.m_c = cache->m;
     aa.l_c = cache->l;
-    aa.o_c = cache->o_acc;
-    aa.part_ml = part_ml;
-    aa.part_o = part_o;
+    aa.o_c = cache->o;
+    aa.part_ml = part.ml;
+    aa.part_o = part.o;
     aa.qmode = 0;
     aa.omode = 0;
     aa.row_base = row_base;
     aa.part_base = part_base;
     aa.H = H;
     aa.Hkv = ctx->cfg.n_kv_heads;
-    aa.split_keys = ctx->split_keys;
+    aa.split_keys = split;
     aa.scale_log2 = scale_log2(ctx);
-    aa.nA = sa.pre[1][ns] * H;
-    e = timed(ctx, LACACHE_KERNEL_STEP_ATTN, s, [&](const lc::LaunchEvents &ev) {
-      return lc::launch_step_attn(dt, dh, sa, aa, (sa.pre[1][ns] + sa.pre[2][ns]) * H, s, ev);
+    e = timed(ctx, LACACHE_KERNEL_BLOCK_ROWS, s, [&](const lc::LaunchEvents &ev) {
+      return lc::launch_block_rows(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
     });
-    if (e != hipSuccess) return hip_fail(ctx, "block-step attention launch", e);
-    e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
-    if (e != hipSuccess) return hip_fail(ctx, "block-step merge launch", e);
+    if (e != hipSuccess) return hip_fail(ctx, "block-step block-rows launch", e);
+    e = timed(ctx, LACACHE_KERNEL_INVARIANT_ROWS, s, [&](const lc::LaunchEvents &ev) {
+      return lc::launch_invariant_rows(dt, dh, sa, aa, sa.pre[2][ns] * H, M, s, ev);
+    });
+    if (e != hipSuccess) return hip_fail(ctx, "block-step invariant-rows launch", e);
     row_base += M;
     part_base += sa.pre[3][ns];
   }
@@ -452,7 +489,8 @@ lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *q_block, con
     return fail(ctx, LACACHE_ERR_INVALID_ARG, "q_block, k, v and out_block must be 16-byte aligned");
   if (n_rows < 1) return fail(ctx, LACACHE_ERR_INVALID_ARG, "n_rows must be >= 1");
   if ((st = check_table(ctx, seqs, batch, n_rows)) != LACACHE_OK) return st;
-  const int64_t P = partial_rows(ctx, seqs, batch);
+  const int split = split_keys(ctx, seqs, batch);
+  const int64_t P = partial_rows(split, seqs, batch);
   const size_t need = partial_bytes(ctx, P);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
@@ -460,14 +498,13 @@ lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *q_block, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lc::DType dt = dtype_of(ctx);
   const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads;
-  float2 *part_ml = static_cast<float2 *>(workspace);
-  float *part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)P * H * sizeof(float2)));
+  const Partials part = partial_layout(ctx, workspace, P);
 
   int row_base = 0, part_base = 0;
   for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
     const int ns = std::min(kMaxInline, batch - s0);
     lc::SeqArgs sa = slice_args(seqs, s0, ns);
-    plan_block_rows(ctx, sa);
+    plan_block_rows(split, sa);
     const int M = sa.pre[0][ns];
     lc::AttnArgs aa;
     std::memset(&aa, 0, sizeof(aa));
@@ -476,18 +513,19 @@ lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *q_block, con
     aa.v = v;
     aa.out = out_block;
     aa.lse = lse_block;
-    aa.part_ml = part_ml;
-    aa.part_o = part_o;
+    aa.part_ml = part.ml;
+    aa.part_o = part.o;
     aa.qmode = 1;
     aa.omode = 1;
     aa.row_base = row_base;
     aa.part_base = part_base;
     aa.H = H;
     aa.Hkv = ctx->cfg.n_kv_heads;
-    aa.split_keys = ctx->split_keys;
+    aa.split_keys = split;
     aa.scale_log2 = scale_log2(ctx);
-    aa.nA = sa.pre[1][ns] * H;
-    hipError_t e = timed(ctx, LACACHE_KERNEL_DUAL_ATTN, s, [&](const lc::LaunchEvents &ev) { return lc::launch_block_attn(dt, dh, sa, aa, aa.nA, s, ev); });
+    hipError_t e = timed(ctx, LACACHE_KERNEL_BLOCK_ROWS, s, [&](const lc::LaunchEvents &ev) {
+      return lc::launch_block_rows(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
+    });
     if (e != hipSuccess) return hip_fail(ctx, "dualcache attention launch", e);
     e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
     if (e != hipSuccess) return hip_fail(ctx, "dualcache merge launch", e);

@@ -3,77 +3,188 @@
 //
 // All of them share one 32-key step on MFMA (attend_step):
 //   S^T = K Q^T       A = 16 keys x 32 head-dim slots, B = Q^T; the key rows
-//                     of a block are loaded in an order that leaves lane group
+//                     of a step are loaded in an order that leaves lane group
 //                     g holding keys 8g..8g+7 of the step in the result.
 //   online softmax    per query row (lane%16), max shared by the 4 lane
 //                     groups, scores in log2 units so exp is v_exp_f32.
-//   O^T += V^T P^T    A = V^T read from LDS (V is transposed while staged),
-//                     B = P^T straight from the softmax registers; the result
-//                     keeps each query row in one lane, so the per-row rescale
-//                     is lane-local.
-// K fragments are read straight from HBM (16 or 32 contiguous bytes per lane,
-// full 128-byte lines per instruction); only V goes through LDS.
+//   O^T += V^T P^T    A = V^T read from LDS, B = P^T straight from the
+//                     softmax registers; the result keeps each query row in
+//                     one lane, so the per-row rescale is lane-local.
+// K fragments are read straight from HBM; only V goes through LDS.  Every
+// work item issues all of its global loads before its first wait, and its
+// workgroup barriers order LDS traffic only, so one item costs one memory
+// round trip per key tile.
 //
-// Work items (one workgroup of 4 waves each, times the head count):
+// Work items (one workgroup of 4 waves each, times the head count); the
+// block step runs type A, then type B together with the merge:
 //   type A  block rows (<= 32) of one sample against one chunk of its keys
-//           [prefix | fresh block | suffix]; the 4 waves take alternate 32-key
-//           steps and merge their states in LDS; the chunk's (m, l, O~) goes to
-//           the workspace (split-KV).  This is also the DualCache step.
+//           [prefix | fresh block | suffix]; wave w takes the w-th 32-key step
+//           of every 128-key tile for all 32 rows, and the 4 waves merge their
+//           states in LDS; the chunk's (m, l, O~/l) goes to the workspace
+//           (split-KV).  This is also the DualCache step.
 //   type B  64 invariant rows of one sample: the state starts from FACache and
 //           streams only the block's keys, then O = O~/l and LSE = m + ln l.
 //   merge   combines the type-A chunks of every block row into O and LSE.
 //   refresh 64 rows of one sample against every key: invariant keys first,
-//           a snapshot of (m, l, O~) into FACache for invariant rows, then the
-//           block's keys, then O and LSE.
+//           a snapshot of (m, l, O~/l) into FACache for invariant rows, then
+//           the block's keys, then O and LSE.
+//
+// FACache and the partials hold O~/l (the state's output, normalised) in the
+// cache type with l beside it: the state (m, l, O~) is restored exactly up to
+// that one rounding, at half the bytes of an fp32 O~ for 16-bit caches.
 
 #include "internal.h"
 
 namespace lc {
 
 // ---------------------------------------------------------------------------
+// Output slots.  In the P*V result of feature block db, lane (g, r16) slot v
+// holds query row r16 and feature OMap<DH>::feat(g, db, v):
+//   DH = 128: lane group g owns the 32 contiguous features 32g..32g+31, so a
+//             lane moves its part of a row with 16-byte accesses;
+//   DH = 64:  block db is features 16db..16db+15, 4 per lane group.
+// The V^T operand is read in the matching order (vtile_frag).
+// ---------------------------------------------------------------------------
+template <int DH> struct OMap {
+  static constexpr bool kWide = DH == 128;
+  static constexpr int NDB = DH / 16;
+  __device__ static constexpr int feat(int g, int db, int v) {
+    return kWide ? 32 * g + 4 * db + v : 16 * db + 4 * g + v;
+  }
+};
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float2 unpack2(f16_t, uint32_t u) {
+  const h2_t v = __builtin_bit_cast(h2_t, u);
+  return make_float2((float)v[0], (float)v[1]);
+}
+__device__ __forceinline__ float2 unpack2(bf16_t, uint32_t u) {
+  return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+}
+template <typename T> __device__ __forceinline__ f32x4_t unpack4(uint32_t lo, uint32_t hi) {
+  const float2 a = unpack2(T{}, lo), b = unpack2(T{}, hi);
+  return f32x4_t{a.x, a.y, b.x, b.y};
+}
+__device__ __forceinline__ uint32_t pack2(f16_t, float a, float b) {
+  const h2_t v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t pack2(bf16_t, float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// 4 consecutive elements <-> f32x4 (8-byte aligned for 16-bit types).
+template <typename T> __device__ __forceinline__ f32x4_t ld4(const T *p) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const f32x4_t *>(p);
+  } else {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    return unpack4<T>(u.x, u.y);
+  }
+}
+template <typename T> __device__ __forceinline__ void st4(T *p, f32x4_t x) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4_t *>(p) = x;
+  } else {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(pack2(T{}, x[0], x[1]), pack2(T{}, x[2], x[3]));
+  }
+}
+
+// This lane's features of one row: x[db][v] = row[feat(g, db, v)].
+template <typename T, int DH>
+__device__ __forceinline__ void load_row(f32x4_t (&x)[DH / 16], const T *row, int g) {
+  if constexpr (OMap<DH>::kWide && sizeof(T) == 2) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(row + 32 * g);
+#pragma unroll
+    for (int j = 0; j < DH / 32; ++j) {
+      const uint4 u = p[j];
+      x[2 * j] = unpack4<T>(u.x, u.y);
+      x[2 * j + 1] = unpack4<T>(u.z, u.w);
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db) x[db] = ld4(row + OMap<DH>::feat(g, db, 0));
+  }
+}
+
+// row[feat(g, db, v)] = x[db][v] * scale.
+template <typename T, int DH>
+__device__ __forceinline__ void store_row(T *row, const f32x4_t (&x)[DH / 16], float scale, int g) {
+  if constexpr (OMap<DH>::kWide && sizeof(T) == 2) {
+    uint4 *p = reinterpret_cast<uint4 *>(row + 32 * g);
+#pragma unroll
+    for (int j = 0; j < DH / 32; ++j) {
+      const f32x4_t a = x[2 * j] * scale, b = x[2 * j + 1] * scale;
+      p[j] = make_uint4(pack2(T{}, a[0], a[1]), pack2(T{}, a[2], a[3]), pack2(T{}, b[0], b[1]),
+                        pack2(T{}, b[2], b[3]));
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db) st4(row + OMap<DH>::feat(g, db, 0), x[db] * scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // V of up to MAXC keys staged in LDS, read back as the A operand of P*V (one
-// head-dim row, 8 consecutive keys per lane).
-//   16-bit types: V is kept row-major (key rows of DH + 16 elements; the pad
-//   puts 8 consecutive rows on disjoint bank groups) and written with 16-byte
-//   stores; the operand is read with ds_read_b64_tr_b16, which hands lane i
-//   of a 16-lane group element i%4 of the 8-byte chunks addressed by lanes
-//   4j + i/4 (j = 0..3).  Lane t of group g points at key 8g + t/4 (+4 for the
-//   second read), features 16*db + 4*(t%4): lane i then holds keys 8g..8g+7
-//   of feature 16*db + i.
-//   fp32: V is stored transposed, V^T[d][c], and read with plain loads.
+// feature block, 8 consecutive keys per lane).
+//   16-bit types: V is copied global -> LDS by the load unit itself
+//   (global_load_lds_dwordx4: lane l of an instruction fills 16 bytes at the
+//   wave's LDS base + 16 l), key rows of DH elements, their 16-byte pieces
+//   permuted within the row: piece p of key c sits in slot p ^ (c & 3).  The
+//   operand is read with ds_read_b64_tr_b16, which hands lane i of a 16-lane
+//   group element i%4 of the 8-byte chunks addressed by lanes 4j + i/4
+//   (j = 0..3).  Lane t of group g points at key 8g + t/4 (+4 for the second
+//   read) and the 4 features feat(t%4, db, 0..3): lane i then holds keys
+//   8g..8g+7 of feature feat(i/4, db, i%4), which is A row i.  The slot
+//   permutation puts the 16 lanes of one read on distinct banks.
+//   fp32: V is staged through registers and stored transposed, V^T[d][c]
+//   (rows of MAXC + 4), and read with plain loads.
 // ---------------------------------------------------------------------------
 template <typename T, int DH, int MAXC> struct VTile {
   static constexpr bool kTr = sizeof(T) == 2;
-  static constexpr int kStride = kTr ? DH + 16 : MAXC + 4;     // elements per LDS row
+  static constexpr int kStride = kTr ? DH : MAXC + 4;       // elements per LDS row
   static constexpr size_t kBytes = (size_t)(kTr ? MAXC : DH) * kStride * sizeof(T);
 };
 
 typedef __fp16 h4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) h4_t lds_h4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Global -> LDS copy, 16 bytes per lane, to the wave-uniform LDS address
+// `lds` + 16 * lane.  The builtin exists in the device pass only.
+__device__ __forceinline__ void load_lds16(const void *src, void *lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds, 16, 0, 0);
+#endif
+}
 
 template <typename T, int DH, int MAXC>
 __device__ __forceinline__ void vtile_frag(Frag<T> &f, const T *buf, int c0, int db, int lane) {
   using VT = VTile<T, DH, MAXC>;
   const int g = lane >> 4, r16 = lane & 15;
   if constexpr (VT::kTr) {
-    const T *p = buf + (size_t)(c0 + 8 * g + (r16 >> 2)) * VT::kStride + 16 * db + 4 * (r16 & 3);
+    const int c = c0 + 8 * g + (r16 >> 2);
+    const int fe = OMap<DH>::feat(r16 & 3, db, 0);
+    const T *p = buf + (size_t)c * DH + (((fe >> 3) ^ (c & 3)) << 3) + (fe & 4);
     const h4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4_t *)(p));
-    const h4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4_t *)(p + 4 * VT::kStride));
+    const h4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4_t *)(p + 4 * DH));
     typedef short s4_t __attribute__((ext_vector_type(4)));
     typedef short s8_t __attribute__((ext_vector_type(8)));
     const s4_t a = __builtin_bit_cast(s4_t, lo), b = __builtin_bit_cast(s4_t, hi);
     const s8_t v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     f.v = __builtin_bit_cast(decltype(f.v), v);
   } else {
-    frag_load(f, buf + (16 * db + r16) * VT::kStride + c0 + 8 * g);
+    frag_load(f, buf + OMap<DH>::feat(r16 >> 2, db, r16 & 3) * VT::kStride + c0 + 8 * g);
   }
 }
 
 // Stage MAXC keys starting at vbase; keys >= nvalid (>= 1) get a copy of key
 // nvalid-1 (finite values; their probabilities are zero).  NTHR threads
-// cooperate; consecutive threads take consecutive 16-byte pieces of one key
-// row.  Loads and stores are unconditional: any guard lets the compiler sink
-// each load next to its store and serialise the round trips.
+// cooperate.  16-bit types: the copies are in flight when this returns and
+// vtile_wait() (before the barrier that publishes the tile) completes them.
+// fp32: loads, then transposed stores (unconditional: any guard lets the
+// compiler sink each load next to its store and serialise the round trips).
 template <typename T, int DH, int MAXC, int NTHR>
 __device__ __forceinline__ void vtile_stage(T *buf, const T *vbase, size_t vstride, int nvalid, int t) {
   using VT = VTile<T, DH, MAXC>;
@@ -81,20 +192,29 @@ __device__ __forceinline__ void vtile_stage(T *buf, const T *vbase, size_t vstri
   constexpr int CPK = DH / EPC;                  // pieces per key row
   static_assert((MAXC * CPK) % NTHR == 0, "staging threads must tile the buffer");
   constexpr int ITER = MAXC * CPK / NTHR;
-  uint4 u[ITER];
+  if constexpr (VT::kTr) {
+    const int lane = t & 63, w = t >> 6;
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int idx = t + it * NTHR;
-    const int c = min(idx / CPK, nvalid - 1), ch = idx % CPK;
-    u[it] = *reinterpret_cast<const uint4 *>(vbase + (size_t)c * vstride + ch * EPC);
-  }
+    for (int it = 0; it < ITER; ++it) {
+      const int base = (it * (NTHR / 64) + w) * 64;        // first LDS slot of this wave's instruction
+      const int idx = base + lane;
+      const int c = idx / CPK, slot = idx % CPK;
+      const int piece = slot ^ (c & 3);
+      const T *src = vbase + (size_t)min(c, nvalid - 1) * vstride + piece * EPC;
+      load_lds16(src, buf + (size_t)base * EPC);
+    }
+  } else {
+    uint4 u[ITER];
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int idx = t + it * NTHR;
-    const int c = idx / CPK, ch = idx % CPK;
-    if constexpr (VT::kTr) {
-      *reinterpret_cast<uint4 *>(buf + (size_t)c * VT::kStride + ch * EPC) = u[it];
-    } else {
+    for (int it = 0; it < ITER; ++it) {
+      const int idx = t + it * NTHR;
+      const int c = min(idx / CPK, nvalid - 1), ch = idx % CPK;
+      u[it] = *reinterpret_cast<const uint4 *>(vbase + (size_t)c * vstride + ch * EPC);
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int idx = t + it * NTHR;
+      const int c = idx / CPK, ch = idx % CPK;
       const uint32_t wd[4] = {u[it].x, u[it].y, u[it].z, u[it].w};
       uint32_t *v32 = reinterpret_cast<uint32_t *>(buf);
 #pragma unroll
@@ -103,10 +223,16 @@ __device__ __forceinline__ void vtile_stage(T *buf, const T *vbase, size_t vstri
   }
 }
 
+// Completes this wave's global->LDS copies (and every other global load it
+// has in flight); a barrier must follow before other waves read the tile.
+__device__ __forceinline__ void vtile_wait() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0), expcnt and lgkmcnt untouched
+}
+
 template <int MB, int DH> struct AttnState {
   float m[MB];                 // running max, log2 units (same in the 4 lane groups)
   float l[MB];                 // this lane's share of the normaliser
-  f32x4_t o[MB][DH / 16];      // O~ of row lane%16, features 16*db + 4*g + i
+  f32x4_t o[MB][DH / 16];      // O~ of row lane%16, features feat(g, db, 0..3)
 };
 
 template <int MB, int DH> __device__ __forceinline__ void state_init_empty(AttnState<MB, DH> &st) {
@@ -161,24 +287,14 @@ __device__ __forceinline__ void load_k_step(KStep<T, DH> &kf, const T *kbase, si
   }
 }
 
-// One step of up to 32 keys with its key fragments already loaded; V of the
-// step is keys c0 .. c0+31 of the staged tile `vbuf`.  Keys >= nvalid are
-// masked; their staged V must be finite (the stager copies a valid key).
+// Online-softmax update and P*V of one step of up to 32 keys, from its
+// scores S^T (s[kb][mb]: key block kb, row block mb).  V of the step is keys
+// c0 .. c0+31 of the staged tile `vbuf`.  Keys >= nvalid are masked; their
+// staged V must be finite (the stager copies a valid key).
 template <typename T, int MB, int DH, int MAXC>
-__device__ __forceinline__ void attend_step_pre(AttnState<MB, DH> &st, const Frag<T> (&qf)[MB][DH / 32],
-                                                const KStep<T, DH> &kf, int nvalid, const T *vbuf, int c0,
-                                                float scale_log2, int lane) {
+__device__ __forceinline__ void softmax_pv(AttnState<MB, DH> &st, const f32x4_t (&s)[2][MB], int nvalid,
+                                           const T *vbuf, int c0, float scale_log2, int lane) {
   const int g = lane >> 4;
-  f32x4_t s[2][MB];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      s[kb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kd = 0; kd < DH / 32; ++kd) mma16(s[kb][mb], kf.f[kb][kd], qf[mb][kd]);
-    }
-  }
   Frag<T> pf[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -213,6 +329,25 @@ __device__ __forceinline__ void attend_step_pre(AttnState<MB, DH> &st, const Fra
   }
 }
 
+// One step of up to 32 keys with its key fragments and query fragments in
+// registers.
+template <typename T, int MB, int DH, int MAXC>
+__device__ __forceinline__ void attend_step_pre(AttnState<MB, DH> &st, const Frag<T> (&qf)[MB][DH / 32],
+                                                const KStep<T, DH> &kf, int nvalid, const T *vbuf, int c0,
+                                                float scale_log2, int lane) {
+  f32x4_t s[2][MB];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      s[kb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kd = 0; kd < DH / 32; ++kd) mma16(s[kb][mb], kf.f[kb][kd], qf[mb][kd]);
+    }
+  }
+  softmax_pv<T, MB, DH, MAXC>(st, s, nvalid, vbuf, c0, scale_log2, lane);
+}
+
 template <typename T, int MB, int DH, int MAXC>
 __device__ __forceinline__ void attend_step(AttnState<MB, DH> &st, const Frag<T> (&qf)[MB][DH / 32],
                                             const T *kbase, size_t kstride, int nvalid, const T *vbuf, int c0,
@@ -223,16 +358,54 @@ __device__ __forceinline__ void attend_step(AttnState<MB, DH> &st, const Frag<T>
 }
 
 // ---------------------------------------------------------------------------
+// Query rows staged in LDS (type A): row r of DH elements, its 16-byte piece
+// p in slot p ^ (r & SWZ), so that the 16 rows of one operand read fall on
+// distinct banks.  Filled with global -> LDS copies.
+// ---------------------------------------------------------------------------
+template <typename T, int DH> struct QTile {
+  static constexpr int EPC = 16 / (int)sizeof(T);        // elements per piece
+  static constexpr int PPR = DH / EPC;                   // pieces per row
+  static constexpr int SWZ = (PPR < 16 ? PPR : 16) - 1;
+};
+
+// B-operand fragment of Q^T: row `row`, head-dim step kd (the slot mapping
+// of load_q).
+template <typename T, int DH>
+__device__ __forceinline__ void qtile_frag(Frag<T> &f, const T *qbuf, int row, int kd, int g) {
+  using QT = QTile<T, DH>;
+  const int e0 = 64 * (kd >> 1) + 16 * g + 8 * (kd & 1);
+  const T *rp = qbuf + (size_t)row * DH;
+  if constexpr (sizeof(T) == 2) {
+    frag_load(f, rp + ((e0 / QT::EPC) ^ (row & QT::SWZ)) * QT::EPC);
+  } else {
+    const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(rp + ((e0 / 4) ^ (row & QT::SWZ)) * 4);
+    const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(rp + ((e0 / 4 + 1) ^ (row & QT::SWZ)) * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f.v[i] = lo[i];
+      f.v[4 + i] = hi[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Type A: 32 block rows x one key chunk -> partial state in the workspace.
-// Wave w takes row block w%2 and key half w/2 of every staged 128-key tile.
+// Per 128-key tile, wave w takes keys 32w..32w+31 for both 16-row blocks.
 // ---------------------------------------------------------------------------
 constexpr int kTileA = 128;     // keys staged in LDS per tile (type A, refresh)
 
+// LDS of the type-A state merge: per wave (m, l) of 32 rows, and the feature
+// blocks each wave hands to the three others.
+template <int DH> constexpr size_t merge_a_bytes() {
+  return 4 * 2 * 32 * sizeof(float) + (size_t)(DH / 16) * 3 * 2 * 64 * sizeof(f32x4_t);
+}
+
+
 template <typename T, typename TO, int DH>
 __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int item, int h, char *smem) {
+  constexpr int MB = 2, NDB = DH / 16, DPW = NDB / 4;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int rb = w & 1, kh = w >> 1;
 
   const int b = find_sample(sa.pre[1], sa.n, item);
   const int t = item - sa.pre[1][b];
@@ -244,80 +417,120 @@ __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int ite
   const int hk = h / (a.H / a.Hkv);
   const size_t kvstride = (size_t)a.Hkv * DH;
 
-  const int r = rg * kRowsA + rb * 16 + r16;
-  const bool qvalid1 = r < B;
-  const int rq = min(r, B - 1);
-  const int qrow_i = a.qmode == 0 ? sa.off[b] + sa.bs[b] + rq : a.row_base + sa.pre[0][b] + rq;
-  const T *qrow[1] = {static_cast<const T *>(a.q) + ((size_t)qrow_i * a.H + h) * DH};
-  Frag<T> qf[1][DH / 32];
-  load_q<T, 1, DH>(qf, qrow, g);
+  // The 32 query rows go to LDS once (rows past the block repeat its last
+  // row; their results are dropped); each wave reads the fragments of one
+  // head-dim step at a time.
+  using QT = QTile<T, DH>;
+  T *qbuf = reinterpret_cast<T *>(smem);
+  T *vbuf = qbuf + kRowsA * DH;
+  {
+    const int qrow0 = a.qmode == 0 ? sa.off[b] + sa.bs[b] : a.row_base + sa.pre[0][b];
+#pragma unroll
+    for (int it = 0; it < kRowsA * QT::PPR / 256; ++it) {
+      const int base = (it * 4 + w) * 64;
+      const int idx = base + lane;
+      const int r = idx / QT::PPR, slot = idx % QT::PPR;
+      const int rq = min(rg * kRowsA + r, B - 1);
+      const T *src = static_cast<const T *>(a.q) + ((size_t)(qrow0 + rq) * a.H + h) * DH +
+                     (slot ^ (r & QT::SWZ)) * QT::EPC;
+      load_lds16(src, qbuf + (size_t)base * QT::EPC);
+    }
+  }
 
-  AttnState<1, DH> st;
+  AttnState<MB, DH> st;
   state_init_empty(st);
-  T *vbuf = reinterpret_cast<T *>(smem);
   const T *kbase0 = static_cast<const T *>(a.k) + ((size_t)(sa.off[b] + key0)) * kvstride + hk * DH;
   const T *vbase0 = static_cast<const T *>(a.v) + ((size_t)(sa.off[b] + key0)) * kvstride + hk * DH;
   for (int t0 = 0; t0 < nkeys; t0 += kTileA) {
     const int nk = min(kTileA, nkeys - t0);
-    // This wave's two steps of the tile: keys [64*kh, 64*kh + 64).
-    KStep<T, DH> kf[2];
-    int nv[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int c0 = 64 * kh + 32 * s2;
-      nv[s2] = max(0, min(32, nk - c0));
-      // A step past the tile's end reads the tile's first keys (and is skipped).
-      load_k_step<T, DH>(kf[s2], kbase0 + (size_t)(t0 + (nv[s2] > 0 ? c0 : 0)) * kvstride, kvstride, max(nv[s2], 1),
-                         lane);
-    }
-    __syncthreads();
+    const int c0 = 32 * w;
+    const int nv = max(0, min(32, nk - c0));
+    // A step past the tile's end reads the tile's first keys (and is skipped).
+    KStep<T, DH> kf;
+    load_k_step<T, DH>(kf, kbase0 + (size_t)(t0 + (nv > 0 ? c0 : 0)) * kvstride, kvstride, max(nv, 1), lane);
+    if (t0 > 0) lds_barrier();                 // the previous tile's V reads are done
     vtile_stage<T, DH, kTileA, 256>(vbuf, vbase0 + (size_t)t0 * kvstride, kvstride, nk, tid);
-    __syncthreads();
+    vtile_wait();
+    lds_barrier();
+    if (nv > 0) {
+      f32x4_t sc[2][MB];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      if (nv[s2] > 0)
-        attend_step_pre<T, 1, DH, kTileA>(st, qf, kf[s2], nv[s2], vbuf, 64 * kh + 32 * s2, a.scale_log2, lane);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) sc[kb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kd = 0; kd < DH / 32; ++kd) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          Frag<T> qf;
+          qtile_frag<T, DH>(qf, qbuf, mb * 16 + r16, kd, g);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) mma16(sc[kb][mb], kf.f[kb][kd], qf);
+        }
+      }
+      softmax_pv<T, MB, DH, kTileA>(st, sc, nv, vbuf, c0, a.scale_log2, lane);
+    }
   }
-  __syncthreads();
 
-  // Merge the two key halves of each row block in LDS, then write the partial.
-  float *s_m = reinterpret_cast<float *>(smem);     // [2 row blocks][16]
-  float *s_l = s_m + 32;
-  float *s_o = s_l + 32;                            // [2][16][DH]
-  const float lt = group_sum(st.l[0]);
-  if (kh == 1) {
+  // Merge the 4 waves' states.  Wave w finalises feature blocks
+  // [w*DPW, (w+1)*DPW) of all 32 rows; the others hand it those blocks.
+  lds_barrier();                               // V reads are done; reuse the LDS
+  float *s_m = reinterpret_cast<float *>(smem);               // [wave][32 rows]
+  float *s_l = s_m + 4 * 32;
+  f32x4_t *s_o = reinterpret_cast<f32x4_t *>(s_l + 4 * 32);   // [db][3 givers][mb][lane]
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const float lt = group_sum(st.l[mb]);
     if (g == 0) {
-      s_m[rb * 16 + r16] = st.m[0];
-      s_l[rb * 16 + r16] = lt;
+      s_m[w * 32 + mb * 16 + r16] = st.m[mb];
+      s_l[w * 32 + mb * 16 + r16] = lt;
     }
 #pragma unroll
-    for (int db = 0; db < DH / 16; ++db)
-      *reinterpret_cast<f32x4_t *>(s_o + (rb * 16 + r16) * DH + 16 * db + 4 * g) = st.o[0][db];
+    for (int db = 0; db < NDB; ++db) {
+      const int owner = db / DPW;
+      if (owner != w) s_o[((db * 3 + (w < owner ? w : w - 1)) * MB + mb) * 64 + lane] = st.o[mb][db];
+    }
   }
-  __syncthreads();
-  const size_t pbase = (size_t)(a.part_base + sa.pre[3][b]) + r;      // chunk c: pbase + c*B
-  if (kh == 0 && qvalid1) {
-    const float m1 = s_m[rb * 16 + r16], l1 = s_l[rb * 16 + r16];
-    const float mx = fmaxf(st.m[0], m1);
-    const float e0 = fast_exp2(st.m[0] - mx), e1 = fast_exp2(m1 - mx);
-    const size_t prow = (pbase + (size_t)chunk * B) * a.H + h;
-    float *po = a.part_o + prow * DH;
+  lds_barrier();
+  const size_t p0 = (size_t)(a.part_base + sa.pre[3][b]);         // partial row of (chunk c, row r): p0 + c*B + r
+  T *part_o = static_cast<T *>(a.part_o);
 #pragma unroll
-    for (int db = 0; db < DH / 16; ++db) {
-      const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(s_o + (rb * 16 + r16) * DH + 16 * db + 4 * g);
-      *reinterpret_cast<f32x4_t *>(po + 16 * db + 4 * g) = st.o[0][db] * e0 + o1 * e1;
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = rg * kRowsA + mb * 16 + r16;
+    float e[4], mx = -INFINITY;
+#pragma unroll
+    for (int ws = 0; ws < 4; ++ws) mx = fmaxf(mx, s_m[ws * 32 + mb * 16 + r16]);
+    float L = 0.f;
+#pragma unroll
+    for (int ws = 0; ws < 4; ++ws) {
+      e[ws] = fast_exp2(s_m[ws * 32 + mb * 16 + r16] - mx);
+      L = fmaf(e[ws], s_l[ws * 32 + mb * 16 + r16], L);
     }
-    if (g == 0) a.part_ml[prow] = make_float2(mx, lt * e0 + l1 * e1);
+    const float inv = 1.0f / L;
+    const size_t prow = (p0 + (size_t)chunk * B + r) * a.H + h;
+    // db runs over compile-time values (a register array indexed by the wave
+    // number would be placed in scratch memory); the branch is wave-uniform.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      if (db / DPW != w) continue;
+      f32x4_t acc = st.o[mb][db] * e[w];
+#pragma unroll
+      for (int ws = 0; ws < 4; ++ws)
+        if (ws != w) acc += s_o[((db * 3 + (ws < w ? ws : ws - 1)) * MB + mb) * 64 + lane] * e[ws];
+      if (r < B) st4(part_o + prow * DH + OMap<DH>::feat(g, db, 0), acc * inv);
+    }
+    if (r < B && w == 0 && g == 0) a.part_ml[prow] = make_float2(mx, L);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Type B: 64 invariant rows, state from FACache, stream the block's keys.
-// All global loads (queries, FACache, first key step, V^T) are issued before
+// All global loads (queries, FACache, first key step, V) are issued before
 // the first wait.
 // ---------------------------------------------------------------------------
 template <typename T, typename TO, int DH, int BMAX>
 __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, int h, char *smem) {
+  constexpr int NDB = DH / 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
 
@@ -339,14 +552,10 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
   load_q<T, 1, DH>(qf, qrow, g);
 
   // FACache state of this row (Algorithm 1: initialise with the cache).
-  AttnState<1, DH> st;
   const size_t crow = (size_t)row * a.H + h;
-  st.m[0] = a.m_c[crow] * kLog2e;
-  const float lc = a.l_c[crow];
-  st.l[0] = g == 0 ? lc : 0.f;
-#pragma unroll
-  for (int db = 0; db < DH / 16; ++db)
-    st.o[0][db] = *reinterpret_cast<const f32x4_t *>(a.o_c + crow * DH + 16 * db + 4 * g);
+  const float mc = a.m_c[crow], lc = a.l_c[crow];
+  f32x4_t oc[NDB];
+  load_row<T, DH>(oc, static_cast<const T *>(a.o_c) + crow * DH, g);
   const T *kbase = static_cast<const T *>(a.k) + (size_t)(off + bs) * kvstride + hk * DH;
   KStep<T, DH> kf[2];
   load_k_step<T, DH>(kf[0], kbase, kvstride, min(32, B), lane);
@@ -354,7 +563,14 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
   T *vbuf = reinterpret_cast<T *>(smem);
   vtile_stage<T, DH, BMAX, 256>(vbuf, static_cast<const T *>(a.v) + (size_t)(off + bs) * kvstride + hk * DH, kvstride,
                                 B, tid);
-  __syncthreads();
+  vtile_wait();
+  lds_barrier();
+
+  AttnState<1, DH> st;
+  st.m[0] = mc * kLog2e;
+  st.l[0] = g == 0 ? lc : 0.f;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) st.o[0][db] = oc[db] * lc;
 
   // Up to 4 steps (block <= 128 keys); the next step's keys load during this one.
   for (int c0 = 0; c0 < B; c0 += 64) {
@@ -368,44 +584,28 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
 
   const float lt = group_sum(st.l[0]);
   if (uvalid) {
-    const float inv = 1.0f / lt;
-    TO *out = static_cast<TO *>(a.out) + crow * DH;
-#pragma unroll
-    for (int db = 0; db < DH / 16; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out[16 * db + 4 * g + i] = from_f32<TO>(st.o[0][db][i] * inv);
+    store_row<TO, DH>(static_cast<TO *>(a.out) + crow * DH, st.o[0], 1.0f / lt, g);
     if (a.lse && g == 0) a.lse[crow] = (st.m[0] + __log2f(lt)) * kLn2;
   }
 }
 
-// BMAX: staged block keys (32, 64 or 128 >= every block of the launch).
-template <typename T, typename TO, int DH, int BMAX>
-__global__ __launch_bounds__(256) void step_attn_kernel(const SeqArgs sa, const AttnArgs a) {
-  extern __shared__ __align__(16) char smem[];
-  const int gid = blockIdx.x;
-  if (gid < a.nA) {
-    block_rows_partial<T, TO, DH>(sa, a, gid / a.H, gid % a.H, smem);
-  } else {
-    const int j = gid - a.nA;
-    invariant_rows<T, TO, DH, BMAX>(sa, a, j / a.H, j % a.H, smem);
-  }
-}
-
-// Only type-A items: the DualCache block-query attention.
+// Type-A items only: the block rows' partial states (block step and
+// DualCache).
 template <typename T, typename TO, int DH>
-__global__ __launch_bounds__(256) void block_attn_kernel(const SeqArgs sa, const AttnArgs a) {
+__global__ __launch_bounds__(256) void block_rows_kernel(const SeqArgs sa, const AttnArgs a) {
   extern __shared__ __align__(16) char smem[];
   block_rows_partial<T, TO, DH>(sa, a, blockIdx.x / a.H, blockIdx.x % a.H, smem);
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the type-A partial states: one wave per (block row, head).  Lane c
-// reads chunk c's (max, normaliser); the feature sums read all chunks at once.
+// Merge of the type-A partial states of one (block row, head) per wave: each
+// lane owns DH/64 consecutive features.  Chunks are read 8 at a time, every
+// load of a batch before any use (one memory round trip for <= 8 chunks).
 // ---------------------------------------------------------------------------
 template <typename T, typename TO, int DH>
-__global__ __launch_bounds__(256) void merge_kernel(const SeqArgs sa, const AttnArgs a, int M) {
+__device__ void merge_wave(const SeqArgs &sa, const AttnArgs &a, int M, int wid) {
+  constexpr int FPL = DH / 64, CB = 8;
   const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wid >= M * a.H) return;
   const int m = wid / a.H, h = wid % a.H;
   const int b = find_sample(sa.pre[0], sa.n, m);
@@ -414,48 +614,76 @@ __global__ __launch_bounds__(256) void merge_kernel(const SeqArgs sa, const Attn
   const int nch = (sa.len[b] + a.split_keys - 1) / a.split_keys;
   const size_t pb = (size_t)(a.part_base + sa.pre[3][b] + r) * a.H + h;   // chunk c at pb + c*B*H
   const size_t cstride = (size_t)B * a.H;
+  const T *part_o = static_cast<const T *>(a.part_o);
 
-  float mx = -INFINITY;
-  for (int c = lane; c < nch; c += 64) mx = fmaxf(mx, a.part_ml[pb + c * cstride].x);
+  float mx = -INFINITY, lsum = 0.f;
+  float acc[FPL] = {};
+  for (int c0 = 0; c0 < nch; c0 += CB) {
+    float2 ml[CB];
+    float v[CB][FPL];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  float lsum = 0.f;
-  for (int c = lane; c < nch; c += 64) {
-    const float2 ml = a.part_ml[pb + c * cstride];
-    lsum = fmaf(fast_exp2(ml.x - mx), ml.y, lsum);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
-
-  constexpr int PER = DH / 64;
-  float acc[PER] = {};
-  for (int c0 = 0; c0 < nch; c0 += 8) {
-    float v[8][PER], e[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = c0 + j;
-      e[j] = 0.f;
-      if (c < nch) {
-        const size_t prow = pb + c * cstride;
-        e[j] = fast_exp2(a.part_ml[prow].x - mx);
-#pragma unroll
-        for (int k = 0; k < PER; ++k) v[j][k] = a.part_o[prow * DH + lane + 64 * k];
+    for (int j = 0; j < CB; ++j) {
+      const size_t prow = pb + (size_t)min(c0 + j, nch - 1) * cstride;
+      ml[j] = a.part_ml[prow];
+      const T *src = part_o + prow * DH + lane * FPL;
+      if constexpr (FPL == 2 && sizeof(T) == 2) {
+        const float2 p2 = unpack2(T{}, *reinterpret_cast<const uint32_t *>(src));
+        v[j][0] = p2.x;
+        v[j][1] = p2.y;
       } else {
 #pragma unroll
-        for (int k = 0; k < PER; ++k) v[j][k] = 0.f;
+        for (int k = 0; k < FPL; ++k) v[j][k] = to_f32(src[k]);
       }
     }
+    float bm = mx;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < CB; ++j)
+      if (c0 + j < nch) bm = fmaxf(bm, ml[j].x);
+    const float sc = fast_exp2(mx - bm);
+    lsum *= sc;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] = fmaf(e[j], v[j][k], acc[k]);
+    for (int k = 0; k < FPL; ++k) acc[k] *= sc;
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const float e = c0 + j < nch ? fast_exp2(ml[j].x - bm) * ml[j].y : 0.f;
+      lsum += e;
+#pragma unroll
+      for (int k = 0; k < FPL; ++k) acc[k] = fmaf(e, v[j][k], acc[k]);
+    }
+    mx = bm;
   }
   const int orow = a.omode == 0 ? sa.off[b] + sa.bs[b] + r : a.row_base + m;
   const float inv = 1.0f / lsum;
-  TO *out = static_cast<TO *>(a.out) + ((size_t)orow * a.H + h) * DH;
+  TO *out = static_cast<TO *>(a.out) + ((size_t)orow * a.H + h) * DH + lane * FPL;
+  if constexpr (FPL == 2 && sizeof(TO) == 2) {
+    *reinterpret_cast<uint32_t *>(out) = pack2(TO{}, acc[0] * inv, acc[1] * inv);
+  } else {
 #pragma unroll
-  for (int k = 0; k < PER; ++k) out[lane + 64 * k] = from_f32<TO>(acc[k] * inv);
+    for (int k = 0; k < FPL; ++k) out[k] = from_f32<TO>(acc[k] * inv);
+  }
   if (a.lse && lane == 0) a.lse[(size_t)orow * a.H + h] = (mx + __log2f(lsum)) * kLn2;
+}
+
+// DualCache: the merge alone, 4 (row, head) pairs per workgroup.
+template <typename T, typename TO, int DH>
+__global__ __launch_bounds__(256) void merge_kernel(const SeqArgs sa, const AttnArgs a, int M) {
+  merge_wave<T, TO, DH>(sa, a, M, blockIdx.x * 4 + (threadIdx.x >> 6));
+}
+
+// Block step, after the type-A kernel: the first ceil(M*H/4) workgroups merge
+// the block rows' partials, the rest are type-B items (invariant rows).  Both
+// only read what earlier kernels wrote, so no workgroup waits for another.
+// BMAX: staged block keys (32, 64 or 128 >= every block of the launch).
+template <typename T, typename TO, int DH, int BMAX>
+__global__ __launch_bounds__(256) void invariant_rows_kernel(const SeqArgs sa, const AttnArgs a, int M) {
+  extern __shared__ __align__(16) char smem[];
+  const int nmw = (M * a.H + 3) / 4;
+  if ((int)blockIdx.x < nmw) {
+    merge_wave<T, TO, DH>(sa, a, M, blockIdx.x * 4 + (threadIdx.x >> 6));
+    return;
+  }
+  const int j = blockIdx.x - nmw;
+  invariant_rows<T, TO, DH, BMAX>(sa, a, j / a.H, j % a.H, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -506,15 +734,14 @@ __global__ __launch_bounds__(256) void refresh_attn_kernel(const SeqArgs sa, con
           a.m_w[crow] = st.m[0] * kLn2;
           a.l_w[crow] = lt;
         }
-#pragma unroll
-        for (int db = 0; db < DH / 16; ++db)
-          *reinterpret_cast<f32x4_t *>(a.o_w + crow * DH + 16 * db + 4 * g) = st.o[0][db];
+        store_row<T, DH>(static_cast<T *>(a.o_w) + crow * DH, st.o[0], 1.0f / lt, g);
       }
     }
     for (int k0 = seg_lo[sgi]; k0 < seg_hi[sgi]; k0 += TK) {
       const int nk = min(TK, seg_hi[sgi] - k0);
       __syncthreads();
       vtile_stage<T, DH, TK, 256>(vbuf, vb + (size_t)k0 * kvstride, kvstride, nk, tid);
+      vtile_wait();
       __syncthreads();
       for (int c0 = 0; c0 < nk; c0 += 32)
         attend_step<T, MB, DH, TK>(st, qf, kb + (size_t)(k0 + c0) * kvstride, kvstride, min(32, nk - c0), vbuf, c0,
@@ -523,12 +750,7 @@ __global__ __launch_bounds__(256) void refresh_attn_kernel(const SeqArgs sa, con
   }
   const float lt = group_sum(st.l[0]);
   if (tvalid) {
-    const float inv = 1.0f / lt;
-    TO *out = static_cast<TO *>(a.out) + crow * DH;
-#pragma unroll
-    for (int db = 0; db < DH / 16; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out[16 * db + 4 * g + i] = from_f32<TO>(st.o[0][db][i] * inv);
+    store_row<TO, DH>(static_cast<TO *>(a.out) + crow * DH, st.o[0], 1.0f / lt, g);
     if (a.lse && g == 0) a.lse[crow] = (st.m[0] + __log2f(lt)) * kLn2;
   }
 }
@@ -536,10 +758,15 @@ __global__ __launch_bounds__(256) void refresh_attn_kernel(const SeqArgs sa, con
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <typename T, int DH> constexpr size_t step_smem() {
-  constexpr size_t vt = VTile<T, DH, 128>::kBytes;                  // type A tile, type B block keys
-  constexpr size_t merge_a = (64 + 32 * DH) * sizeof(float);
-  return vt > merge_a ? vt : merge_a;
+// type A: query rows + key tile, then the state merge
+template <typename T, int DH> constexpr size_t block_rows_smem() {
+  constexpr size_t tile_a = (size_t)kRowsA * DH * sizeof(T) + VTile<T, DH, kTileA>::kBytes;
+  constexpr size_t merge_a = merge_a_bytes<DH>();
+  return tile_a > merge_a ? tile_a : merge_a;
+}
+// type B: the block's keys
+template <typename T, int DH, int BMAX> constexpr size_t invariant_rows_smem() {
+  return VTile<T, DH, BMAX>::kBytes;
 }
 template <typename T, int DH> constexpr size_t refresh_smem() {
   return VTile<T, DH, 128>::kBytes;
@@ -557,24 +784,25 @@ template <typename T, int DH> constexpr size_t refresh_smem() {
     }                                                                                    \
   } while (0)
 
-hipError_t launch_step_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
-                            const LaunchEvents &ev) {
+hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
+                             const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
-  int bmax = 0;
-  for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
-  if (bmax <= 32)
-    LC_DISPATCH(dt, dh, (lc_launch(step_attn_kernel<T, TO, DH, 32>, dim3(n_blocks), dim3(256), step_smem<T, DH>(), s, ev, sa, a)));
-  else if (bmax <= 64)
-    LC_DISPATCH(dt, dh, (lc_launch(step_attn_kernel<T, TO, DH, 64>, dim3(n_blocks), dim3(256), step_smem<T, DH>(), s, ev, sa, a)));
-  else
-    LC_DISPATCH(dt, dh, (lc_launch(step_attn_kernel<T, TO, DH, 128>, dim3(n_blocks), dim3(256), step_smem<T, DH>(), s, ev, sa, a)));
+  LC_DISPATCH(dt, dh, (lc_launch(block_rows_kernel<T, TO, DH>, dim3(n_blocks), dim3(256), block_rows_smem<T, DH>(), s, ev, sa, a)));
   return hipGetLastError();
 }
 
-hipError_t launch_block_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
-                             const LaunchEvents &ev) {
-  if (n_blocks <= 0) return hipSuccess;
-  LC_DISPATCH(dt, dh, (lc_launch(block_attn_kernel<T, TO, DH>, dim3(n_blocks), dim3(256), step_smem<T, DH>(), s, ev, sa, a)));
+hipError_t launch_invariant_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, int M,
+                                 hipStream_t s, const LaunchEvents &ev) {
+  const int grid = (M * a.H + 3) / 4 + n_blocks;
+  if (grid <= 0) return hipSuccess;
+  int bmax = 0;
+  for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
+#define LC_INV(BM) \
+  LC_DISPATCH(dt, dh, (lc_launch(invariant_rows_kernel<T, TO, DH, BM>, dim3(grid), dim3(256), invariant_rows_smem<T, DH, BM>(), s, ev, sa, a, M)))
+  if (bmax <= 32) LC_INV(32);
+  else if (bmax <= 64) LC_INV(64);
+  else LC_INV(128);
+#undef LC_INV
   return hipGetLastError();
 }
 
@@ -599,19 +827,19 @@ hipError_t setup_kernel_attributes() {
   if (e == hipSuccess)                                                                           \
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(K), hipFuncAttributeMaxDynamicSharedMemorySize, \
                             (int)(BYTES));
-#define LC_ATTR_STEP(BM)                                                   \
-  LC_ATTR((step_attn_kernel<f16_t, bf16_t, 128, BM>), (step_smem<f16_t, 128>())); \
-  LC_ATTR((step_attn_kernel<f16_t, bf16_t, 64, BM>), (step_smem<f16_t, 64>()));   \
-  LC_ATTR((step_attn_kernel<float, float, 128, BM>), (step_smem<float, 128>()));  \
-  LC_ATTR((step_attn_kernel<float, float, 64, BM>), (step_smem<float, 64>()));
-  LC_ATTR_STEP(32)
-  LC_ATTR_STEP(64)
-  LC_ATTR_STEP(128)
-#undef LC_ATTR_STEP
-  LC_ATTR((block_attn_kernel<f16_t, bf16_t, 128>), (step_smem<f16_t, 128>()));
-  LC_ATTR((block_attn_kernel<f16_t, bf16_t, 64>), (step_smem<f16_t, 64>()));
-  LC_ATTR((block_attn_kernel<float, float, 128>), (step_smem<float, 128>()));
-  LC_ATTR((block_attn_kernel<float, float, 64>), (step_smem<float, 64>()));
+#define LC_ATTR_INV(BM)                                                   \
+  LC_ATTR((invariant_rows_kernel<f16_t, bf16_t, 128, BM>), (invariant_rows_smem<f16_t, 128, BM>())); \
+  LC_ATTR((invariant_rows_kernel<f16_t, bf16_t, 64, BM>), (invariant_rows_smem<f16_t, 64, BM>()));   \
+  LC_ATTR((invariant_rows_kernel<float, float, 128, BM>), (invariant_rows_smem<float, 128, BM>()));  \
+  LC_ATTR((invariant_rows_kernel<float, float, 64, BM>), (invariant_rows_smem<float, 64, BM>()));
+  LC_ATTR_INV(32)
+  LC_ATTR_INV(64)
+  LC_ATTR_INV(128)
+#undef LC_ATTR_INV
+  LC_ATTR((block_rows_kernel<f16_t, bf16_t, 128>), (block_rows_smem<f16_t, 128>()));
+  LC_ATTR((block_rows_kernel<f16_t, bf16_t, 64>), (block_rows_smem<f16_t, 64>()));
+  LC_ATTR((block_rows_kernel<float, float, 128>), (block_rows_smem<float, 128>()));
+  LC_ATTR((block_rows_kernel<float, float, 64>), (block_rows_smem<float, 64>()));
   LC_ATTR((refresh_attn_kernel<f16_t, bf16_t, 128>), (refresh_smem<f16_t, 128>()));
   LC_ATTR((refresh_attn_kernel<f16_t, bf16_t, 64>), (refresh_smem<f16_t, 64>()));
   LC_ATTR((refresh_attn_kernel<float, float, 128>), (refresh_smem<float, 128>()));

@@ -36,16 +36,17 @@ struct AttnArgs {
   const void *k, *v;       // [rows, Hkv, dh]
   void *out;               // omode 0: [rows, H, dh]; omode 1: out_block [M, H, dh]
   float *lse;              // matching rows, [.., H], or null
-  const float *m_c, *l_c, *o_c;   // FACache read (block step)
-  float *m_w, *l_w, *o_w;         // FACache write (refresh)
+  const float *m_c, *l_c;  // FACache read (block step): max (natural log), normaliser
+  const void *o_c;         //   O~ / l in the cache type [rows, H, dh]
+  float *m_w, *l_w;        // FACache write (refresh)
+  void *o_w;
   float2 *part_ml;         // [P, H] (max in log2 units, normaliser)
-  float *part_o;           // [P, H, dh]
+  void *part_o;            // [P, H, dh] O~ / l of the chunk, cache type
   int qmode, omode;
   int row_base;            // index of the slice's first block row in q_block/out_block
   int part_base;           // index of the slice's first partial row
   int H, Hkv;
   int split_keys;          // keys per type-A chunk (multiple of 32)
-  int nA;                  // type-A workgroups (items * H); the rest are type B
   float scale_log2;        // sm_scale * log2(e)
 };
 
@@ -68,10 +69,10 @@ inline void lc_launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned 
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipStream_t s, const LaunchEvents &ev);
-hipError_t launch_step_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
-                            hipStream_t s, const LaunchEvents &ev);
-hipError_t launch_block_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
+hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                              hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_invariant_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, int M,
+                                 hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int M, hipStream_t s,
                         const LaunchEvents &ev);
 hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,

@@ -44,51 +44,11 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
   const int cb0 = blockIdx.x * NB;
   const int m0 = blockIdx.y * BM;
 
-  if (tid < BM) {
-    const int m = m0 + tid;
-    int id = -1, dst = -1, pos = 0;
-    if (m < a.M) {
-      const int b = find_sample(sa.pre[0], sa.n, m);
-      const int local = m - sa.pre[0][b];
-      if (a.mode == 0) {
-        dst = sa.off[b] + sa.bs[b] + local;
-        pos = sa.bs[b] + local;
-        id = a.ids[a.ids_base + m];
-      } else {
-        dst = sa.off[b] + local;
-        pos = local;
-        id = a.ids[dst];
-      }
-      if (id < 0 || id >= a.vocab) {
-        atomicOr(a.flags, 1u);
-        id = -1;
-      }
-    }
-    s_id[tid] = id;
-    s_dst[tid] = dst;
-    s_pos[tid] = pos;
-  }
-  __syncthreads();
-
   const T *E = static_cast<const T *>(a.E);
   const T *W = static_cast<const T *>(a.W);
-  {
-    // RMSNorm gain: staged once per workgroup, read per step from LDS.
-    const uint4 *gsrc = static_cast<const uint4 *>(a.gamma);
-    uint4 *gdst = reinterpret_cast<uint4 *>(s_gamma);
-    for (int i = tid; i < D * (int)sizeof(T) / 16; i += blockDim.x) gdst[i] = gsrc[i];
-  }
-  __syncthreads();
-
-  // Rows without a valid token read row 0 and are zeroed in the epilogue;
-  // column blocks past the last feature read row 0 and are dropped there, so
+  // Column blocks past the last feature read row 0 and are dropped in the
+  // epilogue; rows without a valid token read row 0 and are zeroed there, so
   // every load of the main loop is unconditional.
-  const T *arow[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int id = s_id[mb * 16 + r16];
-    arow[mb] = E + (size_t)(id >= 0 ? id : 0) * D;
-  }
   const T *brow[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -97,6 +57,7 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
     const int wrow = hh * dh + (r16 < 8 ? p0 + r16 : dh / 2 + p0 + (r16 - 8));
     brow[nb] = W + (size_t)wrow * D;
   }
+  const T *arow[MB];
 
   f32x4_t acc[MB][NB];
 #pragma unroll
@@ -107,31 +68,38 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) ssq[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Contraction range of this wave, in steps of 32, processed in groups of U
-  // steps (U divides the step count); the loads of group i+1 are in flight
-  // while group i is multiplied.
+  // Contraction steps of 32, in groups of U steps (U divides the step count).
+  // The waves interleave: group i of wave w is steps (i*KW + w)*U .. +U-1, so
+  // at any time the workgroup reads one contiguous KW*U*64-byte stretch of
+  // each weight row (whole DRAM pages) rather than KW scattered pieces.
   const int kper = D / KW;
-  const int kbeg = w * kper;
   const int ngroups = kper / (32 * U);
+  auto kstep = [&](int grp, int u) { return ((grp * KW + w) * U + u) * 32; };
 
   struct Group {
     Frag<T> w[U][NB], e[U][MB];
   };
+  auto load_w = [&](Group &G, int grp) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) frag_load(G.w[u][nb], brow[nb] + kstep(grp, u) + 8 * g);
+  };
+  auto load_e = [&](Group &G, int grp) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) frag_load(G.e[u][mb], arow[mb] + kstep(grp, u) + 8 * g);
+  };
   auto load_group = [&](Group &G, int grp) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = kbeg + (grp * U + u) * 32 + 8 * g;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) frag_load(G.w[u][nb], brow[nb] + kk);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) frag_load(G.e[u][mb], arow[mb] + kk);
-    }
+    load_w(G, grp);
+    load_e(G, grp);
   };
   auto compute_group = [&](const Group &G, int grp) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       Frag<T> gm;
-      frag_load(gm, s_gamma + kbeg + (grp * U + u) * 32 + 8 * g);
+      frag_load(gm, s_gamma + kstep(grp, u) + 8 * g);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         // Sum of squares on the matrix core: E_rows * E_rows^T, whose diagonal
@@ -153,11 +121,87 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
     }
   };
 
+  // The weights of the first groups go out before anything else: their
+  // addresses do not depend on the tokens.
+  Group gbuf[3];
+  load_w(gbuf[0], 0);
+  if constexpr (NG > 1) load_w(gbuf[1], 1);
+
+  // Prologue, one memory round trip: the RMSNorm gain (staged in LDS, read
+  // per step) and the tile's token ids are loaded together.  When the tile
+  // lies within one sample (always for one sample per launch) the block-table
+  // lookup is uniform; otherwise each token searches the table.
+  constexpr int GMAX = kQkvMaxD * (int)sizeof(T) / 16 / (64 * KW);   // gain pieces per thread, at most
+  static_assert(GMAX <= 4, "gain staging registers");
+  const int gpieces = D * (int)sizeof(T) / 16;
+  const uint4 *gsrc = static_cast<const uint4 *>(a.gamma);
+  const int mc = min(m0 + min(tid, BM - 1), a.M - 1);
+  const int b0 = find_sample(sa.pre[0], sa.n, m0);
+  int tdst, tpos;
+  if (min(m0 + BM, a.M) <= sa.pre[0][b0 + 1]) {          // uniform
+    const int local = mc - sa.pre[0][b0];
+    tdst = a.mode == 0 ? sa.off[b0] + sa.bs[b0] + local : sa.off[b0] + local;
+    tpos = a.mode == 0 ? sa.bs[b0] + local : local;
+  } else {
+    const int tb = find_sample(sa.pre[0], sa.n, mc);
+    const int local = mc - sa.pre[0][tb];
+    tdst = a.mode == 0 ? sa.off[tb] + sa.bs[tb] + local : sa.off[tb] + local;
+    tpos = a.mode == 0 ? sa.bs[tb] + local : local;
+  }
+  const int tid_raw = a.ids[a.mode == 0 ? a.ids_base + mc : tdst];
+  uint4 gv0 = gsrc[min(tid, gpieces - 1)], gv1 = gv0, gv2 = gv0, gv3 = gv0;
+  if constexpr (GMAX > 1) gv1 = gsrc[min(tid + 64 * KW, gpieces - 1)];
+  if constexpr (GMAX > 2) gv2 = gsrc[min(tid + 2 * 64 * KW, gpieces - 1)];
+  if constexpr (GMAX > 3) gv3 = gsrc[min(tid + 3 * 64 * KW, gpieces - 1)];
+  if (tid < BM) {
+    const bool valid = m0 + tid < a.M;
+    int id = valid ? tid_raw : -1;
+    if (valid && (id < 0 || id >= a.vocab)) {
+      atomicOr(a.flags, 1u);
+      id = -1;
+    }
+    s_id[tid] = id;
+    s_dst[tid] = valid ? tdst : -1;
+    s_pos[tid] = valid ? tpos : 0;
+  }
+  uint4 *gdst = reinterpret_cast<uint4 *>(s_gamma);
+  if (tid < gpieces) gdst[tid] = gv0;
+  if constexpr (GMAX > 1) if (tid + 64 * KW < gpieces) gdst[tid + 64 * KW] = gv1;
+  if constexpr (GMAX > 2) if (tid + 2 * 64 * KW < gpieces) gdst[tid + 2 * 64 * KW] = gv2;
+  if constexpr (GMAX > 3) if (tid + 3 * 64 * KW < gpieces) gdst[tid + 3 * 64 * KW] = gv3;
+  lds_barrier();
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int id = s_id[mb * 16 + r16];
+    arow[mb] = E + (size_t)(id >= 0 ? id : 0) * D;
+  }
+  load_e(gbuf[0], 0);
+  if constexpr (NG > 1) load_e(gbuf[1], 1);
+
+  // Epilogue operands fetched now, so that no load is waited for after the
+  // main loop: the RoPE (cos, sin) of this wave's output slots (wave w
+  // finalises (row block, column block) item w) and this thread's first
+  // EmbedCache piece (the tile's embedding rows are copied to h, spread over
+  // the column tiles of the grid; rows with a bad id get zeros).
+  static_assert(MB * NB <= KW, "one epilogue item per wave");
+  const int nrot = (a.H + a.Hkv) * dh;     // features that get RoPE (Q and K)
+  const int ep_mb = min(w, MB * NB - 1) / NB, ep_nb = min(w, MB * NB - 1) % NB;
+  const int ep_cb = min(cb0 + ep_nb, ncb - 1);
+  const int ep_pair = (ep_cb % cbh) * 8 + (r16 & 7);
+  float2 ep_cs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ep_cs[i] = a.rope[(size_t)s_pos[ep_mb * 16 + 4 * g + i] * (dh / 2) + ep_pair];
+  constexpr int NV = sizeof(T) * 8 / 16;   // uint4 pieces per 8 elements
+  const int h_pieces = BM * (D / 8);
+  const int h_per = (h_pieces + gridDim.x - 1) / gridDim.x;
+  const int h_c = blockIdx.x * h_per + tid;
+  const int h_row = min(h_c / (D / 8), BM - 1), h_col = (h_c % (D / 8)) * 8;
+  const uint4 *h_src = reinterpret_cast<const uint4 *>(E + (size_t)max(s_id[h_row], 0) * D + h_col);
+  const uint4 h_v0 = h_src[0], h_v1 = h_src[NV - 1];
+
   if constexpr (NG > 0) {
     // Two groups in flight while a third is multiplied.
-    Group gbuf[3];
-    load_group(gbuf[0], 0);
-    if (NG > 1) load_group(gbuf[1], 1);
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       // Keep the schedule as written: loads two groups ahead, then this
@@ -169,36 +213,13 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-    Group ga, gb;
-    load_group(ga, 0);
+    Group &ga = gbuf[0], &gb = gbuf[1];
     for (int grp = 0; grp < ngroups; grp += 2) {
       if (grp + 1 < ngroups) load_group(gb, grp + 1);
       compute_group(ga, grp);
       if (grp + 1 < ngroups) {
         if (grp + 2 < ngroups) load_group(ga, grp + 2);
         compute_group(gb, grp + 1);
-      }
-    }
-  }
-
-  // EmbedCache: copy this token tile's embedding rows to h, spread over the
-  // column tiles of the grid (16-byte pieces; rows with a bad id get zeros).
-  {
-    const int pieces = BM * (D / 8);
-    const int per = (pieces + gridDim.x - 1) / gridDim.x;
-    for (int t = tid; t < per; t += blockDim.x) {
-      const int c = blockIdx.x * per + t;
-      if (c >= pieces) break;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int dst = s_dst[row], id = s_id[row];
-      if (dst < 0) continue;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      constexpr int NV = sizeof(T) * 8 / 16;   // uint4 pieces per 8 elements
-      T *hp = static_cast<T *>(a.h) + (size_t)dst * D + col;
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        if (id >= 0) v = reinterpret_cast<const uint4 *>(E + (size_t)id * D + col)[j];
-        reinterpret_cast<uint4 *>(hp)[j] = v;
       }
     }
   }
@@ -213,14 +234,12 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s_red[w][mb][nb][lane] = acc[mb][nb];
   }
-  __syncthreads();
+  lds_barrier();
 
   const float invD = 1.0f / (float)D;
-  const int nrot = (a.H + a.Hkv) * dh;     // features that get RoPE (Q and K)
-  for (int c = w; c < MB * NB; c += KW) {
-    const int mb = c / NB, nb = c % NB;
+  if (w < MB * NB && cb0 + ep_nb < ncb) {   // wave-uniform
+    const int mb = ep_mb, nb = ep_nb;
     const int cb = cb0 + nb;
-    if (cb >= ncb) continue;                // wave-uniform
     f32x4_t sum = s_red[0][mb][nb][lane];
 #pragma unroll
     for (int ww = 1; ww < KW; ++ww) sum += s_red[ww][mb][nb][lane];
@@ -238,10 +257,7 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
       const float y = s_id[row] >= 0 ? sum[i] * rsqrtf(ss * invD + a.eps) : 0.f;
       const float other = __shfl_xor(y, 8);
       float o = y;
-      if (rot) {
-        const float2 cs = a.rope[(size_t)s_pos[row] * (dh / 2) + pair];
-        o = first ? (y * cs.x - other * cs.y) : (other * cs.y + y * cs.x);
-      }
+      if (rot) o = first ? (y * ep_cs[i].x - other * ep_cs[i].y) : (other * ep_cs[i].y + y * ep_cs[i].x);
       const int dst = s_dst[row];
       if (dst >= 0) {
         if constexpr (sizeof(TC) == 2) {
@@ -256,6 +272,23 @@ __global__ __launch_bounds__(64 * KW) void qkv_fused_kernel(const SeqArgs sa, co
           static_cast<TC *>(a.v)[(size_t)dst * kf + (feat - qf - kf)] = from_f32<TC>(o);
         }
       }
+    }
+  }
+
+  // EmbedCache stores: the prefetched piece, then (only for very wide rows)
+  // any further pieces of this thread.
+  for (int t = tid; t < h_per; t += blockDim.x) {
+    const int c = blockIdx.x * h_per + t;
+    if (c >= h_pieces) break;
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    const int dst = s_dst[row], id = s_id[row];
+    if (dst < 0) continue;
+    T *hp = static_cast<T *>(a.h) + (size_t)dst * D + col;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (id >= 0) v = t == tid ? (j == 0 ? h_v0 : h_v1) : reinterpret_cast<const uint4 *>(E + (size_t)id * D + col)[j];
+      reinterpret_cast<uint4 *>(hp)[j] = v;
     }
   }
 }

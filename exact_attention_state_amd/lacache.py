@@ -27,7 +27,7 @@ EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "laca
             "lacache_block_step", "lacache_dualcache_attn", "lacache_read_device_status",
             "lacache_profile_enable", "lacache_profile_read", "lacache_status_string", "lacache_last_error")
 KERNEL_QKV, KERNEL_STEP_ATTN, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_DUAL_ATTN = range(5)
-KERNEL_NAMES = ("qkv", "step_attn", "merge", "refresh_attn", "dual_attn")
+KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn")
 
 
 class Config(ctypes.Structure):
@@ -43,7 +43,7 @@ class Weights(ctypes.Structure):
 
 class Cache(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("m", ctypes.c_void_p), ("l", ctypes.c_void_p), ("o_acc", ctypes.c_void_p),
+                ("m", ctypes.c_void_p), ("l", ctypes.c_void_p), ("o", ctypes.c_void_p),
                 ("n_rows", ctypes.c_int64)]
 
 
@@ -125,7 +125,7 @@ class CacheTensors:
     v: torch.Tensor
     m: torch.Tensor
     l: torch.Tensor
-    o_acc: torch.Tensor
+    o: torch.Tensor
     out: torch.Tensor
     lse: torch.Tensor
 
@@ -180,7 +180,7 @@ class Context:
             v=torch.empty(n_rows, c.n_kv_heads, c.head_dim, dtype=ct, **e),
             m=torch.empty(n_rows, c.n_heads, dtype=torch.float32, **e),
             l=torch.empty(n_rows, c.n_heads, dtype=torch.float32, **e),
-            o_acc=torch.empty(n_rows, c.n_heads, c.head_dim, dtype=torch.float32, **e),
+            o=torch.empty(n_rows, c.n_heads, c.head_dim, dtype=ct, **e),
             out=torch.empty(n_rows, c.n_heads, c.head_dim, dtype=dt, **e),
             lse=torch.empty(n_rows, c.n_heads, dtype=torch.float32, **e),
         )
@@ -205,7 +205,7 @@ class Context:
     @staticmethod
     def _cache(ct: CacheTensors):
         return Cache(ct.h.data_ptr(), ct.q.data_ptr(), ct.k.data_ptr(), ct.v.data_ptr(), ct.m.data_ptr(),
-                     ct.l.data_ptr(), ct.o_acc.data_ptr(), ct.n_rows)
+                     ct.l.data_ptr(), ct.o.data_ptr(), ct.n_rows)
 
     @staticmethod
     def _ids(t):

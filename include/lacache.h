@@ -37,7 +37,8 @@
  *   k, v   [n_rows, H_kv, d_h]                ctype  (RoPECache; v not rotated)
  *   m, l   [n_rows, H]                        fp32   (FACache running max in
  *          natural-log units of the scaled scores, and normaliser)
- *   o_acc  [n_rows, H, d_h]                   fp32   (FACache unnormalised O~)
+ *   o      [n_rows, H, d_h]                   ctype  (FACache output O~ / l: the
+ *          unnormalised accumulator divided by the normaliser l)
  *   out    [n_rows, H, d_h]                   dtype
  *   lse    [n_rows, H]                        fp32   (natural log)
  *   dtype is fp32 or bf16 (lacache_config.dtype).  ctype, the RoPECache
@@ -123,7 +124,7 @@ typedef struct {
   void *v;
   float *m;
   float *l;
-  float *o_acc;
+  void *o;
   int64_t n_rows;
 } lacache_cache;
 
@@ -160,7 +161,11 @@ LACACHE_API lacache_status lacache_create(const lacache_config *cfg, lacache_ctx
 LACACHE_API lacache_status lacache_destroy(lacache_ctx *ctx);
 
 /* Bytes of device workspace an operation needs for this block table
- * (0 is possible).  seqs: host, `batch` rows. */
+ * (0 is possible).  seqs: host, `batch` rows.  The block step and the
+ * DualCache attention keep partial softmax states of the block rows there:
+ * per block row, head and chunk of keys a (max, normaliser) pair in fp32 and
+ * d_h outputs in ctype; the chunk length is chosen per call from the table
+ * (128 keys while that gives at most ~4 workgroups per CU, longer beyond). */
 LACACHE_API lacache_status lacache_workspace_size(const lacache_ctx *ctx, int32_t op,
                                       const lacache_seq *seqs, int32_t batch,
                                       size_t *bytes);
@@ -170,7 +175,7 @@ LACACHE_API lacache_status lacache_workspace_size(const lacache_ctx *ctx, int32_
  * flag set): the full layer-0 forward of every row of every sample.
  *   ids      device int32 [n_rows]: token id of every row (rows outside all
  *            samples are not read).
- * Writes h, q, k, v for every row of every sample; m, l, o_acc for every row
+ * Writes h, q, k, v for every row of every sample; m, l, o for every row
  * of U (the state over the keys of U only); out and lse (lse may be NULL) for
  * every row.  FACache rows of C are left unspecified. */
 LACACHE_API lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
@@ -219,15 +224,17 @@ LACACHE_API lacache_status lacache_read_device_status(lacache_ctx *ctx, void *st
 
 /* Optional per-kernel timing (diagnostics, off by default).  While enabled,
  * every kernel launch of this context carries two HIP events that the
- * dispatch itself stamps with its start and end (hipExtLaunchKernelGGL).  lacache_profile_read synchronises those events and returns,
+ * dispatch itself stamps with its start and end (hipExtLaunchKernelGGL).
+ * lacache_profile_read synchronises those events and returns,
  * for one kernel class, the summed event time in milliseconds and the number
  * of launches since the last read of that class (then resets that class). */
 typedef enum {
-  LACACHE_KERNEL_QKV = 0,          /* embed + RMSNorm + QKV + RoPE + cache write */
-  LACACHE_KERNEL_STEP_ATTN = 1,    /* block-row split partials + invariant rows  */
-  LACACHE_KERNEL_MERGE = 2,        /* merge of the block-row partials           */
-  LACACHE_KERNEL_REFRESH_ATTN = 3, /* refresh attention with FACache snapshot   */
-  LACACHE_KERNEL_DUAL_ATTN = 4,    /* DualCache block-query partials            */
+  LACACHE_KERNEL_QKV = 0,            /* embed + RMSNorm + QKV + RoPE + cache write  */
+  LACACHE_KERNEL_BLOCK_ROWS = 1,     /* block rows x key chunks: partial states     */
+  LACACHE_KERNEL_INVARIANT_ROWS = 2, /* block step: invariant rows from FACache and
+                                        the merge of the block rows' partials      */
+  LACACHE_KERNEL_MERGE = 3,          /* DualCache: merge of the partials            */
+  LACACHE_KERNEL_REFRESH_ATTN = 4,   /* refresh attention with FACache snapshot     */
   LACACHE_KERNEL_COUNT = 5
 } lacache_kernel;
 

@@ -26,8 +26,8 @@ def _say(*a):
 
 
 def _facache_pair(dw, rows):
-    m, l, o = host(dw.ct.m)[rows], host(dw.ct.l)[rows], host(dw.ct.o_acc)[rows]
-    return o / l[..., None], m + np.log(l)
+    m, l, o = host(dw.ct.m)[rows], host(dw.ct.l)[rows], host(dw.ct.o)[rows]
+    return o, m + np.log(l)
 
 
 def _compare_refresh(dw, ref, what):
@@ -225,7 +225,7 @@ def test_batched_equals_per_sample_bitwise():
     blk = dw.next_block_ids()
     dw.block_step(blk)
     torch.cuda.synchronize()
-    full = {k: getattr(dw.ct, k).clone() for k in ("h", "q", "k", "v", "out", "lse", "m", "l", "o_acc")}
+    full = {k: getattr(dw.ct, k).clone() for k in ("h", "q", "k", "v", "out", "lse", "m", "l", "o")}
     crow0 = 0
     for b, (off, n, bs, be) in enumerate(dw.table):
         B = be - bs
@@ -240,7 +240,7 @@ def test_batched_equals_per_sample_bitwise():
         for k in ("h", "q", "k", "v", "out", "lse"):
             assert torch.equal(getattr(one.ct, k)[rows], full[k][rows]), f"sample {b}: {k} differs"
         urows = torch.from_numpy(off + np.r_[0:bs, be:n]).to("cuda")
-        for k in ("m", "l", "o_acc"):
+        for k in ("m", "l", "o"):
             assert torch.equal(getattr(one.ct, k).index_select(0, urows), full[k].index_select(0, urows)), k
         crow0 += B
 
@@ -280,10 +280,10 @@ def test_rows_outside_the_block_table_are_untouched():
     dw.ctx.prefill_cache(dw.weights, torch.from_numpy(ids).cuda(), table, dw.ct)
     torch.cuda.synchronize()
     outside = np.r_[0:3, 75:92, 174:n_rows]
-    for k in ("h", "q", "k", "v", "out", "lse", "m", "l", "o_acc"):
+    for k in ("h", "q", "k", "v", "out", "lse", "m", "l", "o"):
         t = getattr(dw.ct, k).float().cpu().numpy()
         assert (t[outside] == -1024.0).all(), f"{k}: rows outside the table were written"
-    snap = {k: getattr(dw.ct, k).clone() for k in ("h", "q", "k", "v", "m", "l", "o_acc")}
+    snap = {k: getattr(dw.ct, k).clone() for k in ("h", "q", "k", "v", "m", "l", "o")}
     blk = torch.from_numpy(np.concatenate([ids[3 + 56:3 + 72], ids[92 + 50:92 + 66]])[::-1].copy()).cuda()
     ws = dw.ctx.alloc_workspace(lacache.OP_BLOCK_STEP, table)
     dw.ctx.block_step(dw.weights, blk, table, dw.ct, ws)
@@ -293,7 +293,7 @@ def test_rows_outside_the_block_table_are_untouched():
     for k in ("h", "q", "k", "v"):
         a, b_ = getattr(dw.ct, k).float().cpu().numpy(), snap[k].float().cpu().numpy()
         assert np.array_equal(a[keep], b_[keep]), f"{k}: non-block rows changed"
-    for k in ("m", "l", "o_acc"):
+    for k in ("m", "l", "o"):
         assert torch.equal(getattr(dw.ct, k), snap[k]), f"{k}: FACache was written by a block step"
 
 
