@@ -150,6 +150,49 @@ Partials partial_layout(const lacache_ctx *ctx, void *ws, int64_t P) {
   return r;
 }
 
+// Many-token QKV path (prep + MFMA GEMM): bf16 parameters with d_model a
+// multiple of 512; always for the refresh, for block steps of at least
+// kGemmMinTokens tokens.
+bool gemm_capable(const lacache_ctx *ctx) { return ctx->cfg.dtype == LACACHE_BF16 && ctx->cfg.d_model % 512 == 0; }
+bool step_uses_gemm(const lacache_ctx *ctx, int64_t M) { return gemm_capable(ctx) && M >= lc::kGemmMinTokens; }
+int64_t block_tokens(const lacache_seq *seqs, int32_t batch) {
+  int64_t M = 0;
+  for (int i = 0; i < batch; ++i) M += seqs[i].block_end - seqs[i].block_start;
+  return M;
+}
+// Workspace of one prep + GEMM pass over up to `rows` tokens: A [rows_pad, D] fp16 and the token map.
+size_t gemm_bytes(const lacache_ctx *ctx, int64_t rows) {
+  const size_t Mp = (size_t)lc::gemm_rows_padded((int)rows);
+  return align256(Mp * ctx->cfg.d_model * 2) + align256(Mp * sizeof(int2)) +
+         align256(Mp * (ctx->cfg.head_dim / 2) * sizeof(float2));
+}
+struct GemmWs {
+  void *A;
+  int2 *map;
+  float2 *cs;
+};
+GemmWs gemm_layout(const lacache_ctx *ctx, void *ws, int64_t rows) {
+  const size_t Mp = (size_t)lc::gemm_rows_padded((int)rows);
+  char *p = static_cast<char *>(ws);
+  GemmWs g;
+  g.A = p;
+  p += align256(Mp * ctx->cfg.d_model * 2);
+  g.map = reinterpret_cast<int2 *>(p);
+  p += align256(Mp * sizeof(int2));
+  g.cs = reinterpret_cast<float2 *>(p);
+  return g;
+}
+// Largest number of rows one refresh pass handles for this table.
+int64_t prefill_pass_rows(const lacache_seq *seqs, int32_t batch) {
+  int64_t most = 0;
+  for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
+    int64_t t = 0;
+    for (int i = s0; i < std::min(batch, s0 + kMaxInline); ++i) t += seqs[i].seq_len;
+    most = std::max(most, std::min<int64_t>(t, lc::kPrefillChunk));
+  }
+  return most;
+}
+
 lc::SeqArgs slice_args(const lacache_seq *seqs, int s0, int ns) {
   lc::SeqArgs sa;
   std::memset(&sa, 0, sizeof(sa));
@@ -297,6 +340,7 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   if (e == hipSuccess) e = hipMalloc(&ctx->flags, 256);
   if (e == hipSuccess) e = hipMemset(ctx->flags, 0, 256);
   if (e == hipSuccess) e = lc::setup_kernel_attributes();
+  if (e == hipSuccess) e = lc::setup_gemm_attributes();
   if (e != hipSuccess) {
     if (ctx->rope) (void)hipFree(ctx->rope);
     if (ctx->flags) (void)hipFree(ctx->flags);
@@ -333,8 +377,15 @@ lacache_status lacache_workspace_size(const lacache_ctx *cctx, int32_t op, const
   lacache_status st = check_table(ctx, seqs, batch, -1);
   if (st != LACACHE_OK) return st;
   switch (op) {
-    case LACACHE_OP_PREFILL: *bytes = 0; return LACACHE_OK;
-    case LACACHE_OP_BLOCK_STEP:
+    case LACACHE_OP_PREFILL:
+      *bytes = gemm_capable(ctx) ? gemm_bytes(ctx, prefill_pass_rows(seqs, batch)) : 0;
+      return LACACHE_OK;
+    case LACACHE_OP_BLOCK_STEP: {
+      const int64_t M = block_tokens(seqs, batch);
+      *bytes = partial_bytes(ctx, partial_rows(split_keys(ctx, seqs, batch), seqs, batch)) +
+               (step_uses_gemm(ctx, M) ? gemm_bytes(ctx, M) : 0);
+      return LACACHE_OK;
+    }
     case LACACHE_OP_DUALCACHE_ATTN:
       *bytes = partial_bytes(ctx, partial_rows(split_keys(ctx, seqs, batch), seqs, batch));
       return LACACHE_OK;
@@ -342,11 +393,57 @@ lacache_status lacache_workspace_size(const lacache_ctx *cctx, int32_t op, const
   return fail(ctx, LACACHE_ERR_INVALID_ARG, "unknown op %d", op);
 }
 
+namespace {
+
+// One prep + GEMM pass over tokens [row0, row0 + M) of a slice.
+hipError_t run_qkv_gemm(lacache_ctx *ctx, const lacache_weights *w, const lacache_cache *c, const int32_t *ids,
+                        const lc::SeqArgs &sa, int mode, int row0, int ids_base, int M, const GemmWs &gw,
+                        hipStream_t s) {
+  lc::PrepArgs pa;
+  std::memset(&pa, 0, sizeof(pa));
+  pa.ids = ids;
+  pa.E = w->embed;
+  pa.gamma = w->gamma;
+  pa.h = c->h;
+  pa.A = gw.A;
+  pa.map = gw.map;
+  pa.cs = gw.cs;
+  pa.rope = ctx->rope;
+  pa.flags = ctx->flags;
+  pa.mode = mode;
+  pa.M = M;
+  pa.M_pad = lc::gemm_rows_padded(M);
+  pa.row0 = row0;
+  pa.ids_base = ids_base;
+  pa.vocab = ctx->cfg.vocab;
+  pa.D = ctx->cfg.d_model;
+  pa.dh = ctx->cfg.head_dim;
+  pa.eps = ctx->cfg.rms_eps;
+  hipError_t e = timed(ctx, LACACHE_KERNEL_QKV_PREP, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv_prep(sa, pa, s, ev); });
+  if (e != hipSuccess) return e;
+  lc::GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.A = gw.A;
+  ga.W = w->w_qkv;
+  ga.map = gw.map;
+  ga.cs = gw.cs;
+  ga.q = c->q;
+  ga.k = c->k;
+  ga.v = c->v;
+  ga.flags = ctx->flags;
+  ga.M = M;
+  ga.D = ctx->cfg.d_model;
+  ga.F = features(ctx);
+  ga.H = ctx->cfg.n_heads;
+  ga.Hkv = ctx->cfg.n_kv_heads;
+  return timed(ctx, LACACHE_KERNEL_QKV_GEMM, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv_gemm(ctx->cfg.head_dim, ga, s, ev); });
+}
+
+}  // namespace
+
 lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w, const int32_t *ids,
                                      const lacache_seq *seqs, int32_t batch, const lacache_cache *cache, void *out,
                                      float *lse, void *workspace, size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!ctx) return LACACHE_ERR_INVALID_ARG;
   lacache_status st;
   if ((st = check_device(ctx)) != LACACHE_OK) return st;
@@ -355,6 +452,11 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
   if (!ids) return fail(ctx, LACACHE_ERR_INVALID_ARG, "ids is NULL");
   if (!out || !aligned16(out)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
   if ((st = check_table(ctx, seqs, batch, cache->n_rows)) != LACACHE_OK) return st;
+  const bool gemm = gemm_capable(ctx);
+  const size_t need = gemm ? gemm_bytes(ctx, prefill_pass_rows(seqs, batch)) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
+                workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lc::DType dt = dtype_of(ctx);
   const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads;
@@ -366,10 +468,21 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
       sa.pre[0][i + 1] = sa.pre[0][i] + sa.len[i];
       sa.pre[1][i + 1] = sa.pre[1][i] + (sa.len[i] + lc::kRowsR - 1) / lc::kRowsR;
     }
-    lc::QkvArgs qa = qkv_args(ctx, w, cache, ids, 1);
-    qa.M = sa.pre[0][ns];
-    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv(dt, sa, qa, features(ctx), s, ev); });
-    if (e != hipSuccess) return hip_fail(ctx, "prefill qkv launch", e);
+    hipError_t e = hipSuccess;
+    if (gemm) {
+      // Rows of the slice in passes of at most kPrefillChunk tokens.
+      for (int r0 = 0; r0 < sa.pre[0][ns]; r0 += lc::kPrefillChunk) {
+        const int Mc = std::min(lc::kPrefillChunk, sa.pre[0][ns] - r0);
+        const GemmWs gw = gemm_layout(ctx, workspace, Mc);
+        e = run_qkv_gemm(ctx, w, cache, ids, sa, 1, r0, 0, Mc, gw, s);
+        if (e != hipSuccess) return hip_fail(ctx, "prefill qkv launch", e);
+      }
+    } else {
+      lc::QkvArgs qa = qkv_args(ctx, w, cache, ids, 1);
+      qa.M = sa.pre[0][ns];
+      e = timed(ctx, LACACHE_KERNEL_QKV, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv(dt, sa, qa, features(ctx), s, ev); });
+      if (e != hipSuccess) return hip_fail(ctx, "prefill qkv launch", e);
+    }
 
     lc::AttnArgs aa;
     std::memset(&aa, 0, sizeof(aa));
@@ -419,7 +532,9 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
   if ((st = check_table(ctx, seqs, batch, cache->n_rows)) != LACACHE_OK) return st;
   const int split = split_keys(ctx, seqs, batch);
   const int64_t P = partial_rows(split, seqs, batch);
-  const size_t need = partial_bytes(ctx, P);
+  const int64_t Mall = block_tokens(seqs, batch);
+  const bool gemm = step_uses_gemm(ctx, Mall);
+  const size_t need = partial_bytes(ctx, P) + (gemm ? gemm_bytes(ctx, Mall) : 0);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
                 workspace);
@@ -427,6 +542,7 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
   const lc::DType dt = dtype_of(ctx);
   const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads;
   const Partials part = partial_layout(ctx, workspace, P);
+  char *gemm_ws = static_cast<char *>(workspace) + partial_bytes(ctx, P);
 
   int row_base = 0, part_base = 0;
   for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
@@ -437,10 +553,15 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
       sa.pre[2][i + 1] = sa.pre[2][i] + (sa.len[i] - (sa.be[i] - sa.bs[i]) + lc::kRowsB - 1) / lc::kRowsB;
     const int M = sa.pre[0][ns];
 
-    lc::QkvArgs qa = qkv_args(ctx, w, cache, block_ids, 0);
-    qa.M = M;
-    qa.ids_base = row_base;
-    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv(dt, sa, qa, features(ctx), s, ev); });
+    hipError_t e = hipSuccess;
+    if (gemm) {
+      e = run_qkv_gemm(ctx, w, cache, block_ids, sa, 0, 0, row_base, M, gemm_layout(ctx, gemm_ws, M), s);
+    } else {
+      lc::QkvArgs qa = qkv_args(ctx, w, cache, block_ids, 0);
+      qa.M = M;
+      qa.ids_base = row_base;
+      e = timed(ctx, LACACHE_KERNEL_QKV, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv(dt, sa, qa, features(ctx), s, ev); });
+    }
     if (e != hipSuccess) return hip_fail(ctx, "block-step qkv launch", e);
 
     lc::AttnArgs aa;

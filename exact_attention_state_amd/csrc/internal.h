@@ -29,6 +29,38 @@ struct QkvArgs {
   float eps;
 };
 
+// Many-token path (bf16 parameters): prep kernel (gather, EmbedCache write,
+// normalised fp16 activation, per-token cache row and position), then the
+// MFMA GEMM with RoPE and the cache write in its epilogue.
+struct PrepArgs {
+  const int *ids;          // as QkvArgs
+  const void *E, *gamma;   // bf16
+  void *h;                 // EmbedCache
+  void *A;                 // [M_pad, D] fp16 normalised activations (workspace)
+  int2 *map;               // [M_pad] (cache row, position) per token (workspace)
+  float2 *cs;              // [M_pad, dh/2] (cos, sin) of each token's position (workspace)
+  const float2 *rope;      // [max_pos, dh/2] (cos, sin)
+  unsigned *flags;
+  int mode;                // 0: block step, 1: prefill
+  int M, M_pad;            // tokens of this launch, rounded up to the GEMM row tile
+  int row0;                // index of the launch's first token among the slice's tokens
+  int ids_base;            // mode 0: index of the slice's first token in `ids`
+  int vocab, D, dh;
+  float eps;
+};
+struct GemmArgs {
+  const void *A;           // [M_pad, D] fp16
+  const void *W;           // [F, D] bf16
+  const int2 *map;         // [M] (cache row, position)
+  const float2 *cs;        // [M_pad, dh/2] (cos, sin) per token
+  void *q, *k, *v;         // fp16 RoPECache
+  unsigned *flags;
+  int M, D, F, H, Hkv;
+};
+constexpr int kGemmMinTokens = 128;    // block steps with fewer tokens use the streaming kernel
+constexpr int kPrefillChunk = 4096;    // refresh rows per prep + GEMM pass
+int gemm_rows_padded(int M);
+
 // Attention kernels: block-row split partials (type A), invariant rows from
 // FACache (type B), the refresh, and the merge of partials.
 struct AttnArgs {
@@ -69,6 +101,9 @@ inline void lc_launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned 
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_qkv_prep(const SeqArgs &sa, const PrepArgs &a, hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const LaunchEvents &ev);
+hipError_t setup_gemm_attributes();
 hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                              hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_invariant_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, int M,

@@ -27,7 +27,7 @@ EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "laca
             "lacache_block_step", "lacache_dualcache_attn", "lacache_read_device_status",
             "lacache_profile_enable", "lacache_profile_read", "lacache_status_string", "lacache_last_error")
 KERNEL_QKV, KERNEL_STEP_ATTN, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_DUAL_ATTN = range(5)
-KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn")
+KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn", "qkv_prep", "qkv_gemm")
 
 
 class Config(ctypes.Structure):

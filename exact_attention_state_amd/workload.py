@@ -42,7 +42,9 @@ class DeviceWorkload:
         return t.to(self.device)
 
     def prefill(self, stream=None):
-        self.ctx.prefill_cache(self.weights, self.upload_ids(self.ids_host), self.table, self.ct, stream=stream)
+        ws = self.ctx.alloc_workspace(lacache.OP_PREFILL, self.table, self.device)
+        self.ctx.prefill_cache(self.weights, self.upload_ids(self.ids_host), self.table, self.ct, workspace=ws,
+                               stream=stream)
 
     def next_block_ids(self):
         """Advance the host ids by one edit step; returns the device block ids."""

@@ -235,7 +235,9 @@ typedef enum {
                                         the merge of the block rows' partials      */
   LACACHE_KERNEL_MERGE = 3,          /* DualCache: merge of the partials            */
   LACACHE_KERNEL_REFRESH_ATTN = 4,   /* refresh attention with FACache snapshot     */
-  LACACHE_KERNEL_COUNT = 5
+  LACACHE_KERNEL_QKV_PREP = 5,       /* many tokens: gather, EmbedCache, RMSNorm    */
+  LACACHE_KERNEL_QKV_GEMM = 6,       /* many tokens: QKV GEMM + RoPE + cache write  */
+  LACACHE_KERNEL_COUNT = 7
 } lacache_kernel;
 
 LACACHE_API lacache_status lacache_profile_enable(lacache_ctx *ctx, int enable);

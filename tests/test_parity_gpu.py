@@ -277,7 +277,8 @@ def test_rows_outside_the_block_table_are_untouched():
     for t in dw.ct.__dict__.values():
         if t.dtype in (torch.float32, torch.float16, torch.bfloat16):
             t.fill_(-1024.0)
-    dw.ctx.prefill_cache(dw.weights, torch.from_numpy(ids).cuda(), table, dw.ct)
+    dw.ctx.prefill_cache(dw.weights, torch.from_numpy(ids).cuda(), table, dw.ct,
+                         workspace=dw.ctx.alloc_workspace(lacache.OP_PREFILL, table))
     torch.cuda.synchronize()
     outside = np.r_[0:3, 75:92, 174:n_rows]
     for k in ("h", "q", "k", "v", "out", "lse", "m", "l", "o"):
