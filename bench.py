@@ -195,7 +195,10 @@ def main():
         # An independent copy of the layer: its own W_qkv, caches and workspace.
         s = DeviceWorkload.__new__(DeviceWorkload)
         s.__dict__.update(base.__dict__)
-        s.weights = (base.weights[0], base.weights[1], base.weights[2].clone())
+        w2 = base.weights[2].clone()
+        s.weights = (base.weights[0], base.weights[1], w2)
+        if len(base.weights) > 3:
+            s.weights = s.weights + (ctx.pack_qkv_weight(w2),)
         s.ct = ctx.alloc_cache(base.n_rows, dev)
         s.ws = ctx.alloc_workspace(lacache.OP_BLOCK_STEP, base.table, dev)
         sets.append(s)

@@ -256,8 +256,10 @@ lacache_status check_cache(lacache_ctx *ctx, const lacache_cache *c, bool facach
 
 lacache_status check_weights(lacache_ctx *ctx, const lacache_weights *w) {
   if (!w || !w->embed || !w->gamma || !w->w_qkv) return fail(ctx, LACACHE_ERR_INVALID_ARG, "weights or a weight pointer is NULL");
-  if (!aligned16(w->embed) || !aligned16(w->gamma) || !aligned16(w->w_qkv))
+  if (!aligned16(w->embed) || !aligned16(w->gamma) || !aligned16(w->w_qkv) || !aligned16(w->w_qkv_packed))
     return fail(ctx, LACACHE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  if (w->w_qkv_packed && !gemm_capable(ctx))
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "w_qkv_packed given, but this configuration has no packed form");
   return LACACHE_OK;
 }
 
@@ -425,6 +427,7 @@ hipError_t run_qkv_gemm(lacache_ctx *ctx, const lacache_weights *w, const lacach
   std::memset(&ga, 0, sizeof(ga));
   ga.A = gw.A;
   ga.W = w->w_qkv;
+  ga.Wp = w->w_qkv_packed;
   ga.map = gw.map;
   ga.cs = gw.cs;
   ga.q = c->q;
@@ -653,6 +656,30 @@ lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *q_block, con
     row_base += M;
     part_base += sa.pre[3][ns];
   }
+  return LACACHE_OK;
+}
+
+lacache_status lacache_packed_weight_size(const lacache_ctx *ctx, size_t *bytes) {
+  if (!ctx || !bytes) return LACACHE_ERR_INVALID_ARG;
+  *bytes = gemm_capable(ctx) ? lc::packed_qkv_weight_bytes(ctx->cfg.d_model, features(ctx)) : 0;
+  return LACACHE_OK;
+}
+
+lacache_status lacache_pack_qkv_weight(lacache_ctx *ctx, const void *w_qkv, void *w_packed, size_t packed_bytes,
+                                       void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if (!gemm_capable(ctx))
+    return fail(ctx, LACACHE_ERR_UNSUPPORTED, "packed weights need bf16 and d_model a multiple of 512");
+  if (!w_qkv || !w_packed || !aligned16(w_qkv) || !aligned16(w_packed))
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "w_qkv or w_packed is NULL or not 16-byte aligned");
+  const size_t need = lc::packed_qkv_weight_bytes(ctx->cfg.d_model, features(ctx));
+  if (packed_bytes < need)
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "w_packed holds %zu bytes, %zu needed", packed_bytes, need);
+  const hipError_t e = lc::launch_pack_qkv_weight(w_qkv, w_packed, ctx->cfg.d_model, features(ctx),
+                                                  ctx->cfg.head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(ctx, "pack launch", e);
   return LACACHE_OK;
 }
 

@@ -11,23 +11,37 @@
 //   gemm   C = A W^T on v_mfma_f32_16x16x32_f16, then RoPE and the fp16
 //          cache write in the epilogue.
 //
-// Tiling of the GEMM (128 tokens x 192 features per workgroup, 8 waves of
-// 64 x 48, 64-wide contraction tiles): A (fp16) and W (bf16, as stored) are
-// copied global -> LDS by the load unit (global_load_lds_dwordx4) into a
-// 3-stage ring, 16-byte pieces XOR-swizzled by row so the operand reads hit
-// distinct banks; each wave converts the W pieces it copied to fp16 in
-// place, one tile ahead of their use (exact for weights in fp16's normal
-// range).  One workgroup barrier per contraction tile.  GEMM column j of a 16-column block holds RoPE pairs as
-// in the small-batch kernel (features p..p+7 and p+d_h/2..p+d_h/2+7), so a
-// rotation partner is 8 lanes away.  Consecutive workgroups take consecutive
-// column tiles, so the row tiles of one column tile land on one XCD and
-// share its weight tile in that XCD's L2.
+// Operand tiles: 128 tokens x 64 contraction elements of A (16 KB) and 192
+// GEMM columns x 64 elements of W (24 KB) per stage of a 4-stage LDS ring,
+// filled global -> LDS by the load unit (global_load_lds_dwordx4).  A tile
+// row is 128 bytes; its 16-byte piece p sits in slot p ^ ((r >> 1) & 7), so
+// the 16 rows of one MFMA operand read hit all 64 banks once.  prep writes A
+// in exactly that tile order ([row tile][contraction tile][128 x 64],
+// swizzled), so each 1 KB copy instruction reads 1 KB of contiguous memory.
+//
+// Two GEMM kernels, by the form of W:
+//   packed  W converted once to fp16 in the same tile order (see
+//           pack_qkv_weight_kernel): contiguous copies, no conversion in the
+//           loop.  The contraction is split over two groups of four waves
+//           (64 tokens x 96 columns per wave); the kernel computes C^T so a
+//           lane's four accumulator values are four GEMM columns of one token,
+//           and the column order puts both members of two RoPE pairs in one
+//           lane: RoPE needs no lane exchange.
+//   bf16    W as stored, row-major bf16: rows gathered per copy, each wave
+//           converts the pieces it copied to fp16 in place one tile ahead,
+//           between the MFMAs of the current tile; 8 waves of 64 x 48.
+// Both convert bf16 weights to fp16 the same way (exact for weights in
+// fp16's normal range).  Consecutive workgroups take consecutive column
+// tiles, so the row tiles of one column tile land on one XCD and share its
+// weight tile in that XCD's L2.
 //
 // Precision: one fp16 rounding of the normalised activation (11-bit
 // significand, 8x finer than bf16) and fp32 accumulation; the small-batch
 // kernel instead keeps gamma * E exact with a bf16 hi/lo split, which costs
 // twice the matrix-core work - affordable only where the step is bound by
 // streaming the weights.
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -58,6 +72,28 @@ __device__ __forceinline__ uint32_t f16pair(float a, float b) {
 }
 
 // ---------------------------------------------------------------------------
+// tiling shared by prep, the pack kernel and the GEMMs
+// ---------------------------------------------------------------------------
+constexpr int kGBM = 128, kGBN = 192, kGBK = 64, kGStages = 4, kGWaves = 8;
+constexpr int kGStageA = kGBM * kGBK * 2;          // bytes: fp16 A tile
+constexpr int kGStageW = kGBN * kGBK * 2;          // bytes: W tile (fp16; bf16 until converted)
+constexpr int kGStage = kGStageA + kGStageW;
+constexpr int kGemmSmem = kGStages * kGStage;      // 160 KB
+constexpr int kGCopyA = kGStageA / 1024 / kGWaves;  // copy instructions per wave per stage (1 KB each)
+constexpr int kGCopyW = kGStageW / 1024 / kGWaves;
+constexpr int kGCopies = kGCopyA + kGCopyW;
+static_assert(kGCopyA * 1024 * kGWaves == kGStageA && kGCopyW * 1024 * kGWaves == kGStageW, "copy tiling");
+
+__device__ __forceinline__ int gslot(int r, int p) { return p ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int gswz(int r, int p) { return r * 128 + (gslot(r, p) << 4); }
+
+// Byte offset, in the tiled A, of the 8-element piece starting at element e
+// (a multiple of 8) of token row m; nk = D / 64.
+__device__ __forceinline__ size_t a_piece(int m, int e, int nk) {
+  return ((size_t)(m >> 7) * nk + (e >> 6)) * kGStageA + (m & 127) * 128 + (gslot(m & 127, (e >> 3) & 7) << 4);
+}
+
+// ---------------------------------------------------------------------------
 // prep: one wave per token row m of the launch (rows past M of the padded
 // tile are written as zeros).  Each lane owns D/64 consecutive elements.
 // ---------------------------------------------------------------------------
@@ -67,10 +103,11 @@ __global__ __launch_bounds__(256) void qkv_prep_kernel(const SeqArgs sa, const P
   if (m >= a.M_pad) return;
   const int D = a.D;
   const int per = D / 64;                          // elements per lane (multiple of 4)
-  _Float16 *arow = static_cast<_Float16 *>(a.A) + (size_t)m * D + lane * per;
+  char *abase = static_cast<char *>(a.A);
+  const int nk = D / kGBK;
   float2 *csrow = a.cs + (size_t)m * (a.dh / 2);
   if (m >= a.M) {
-    for (int j = 0; j < per; j += 8) *reinterpret_cast<uint4 *>(arow + j) = make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < per; j += 8) *reinterpret_cast<uint4 *>(abase + a_piece(m, lane * per + j, nk)) = make_uint4(0, 0, 0, 0);
     if (lane < a.dh / 2) csrow[lane] = make_float2(0.f, 0.f);
     return;
   }
@@ -119,48 +156,21 @@ __global__ __launch_bounds__(256) void qkv_prep_kernel(const SeqArgs sa, const P
       range = range && fabsf(y0) <= kF16Max && fabsf(y1) <= kF16Max;
       o[q] = f16pair(y0, y1);
     }
-    *reinterpret_cast<uint4 *>(arow + j) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4 *>(abase + a_piece(m, lane * per + j, nk)) = make_uint4(o[0], o[1], o[2], o[3]);
   }
   if (!range) atomicOr(a.flags, 2u);
   if (lane == 0) a.map[m] = make_int2(dst, pos);
   if (lane < a.dh / 2) csrow[lane] = a.rope[(size_t)pos * (a.dh / 2) + lane];
 }
 
-// ---------------------------------------------------------------------------
-// gemm
-// ---------------------------------------------------------------------------
-#ifndef LC_GEMM_IL
-#define LC_GEMM_IL 1
-#endif
-constexpr int kGBM = 128, kGBN = 192, kGBK = 64, kGStages = LC_GEMM_IL ? 4 : 3;
-#ifndef LC_GEMM_WM
-#define LC_GEMM_WM 2
-#define LC_GEMM_WN 4
-#endif
-constexpr int kGWM = LC_GEMM_WM, kGWN = LC_GEMM_WN;   // wave grid (rows x columns of the tile)
-constexpr int kGWaves = kGWM * kGWN;
-constexpr int kGRB = kGBM / kGWM / 16, kGCB = kGBN / kGWN / 16;   // 16x16 blocks per wave
-constexpr int kGStageA = kGBM * kGBK * 2;          // bytes: fp16 A tile
-constexpr int kGStageW = kGBN * kGBK * 2;          // bytes: W tile (bf16 as copied, fp16 once converted)
-constexpr int kGStage = kGStageA + kGStageW;
-constexpr int kGemmSmem = kGStages * kGStage;
-constexpr int kGCopyA = kGStageA / 1024 / kGWaves;  // copy instructions per wave per stage (1 KB each)
-constexpr int kGCopyW = kGStageW / 1024 / kGWaves;
-constexpr int kGCopies = kGCopyA + kGCopyW;
-static_assert(kGCopyA * 1024 * kGWaves == kGStageA && kGCopyW * 1024 * kGWaves == kGStageW, "copy tiling");
-
-// Tile rows are 128 bytes (64 contraction elements); 16-byte piece p of row r
-// sits in slot p ^ ((r >> 1) & 7): the 16 consecutive rows of one operand
-// read then cover all 64 banks once.
-__device__ __forceinline__ int gslot(int r, int p) { return p ^ ((r >> 1) & 7); }
-__device__ __forceinline__ int gswz(int r, int p) { return r * 128 + (gslot(r, p) << 4); }
+constexpr int kGWN = 4, kGRB = kGBM / 2 / 16, kGCB = kGBN / kGWN / 16;   // 2 x 4 waves of 64 x 48
 
 template <int DH>
-__global__ __launch_bounds__(64 * kGWaves) void qkv_gemm_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(64 * kGWaves) void qkv_gemm_bf16_kernel(const GemmArgs a) {
   extern __shared__ __align__(16) char smem[];    // kGStages x (A tile, W tile)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int wm = w / kGWN, wn = w % kGWN;          // this wave: rows 16*kGRB*wm.., columns 16*kGCB*wn..
+  const int wm = w / kGWN, wn = w % kGWN;          // this wave: rows 64*wm.., columns 48*wn..
   const int n0 = blockIdx.x * kGBN, m0 = blockIdx.y * kGBM;
   const int D = a.D;
   const int cbh = DH / 16;
@@ -169,15 +179,16 @@ __global__ __launch_bounds__(64 * kGWaves) void qkv_gemm_kernel(const GemmArgs a
 
   // Sources of this wave's copy instructions: instruction j fills LDS pieces
   // [(j*kGWaves + w)*64, +64) of the tile, 8 rows of 8 pieces; piece slot s
-  // of row r receives global piece s ^ ((r >> 1) & 7).  W tile rows are GEMM
-  // columns, mapped to weight rows (columns past F repeat the last block).
-  const _Float16 *asrc[kGCopyA];
+  // of row r receives global piece s ^ ((r >> 1) & 7).  A is tiled already;
+  // W tile rows are GEMM columns, mapped to weight rows (columns past F
+  // repeat the last block).
+  const int nk = D / kGBK;
+  const char *asrc[kGCopyA];
   int aoff[kGCopyA];
 #pragma unroll
   for (int j = 0; j < kGCopyA; ++j) {
-    const int base = (j * kGWaves + w) * 64, idx = base + lane;
-    const int r = idx >> 3, slot = idx & 7;
-    asrc[j] = static_cast<const _Float16 *>(a.A) + (size_t)(m0 + r) * D + (gslot(r, slot) << 3);
+    const int base = (j * kGWaves + w) * 64;
+    asrc[j] = static_cast<const char *>(a.A) + (size_t)blockIdx.y * nk * kGStageA + (size_t)(base + lane) * 16;
     aoff[j] = __builtin_amdgcn_readfirstlane(base * 16);
   }
   const bf16_t *wsrc[kGCopyW];
@@ -196,7 +207,7 @@ __global__ __launch_bounds__(64 * kGWaves) void qkv_gemm_kernel(const GemmArgs a
     const uint32_t st = smem_lds + (kt % kGStages) * kGStage;
     const int k0 = kt * kGBK;
 #pragma unroll
-    for (int j = 0; j < kGCopyA; ++j) dma16(asrc[j] + k0, st + aoff[j]);
+    for (int j = 0; j < kGCopyA; ++j) dma16(asrc[j] + (size_t)kt * kGStageA, st + aoff[j]);
 #pragma unroll
     for (int j = 0; j < kGCopyW; ++j) dma16(wsrc[j] + k0, st + woff[j]);
   };
@@ -221,10 +232,8 @@ __global__ __launch_bounds__(64 * kGWaves) void qkv_gemm_kernel(const GemmArgs a
 #pragma unroll
     for (int j = 0; j < kGCB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = D / kGBK;
-#if LC_GEMM_IL
-  // 4-stage ring: tile kt+1 is converted during iteration kt, its conversion
-  // arithmetic interleaved with the MFMAs of tile kt.
+  // Tile kt+1 is converted during iteration kt, its conversion arithmetic
+  // interleaved with the MFMAs of tile kt.
   issue(0);
   if (nk > 1) issue(1);
   if (nk > 2) issue(2);
@@ -287,49 +296,6 @@ __global__ __launch_bounds__(64 * kGWaves) void qkv_gemm_kernel(const GemmArgs a
     __builtin_amdgcn_sched_group_barrier(0x200, kGCopyW, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, kGRB * kGCB, 0);
   }
-#else
-  issue(0);
-  if (nk > 1) {
-    issue(1);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | kGCopies);            // vmcnt(kGCopies): tile 0 landed
-  } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-  }
-  convert(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // After the barrier tile kt is converted and visible, and the stage read
-    // in iteration kt-1 is free for tile kt+2.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    if (kt + 2 < nk) issue(kt + 2);
-    const char *st = smem + (kt % kGStages) * kGStage;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      Frag<f16_t> af[kGRB], wf[kGCB];
-#pragma unroll
-      for (int i = 0; i < kGRB; ++i) {
-        const int r = (wm * kGRB + i) * 16 + r16;
-        af[i].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + gswz(r, 4 * ks + g)));
-      }
-#pragma unroll
-      for (int j = 0; j < kGCB; ++j) {
-        const int c = (wn * kGCB + j) * 16 + r16;
-        wf[j].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + kGStageA + gswz(c, 4 * ks + g)));
-      }
-#pragma unroll
-      for (int i = 0; i < kGRB; ++i)
-#pragma unroll
-        for (int j = 0; j < kGCB; ++j) mma16(acc[i][j], af[i], wf[j]);
-    }
-    if (kt + 1 < nk) {
-      // Tile kt+1: this wave's copies landed (tile kt+2's may stay in flight).
-      if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | kGCopies);
-      else __builtin_amdgcn_s_waitcnt(0x0F70);
-      convert(kt + 1);
-    }
-  }
-#endif
 
   // Epilogue.  The ring is free once every wave is past its last reads: the
   // tile's per-token (cos, sin) rows are copied into it, RoPE is applied to
@@ -400,6 +366,236 @@ __global__ __launch_bounds__(64 * kGWaves) void qkv_gemm_kernel(const GemmArgs a
   }
 }
 
+// ---------------------------------------------------------------------------
+// packed GEMM.  The 8 waves form two groups of 2 x 2; both groups cover the
+// whole 128 x 192 tile (64 tokens x 96 columns per wave, 6 x 4 accumulator
+// blocks), group 0 on the first 32 of each tile's 64 contraction elements
+// and group 1 on the second.  Per contraction tile a wave reads 10 operand
+// fragments for 24 MFMAs; the fragments of tile kt+1 are read right after
+// the barrier that publishes it, interleaved with the MFMAs of tile kt.
+// At the end each wave hands half of its blocks to its partner in the other
+// group through LDS, and each finishes the half it keeps.
+//
+// Column order inside a 16-column block cb of head hh (pairs p0..p0+7,
+// p0 = 8 * (cb mod d_h/16)): column 4g + v is feature p0 + 2g + (v >> 1)
+// of the head's first half for even v and its RoPE partner in the second
+// half for odd v.  With C^T on the matrix core, lane (g, t) holds columns
+// 4g..4g+3 of token t: two complete pairs.
+// ---------------------------------------------------------------------------
+constexpr int kPRB = 4, kPCB = 6;                     // token blocks x column blocks per wave
+constexpr int kPRedBytes = kGWaves * kPCB * 2 * 1024;  // blocks handed over: 96 KB
+
+__device__ __forceinline__ int packed_weight_row(int gc, int F, int dh) {
+  const int ncb = F / 16, cbh = dh / 16;
+  const int cb = min(gc >> 4, ncb - 1), cc = gc & 15;  // columns past F repeat the last block
+  const int hh = cb / cbh, p0 = (cb % cbh) * 8;
+  return hh * dh + (cc & 1) * (dh / 2) + p0 + 2 * (cc >> 2) + ((cc >> 1) & 1);
+}
+
+// Wp[n][kt][c][s] (16-byte pieces): column tile n of kGBN GEMM columns,
+// contraction tile kt; piece slot s of row c holds elements
+// kt*64 + 8*(s ^ ((c >> 1) & 7)) .. +7 of weight row
+// packed_weight_row(n*kGBN + c), as fp16.
+__global__ __launch_bounds__(256) void pack_qkv_weight_kernel(const bf16_t *W, uint4 *Wp, int D, int F, int dh,
+                                                              size_t n_pieces) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_pieces) return;
+  const int nk = D / kGBK;
+  const int s = (int)(idx & 7);
+  const size_t rest = idx >> 3;
+  const int c = (int)(rest % kGBN);
+  const size_t tk = rest / kGBN;
+  const int kt = (int)(tk % nk), n = (int)(tk / nk);
+  const int wrow = packed_weight_row(n * kGBN + c, F, dh);
+  const uint4 u = *reinterpret_cast<const uint4 *>(W + (size_t)wrow * D + kt * kGBK + 8 * gslot(c, s));
+  Wp[idx] = make_uint4(f16pair(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u)),
+                       f16pair(__uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)),
+                       f16pair(__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u)),
+                       f16pair(__uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u)));
+}
+
+template <int DH>
+__global__ __launch_bounds__(512) void qkv_gemm_packed_kernel(const GemmArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int kg = w >> 2, wq = w & 3, wm = wq >> 1, wn = wq & 1;
+  const int D = a.D, nk = D / kGBK;                  // nk: a multiple of 8
+  const int cbh = DH / 16, ncb = a.F / 16;
+  const int n0 = blockIdx.x * kGBN, m0 = blockIdx.y * kGBM;
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  // Cache row of tile row tid, for the stores; its latency hides behind the loop.
+  const int my_dst = tid < kGBM ? a.map[min(m0 + tid, a.M - 1)].x : 0;
+
+  // Copy j of wave w moves pieces [(j*8 + w)*64, +64) of a stage: 1 KB at
+  // byte j*8192 + w*1024 of both the tiled source and the LDS tile.
+  const uint32_t lw = __builtin_amdgcn_readfirstlane(w * 1024);
+  const char *asrc = static_cast<const char *>(a.A) + (size_t)blockIdx.y * nk * kGStageA + (size_t)(w * 64 + lane) * 16;
+  const char *wsrc = static_cast<const char *>(a.Wp) + (size_t)blockIdx.x * nk * kGStageW + (size_t)(w * 64 + lane) * 16;
+  auto issue = [&](int kt) {
+    const uint32_t st = smem_lds + (kt % kGStages) * kGStage + lw;
+    const char *as = asrc + (size_t)kt * kGStageA, *ws = wsrc + (size_t)kt * kGStageW;
+#pragma unroll
+    for (int j = 0; j < kGCopyA; ++j) dma16(as + j * 8192, st + j * 8192);
+#pragma unroll
+    for (int j = 0; j < kGCopyW; ++j) dma16(ws + j * 8192, st + kGStageA + j * 8192);
+  };
+  auto frags = [&](int kt, Frag<f16_t> (&fa)[kPRB], Frag<f16_t> (&fw)[kPCB]) {
+    const char *st = smem + (kt % kGStages) * kGStage;
+#pragma unroll
+    for (int i = 0; i < kPRB; ++i)
+      fa[i].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + gswz((wm * kPRB + i) * 16 + r16, 4 * kg + g)));
+#pragma unroll
+    for (int j = 0; j < kPCB; ++j)
+      fw[j].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + kGStageA + gswz((wn * kPCB + j) * 16 + r16, 4 * kg + g)));
+  };
+
+  f32x4_t acc[kPCB][kPRB];                           // C^T blocks: lane (g, t) holds columns 4g..4g+3 of token t
+#pragma unroll
+  for (int j = 0; j < kPCB; ++j)
+#pragma unroll
+    for (int i = 0; i < kPRB; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // One contraction tile (kt + 1 < nk): tile kt+1 published (this wave's
+  // copies landed, then the barrier), the fragments of tile kt+1 read, the
+  // MFMAs of tile kt, and the copy of tile kt+3 issued into the stage tile
+  // kt-1 left (its fragments were consumed before the barrier).  Copies in
+  // flight on entry: tiles kt+1 and kt+2.
+  auto step = [&](int kt, const Frag<f16_t> (&ca)[kPRB], const Frag<f16_t> (&cw)[kPCB],
+                  Frag<f16_t> (&na)[kPRB], Frag<f16_t> (&nw)[kPCB]) {
+    if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | kGCopies);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
+    frags(kt + 1, na, nw);
+    // Fragment reads first, interleaved with the first half of the MFMAs;
+    // the copy of tile kt+3 goes out after them, so its LDS writes do not
+    // compete with this wave's reads.
+    constexpr int H1 = kPCB / 2, F1 = kPRB * H1, R = kPRB + kPCB;
+    static_assert(F1 >= R, "reads fit in the first half");
+#pragma unroll
+    for (int j = 0; j < H1; ++j)
+#pragma unroll
+      for (int i = 0; i < kPRB; ++i) mma16(acc[j][i], cw[j], ca[i]);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, F1 - R, 0);
+    if (kt + kGStages - 1 < nk) issue(kt + kGStages - 1);
+#pragma unroll
+    for (int j = H1; j < kPCB; ++j)
+#pragma unroll
+      for (int i = 0; i < kPRB; ++i) mma16(acc[j][i], cw[j], ca[i]);
+  };
+  issue(0);
+  issue(1);
+  issue(2);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kGCopies));
+  lds_barrier();
+  Frag<f16_t> fa0[kPRB], fw0[kPCB], fa1[kPRB], fw1[kPCB];
+  frags(0, fa0, fw0);
+  // No branch around the fragment reads inside the loop: the wait before the
+  // MFMAs then covers only the previous tile's reads.
+  for (int kt = 0; kt < nk - 2; kt += 2) {
+    step(kt, fa0, fw0, fa1, fw1);
+    step(kt + 1, fa1, fw1, fa0, fw0);
+  }
+  step(nk - 2, fa0, fw0, fa1, fw1);
+#pragma unroll
+  for (int j = 0; j < kPCB; ++j)
+#pragma unroll
+    for (int i = 0; i < kPRB; ++i) mma16(acc[j][i], fw1[j], fa1[i]);
+
+  // Epilogue.  Group kg keeps token blocks 2kg, 2kg+1 of its wave's four and
+  // hands the other two to its partner (wave w ^ 4, same region, other half
+  // of the contraction).  Then RoPE per lane into an fp16 output tile [128
+  // tokens][192 columns in run order: per block the 8 first-half features,
+  // then their 8 partners], which all waves store as 16-byte runs.
+  constexpr int OST = kGBN + 8;                      // fp16 elements per output row (pad: banks)
+  constexpr int OT_BYTES = kGBM * OST * 2;
+  static_assert(OT_BYTES + kGBM * 4 <= kPRedBytes && kPRedBytes <= kGemmSmem, "epilogue fits the ring");
+  f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
+  _Float16 *otile = reinterpret_cast<_Float16 *>(smem);
+  int *s_dst = reinterpret_cast<int *>(smem + OT_BYTES);
+  const int nrot = (a.H + a.Hkv) * DH;
+  bool range = true;
+  auto finish = [&](auto KG) {
+    constexpr int own = 2 * decltype(KG)::value, other = 2 - own;
+    // (cos, sin) of pairs p0+2g and p0+2g+1 for each kept block's token.
+    uint4 csv[kPCB][2];
+#pragma unroll
+    for (int j = 0; j < kPCB; ++j) {
+      const int cb = min((n0 >> 4) + wn * kPCB + j, ncb - 1);
+      const int hh = cb / cbh, p0 = (cb % cbh) * 8;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int t = (wm * kPRB + own + ii) * 16 + r16;
+        csv[j][ii] = hh * DH < nrot ? *reinterpret_cast<const uint4 *>(a.cs + (size_t)(m0 + t) * (DH / 2) + p0 + 2 * g)
+                                    : make_uint4(0, 0, 0, 0);
+      }
+    }
+    lds_barrier();                                   // every wave is past its last ring reads
+#pragma unroll
+    for (int j = 0; j < kPCB; ++j)
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) red[(w * kPCB * 2 + j * 2 + ii) * 64 + lane] = acc[j][other + ii];
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < kPCB; ++j)
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) acc[j][own + ii] += red[((w ^ 4) * kPCB * 2 + j * 2 + ii) * 64 + lane];
+    lds_barrier();                                   // hand-over area free for the output tile
+#pragma unroll
+    for (int j = 0; j < kPCB; ++j) {
+      const int jb = wn * kPCB + j;
+      const int cb = min((n0 >> 4) + jb, ncb - 1);
+      const bool rot = cb / cbh * DH < nrot;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int t = (wm * kPRB + own + ii) * 16 + r16;
+        const f32x4_t y = acc[j][own + ii];
+        float o0 = y[0], o1 = y[1], o2 = y[2], o3 = y[3];
+        if (rot) {
+          const uint4 c = csv[j][ii];
+          const float c0 = __uint_as_float(c.x), s0 = __uint_as_float(c.y);
+          const float c1 = __uint_as_float(c.z), s1 = __uint_as_float(c.w);
+          o0 = y[0] * c0 - y[1] * s0;
+          o1 = y[1] * c0 + y[0] * s0;
+          o2 = y[2] * c1 - y[3] * s1;
+          o3 = y[3] * c1 + y[2] * s1;
+        }
+        range = range && fabsf(o0) <= kF16Max && fabsf(o1) <= kF16Max && fabsf(o2) <= kF16Max && fabsf(o3) <= kF16Max;
+        *reinterpret_cast<uint32_t *>(otile + t * OST + jb * 16 + 2 * g) = f16pair(o0, o2);
+        *reinterpret_cast<uint32_t *>(otile + t * OST + jb * 16 + 8 + 2 * g) = f16pair(o1, o3);
+      }
+    }
+  };
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (kg == 0) finish(std::integral_constant<int, 0>{});
+  else finish(std::integral_constant<int, 1>{});
+  if (tid < kGBM) s_dst[tid] = my_dst;
+  if (!range) atomicOr(a.flags, 2u);
+  lds_barrier();
+  // 128 rows x 24 runs of 8 features per tile.
+  const int qf = a.H * DH, kf = a.Hkv * DH;
+  for (int t = tid; t < kGBM * (kGBN / 8); t += 64 * kGWaves) {
+    const int row = t / (kGBN / 8), run = t % (kGBN / 8);
+    const int m = m0 + row;
+    const int cb = (n0 >> 4) + (run >> 1);
+    if (m >= a.M || cb >= ncb) continue;
+    const int hh = cb / cbh, p0 = (cb % cbh) * 8;
+    const int feat = hh * DH + ((run & 1) ? DH / 2 + p0 : p0);
+    const int dst = s_dst[row];
+    const uint4 val = *reinterpret_cast<const uint4 *>(otile + row * OST + run * 8);
+    f16_t *out;
+    if (feat < qf) out = static_cast<f16_t *>(a.q) + (size_t)dst * qf + feat;
+    else if (feat < qf + kf) out = static_cast<f16_t *>(a.k) + (size_t)dst * kf + (feat - qf);
+    else out = static_cast<f16_t *>(a.v) + (size_t)dst * kf + (feat - qf - kf);
+    *reinterpret_cast<uint4 *>(out) = val;
+  }
+}
+
 int gemm_rows_padded(int M) { return (M + kGBM - 1) / kGBM * kGBM; }
 
 hipError_t launch_qkv_prep(const SeqArgs &sa, const PrepArgs &a, hipStream_t s, const LaunchEvents &ev) {
@@ -408,21 +604,39 @@ hipError_t launch_qkv_prep(const SeqArgs &sa, const PrepArgs &a, hipStream_t s, 
   return hipGetLastError();
 }
 
+size_t packed_qkv_weight_bytes(int D, int F) { return (size_t)((F + kGBN - 1) / kGBN) * kGBN * D * 2; }
+
+hipError_t launch_pack_qkv_weight(const void *W, void *Wp, int D, int F, int dh, hipStream_t s) {
+  const size_t n = packed_qkv_weight_bytes(D, F) / 16;
+  if (n == 0) return hipSuccess;
+  pack_qkv_weight_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+      static_cast<const bf16_t *>(W), static_cast<uint4 *>(Wp), D, F, dh, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const LaunchEvents &ev) {
   if (a.M <= 0) return hipSuccess;
   dim3 grid((a.F + kGBN - 1) / kGBN, (a.M + kGBM - 1) / kGBM);
-  if (dh == 128) lc_launch(qkv_gemm_kernel<128>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
-  else lc_launch(qkv_gemm_kernel<64>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
+  if (a.Wp) {
+    if (dh == 128) lc_launch(qkv_gemm_packed_kernel<128>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
+    else lc_launch(qkv_gemm_packed_kernel<64>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
+  } else {
+    if (dh == 128) lc_launch(qkv_gemm_bf16_kernel<128>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
+    else lc_launch(qkv_gemm_bf16_kernel<64>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t setup_gemm_attributes() {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(qkv_gemm_kernel<128>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, kGemmSmem);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(qkv_gemm_kernel<64>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kGemmSmem);
-  return e;
+  const void *kernels[] = {reinterpret_cast<const void *>(qkv_gemm_bf16_kernel<128>),
+                           reinterpret_cast<const void *>(qkv_gemm_bf16_kernel<64>),
+                           reinterpret_cast<const void *>(qkv_gemm_packed_kernel<128>),
+                           reinterpret_cast<const void *>(qkv_gemm_packed_kernel<64>)};
+  for (const void *k : kernels) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmSmem);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace lc

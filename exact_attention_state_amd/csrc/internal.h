@@ -36,7 +36,7 @@ struct PrepArgs {
   const int *ids;          // as QkvArgs
   const void *E, *gamma;   // bf16
   void *h;                 // EmbedCache
-  void *A;                 // [M_pad, D] fp16 normalised activations (workspace)
+  void *A;                 // [M_pad, D] fp16 normalised activations, GEMM tile order (workspace)
   int2 *map;               // [M_pad] (cache row, position) per token (workspace)
   float2 *cs;              // [M_pad, dh/2] (cos, sin) of each token's position (workspace)
   const float2 *rope;      // [max_pos, dh/2] (cos, sin)
@@ -49,8 +49,9 @@ struct PrepArgs {
   float eps;
 };
 struct GemmArgs {
-  const void *A;           // [M_pad, D] fp16
-  const void *W;           // [F, D] bf16
+  const void *A;           // fp16 activations, tiled: [M_pad/128][D/64][128 x 64] (see a_piece)
+  const void *W;           // [F, D] bf16 (used when Wp is null)
+  const void *Wp;          // fp16 weights in GEMM tile order (launch_pack_qkv_weight), or null
   const int2 *map;         // [M] (cache row, position)
   const float2 *cs;        // [M_pad, dh/2] (cos, sin) per token
   void *q, *k, *v;         // fp16 RoPECache
@@ -103,6 +104,8 @@ inline void lc_launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned 
 hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_qkv_prep(const SeqArgs &sa, const PrepArgs &a, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const LaunchEvents &ev);
+size_t packed_qkv_weight_bytes(int D, int F);
+hipError_t launch_pack_qkv_weight(const void *W, void *Wp, int D, int F, int dh, hipStream_t s);
 hipError_t setup_gemm_attributes();
 hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                              hipStream_t s, const LaunchEvents &ev);

@@ -25,8 +25,10 @@ DEVFLAG_CACHE_RANGE = 2
 
 EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "lacache_prefill_cache",
             "lacache_block_step", "lacache_dualcache_attn", "lacache_read_device_status",
-            "lacache_profile_enable", "lacache_profile_read", "lacache_status_string", "lacache_last_error")
-KERNEL_QKV, KERNEL_STEP_ATTN, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_DUAL_ATTN = range(5)
+            "lacache_profile_enable", "lacache_profile_read", "lacache_status_string", "lacache_last_error",
+            "lacache_packed_weight_size", "lacache_pack_qkv_weight")
+(KERNEL_QKV, KERNEL_BLOCK_ROWS, KERNEL_INVARIANT_ROWS, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_QKV_PREP,
+ KERNEL_QKV_GEMM) = range(7)
 KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn", "qkv_prep", "qkv_gemm")
 
 
@@ -38,7 +40,8 @@ class Config(ctypes.Structure):
 
 
 class Weights(ctypes.Structure):
-    _fields_ = [("embed", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p)]
+    _fields_ = [("embed", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p),
+                ("w_qkv_packed", ctypes.c_void_p)]
 
 
 class Cache(ctypes.Structure):
@@ -80,6 +83,8 @@ def load_library(path: str = LIB_PATH):
         "lacache_block_step": (st, [P, ctypes.POINTER(Weights), P, ctypes.POINTER(Seq), I32,
                                     ctypes.POINTER(Cache), P, P, P, SZ, P]),
         "lacache_dualcache_attn": (st, [P, P, P, P, I64, ctypes.POINTER(Seq), I32, P, P, P, SZ, P]),
+        "lacache_packed_weight_size": (st, [P, ctypes.POINTER(SZ)]),
+        "lacache_pack_qkv_weight": (st, [P, P, P, SZ, P]),
         "lacache_read_device_status": (st, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
         "lacache_profile_enable": (st, [P, ctypes.c_int]),
         "lacache_profile_read": (st, [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
@@ -196,11 +201,32 @@ class Context:
         n = self.workspace_size(op, table)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
-    def _weights(self, embed, gamma, w_qkv):
+    def _weights(self, embed, gamma, w_qkv, w_qkv_packed=None):
         for name, t in (("embed", embed), ("gamma", gamma), ("w_qkv", w_qkv)):
             if t.dtype != self.torch_dtype or not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous {self.torch_dtype} CUDA tensor")
-        return Weights(embed.data_ptr(), gamma.data_ptr(), w_qkv.data_ptr())
+        if w_qkv_packed is not None and (not w_qkv_packed.is_cuda or not w_qkv_packed.is_contiguous()):
+            raise ValueError("w_qkv_packed must be a contiguous CUDA tensor")
+        return Weights(embed.data_ptr(), gamma.data_ptr(), w_qkv.data_ptr(),
+                       None if w_qkv_packed is None else w_qkv_packed.data_ptr())
+
+    def packed_weight_size(self):
+        """Bytes of the packed projection weight (0: this configuration has none)."""
+        n = ctypes.c_size_t()
+        self._check(self.lib.lacache_packed_weight_size(self.handle, ctypes.byref(n)), "lacache_packed_weight_size")
+        return n.value
+
+    def pack_qkv_weight(self, w_qkv, stream=None):
+        """fp16 copy of w_qkv in the projection's tile order (uint8 CUDA tensor), or None if unsupported."""
+        n = self.packed_weight_size()
+        if n == 0:
+            return None
+        if w_qkv.dtype != self.torch_dtype or not w_qkv.is_cuda or not w_qkv.is_contiguous():
+            raise ValueError(f"w_qkv must be a contiguous {self.torch_dtype} CUDA tensor")
+        out = torch.empty(n, dtype=torch.uint8, device=w_qkv.device)
+        self._check(self.lib.lacache_pack_qkv_weight(self.handle, _ptr(w_qkv), _ptr(out), n, _stream(stream)),
+                    "lacache_pack_qkv_weight")
+        return out
 
     @staticmethod
     def _cache(ct: CacheTensors):

@@ -22,13 +22,19 @@ def to_device_array(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 class DeviceWorkload:
     """Parameters, ids, caches and workspace of one synthetic workload on the GPU."""
 
-    def __init__(self, wl: synth.Workload, device="cuda", ctx: lacache.Context | None = None, n_rows=None):
+    def __init__(self, wl: synth.Workload, device="cuda", ctx: lacache.Context | None = None, n_rows=None,
+                 packed=True):
+        """packed: also hand the library the packed fp16 projection weight (where the configuration has one)."""
         self.wl = wl
         self.device = device
         p = synth.params(wl)
         self.params = p
         self.weights = tuple(to_device_array(p[k], wl.dtype, device) for k in ("embed", "gamma", "w_qkv"))
         self.ctx = ctx or lacache.context_for(wl)
+        if packed:
+            wp = self.ctx.pack_qkv_weight(self.weights[2])
+            if wp is not None:
+                self.weights = self.weights + (wp,)
         self.table = wl.table()
         self.n_rows = n_rows or wl.total_tokens
         self.ct = self.ctx.alloc_cache(self.n_rows, device)

@@ -109,11 +109,18 @@ typedef struct {
   int32_t dtype;                  /* lacache_dtype */
 } lacache_config;
 
-/* Layer-0 parameters, device, layouts above. */
+/* Layer-0 parameters, device, layouts above.  w_qkv_packed is optional:
+ * NULL, or w_qkv as converted by lacache_pack_qkv_weight.  Calls that
+ * project 128 or more tokens at once (prefill, block steps with that many
+ * block tokens; bf16 contexts with d_model a multiple of 512) then read it
+ * instead of converting w_qkv to fp16 tile by tile inside the projection;
+ * both forms hold the same fp16 values, and the projections differ only in
+ * the order of the fp32 accumulation.  It must be packed from this w_qkv. */
 typedef struct {
   const void *embed;
   const void *gamma;
   const void *w_qkv;
+  const void *w_qkv_packed;
 } lacache_weights;
 
 /* The caches (device), layouts above; n_rows = rows every buffer holds. */
@@ -216,6 +223,23 @@ LACACHE_API lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *
                                       void *out_block, float *lse_block,
                                       void *workspace, size_t workspace_bytes,
                                       void *stream);
+
+/* Bytes of the packed projection weight for this context: 0 where the
+ * configuration has no many-token projection (fp32, or d_model not a
+ * multiple of 512). */
+LACACHE_API lacache_status lacache_packed_weight_size(const lacache_ctx *ctx, size_t *bytes);
+
+/* Enqueues the conversion of w_qkv (device, bf16, layout above) into
+ * w_packed (device, caller-owned, at least lacache_packed_weight_size bytes):
+ * every weight as IEEE fp16 (round to nearest even; exact for weights of
+ * magnitude in [2^-14, 65504], the fp16 normal range), arranged in the
+ * column-tile / contraction-tile order the many-token projection copies
+ * from, so each copy reads contiguous memory.  A one-time step per weight
+ * set: pass the result as lacache_weights.w_qkv_packed.  Returns
+ * LACACHE_ERR_UNSUPPORTED where the size is 0 and LACACHE_ERR_INVALID_ARG
+ * for a NULL or unaligned pointer or packed_bytes below the size. */
+LACACHE_API lacache_status lacache_pack_qkv_weight(lacache_ctx *ctx, const void *w_qkv, void *w_packed,
+                                                   size_t packed_bytes, void *stream);
 
 /* Reads and clears the device status word (LACACHE_DEVFLAG_*), after
  * synchronising `stream`. */

@@ -60,10 +60,10 @@ def _compare_step(dw, ref, what):
     return stats
 
 
-def _run_full(wl, steps):
+def _run_full(wl, steps, packed=True):
     _say(f"[parity] {wl.name}: dtype {wl.dtype} D {wl.d_model} H {wl.n_heads}x{wl.head_dim} "
-         f"batch {wl.batch} seq_lens {wl.seq_lens[:4]}... block {wl.block_size} seed {wl.seed}")
-    dw = DeviceWorkload(wl)
+         f"batch {wl.batch} seq_lens {wl.seq_lens[:4]}... block {wl.block_size} seed {wl.seed} packed {packed}")
+    dw = DeviceWorkload(wl, packed=packed)
     cfg = cfg_of(wl)
     dw.prefill()
     torch.cuda.synchronize()
@@ -98,6 +98,25 @@ def test_small_fp32_head64_multi_tile():
                       prompt_lens=(300, 77), gen_len=96, block_size=32, block_idx=(1, 2), steps=2,
                       embed_std=0.02, seed=22)
     _run_full(wl, 2)
+
+
+@pytest.mark.parametrize("packed", [True, False])
+@pytest.mark.parametrize("shape", ["h128_gqa", "h64"])
+def test_many_token_projection_every_row(shape, packed):
+    """Block steps of >= 128 tokens run the MFMA GEMM projection (and so does
+    every refresh): both weight forms, every row against the oracle.  h128_gqa:
+    F = 2048 is not a multiple of the 192-column tile (a partial last tile) and
+    K/V head boundaries fall inside tiles; 320 block tokens are 2.5 row tiles."""
+    if shape == "h128_gqa":
+        wl = synth.custom("gemm_h128_gqa", dtype="bf16", d_model=1024, n_heads=8, n_kv_heads=4, head_dim=128,
+                          vocab=2000, prompt_lens=(40, 7, 96, 130, 3, 64, 21, 50, 77, 12), gen_len=64,
+                          block_size=32, block_idx=(0, 1, 1, 0, 1, 0, 1, 0, 1, 1), steps=2, seed=41)
+    else:
+        wl = synth.custom("gemm_h64", dtype="bf16", d_model=512, n_heads=8, head_dim=64, vocab=1500,
+                          prompt_lens=(20, 33, 48, 9, 60, 17, 40, 28), gen_len=32, block_size=16,
+                          block_idx=(0, 1, 1, 0, 0, 1, 0, 1), steps=2, seed=42)
+    assert wl.block_tokens >= 128
+    _run_full(wl, 2, packed=packed)
 
 
 def test_tiny_batched16_fp32():
