@@ -510,6 +510,28 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
 namespace {
 
 // Type-A items (block rows x key chunks) and partial rows of each sample.
+// Rows per wave of the streaming invariant-row kernel (bf16 contexts): a
+// multiple of 64 that gives about kStreamItems (sample, head, segment) items
+// per launch.  0 (the one-tile-per-workgroup kernel with the merge folded
+// in) for fp32, where a block of the slice exceeds what the streaming kernel
+// serves, or where the launch is small enough that each item would get one
+// 64-row tile: then nothing is left to overlap and the separate merge launch
+// only adds.
+constexpr int64_t kStreamItems = 2048;
+int stream_segment_rows(const lc::SeqArgs &sa, int H, lc::DType dt) {
+  if (dt != lc::kBF16) return 0;
+  int64_t tiles = 0;
+  for (int i = 0; i < sa.n; ++i) {
+    const int B = sa.be[i] - sa.bs[i];
+    if (B > lc::kStreamMaxBlock) return 0;
+    tiles += (sa.len[i] - B + 63) / 64;
+  }
+  const char *env = getenv("LC_STREAM_ITEMS");
+  const int64_t target = env ? atoll(env) : kStreamItems;
+  if (tiles * H <= target) return 0;
+  return 64 * (int)((tiles * H + target - 1) / target);
+}
+
 void plan_block_rows(int split, lc::SeqArgs &sa) {
   for (int i = 0; i < sa.n; ++i) {
     const int B = sa.be[i] - sa.bs[i];
@@ -552,8 +574,11 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     const int ns = std::min(kMaxInline, batch - s0);
     lc::SeqArgs sa = slice_args(seqs, s0, ns);
     plan_block_rows(split, sa);
-    for (int i = 0; i < ns; ++i)
-      sa.pre[2][i + 1] = sa.pre[2][i] + (sa.len[i] - (sa.be[i] - sa.bs[i]) + lc::kRowsB - 1) / lc::kRowsB;
+    const int seg_rows = stream_segment_rows(sa, H, dt);
+    for (int i = 0; i < ns; ++i) {
+      const int nU = sa.len[i] - (sa.be[i] - sa.bs[i]);
+      sa.pre[2][i + 1] = sa.pre[2][i] + (seg_rows ? (nU + seg_rows - 1) / seg_rows : (nU + lc::kRowsB - 1) / lc::kRowsB);
+    }
     const int M = sa.pre[0][ns];
 
     hipError_t e = hipSuccess;
@@ -586,14 +611,25 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     aa.H = H;
     aa.Hkv = ctx->cfg.n_kv_heads;
     aa.split_keys = split;
+    aa.seg_rows = seg_rows;
     aa.scale_log2 = scale_log2(ctx);
     e = timed(ctx, LACACHE_KERNEL_BLOCK_ROWS, s, [&](const lc::LaunchEvents &ev) {
       return lc::launch_block_rows(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
     });
     if (e != hipSuccess) return hip_fail(ctx, "block-step block-rows launch", e);
-    e = timed(ctx, LACACHE_KERNEL_INVARIANT_ROWS, s, [&](const lc::LaunchEvents &ev) {
-      return lc::launch_invariant_rows(dt, dh, sa, aa, sa.pre[2][ns] * H, M, s, ev);
-    });
+    if (seg_rows) {
+      // Blocks of at most 64 keys: the block rows' merge, then the streaming
+      // invariant-row kernel.
+      e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
+      if (e != hipSuccess) return hip_fail(ctx, "block-step merge launch", e);
+      e = timed(ctx, LACACHE_KERNEL_INVARIANT_ROWS, s, [&](const lc::LaunchEvents &ev) {
+        return lc::launch_invariant_stream(dt, dh, sa, aa, sa.pre[2][ns] * H, s, ev);
+      });
+    } else {
+      e = timed(ctx, LACACHE_KERNEL_INVARIANT_ROWS, s, [&](const lc::LaunchEvents &ev) {
+        return lc::launch_invariant_rows(dt, dh, sa, aa, sa.pre[2][ns] * H, M, s, ev);
+      });
+    }
     if (e != hipSuccess) return hip_fail(ctx, "block-step invariant-rows launch", e);
     row_base += M;
     part_base += sa.pre[3][ns];

@@ -33,6 +33,8 @@
 // cache type with l beside it: the state (m, l, O~) is restored exactly up to
 // that one rounding, at half the bytes of an fp32 O~ for 16-bit caches.
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace lc {
@@ -589,6 +591,216 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Type B, streaming (16-bit caches, blocks of at most 32 * NKS keys): one
+// wave per item (sample, head, segment of a.seg_rows invariant rows), taken
+// in groups of 16 rows.  The load unit only reaches full rate when
+// consecutive lanes move consecutive 16-byte pieces, which the MFMA layouts
+// (lane = row) never do; so every global access of the loop is row-wise:
+// the queries, FACache rows and (m, l) of a group arrive by global -> LDS
+// copies (pieces swizzled as in QTile), three groups ahead of their use,
+// and the outputs leave through an LDS tile read back row-wise.  The block's
+// K fragments stay in registers and its V in LDS for the whole item.
+// ---------------------------------------------------------------------------
+template <int DH, int NKS> struct StreamLds {
+  static constexpr int ROWB = DH * 2;                         // bytes per 16-bit row
+  static constexpr int PPR = ROWB / 16;                       // 16-byte pieces per row (<= 16)
+  static constexpr int SWZ = PPR - 1;
+  static constexpr int RPC = 1024 / ROWB;                     // rows per 1 KB copy
+  static constexpr int TILE = 16 * ROWB;                      // a group's 16 rows
+  static constexpr int CPT = TILE / 1024;                     // copies (or row-wise accesses) per tile
+  static constexpr int V = (int)VTile<f16_t, DH, 32 * NKS>::kBytes;
+  static constexpr int SLOT = TILE + 256;                     // queries, (m, l)
+  static constexpr int NSLOT = 3;
+  static constexpr int OUT = V + NSLOT * SLOT;                // P*V / l tile (fp16), then 16 row coefficients
+  static constexpr int BYTES = OUT + TILE + 64;
+  static constexpr int COPIES = CPT + 1;                      // copy instructions per group
+  static constexpr int LOADS = CPT;                           // FACache row loads per group (row-wise, to registers)
+};
+
+// V of up to MAXC keys into a VTile (16-bit) by one wave, with dma16.
+template <int DH, int MAXC>
+__device__ __forceinline__ void vtile_stage_wave(uint32_t lds, const f16_t *vbase, size_t vstride, int nvalid,
+                                                 int lane) {
+  constexpr int CPK = DH / 8;                                 // pieces per key row
+  constexpr int ITER = MAXC * CPK / 64;
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int idx = it * 64 + lane;
+    const int c = idx / CPK, slot = idx % CPK;
+    dma16(vbase + (size_t)min(c, nvalid - 1) * vstride + ((slot ^ (c & 3)) << 3), lds + it * 1024);
+  }
+}
+
+template <typename TO, int DH, int NKS>
+__global__ __launch_bounds__(64) void invariant_stream_kernel(const SeqArgs sa, const AttnArgs a) {
+  using T = f16_t;
+  using L = StreamLds<DH, NKS>;
+  constexpr int NDB = DH / 16, BMAX = 32 * NKS;
+  extern __shared__ __align__(16) char smem[];
+  const int lane = threadIdx.x, g = lane >> 4, r16 = lane & 15;
+  const int item = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int b = find_sample(sa.pre[2], sa.n, item);
+  const int seg = item - sa.pre[2][b];
+  const int bs = sa.bs[b], B = sa.be[b] - bs, nU = sa.len[b] - B;
+  const int hk = h / (a.H / a.Hkv);
+  const size_t kvstride = (size_t)a.Hkv * DH;
+  const int off = sa.off[b];
+  const int u0 = seg * a.seg_rows, u1 = min(nU, u0 + a.seg_rows);   // u0 < u1 by construction
+  const int ngroups = (u1 - u0 + 15) >> 4;
+  const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  const int rw0 = lane / L::PPR, piece = lane % L::PPR;           // row-wise lane: row rw0 (+ RPC c), piece
+
+  // (cache row * H + h) of row r of group grp; rows past the segment repeat
+  // its last row, whose results they reproduce bit for bit (so their stores
+  // need no guard).
+  auto crow_of = [&](int grp, int r) -> size_t {
+    const int u = min(u0 + grp * 16 + r, u1 - 1);
+    return (size_t)(off + (u < bs ? u : u + B)) * a.H + h;
+  };
+  // Copies of group grp's queries into slot sl (copy c: rows c*RPC.., LDS
+  // slot s of row r <- piece s ^ (r & SWZ)) and its (m, l) (lanes 0-15: m
+  // of rows 0-15, 16-31: l; the upper half repeats them).
+  auto issue = [&](int grp, int sl) {
+    const uint32_t sb = lbase + L::V + sl * L::SLOT;
+#pragma unroll
+    for (int c = 0; c < L::CPT; ++c) {
+      const int r = c * L::RPC + rw0;
+      dma16(static_cast<const T *>(a.q) + crow_of(grp, r) * DH + ((piece ^ (r & L::SWZ)) << 3), sb + c * 1024);
+    }
+    const size_t cm = crow_of(grp, lane & 15);
+    dma4((lane & 16) ? static_cast<const void *>(a.l_c + cm) : static_cast<const void *>(a.m_c + cm), sb + L::TILE);
+  };
+  // FACache rows of group grp, row-wise into registers.  Ordinary loads:
+  // the compiler waits for them itself before their use, counting only the
+  // memory instructions it knows of (not the copies), so it can only wait
+  // longer than needed, never less.
+  typedef uint4 ORow[L::CPT];
+  auto load_o = [&](ORow &o, int grp) {
+#pragma unroll
+    for (int c = 0; c < L::CPT; ++c)
+      o[c] = *reinterpret_cast<const uint4 *>(static_cast<const T *>(a.o_c) + crow_of(grp, c * L::RPC + rw0) * DH +
+                                              piece * 8);
+  };
+
+  // The block's K fragments (registers) and V (LDS), and the first three
+  // groups' inputs; all complete before the loop.
+  const T *kbase = static_cast<const T *>(a.k) + (size_t)(off + bs) * kvstride + hk * DH;
+  KStep<T, DH> kf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    load_k_step<T, DH>(kf[ks], kbase + (size_t)min(32 * ks, B - 1) * kvstride, kvstride, max(1, min(32, B - 32 * ks)),
+                       lane);
+  // Six register sets: group i reads set i mod 6 and refills set
+  // (i + 3) mod 6, so no set holds two live values at once (with three, the
+  // old and new rows overlap and the loop needs moves that wait for loads).
+  ORow o0, o1, o2, o3, o4, o5;
+  issue(0, 0);
+  load_o(o0, 0);
+  if (ngroups > 1) { issue(1, 1); load_o(o1, 1); }
+  if (ngroups > 2) { issue(2, 2); load_o(o2, 2); }
+  vtile_stage_wave<DH, BMAX>(lbase, static_cast<const T *>(a.v) + (size_t)(off + bs) * kvstride + hk * DH, kvstride,
+                             B, lane);
+  vmcnt_wait<0>();
+  const T *vbuf = reinterpret_cast<const T *>(smem);
+
+  // One group.  Inputs of group i (slot sl, FACache rows in o) landed; in
+  // flight behind them: the stores of groups i-3 .. i-1 (CPT each, plus
+  // possibly an LSE store: not counted, which only waits longer) and the
+  // inputs of the groups after i.
+  auto group = [&](int i, auto SL, ORow &o, ORow &onext, auto REFILL) {
+    constexpr int sl = decltype(SL)::value;
+    if (i >= 3) {
+      const int behind = min(2, ngroups - 1 - i);
+      if (behind == 2) vmcnt_wait<3 * L::CPT + 2 * (L::COPIES + L::LOADS)>();
+      else if (behind == 1) vmcnt_wait<3 * L::CPT + L::COPIES + L::LOADS>();
+      else vmcnt_wait<3 * L::CPT>();
+    }
+    const char *sp = smem + L::V + sl * L::SLOT;
+    Frag<T> qf[1][DH / 32];
+#pragma unroll
+    for (int kd = 0; kd < DH / 32; ++kd) qtile_frag<T, DH>(qf[0][kd], reinterpret_cast<const T *>(sp), r16, kd, g);
+    const float mc = *reinterpret_cast<const float *>(sp + L::TILE + 4 * r16);
+    const float lc = *reinterpret_cast<const float *>(sp + L::TILE + 64 + 4 * r16);
+    // The slot and the registers are refilled only after these reads.
+    __builtin_amdgcn_s_waitcnt(0xC07F);                       // lgkmcnt(0)
+    if (decltype(REFILL)::value || i + 3 < ngroups) {
+      issue(i + 3, sl);
+      load_o(onext, i + 3);
+    }
+
+    // Softmax over the block's keys, starting from the FACache state
+    // (Algorithm 1: initialise with the cache): P*V accumulates from zero,
+    // the cached O~ = (O~/l) * l joins it in the row-wise pass below.
+    AttnState<1, DH> st;
+    st.m[0] = mc * kLog2e;
+    st.l[0] = g == 0 ? lc : 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) st.o[0][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      if (32 * ks < B) attend_step_pre<T, 1, DH, BMAX>(st, qf, kf[ks], min(32, B - 32 * ks), vbuf, 32 * ks, a.scale_log2, lane);
+    // The cached part decayed by exp2(m_c - m): l = lc * alpha + sum p.
+    const float alpha = fast_exp2(mc * kLog2e - st.m[0]);
+    const float lt = group_sum(st.l[0]), inv = 1.0f / lt;
+    // l summed the cached lc * (all alphas of the steps) already; coef
+    // multiplies (O~/l)_cache in the row-wise pass.
+    const float coef = lc * alpha * inv;
+
+    // P*V / l (fp16) and coef per row through LDS, then row-wise:
+    // O = (O~/l)_cache * coef + P*V / l.
+    char *op = smem + L::OUT;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int fe = OMap<DH>::feat(g, db, 0);
+      const f32x4_t x = st.o[0][db] * inv;
+      *reinterpret_cast<uint2 *>(op + r16 * L::ROWB + (((fe >> 3) ^ (r16 & L::SWZ)) << 4) + (fe & 7) * 2) =
+          make_uint2(pack2(T{}, x[0], x[1]), pack2(T{}, x[2], x[3]));
+    }
+    if (g == 0) *reinterpret_cast<float *>(op + L::TILE + 4 * r16) = coef;
+    if (a.lse && g == 0) a.lse[crow_of(i, r16)] = (st.m[0] + __log2f(lt)) * kLn2;
+#pragma unroll
+    for (int c = 0; c < L::CPT; ++c) {
+      const int r = c * L::RPC + rw0;
+      const uint4 pv = *reinterpret_cast<const uint4 *>(op + r * L::ROWB + ((piece ^ (r & L::SWZ)) << 4));
+      const float cf = *reinterpret_cast<const float *>(op + L::TILE + 4 * r);
+      const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w}, ow[4] = {o[c].x, o[c].y, o[c].z, o[c].w};
+      uint32_t res[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float2 x = unpack2(T{}, pw[q]), y = unpack2(T{}, ow[q]);
+        res[q] = pack2(TO{}, fmaf(y.x, cf, x.x), fmaf(y.y, cf, x.y));
+      }
+      *reinterpret_cast<uint4 *>(static_cast<TO *>(a.out) + crow_of(i, r) * DH + piece * 8) =
+          make_uint4(res[0], res[1], res[2], res[3]);
+    }
+  };
+  // While three more groups follow each group, refills are unconditional (a
+  // conditional refill makes the loop carry two definitions of a set, and
+  // merging them costs a wait for everything in flight); the last eight or
+  // fewer groups refill only what exists.
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  int i = 0;
+  for (; i + 8 < ngroups; i += 6) {
+    group(i, C0{}, o0, o3, std::true_type{});
+    group(i + 1, C1{}, o1, o4, std::true_type{});
+    group(i + 2, C2{}, o2, o5, std::true_type{});
+    group(i + 3, C0{}, o3, o0, std::true_type{});
+    group(i + 4, C1{}, o4, o1, std::true_type{});
+    group(i + 5, C2{}, o5, o2, std::true_type{});
+  }
+  for (; i < ngroups; i += 6) {
+    group(i, C0{}, o0, o3, std::false_type{});
+    if (i + 1 < ngroups) group(i + 1, C1{}, o1, o4, std::false_type{});
+    if (i + 2 < ngroups) group(i + 2, C2{}, o2, o5, std::false_type{});
+    if (i + 3 < ngroups) group(i + 3, C0{}, o3, o0, std::false_type{});
+    if (i + 4 < ngroups) group(i + 4, C1{}, o4, o1, std::false_type{});
+    if (i + 5 < ngroups) group(i + 5, C2{}, o5, o2, std::false_type{});
+  }
+}
+
 // Type-A items only: the block rows' partial states (block step and
 // DualCache).
 template <typename T, typename TO, int DH>
@@ -788,6 +1000,26 @@ hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs
                              const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
   LC_DISPATCH(dt, dh, (lc_launch(block_rows_kernel<T, TO, DH>, dim3(n_blocks), dim3(256), block_rows_smem<T, DH>(), s, ev, sa, a)));
+  return hipGetLastError();
+}
+
+hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
+                                   hipStream_t s, const LaunchEvents &ev) {
+  if (n_blocks <= 0) return hipSuccess;
+  int bmax = 0;
+  for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
+  if (bmax > kStreamMaxBlock) return hipErrorInvalidValue;
+  if (dt != kBF16) return hipErrorInvalidValue;
+#define LC_STR(DH, NK) \
+  lc_launch(invariant_stream_kernel<bf16_t, DH, NK>, dim3(n_blocks), dim3(64), StreamLds<DH, NK>::BYTES, s, ev, sa, a)
+  if (dh == 128) {
+    if (bmax <= 32) LC_STR(128, 1);
+    else LC_STR(128, 2);
+  } else {
+    if (bmax <= 32) LC_STR(64, 1);
+    else LC_STR(64, 2);
+  }
+#undef LC_STR
   return hipGetLastError();
 }
 

@@ -152,6 +152,38 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Global -> LDS copies by the load unit: lane l moves 16 (dma16) or 4 (dma4)
+// bytes from its own `src` to LDS byte address lds + 16 l (+ 4 l); `lds` is
+// wave-uniform.  Written as instructions the compiler does not see as LDS
+// stores: it would otherwise wait for every copy in flight before each LDS
+// read.  Callers wait for their copies themselves (vmcnt_wait) before
+// reading what they wrote; M0 is clobbered.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char *)p);
+}
+
+// s_waitcnt vmcnt(N), N in [0, 63] (a compile-time constant); other counters
+// untouched.  Also a compiler memory barrier: LDS filled by dma16/dma4 must
+// not be read before the wait.
+template <int N> __device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" : : : "memory");
+}
+
 // Workgroup barrier that orders LDS traffic only: the waves meet, and LDS
 // stores issued before it are visible after it, while global loads issued
 // before it stay in flight (a full __syncthreads would wait for them).

@@ -49,23 +49,6 @@ namespace lc {
 
 typedef _Float16 gh2_t __attribute__((ext_vector_type(2)));
 
-// Global -> LDS copy of 16 bytes per lane to LDS byte address lds + 16*lane
-// (lds wave-uniform).  Written as an instruction the compiler does not see
-// as an LDS store: it would otherwise wait for every copy in flight before
-// each LDS read, including copies into other stages of the ring.  The kernel
-// waits for its copies itself (vmcnt) before the barrier that publishes a
-// stage; M0 is used by nothing else in the kernel.
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds), "v"(src)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void *p) {
-  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char *)p);
-}
-
 __device__ __forceinline__ uint32_t f16pair(float a, float b) {
   const gh2_t v = {(_Float16)a, (_Float16)b};
   return __builtin_bit_cast(uint32_t, v);

@@ -80,6 +80,7 @@ struct AttnArgs {
   int part_base;           // index of the slice's first partial row
   int H, Hkv;
   int split_keys;          // keys per type-A chunk (multiple of 32)
+  int seg_rows;            // streaming type B: invariant rows per workgroup (multiple of 16)
   float scale_log2;        // sm_scale * log2(e)
 };
 
@@ -113,6 +114,9 @@ hipError_t launch_invariant_rows(DType dt, int dh, const SeqArgs &sa, const Attn
                                  hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int M, hipStream_t s,
                         const LaunchEvents &ev);
+constexpr int kStreamMaxBlock = 64;   // largest block the streaming type-B kernel serves
+hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
+                                   hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                                hipStream_t s, const LaunchEvents &ev);
 hipError_t setup_kernel_attributes();
