@@ -104,7 +104,13 @@ int nchunks(int split, int len) { return (len + split - 1) / split; }
 // Keys per type-A chunk for a batch: one 128-key tile per workgroup while
 // that leaves at most ~4 workgroups per CU; longer chunks (and fewer partial
 // rows to merge) beyond that.  LACACHE_SPLIT_KEYS (a multiple of 32) fixes it.
-int split_keys(const lacache_ctx *ctx, const lacache_seq *seqs, int32_t batch) {
+// Keys per type-A chunk.  bf16: one chunk per sequence when that still gives
+// every CU a workgroup; then *direct is set and the streaming block-row
+// kernel writes O and LSE itself (no merge).  Otherwise chunks of 128 keys
+// and more, doubled while the launch keeps about 1024 items.
+constexpr int64_t kStreamAItems = 256;
+int split_keys(const lacache_ctx *ctx, const lacache_seq *seqs, int32_t batch, int *direct = nullptr) {
+  if (direct) *direct = 0;
   if (ctx->split_keys > 0) return ctx->split_keys;
   auto items = [&](int split) {
     int64_t n = 0;
@@ -116,6 +122,13 @@ int split_keys(const lacache_ctx *ctx, const lacache_seq *seqs, int32_t batch) {
   };
   int max_len = 1;
   for (int i = 0; i < batch; ++i) max_len = std::max(max_len, seqs[i].seq_len);
+  if (ctx->cfg.dtype == LACACHE_BF16) {
+    const int whole = (max_len + 63) / 64 * 64;
+    if (items(whole) >= kStreamAItems) {
+      if (direct) *direct = 1;
+      return whole;
+    }
+  }
   int split = 128;
   while (split < max_len && items(2 * split) >= 1024) split *= 2;
   return split;
@@ -555,7 +568,8 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
   if (!block_ids) return fail(ctx, LACACHE_ERR_INVALID_ARG, "block_ids is NULL");
   if (!out || !aligned16(out)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
   if ((st = check_table(ctx, seqs, batch, cache->n_rows)) != LACACHE_OK) return st;
-  const int split = split_keys(ctx, seqs, batch);
+  int direct = 0;
+  const int split = split_keys(ctx, seqs, batch, &direct);
   const int64_t P = partial_rows(split, seqs, batch);
   const int64_t Mall = block_tokens(seqs, batch);
   const bool gemm = step_uses_gemm(ctx, Mall);
@@ -612,22 +626,26 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     aa.Hkv = ctx->cfg.n_kv_heads;
     aa.split_keys = split;
     aa.seg_rows = seg_rows;
+    aa.direct = direct;
     aa.scale_log2 = scale_log2(ctx);
     e = timed(ctx, LACACHE_KERNEL_BLOCK_ROWS, s, [&](const lc::LaunchEvents &ev) {
       return lc::launch_block_rows(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
     });
     if (e != hipSuccess) return hip_fail(ctx, "block-step block-rows launch", e);
     if (seg_rows) {
-      // Blocks of at most 64 keys: the block rows' merge, then the streaming
-      // invariant-row kernel.
-      e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
-      if (e != hipSuccess) return hip_fail(ctx, "block-step merge launch", e);
+      // Blocks of at most 64 keys: the block rows' merge (unless the block-row
+      // kernel finished them), then the streaming invariant-row kernel.
+      if (!aa.direct) {
+        e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
+        if (e != hipSuccess) return hip_fail(ctx, "block-step merge launch", e);
+      }
       e = timed(ctx, LACACHE_KERNEL_INVARIANT_ROWS, s, [&](const lc::LaunchEvents &ev) {
         return lc::launch_invariant_stream(dt, dh, sa, aa, sa.pre[2][ns] * H, s, ev);
       });
     } else {
+      const int Mmerge = aa.direct ? 0 : M;
       e = timed(ctx, LACACHE_KERNEL_INVARIANT_ROWS, s, [&](const lc::LaunchEvents &ev) {
-        return lc::launch_invariant_rows(dt, dh, sa, aa, sa.pre[2][ns] * H, M, s, ev);
+        return lc::launch_invariant_rows(dt, dh, sa, aa, sa.pre[2][ns] * H, Mmerge, s, ev);
       });
     }
     if (e != hipSuccess) return hip_fail(ctx, "block-step invariant-rows launch", e);
@@ -649,7 +667,8 @@ lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *q_block, con
     return fail(ctx, LACACHE_ERR_INVALID_ARG, "q_block, k, v and out_block must be 16-byte aligned");
   if (n_rows < 1) return fail(ctx, LACACHE_ERR_INVALID_ARG, "n_rows must be >= 1");
   if ((st = check_table(ctx, seqs, batch, n_rows)) != LACACHE_OK) return st;
-  const int split = split_keys(ctx, seqs, batch);
+  int direct = 0;
+  const int split = split_keys(ctx, seqs, batch, &direct);
   const int64_t P = partial_rows(split, seqs, batch);
   const size_t need = partial_bytes(ctx, P);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
@@ -682,13 +701,16 @@ lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *q_block, con
     aa.H = H;
     aa.Hkv = ctx->cfg.n_kv_heads;
     aa.split_keys = split;
+    aa.direct = direct;
     aa.scale_log2 = scale_log2(ctx);
     hipError_t e = timed(ctx, LACACHE_KERNEL_BLOCK_ROWS, s, [&](const lc::LaunchEvents &ev) {
       return lc::launch_block_rows(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
     });
     if (e != hipSuccess) return hip_fail(ctx, "dualcache attention launch", e);
-    e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
-    if (e != hipSuccess) return hip_fail(ctx, "dualcache merge launch", e);
+    if (!aa.direct) {
+      e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
+      if (e != hipSuccess) return hip_fail(ctx, "dualcache merge launch", e);
+    }
     row_base += M;
     part_base += sa.pre[3][ns];
   }

@@ -801,6 +801,188 @@ __global__ __launch_bounds__(64) void invariant_stream_kernel(const SeqArgs sa, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Type A, streaming (16-bit caches): one workgroup of 4 waves per (sample,
+// head, 32 block rows, key chunk).  K and V of 64-key tiles go global -> LDS
+// row-wise through a 4-stage ring (up to three tiles in flight while one is
+// used); wave w takes row block w & 1 and keys 32 (w >> 1) .. +31 of every
+// tile.  The two waves of a row block merge through LDS at the end; the
+// chunk's state goes to the workspace, or, when a.direct (every chunk is a
+// whole sequence), O and LSE go out directly.
+// K tile: key c's 16-byte piece p in slot p ^ kslot(c); the 16 keys of one
+// A-operand read (8a + b + 4kb, a, b < 4) then hit distinct slots.
+// ---------------------------------------------------------------------------
+template <int DH> struct StreamA {
+  static constexpr int ROWB = DH * 2, PPR = ROWB / 16, RPC = 1024 / ROWB;
+  static constexpr int TK = 64;                                 // keys per tile
+  static constexpr int KT = TK * ROWB;                          // bytes of a K (or V) tile
+  static constexpr int STAGE = 2 * KT;
+  static constexpr int NST = 4;
+  static constexpr int QB = kRowsA * ROWB;                      // the 32 query rows
+  static constexpr int BYTES = QB + NST * STAGE;
+  static constexpr int CPW = STAGE / 1024 / 4;                  // copies per wave per tile
+};
+__device__ __forceinline__ int kslot(int c, int ppr) {
+  return ppr == 16 ? (((c >> 1) & 12) | (c & 3)) : (((c >> 1) & 4) | (c & 3));
+}
+
+template <typename TO, int DH>
+__global__ __launch_bounds__(256) void block_rows_stream_kernel(const SeqArgs sa, const AttnArgs a) {
+  using T = f16_t;
+  using S = StreamA<DH>;
+  using QT = QTile<T, DH>;
+  constexpr int NDB = DH / 16, HDB = NDB / 2;
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int mb = w & 1, kh = w >> 1;
+  const int item = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int b = find_sample(sa.pre[1], sa.n, item);
+  const int t = item - sa.pre[1][b];
+  const int B = sa.be[b] - sa.bs[b], N = sa.len[b];
+  const int nrg = (B + kRowsA - 1) / kRowsA;
+  const int chunk = t / nrg, rg = t % nrg;
+  const int key0 = chunk * a.split_keys;
+  const int nkeys = min(a.split_keys, N - key0);
+  const int ntiles = (nkeys + S::TK - 1) / S::TK;
+  const int hk = h / (a.H / a.Hkv);
+  const size_t kvstride = (size_t)a.Hkv * DH;
+  const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  const T *kbase = static_cast<const T *>(a.k) + (size_t)(sa.off[b] + key0) * kvstride + hk * DH;
+  const T *vbase = static_cast<const T *>(a.v) + (size_t)(sa.off[b] + key0) * kvstride + hk * DH;
+  const int rr = lane / S::PPR, slot = lane % S::PPR;             // row-wise lane: row rr (+ RPC q), slot
+
+  // Tile tt into stage tt % NST: wave w does copies q = w, w+4, .. of the
+  // tile's K then V rows (keys past the chunk repeat its last key).
+  auto issue = [&](int tt) {
+    const uint32_t st = lbase + S::QB + (tt % S::NST) * S::STAGE;
+    const int k0 = tt * S::TK;
+#pragma unroll
+    for (int j = 0; j < S::CPW / 2; ++j) {
+      const int q = j * 4 + w;
+      const int c = q * S::RPC + rr;
+      const size_t key = (size_t)min(k0 + c, nkeys - 1) * kvstride;
+      dma16(kbase + key + ((slot ^ kslot(c, S::PPR)) << 3), st + q * 1024);
+      dma16(vbase + key + ((slot ^ (c & 3)) << 3), st + S::KT + q * 1024);
+    }
+  };
+  // The 32 query rows (QTile), rows past the block repeat its last row.
+  {
+    const int qrow0 = a.qmode == 0 ? sa.off[b] + sa.bs[b] : a.row_base + sa.pre[0][b];
+#pragma unroll
+    for (int it = 0; it < S::QB / 1024 / 4; ++it) {
+      const int q = it * 4 + w;
+      const int r = q * S::RPC + rr;
+      const int rq = min(rg * kRowsA + r, B - 1);
+      dma16(static_cast<const T *>(a.q) + ((size_t)(qrow0 + rq) * a.H + h) * DH + ((slot ^ (r & QT::SWZ)) << 3),
+            lbase + q * 1024);
+    }
+  }
+  // All four stages start filling; the queries and tile 0 are waited for.
+  issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
+  if (ntiles > 3) issue(3);
+  {
+    const int behind = min(3, ntiles - 1);
+    if (behind == 3) vmcnt_wait<3 * S::CPW>();
+    else if (behind == 2) vmcnt_wait<2 * S::CPW>();
+    else if (behind == 1) vmcnt_wait<S::CPW>();
+    else vmcnt_wait<0>();
+  }
+  lds_barrier();
+  Frag<T> qf[1][DH / 32];
+#pragma unroll
+  for (int kd = 0; kd < DH / 32; ++kd) qtile_frag<T, DH>(qf[0][kd], reinterpret_cast<const T *>(smem), mb * 16 + r16, kd, g);
+
+  AttnState<1, DH> st;
+  state_init_empty(st);
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const char *stg = smem + S::QB + (tt % S::NST) * S::STAGE;
+    const int nv = max(0, min(32, nkeys - tt * S::TK - 32 * kh));
+    if (nv > 0) {
+      // S^T = K Q^T over this wave's 32 keys: A row r16 of key block kb is key
+      // 32 kh + 8 (r16 >> 2) + 4 kb + (r16 & 3) (lane group g then holds keys
+      // 8g..8g+7 of the step in the result).
+      f32x4_t sc[2][1];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sc[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int c = 32 * kh + 8 * (r16 >> 2) + 4 * kb + (r16 & 3);
+#pragma unroll
+        for (int kd = 0; kd < DH / 32; ++kd) {
+          const int e0 = 64 * (kd >> 1) + 16 * g + 8 * (kd & 1);
+          Frag<T> kfr;
+          frag_load(kfr, reinterpret_cast<const T *>(stg + c * S::ROWB + (((e0 >> 3) ^ kslot(c, S::PPR)) << 4)));
+          mma16(sc[kb][0], kfr, qf[0][kd]);
+        }
+      }
+      softmax_pv<T, 1, DH, S::TK>(st, sc, nv, reinterpret_cast<const T *>(stg + S::KT), 32 * kh, a.scale_log2, lane);
+    }
+    if (tt + 1 < ntiles) {
+      // This wave's copies of tile tt+1 landed (those of tt+2, tt+3 may not
+      // have); the barrier publishes it and frees stage tt for tile tt+4
+      // (tiles 0-3 were issued before the loop).
+      const int behind = min(2, ntiles - 2 - tt);
+      if (behind == 2) vmcnt_wait<2 * S::CPW>();
+      else if (behind == 1) vmcnt_wait<S::CPW>();
+      else vmcnt_wait<0>();
+      lds_barrier();
+      if (tt + 4 < ntiles) issue(tt + 4);
+    }
+  }
+
+  // Merge the two waves of each row block: wave kh finalises feature blocks
+  // [kh*HDB, (kh+1)*HDB) and hands the other half to its partner (w ^ 2).
+  lds_barrier();                                               // ring reads done; reuse the LDS
+  float *s_m = reinterpret_cast<float *>(smem);                 // [wave][16 rows]
+  float *s_l = s_m + 4 * 16;
+  f32x4_t *s_o = reinterpret_cast<f32x4_t *>(s_l + 4 * 16);    // [wave][HDB][lane]
+  const float lw = group_sum(st.l[0]);
+  if (g == 0) {
+    s_m[w * 16 + r16] = st.m[0];
+    s_l[w * 16 + r16] = lw;
+  }
+  // Feature blocks by compile-time index (a register array indexed by the
+  // wave number would go to scratch memory); the branch is wave-uniform.
+  auto hand_over = [&](auto KHC) {
+    constexpr int KH = decltype(KHC)::value;
+#pragma unroll
+    for (int j = 0; j < HDB; ++j) s_o[(w * HDB + j) * 64 + lane] = st.o[0][(1 - KH) * HDB + j];
+  };
+  if (kh == 0) hand_over(std::integral_constant<int, 0>{});
+  else hand_over(std::integral_constant<int, 1>{});
+  lds_barrier();
+  const int pw = w ^ 2;
+  const float mo = s_m[pw * 16 + r16], lo = s_l[pw * 16 + r16];
+  const float mx = fmaxf(st.m[0], mo);
+  const float e_s = fast_exp2(st.m[0] - mx), e_o = fast_exp2(mo - mx);
+  const float L = lw * e_s + lo * e_o, inv = 1.0f / L;
+  const int r = rg * kRowsA + mb * 16 + r16;
+  if (r >= B) return;
+  const int orow = a.omode == 0 ? sa.off[b] + sa.bs[b] + r : a.row_base + sa.pre[0][b] + r;
+  const size_t prow = ((size_t)(a.part_base + sa.pre[3][b]) + (size_t)chunk * B + r) * a.H + h;
+  auto finish = [&](auto KHC) {
+    constexpr int KH = decltype(KHC)::value;
+#pragma unroll
+    for (int j = 0; j < HDB; ++j) {
+      const int db = KH * HDB + j;
+      const f32x4_t o = (st.o[0][KH * HDB + j] * e_s + s_o[(pw * HDB + j) * 64 + lane] * e_o) * inv;
+      if (a.direct) st4(static_cast<TO *>(a.out) + ((size_t)orow * a.H + h) * DH + OMap<DH>::feat(g, db, 0), o);
+      else st4(static_cast<T *>(a.part_o) + prow * DH + OMap<DH>::feat(g, db, 0), o);
+    }
+  };
+  if (kh == 0) finish(std::integral_constant<int, 0>{});
+  else finish(std::integral_constant<int, 1>{});
+  if (kh == 0 && g == 0) {
+    if (a.direct) {
+      if (a.lse) a.lse[(size_t)orow * a.H + h] = (mx + __log2f(L)) * kLn2;
+    } else {
+      a.part_ml[prow] = make_float2(mx, L);
+    }
+  }
+}
+
 // Type-A items only: the block rows' partial states (block step and
 // DualCache).
 template <typename T, typename TO, int DH>
@@ -999,6 +1181,11 @@ template <typename T, int DH> constexpr size_t refresh_smem() {
 hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
                              const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
+  if (dt == kBF16 && a.direct) {
+    if (dh == 128) lc_launch(block_rows_stream_kernel<bf16_t, 128>, dim3(n_blocks), dim3(256), StreamA<128>::BYTES, s, ev, sa, a);
+    else lc_launch(block_rows_stream_kernel<bf16_t, 64>, dim3(n_blocks), dim3(256), StreamA<64>::BYTES, s, ev, sa, a);
+    return hipGetLastError();
+  }
   LC_DISPATCH(dt, dh, (lc_launch(block_rows_kernel<T, TO, DH>, dim3(n_blocks), dim3(256), block_rows_smem<T, DH>(), s, ev, sa, a)));
   return hipGetLastError();
 }
@@ -1076,6 +1263,8 @@ hipError_t setup_kernel_attributes() {
   LC_ATTR((refresh_attn_kernel<f16_t, bf16_t, 64>), (refresh_smem<f16_t, 64>()));
   LC_ATTR((refresh_attn_kernel<float, float, 128>), (refresh_smem<float, 128>()));
   LC_ATTR((refresh_attn_kernel<float, float, 64>), (refresh_smem<float, 64>()));
+  LC_ATTR((block_rows_stream_kernel<bf16_t, 128>), (StreamA<128>::BYTES));
+  LC_ATTR((block_rows_stream_kernel<bf16_t, 64>), (StreamA<64>::BYTES));
 #undef LC_ATTR
   return e;
 }

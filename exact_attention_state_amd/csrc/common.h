@@ -161,13 +161,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
-               : "s"(lds), "v"(src)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void *src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :
-               : "s"(lds), "v"(src)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
                : "memory", "m0");
 }
 

@@ -81,6 +81,7 @@ struct AttnArgs {
   int H, Hkv;
   int split_keys;          // keys per type-A chunk (multiple of 32)
   int seg_rows;            // streaming type B: invariant rows per workgroup (multiple of 16)
+  int direct;              // streaming type A: chunks are whole sequences, write O and LSE
   float scale_log2;        // sm_scale * log2(e)
 };
 
