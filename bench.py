@@ -58,11 +58,14 @@ def parse():
 
 KERNEL_SOURCES = {
     "qkv": ["exact_attention_state_amd/csrc/qkv.hip"],
+    "qkv_prep": ["exact_attention_state_amd/csrc/gemm.hip"],
+    "qkv_gemm": ["exact_attention_state_amd/csrc/gemm.hip"],
     "block_rows": ["exact_attention_state_amd/csrc/attn.hip"],
     "invariant_rows": ["exact_attention_state_amd/csrc/attn.hip"],
 }
 COMMON_SOURCES = ["exact_attention_state_amd/csrc/common.h", "exact_attention_state_amd/csrc/internal.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llada8b_step.json")
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}_step.json")
 
 
 def kernel_source_hash(kernel):
@@ -77,7 +80,7 @@ def kernel_source_hash(kernel):
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter runs, if the kernel is unchanged since."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -124,9 +127,16 @@ def step_accounting(wl):
         b_bytes += U * H * d * c + U * H * (2 * 4 + d * c) + U * H * d * s + U * H * 4
     pairs_c = pairs_a + pairs_b
     qkv_bytes = F * D * s + 2 * M * D * s + D * s + M * F * c + M * 4
-    kern = {"qkv": dict(bytes=qkv_bytes, flops=2 * M * F * D),
-            "block_rows": dict(bytes=a_bytes, flops=4 * d * pairs_a),
+    kern = {"block_rows": dict(bytes=a_bytes, flops=4 * d * pairs_a),
             "invariant_rows": dict(bytes=b_bytes, flops=4 * d * pairs_b)}
+    if wl.dtype == "bf16" and D % 512 == 0 and M >= 128:
+        # Many tokens: prep (embedding rows in, EmbedCache rows and the fp16
+        # activations out) and the GEMM (the packed fp16 weight, activations,
+        # Q/K/V out).  The roofline of the GEMM is the matrix cores'.
+        kern["qkv_prep"] = dict(bytes=2 * M * D * s + D * s + M * D * 2 + M * 4, flops=0)
+        kern["qkv_gemm"] = dict(bytes=F * D * 2 + M * D * 2 + M * F * c, flops=2 * M * F * D)
+    else:
+        kern["qkv"] = dict(bytes=qkv_bytes, flops=2 * M * F * D)
     return dict(M=M, pairs_computed=pairs_c, pairs_equiv=pairs_e, kernels=kern,
                 qkv_bytes=qkv_bytes, attn_bytes=a_bytes + b_bytes)
 
@@ -313,7 +323,7 @@ def main():
     value = acc["pairs_computed"] / (ms * 1e-3)
 
     # Roofline of the dominant kernel.
-    dom = max(kern, key=lambda k: kern[k]["ms_total"])
+    dom = max((k for k in kern if k in acc["kernels"]), key=lambda k: kern[k]["ms_total"])
     t_dom = kern[dom]["us_avg"] * 1e-6
     flops, nbytes = acc["kernels"][dom]["flops"], acc["kernels"][dom]["bytes"]
     peak_flops = (MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS) * 1e12
@@ -360,6 +370,8 @@ def main():
         "kernels_us_avg": {k: v["us_avg"] for k, v in kern.items()},
         "kernels_hbm_frac": {k: acc["kernels"][k]["bytes"] / (v["us_avg"] * 1e-6) / 1e9 / HBM_PEAK_GBS
                              for k, v in kern.items() if k in acc["kernels"]},
+        "kernels_mfma_frac": {k: acc["kernels"][k]["flops"] / (v["us_avg"] * 1e-6) / peak_flops
+                              for k, v in kern.items() if k in acc["kernels"] and acc["kernels"][k]["flops"]},
         "kernel_source_sha256": {k: kernel_source_hash(k) for k in kern},
         "roofline": roof,
         "cpu_baseline": cpu,
