@@ -70,11 +70,21 @@ static_assert(kGCopyA * 1024 * kGWaves == kGStageA && kGCopyW * 1024 * kGWaves =
 __device__ __forceinline__ int gslot(int r, int p) { return p ^ ((r >> 1) & 7); }
 __device__ __forceinline__ int gswz(int r, int p) { return r * 128 + (gslot(r, p) << 4); }
 
-// Byte offset, in the tiled A, of the 8-element piece starting at element e
-// (a multiple of 8) of token row m; nk = D / 64.
+// Fragment-major operand tiles.  An MFMA operand fragment (16 rows x 32
+// contraction elements, lane g*16 + r holding row r, elements 8g..8g+7) is
+// one contiguous KB in lane order, so a wave loads it with consecutive lanes
+// on consecutive 16-byte pieces (the load unit's full-rate pattern) and
+// reads it back from LDS without bank conflicts.  A 64-wide contraction tile
+// of 16*R rows is 2R fragments, fragment (row block rb, half ks) at KB
+// 2 rb + ks.
+// Byte offset, in the tiled A ([M_pad/128][D/64][128 x 64]), of the
+// 8-element piece starting at element e (a multiple of 8) of token row m;
+// nk = D / 64.
 __device__ __forceinline__ size_t a_piece(int m, int e, int nk) {
-  return ((size_t)(m >> 7) * nk + (e >> 6)) * kGStageA + (m & 127) * 128 + (gslot(m & 127, (e >> 3) & 7) << 4);
+  return ((size_t)(m >> 7) * nk + (e >> 6)) * kGStageA + ((((m & 127) >> 4) * 2 + ((e >> 5) & 1)) << 10) +
+         ((((e >> 3) & 3) * 16 + (m & 15)) << 4);
 }
+__device__ __forceinline__ int frag_off(int rb, int ks) { return (rb * 2 + ks) << 10; }
 
 // ---------------------------------------------------------------------------
 // prep: one wave per token row m of the launch (rows past M of the padded
@@ -243,7 +253,7 @@ __global__ __launch_bounds__(64 * kGWaves) void qkv_gemm_bf16_kernel(const GemmA
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int i = 0; i < kGRB; ++i)
-        af[ks][i].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + gswz((wm * kGRB + i) * 16 + r16, 4 * ks + g)));
+        af[ks][i].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + frag_off(wm * kGRB + i, ks) + lane * 16));
 #pragma unroll
       for (int j = 0; j < kGCB; ++j)
         wf[ks][j].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + kGStageA + gswz((wn * kGCB + j) * 16 + r16, 4 * ks + g)));
@@ -375,22 +385,22 @@ __device__ __forceinline__ int packed_weight_row(int gc, int F, int dh) {
   return hh * dh + (cc & 1) * (dh / 2) + p0 + 2 * (cc >> 2) + ((cc >> 1) & 1);
 }
 
-// Wp[n][kt][c][s] (16-byte pieces): column tile n of kGBN GEMM columns,
-// contraction tile kt; piece slot s of row c holds elements
-// kt*64 + 8*(s ^ ((c >> 1) & 7)) .. +7 of weight row
-// packed_weight_row(n*kGBN + c), as fp16.
+// Wp[n][kt][fb][ks][lane] (16-byte pieces): column tile n of kGBN GEMM
+// columns, contraction tile kt, fragment-major (see a_piece): fragment
+// (16-column block fb, half ks), lane g*16 + r holds elements
+// kt*64 + 32 ks + 8 g .. +7 of weight row packed_weight_row(n*kGBN + 16 fb + r),
+// as fp16.
 __global__ __launch_bounds__(256) void pack_qkv_weight_kernel(const bf16_t *W, uint4 *Wp, int D, int F, int dh,
                                                               size_t n_pieces) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n_pieces) return;
   const int nk = D / kGBK;
-  const int s = (int)(idx & 7);
-  const size_t rest = idx >> 3;
-  const int c = (int)(rest % kGBN);
-  const size_t tk = rest / kGBN;
+  const int L = (int)(idx & 63), f = (int)((idx >> 6) % (kGBN / 8));   // 24 fragments per tile
+  const size_t tk = idx / (kGStageW / 16);
   const int kt = (int)(tk % nk), n = (int)(tk / nk);
+  const int c = (f >> 1) * 16 + (L & 15), ks = f & 1, g = L >> 4;
   const int wrow = packed_weight_row(n * kGBN + c, F, dh);
-  const uint4 u = *reinterpret_cast<const uint4 *>(W + (size_t)wrow * D + kt * kGBK + 8 * gslot(c, s));
+  const uint4 u = *reinterpret_cast<const uint4 *>(W + (size_t)wrow * D + kt * kGBK + 32 * ks + 8 * g);
   Wp[idx] = make_uint4(f16pair(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u)),
                        f16pair(__uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)),
                        f16pair(__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u)),
@@ -427,10 +437,10 @@ __global__ __launch_bounds__(512) void qkv_gemm_packed_kernel(const GemmArgs a) 
     const char *st = smem + (kt % kGStages) * kGStage;
 #pragma unroll
     for (int i = 0; i < kPRB; ++i)
-      fa[i].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + gswz((wm * kPRB + i) * 16 + r16, 4 * kg + g)));
+      fa[i].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + frag_off(wm * kPRB + i, kg) + lane * 16));
 #pragma unroll
     for (int j = 0; j < kPCB; ++j)
-      fw[j].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + kGStageA + gswz((wn * kPCB + j) * 16 + r16, 4 * kg + g)));
+      fw[j].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + kGStageA + frag_off(wn * kPCB + j, kg) + lane * 16));
   };
 
   f32x4_t acc[kPCB][kPRB];                           // C^T blocks: lane (g, t) holds columns 4g..4g+3 of token t
