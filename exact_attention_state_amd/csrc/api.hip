@@ -168,6 +168,12 @@ Partials partial_layout(const lacache_ctx *ctx, void *ws, int64_t P) {
 // kGemmMinTokens tokens.
 bool gemm_capable(const lacache_ctx *ctx) { return ctx->cfg.dtype == LACACHE_BF16 && ctx->cfg.d_model % 512 == 0; }
 bool step_uses_gemm(const lacache_ctx *ctx, int64_t M) { return gemm_capable(ctx) && M >= lc::kGemmMinTokens; }
+// Block steps through the prep kernel and a GEMM: many tokens, or few
+// tokens with the packed weight (the skinny GEMM).
+bool step_uses_prep(const lacache_ctx *ctx, const lacache_weights *w, int64_t M) {
+  return step_uses_gemm(ctx, M) ||
+         (gemm_capable(ctx) && w->w_qkv_packed && lc::skinny_supported((int)M, ctx->cfg.d_model));
+}
 int64_t block_tokens(const lacache_seq *seqs, int32_t batch) {
   int64_t M = 0;
   for (int i = 0; i < batch; ++i) M += seqs[i].block_end - seqs[i].block_start;
@@ -397,8 +403,10 @@ lacache_status lacache_workspace_size(const lacache_ctx *cctx, int32_t op, const
       return LACACHE_OK;
     case LACACHE_OP_BLOCK_STEP: {
       const int64_t M = block_tokens(seqs, batch);
+      // The prep/GEMM workspace whenever the configuration has that path (the
+      // weights, packed or not, are known only at the call).
       *bytes = partial_bytes(ctx, partial_rows(split_keys(ctx, seqs, batch), seqs, batch)) +
-               (step_uses_gemm(ctx, M) ? gemm_bytes(ctx, M) : 0);
+               (gemm_capable(ctx) ? gemm_bytes(ctx, M) : 0);
       return LACACHE_OK;
     }
     case LACACHE_OP_DUALCACHE_ATTN:
@@ -427,7 +435,7 @@ hipError_t run_qkv_gemm(lacache_ctx *ctx, const lacache_weights *w, const lacach
   pa.flags = ctx->flags;
   pa.mode = mode;
   pa.M = M;
-  pa.M_pad = lc::gemm_rows_padded(M);
+  pa.M_pad = lc::prep_rows(M, ctx->cfg.d_model, w->w_qkv_packed != nullptr);
   pa.row0 = row0;
   pa.ids_base = ids_base;
   pa.vocab = ctx->cfg.vocab;
@@ -572,7 +580,7 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
   const int split = split_keys(ctx, seqs, batch, &direct);
   const int64_t P = partial_rows(split, seqs, batch);
   const int64_t Mall = block_tokens(seqs, batch);
-  const bool gemm = step_uses_gemm(ctx, Mall);
+  const bool gemm = step_uses_prep(ctx, w, Mall);
   const size_t need = partial_bytes(ctx, P) + (gemm ? gemm_bytes(ctx, Mall) : 0);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,

@@ -90,17 +90,20 @@ __device__ __forceinline__ int frag_off(int rb, int ks) { return (rb * 2 + ks) <
 // prep: one wave per token row m of the launch (rows past M of the padded
 // tile are written as zeros).  Each lane owns D/64 consecutive elements.
 // ---------------------------------------------------------------------------
+// NP = D / 512: 16-byte pieces per lane; lane l moves pieces l, l + 64, ...
+// of a row (consecutive lanes on consecutive pieces), all in one round trip.
+template <int NP>
 __global__ __launch_bounds__(256) void qkv_prep_kernel(const SeqArgs sa, const PrepArgs a) {
+  constexpr int D = NP * 512, nk = D / kGBK;
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= a.M_pad) return;
-  const int D = a.D;
-  const int per = D / 64;                          // elements per lane (multiple of 4)
   char *abase = static_cast<char *>(a.A);
-  const int nk = D / kGBK;
   float2 *csrow = a.cs + (size_t)m * (a.dh / 2);
   if (m >= a.M) {
-    for (int j = 0; j < per; j += 8) *reinterpret_cast<uint4 *>(abase + a_piece(m, lane * per + j, nk)) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+      *reinterpret_cast<uint4 *>(abase + a_piece(m, (j * 64 + lane) * 8, nk)) = make_uint4(0, 0, 0, 0);
     if (lane < a.dh / 2) csrow[lane] = make_float2(0.f, 0.f);
     return;
   }
@@ -119,14 +122,22 @@ __global__ __launch_bounds__(256) void qkv_prep_kernel(const SeqArgs sa, const P
   }
   const bool bad = id < 0 || id >= a.vocab;
   if (bad && lane == 0) atomicOr(a.flags, 1u);
-  const bf16_t *erow = static_cast<const bf16_t *>(a.E) + (size_t)(bad ? 0 : id) * D + lane * per;
-  const bf16_t *grow = static_cast<const bf16_t *>(a.gamma) + lane * per;
-  bf16_t *hrow = static_cast<bf16_t *>(a.h) + (size_t)dst * D + lane * per;
+  // Unconditional loads (a bad id reads row 0 and is zeroed after).
+  const uint4 *erow = reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.E) + (size_t)(bad ? 0 : id) * D);
+  const uint4 *grow = static_cast<const uint4 *>(a.gamma);
+  uint4 ev[NP], gv[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) ev[j] = erow[j * 64 + lane];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) gv[j] = grow[j * 64 + lane];
+  const float2 csv = a.rope[(size_t)pos * (a.dh / 2) + min(lane, a.dh / 2 - 1)];
+  uint4 *hrow = reinterpret_cast<uint4 *>(static_cast<bf16_t *>(a.h) + (size_t)dst * D);
   float ss = 0.f;
-  for (int j = 0; j < per; j += 8) {
-    const uint4 u = bad ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4 *>(erow + j);
-    *reinterpret_cast<uint4 *>(hrow + j) = u;
-    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    if (bad) ev[j] = make_uint4(0, 0, 0, 0);
+    hrow[j * 64 + lane] = ev[j];
+    const uint32_t wd[4] = {ev[j].x, ev[j].y, ev[j].z, ev[j].w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float x0 = __uint_as_float(wd[q] << 16), x1 = __uint_as_float(wd[q] & 0xffff0000u);
@@ -137,10 +148,9 @@ __global__ __launch_bounds__(256) void qkv_prep_kernel(const SeqArgs sa, const P
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
   const float r = rsqrtf(ss / (float)D + a.eps);
   bool range = true;
-  for (int j = 0; j < per; j += 8) {
-    const uint4 u = bad ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4 *>(erow + j);
-    const uint4 gv = *reinterpret_cast<const uint4 *>(grow + j);
-    const uint32_t wd[4] = {u.x, u.y, u.z, u.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const uint32_t wd[4] = {ev[j].x, ev[j].y, ev[j].z, ev[j].w}, gw[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
     uint32_t o[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -149,11 +159,11 @@ __global__ __launch_bounds__(256) void qkv_prep_kernel(const SeqArgs sa, const P
       range = range && fabsf(y0) <= kF16Max && fabsf(y1) <= kF16Max;
       o[q] = f16pair(y0, y1);
     }
-    *reinterpret_cast<uint4 *>(abase + a_piece(m, lane * per + j, nk)) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4 *>(abase + a_piece(m, (j * 64 + lane) * 8, nk)) = make_uint4(o[0], o[1], o[2], o[3]);
   }
   if (!range) atomicOr(a.flags, 2u);
   if (lane == 0) a.map[m] = make_int2(dst, pos);
-  if (lane < a.dh / 2) csrow[lane] = a.rope[(size_t)pos * (a.dh / 2) + lane];
+  if (lane < a.dh / 2) csrow[lane] = csv;
 }
 
 constexpr int kGWN = 4, kGRB = kGBM / 2 / 16, kGCB = kGBN / kGWN / 16;   // 2 x 4 waves of 64 x 48
@@ -593,8 +603,149 @@ int gemm_rows_padded(int M) { return (M + kGBM - 1) / kGBM * kGBM; }
 
 hipError_t launch_qkv_prep(const SeqArgs &sa, const PrepArgs &a, hipStream_t s, const LaunchEvents &ev) {
   if (a.M_pad <= 0) return hipSuccess;
-  lc_launch(qkv_prep_kernel, dim3((a.M_pad + 3) / 4), dim3(256), 0, s, ev, sa, a);
+  const dim3 grid((a.M_pad + 3) / 4);
+  switch (a.D / 512) {
+#define LC_PREP(NPV) \
+  case NPV: lc_launch(qkv_prep_kernel<NPV>, grid, dim3(256), 0, s, ev, sa, a); break;
+    LC_PREP(1) LC_PREP(2) LC_PREP(3) LC_PREP(4) LC_PREP(5) LC_PREP(6) LC_PREP(7) LC_PREP(8)
+    LC_PREP(9) LC_PREP(10) LC_PREP(11) LC_PREP(12) LC_PREP(13) LC_PREP(14) LC_PREP(15) LC_PREP(16)
+#undef LC_PREP
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Skinny GEMM (at most 64 tokens, packed weight): a workgroup of 8 waves owns
+// 48 GEMM columns (column blocks 3q..3q+2 of packed tile n) and the TB
+// 16-token blocks of the launch.  The waves split the contraction by
+// 64-wide tiles (wave w takes tiles w, w+8, ..., NPW of them); every operand
+// fragment is one contiguous KB (fragment-major tiles), loaded straight
+// into registers three tiles ahead, so the weight streams at the load unit's
+// full rate and no LDS staging is needed.  The 8 partial sums meet in LDS
+// in a fixed order (results do not depend on the token count); the
+// epilogue is the packed GEMM's: RoPE in-lane, fp16 cache write.
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyMaxTokens = 64;
+template <int TB> constexpr int skinny_smem() { return 8 * 3 * TB * 64 * 16; }
+
+template <int I, int N> struct Unroll {
+  template <class F> __device__ __forceinline__ static void run(F &f) {
+    f(std::integral_constant<int, I>{});
+    Unroll<I + 1, N>::run(f);
+  }
+};
+template <int N> struct Unroll<N, N> {
+  template <class F> __device__ __forceinline__ static void run(F &) {}
+};
+
+template <int DH, int TB, int NPW>
+__global__ __launch_bounds__(512) void qkv_skinny_kernel(const GemmArgs a) {
+  constexpr int NFB = 3, NBLK = NFB * TB;
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int nk = 8 * NPW;                            // contraction tiles (D / 64)
+  const int cbh = DH / 16, ncb = a.F / 16;
+  const int n = blockIdx.x >> 2, fb0 = 3 * (blockIdx.x & 3);
+  const char *wt = static_cast<const char *>(a.Wp) + (size_t)n * nk * kGStageW + frag_off(fb0, 0) + lane * 16;
+  const char *at = static_cast<const char *>(a.A) + lane * 16;      // row tile 0: the launch's <= 64 tokens
+
+  struct Tile {
+    uint4 w[NFB][2];
+    uint4 x[TB][2];
+  };
+  auto fetch = [&](Tile &t, int kt) {
+    const char *wp = wt + (size_t)kt * kGStageW, *ap = at + (size_t)kt * kGStageA;
+#pragma unroll
+    for (int f = 0; f < NFB; ++f)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) t.w[f][ks] = *reinterpret_cast<const uint4 *>(wp + frag_off(f, ks));
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) t.x[b][ks] = *reinterpret_cast<const uint4 *>(ap + frag_off(b, ks));
+    // Keep the loads here: the scheduler would otherwise sink them next to
+    // their use and collapse the three-tile prefetch.
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  f32x4_t acc[NFB][TB];
+#pragma unroll
+  for (int f = 0; f < NFB; ++f)
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[f][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Tile t0, t1, t2;
+  fetch(t0, w);
+  if (NPW > 1) fetch(t1, w + 8);
+  if (NPW > 2) fetch(t2, w + 16);
+  auto step = [&](auto IC) {
+    constexpr int i = decltype(IC)::value;
+    Tile &cur = i % 3 == 0 ? t0 : (i % 3 == 1 ? t1 : t2);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int f = 0; f < NFB; ++f)
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+          Frag<f16_t> fw, fx;
+          fw.v = __builtin_bit_cast(f16x8_t, cur.w[f][ks]);
+          fx.v = __builtin_bit_cast(f16x8_t, cur.x[b][ks]);
+          mma16(acc[f][b], fw, fx);
+        }
+    if (i + 3 < NPW) fetch(cur, w + 8 * (i + 3));
+  };
+  Unroll<0, NPW>::run(step);
+
+  // Partial sums of the 8 waves, then wave w finishes blocks w, w + 8.
+  f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
+#pragma unroll
+  for (int f = 0; f < NFB; ++f)
+#pragma unroll
+    for (int b = 0; b < TB; ++b) red[(w * NBLK + f * TB + b) * 64 + lane] = acc[f][b];
+  __syncthreads();
+  const int nrot = (a.H + a.Hkv) * DH, qf = a.H * DH, kf = a.Hkv * DH;
+  bool range = true;
+  for (int blk = w; blk < NBLK; blk += 8) {
+    f32x4_t y = red[blk * 64 + lane];
+#pragma unroll
+    for (int ww = 1; ww < 8; ++ww) y += red[(ww * NBLK + blk) * 64 + lane];
+    const int f = blk / TB, b = blk % TB;
+    const int cb = n * (kGBN / 16) + fb0 + f;
+    const int tok = b * 16 + r16;
+    if (cb >= ncb || tok >= a.M) continue;
+    const int hh = cb / cbh, p0 = (cb % cbh) * 8;
+    float o0 = y[0], o1 = y[1], o2 = y[2], o3 = y[3];
+    if (hh * DH < nrot) {
+      const uint4 c = *reinterpret_cast<const uint4 *>(a.cs + (size_t)tok * (DH / 2) + p0 + 2 * g);
+      const float c0 = __uint_as_float(c.x), s0 = __uint_as_float(c.y);
+      const float c1 = __uint_as_float(c.z), s1 = __uint_as_float(c.w);
+      o0 = y[0] * c0 - y[1] * s0;
+      o1 = y[1] * c0 + y[0] * s0;
+      o2 = y[2] * c1 - y[3] * s1;
+      o3 = y[3] * c1 + y[2] * s1;
+    }
+    range = range && fabsf(o0) <= kF16Max && fabsf(o1) <= kF16Max && fabsf(o2) <= kF16Max && fabsf(o3) <= kF16Max;
+    const int dst = a.map[tok].x;
+    const int fa = hh * DH + p0 + 2 * g, fbf = fa + DH / 2;   // first-half pair, partners
+    f16_t *base;
+    int off;
+    if (fa < qf) { base = static_cast<f16_t *>(a.q); off = dst * qf + fa; }
+    else if (fa < qf + kf) { base = static_cast<f16_t *>(a.k); off = dst * kf + (fa - qf); }
+    else { base = static_cast<f16_t *>(a.v); off = dst * kf + (fa - qf - kf); }
+    *reinterpret_cast<uint32_t *>(base + off) = f16pair(o0, o2);
+    *reinterpret_cast<uint32_t *>(base + off + (fbf - fa)) = f16pair(o1, o3);
+  }
+  if (!range) atomicOr(a.flags, 2u);
+}
+
+int prep_rows(int M, int D, bool packed) {
+  if (packed && skinny_supported(M, D)) return M <= 32 ? 32 : 64;   // the token blocks the skinny GEMM reads
+  return gemm_rows_padded(M);
+}
+
+bool skinny_supported(int M, int D) {
+  const int npw = D / 512;
+  return M >= 1 && M <= kSkinnyMaxTokens && D % 512 == 0 && (npw == 1 || npw == 2 || npw == 4 || npw == 8 || npw == 16);
 }
 
 size_t packed_qkv_weight_bytes(int D, int F) { return (size_t)((F + kGBN - 1) / kGBN) * kGBN * D * 2; }
@@ -609,6 +760,27 @@ hipError_t launch_pack_qkv_weight(const void *W, void *Wp, int D, int F, int dh,
 
 hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const LaunchEvents &ev) {
   if (a.M <= 0) return hipSuccess;
+  if (a.Wp && skinny_supported(a.M, a.D)) {
+    const dim3 grid(4 * ((a.F + kGBN - 1) / kGBN));
+#define LC_SK(DHV, TBV, NPWV) \
+  lc_launch(qkv_skinny_kernel<DHV, TBV, NPWV>, grid, dim3(512), skinny_smem<TBV>(), s, ev, a)
+#define LC_SK_NPW(DHV, TBV)                       \
+  switch (a.D / 512) {                             \
+    case 1: LC_SK(DHV, TBV, 1); break;             \
+    case 2: LC_SK(DHV, TBV, 2); break;             \
+    case 4: LC_SK(DHV, TBV, 4); break;             \
+    case 8: LC_SK(DHV, TBV, 8); break;             \
+    default: LC_SK(DHV, TBV, 16); break;           \
+  }
+    if (dh == 128) {
+      if (a.M <= 32) { LC_SK_NPW(128, 2) } else { LC_SK_NPW(128, 4) }
+    } else {
+      if (a.M <= 32) { LC_SK_NPW(64, 2) } else { LC_SK_NPW(64, 4) }
+    }
+#undef LC_SK_NPW
+#undef LC_SK
+    return hipGetLastError();
+  }
   dim3 grid((a.F + kGBN - 1) / kGBN, (a.M + kGBM - 1) / kGBM);
   if (a.Wp) {
     if (dh == 128) lc_launch(qkv_gemm_packed_kernel<128>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
@@ -629,6 +801,15 @@ hipError_t setup_gemm_attributes() {
     const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmSmem);
     if (e != hipSuccess) return e;
   }
+#define LC_SKA(DHV, NPWV)                                                                                    \
+  {                                                                                                          \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(qkv_skinny_kernel<DHV, 4, NPWV>),      \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, skinny_smem<4>());        \
+    if (e != hipSuccess) return e;                                                                           \
+  }
+  LC_SKA(128, 1) LC_SKA(128, 2) LC_SKA(128, 4) LC_SKA(128, 8) LC_SKA(128, 16)
+  LC_SKA(64, 1) LC_SKA(64, 2) LC_SKA(64, 4) LC_SKA(64, 8) LC_SKA(64, 16)
+#undef LC_SKA
   return hipSuccess;
 }
 

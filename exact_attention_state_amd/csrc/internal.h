@@ -107,6 +107,8 @@ hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipS
 hipError_t launch_qkv_prep(const SeqArgs &sa, const PrepArgs &a, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const LaunchEvents &ev);
 size_t packed_qkv_weight_bytes(int D, int F);
+bool skinny_supported(int M, int D);      // the packed-weight projection for <= 64 tokens
+int prep_rows(int M, int D, bool packed); // rows the prep kernel writes (zero rows past M included)
 hipError_t launch_pack_qkv_weight(const void *W, void *Wp, int D, int F, int dh, hipStream_t s);
 hipError_t setup_gemm_attributes();
 hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,

@@ -84,13 +84,16 @@ def test_tiny_fp32_refresh_and_steps():
     _run_full(synth.WORKLOADS["tiny"], 3)
 
 
-def test_small_bf16_ragged_batch():
+@pytest.mark.parametrize("packed", [True, False])
+def test_small_bf16_ragged_batch(packed):
     # Three samples: ragged lengths (not multiples of any tile), a block at the
-    # very start, a block at the very end, and grouped KV heads.
+    # very start, a block at the very end, and grouped KV heads.  42 block
+    # tokens: the skinny packed-weight GEMM (packed) or the streaming
+    # small-batch kernel.
     wl = synth.custom("small_bf16_ragged", dtype="bf16", d_model=512, n_heads=4, n_kv_heads=2, head_dim=128,
                       vocab=3000, prompt_lens=(37, 150, 5), gen_len=70, block_size=14, block_idx=(2, 0, 4),
                       steps=3, seed=21)
-    _run_full(wl, 3)
+    _run_full(wl, 3, packed=packed)
 
 
 def test_small_fp32_head64_multi_tile():
