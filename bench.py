@@ -62,6 +62,7 @@ KERNEL_SOURCES = {
     "qkv_gemm": ["exact_attention_state_amd/csrc/gemm.hip"],
     "block_rows": ["exact_attention_state_amd/csrc/attn.hip"],
     "invariant_rows": ["exact_attention_state_amd/csrc/attn.hip"],
+    "attn": ["exact_attention_state_amd/csrc/attn.hip"],
 }
 COMMON_SOURCES = ["exact_attention_state_amd/csrc/common.h", "exact_attention_state_amd/csrc/internal.h"]
 def traffic_file(workload):
@@ -128,7 +129,9 @@ def step_accounting(wl):
     pairs_c = pairs_a + pairs_b
     qkv_bytes = F * D * s + 2 * M * D * s + D * s + M * F * c + M * 4
     kern = {"block_rows": dict(bytes=a_bytes, flops=4 * d * pairs_a),
-            "invariant_rows": dict(bytes=b_bytes, flops=4 * d * pairs_b)}
+            "invariant_rows": dict(bytes=b_bytes, flops=4 * d * pairs_b),
+            # small steps run both in one launch
+            "attn": dict(bytes=a_bytes + b_bytes, flops=4 * d * (pairs_a + pairs_b))}
     if wl.dtype == "bf16" and D % 512 == 0 and M >= 128:
         # Many tokens: prep (embedding rows in, EmbedCache rows and the fp16
         # activations out) and the GEMM (the packed fp16 weight, activations,

@@ -636,6 +636,19 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     aa.seg_rows = seg_rows;
     aa.direct = direct;
     aa.scale_log2 = scale_log2(ctx);
+    if (!seg_rows && !aa.direct) {
+      // Small launches: the block rows' partials and the invariant rows in one
+      // launch (their latencies overlap), then the merge.
+      e = timed(ctx, LACACHE_KERNEL_ATTN, s, [&](const lc::LaunchEvents &ev) {
+        return lc::launch_attn_ab(dt, dh, sa, aa, sa.pre[1][ns] * H, sa.pre[2][ns] * H, s, ev);
+      });
+      if (e != hipSuccess) return hip_fail(ctx, "block-step attention launch", e);
+      e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
+      if (e != hipSuccess) return hip_fail(ctx, "block-step merge launch", e);
+      row_base += M;
+      part_base += sa.pre[3][ns];
+      continue;
+    }
     e = timed(ctx, LACACHE_KERNEL_BLOCK_ROWS, s, [&](const lc::LaunchEvents &ev) {
       return lc::launch_block_rows(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
     });

@@ -1058,6 +1058,21 @@ __device__ void merge_wave(const SeqArgs &sa, const AttnArgs &a, int M, int wid)
   if (a.lse && lane == 0) a.lse[(size_t)orow * a.H + h] = (mx + __log2f(lsum)) * kLn2;
 }
 
+// Block step, small launches: type-A items (the block rows' partials) and
+// type-B items (invariant rows) in one launch, their latencies overlapping;
+// the merge of the partials follows as its own launch.  The first nA
+// workgroups are type A.
+template <typename T, typename TO, int DH, int BMAX>
+__global__ __launch_bounds__(256) void attn_ab_kernel(const SeqArgs sa, const AttnArgs a, int nA) {
+  extern __shared__ __align__(16) char smem[];
+  if ((int)blockIdx.x < nA) {
+    block_rows_partial<T, TO, DH>(sa, a, blockIdx.x / a.H, blockIdx.x % a.H, smem);
+    return;
+  }
+  const int j = blockIdx.x - nA;
+  invariant_rows<T, TO, DH, BMAX>(sa, a, j / a.H, j % a.H, smem);
+}
+
 // DualCache: the merge alone, 4 (row, head) pairs per workgroup.
 template <typename T, typename TO, int DH>
 __global__ __launch_bounds__(256) void merge_kernel(const SeqArgs sa, const AttnArgs a, int M) {
@@ -1190,6 +1205,25 @@ hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs
   return hipGetLastError();
 }
 
+template <typename T, int DH, int BM> constexpr size_t attn_ab_smem() {
+  return block_rows_smem<T, DH>() > invariant_rows_smem<T, DH, BM>() ? block_rows_smem<T, DH>()
+                                                                     : invariant_rows_smem<T, DH, BM>();
+}
+
+hipError_t launch_attn_ab(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int nA, int nB, hipStream_t s,
+                          const LaunchEvents &ev) {
+  if (nA + nB <= 0) return hipSuccess;
+  int bmax = 0;
+  for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
+#define LC_AB(BM) \
+  LC_DISPATCH(dt, dh, (lc_launch(attn_ab_kernel<T, TO, DH, BM>, dim3(nA + nB), dim3(256), attn_ab_smem<T, DH, BM>(), s, ev, sa, a, nA)))
+  if (bmax <= 32) LC_AB(32);
+  else if (bmax <= 64) LC_AB(64);
+  else LC_AB(128);
+#undef LC_AB
+  return hipGetLastError();
+}
+
 hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                                    hipStream_t s, const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
@@ -1246,6 +1280,15 @@ hipError_t setup_kernel_attributes() {
   if (e == hipSuccess)                                                                           \
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(K), hipFuncAttributeMaxDynamicSharedMemorySize, \
                             (int)(BYTES));
+#define LC_ATTR_AB(BM)                                                                          \
+  LC_ATTR((attn_ab_kernel<f16_t, bf16_t, 128, BM>), (attn_ab_smem<f16_t, 128, BM>()));              \
+  LC_ATTR((attn_ab_kernel<f16_t, bf16_t, 64, BM>), (attn_ab_smem<f16_t, 64, BM>()));                \
+  LC_ATTR((attn_ab_kernel<float, float, 128, BM>), (attn_ab_smem<float, 128, BM>()));               \
+  LC_ATTR((attn_ab_kernel<float, float, 64, BM>), (attn_ab_smem<float, 64, BM>()));
+  LC_ATTR_AB(32)
+  LC_ATTR_AB(64)
+  LC_ATTR_AB(128)
+#undef LC_ATTR_AB
 #define LC_ATTR_INV(BM)                                                   \
   LC_ATTR((invariant_rows_kernel<f16_t, bf16_t, 128, BM>), (invariant_rows_smem<f16_t, 128, BM>())); \
   LC_ATTR((invariant_rows_kernel<f16_t, bf16_t, 64, BM>), (invariant_rows_smem<f16_t, 64, BM>()));   \

@@ -117,6 +117,8 @@ hipError_t launch_invariant_rows(DType dt, int dh, const SeqArgs &sa, const Attn
                                  hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int M, hipStream_t s,
                         const LaunchEvents &ev);
+hipError_t launch_attn_ab(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int nA, int nB, hipStream_t s,
+                          const LaunchEvents &ev);
 constexpr int kStreamMaxBlock = 64;   // largest block the streaming type-B kernel serves
 hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                                    hipStream_t s, const LaunchEvents &ev);

@@ -28,8 +28,8 @@ EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "laca
             "lacache_profile_enable", "lacache_profile_read", "lacache_status_string", "lacache_last_error",
             "lacache_packed_weight_size", "lacache_pack_qkv_weight")
 (KERNEL_QKV, KERNEL_BLOCK_ROWS, KERNEL_INVARIANT_ROWS, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_QKV_PREP,
- KERNEL_QKV_GEMM) = range(7)
-KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn", "qkv_prep", "qkv_gemm")
+ KERNEL_QKV_GEMM, KERNEL_ATTN) = range(8)
+KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn", "qkv_prep", "qkv_gemm", "attn")
 
 
 class Config(ctypes.Structure):

@@ -259,9 +259,11 @@ typedef enum {
                                         the merge of the block rows' partials      */
   LACACHE_KERNEL_MERGE = 3,          /* DualCache: merge of the partials            */
   LACACHE_KERNEL_REFRESH_ATTN = 4,   /* refresh attention with FACache snapshot     */
-  LACACHE_KERNEL_QKV_PREP = 5,       /* many tokens: gather, EmbedCache, RMSNorm    */
-  LACACHE_KERNEL_QKV_GEMM = 6,       /* many tokens: QKV GEMM + RoPE + cache write  */
-  LACACHE_KERNEL_COUNT = 7
+  LACACHE_KERNEL_QKV_PREP = 5,       /* gather, EmbedCache, RMSNorm (GEMM path)     */
+  LACACHE_KERNEL_QKV_GEMM = 6,       /* prep'd tokens: QKV GEMM + RoPE + cache write */
+  LACACHE_KERNEL_ATTN = 7,           /* small block steps: block-row partials and
+                                        invariant rows in one launch               */
+  LACACHE_KERNEL_COUNT = 8
 } lacache_kernel;
 
 LACACHE_API lacache_status lacache_profile_enable(lacache_ctx *ctx, int enable);
