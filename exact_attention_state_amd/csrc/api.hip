@@ -154,7 +154,7 @@ size_t partial_bytes(const lacache_ctx *ctx, int64_t P) {
   return align256((size_t)P * H * sizeof(float2)) + align256((size_t)P * H * d * cache_elem_bytes(ctx));
 }
 Partials partial_layout(const lacache_ctx *ctx, void *ws, int64_t P) {
-  const size_t H = ctx->cfg.n_heads, d = ctx->cfg.head_dim;
+  const size_t H = ctx->cfg.n_heads;
   char *p = static_cast<char *>(ws);
   Partials r;
   r.ml = reinterpret_cast<float2 *>(p);
@@ -601,6 +601,22 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
       const int nU = sa.len[i] - (sa.be[i] - sa.bs[i]);
       sa.pre[2][i + 1] = sa.pre[2][i] + (seg_rows ? (nU + seg_rows - 1) / seg_rows : (nU + lc::kRowsB - 1) / lc::kRowsB);
     }
+    // Small launches run the block rows' partials and the invariant rows in
+    // one launch.  A second round of workgroups would pay the memory latency
+    // again, so the key chunks grow (fewer partials, more tiles per
+    // workgroup) until the launch is resident at once, if it can be.  Fewer
+    // partial rows than the workspace was sized for.
+    const bool combined = !seg_rows && !direct;
+    int split_s = split;
+    if (combined && ctx->split_keys <= 0) {
+      const int cap = lc::attn_ab_capacity(dt, dh, sa);
+      int max_len = 1;
+      for (int i = 0; i < ns; ++i) max_len = std::max(max_len, sa.len[i]);
+      while (sa.pre[1][ns] * H + sa.pre[2][ns] * H > cap && split_s < max_len) {
+        split_s *= 2;
+        plan_block_rows(split_s, sa);
+      }
+    }
     const int M = sa.pre[0][ns];
 
     hipError_t e = hipSuccess;
@@ -632,11 +648,11 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     aa.part_base = part_base;
     aa.H = H;
     aa.Hkv = ctx->cfg.n_kv_heads;
-    aa.split_keys = split;
+    aa.split_keys = split_s;
     aa.seg_rows = seg_rows;
     aa.direct = direct;
     aa.scale_log2 = scale_log2(ctx);
-    if (!seg_rows && !aa.direct) {
+    if (combined) {
       // Small launches: the block rows' partials and the invariant rows in one
       // launch (their latencies overlap), then the merge.
       e = timed(ctx, LACACHE_KERNEL_ATTN, s, [&](const lc::LaunchEvents &ev) {

@@ -526,11 +526,11 @@ __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int ite
 }
 
 // ---------------------------------------------------------------------------
-// Type B: 64 invariant rows, state from FACache, stream the block's keys.
-// All global loads (queries, FACache, first key step, V) are issued before
-// the first wait.
+// Type B: 64*MB invariant rows (MB row blocks of 16 per wave), state from
+// FACache, stream the block's keys.  All global loads (queries, FACache,
+// first key step, V) are issued before the first wait.
 // ---------------------------------------------------------------------------
-template <typename T, typename TO, int DH, int BMAX>
+template <typename T, typename TO, int DH, int BMAX, int MB>
 __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, int h, char *smem) {
   constexpr int NDB = DH / 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -544,20 +544,32 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
   const size_t kvstride = (size_t)a.Hkv * DH;
   const int off = sa.off[b];
 
+  // Wave w owns row blocks w*MB .. w*MB+MB-1 of the item's 64*MB rows.
   // Rows past the last invariant row load the last one (results dropped).
-  const int u = tile * kRowsB + w * 16 + r16;
-  const bool uvalid = u < nU;
-  const int uc = min(u, nU - 1);
-  const int row = off + (uc < bs ? uc : uc + B);
-  const T *qrow[1] = {static_cast<const T *>(a.q) + ((size_t)row * a.H + h) * DH};
-  Frag<T> qf[1][DH / 32];
-  load_q<T, 1, DH>(qf, qrow, g);
+  const T *qrow[MB];
+  size_t crow[MB];
+  bool uvalid[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int u = tile * (kRowsB * MB) + (w * MB + mb) * 16 + r16;
+    uvalid[mb] = u < nU;
+    const int uc = min(u, nU - 1);
+    const int row = off + (uc < bs ? uc : uc + B);
+    crow[mb] = (size_t)row * a.H + h;
+    qrow[mb] = static_cast<const T *>(a.q) + crow[mb] * DH;
+  }
+  Frag<T> qf[MB][DH / 32];
+  load_q<T, MB, DH>(qf, qrow, g);
 
-  // FACache state of this row (Algorithm 1: initialise with the cache).
-  const size_t crow = (size_t)row * a.H + h;
-  const float mc = a.m_c[crow], lc = a.l_c[crow];
-  f32x4_t oc[NDB];
-  load_row<T, DH>(oc, static_cast<const T *>(a.o_c) + crow * DH, g);
+  // FACache state of these rows (Algorithm 1: initialise with the cache).
+  float mc[MB], lc[MB];
+  f32x4_t oc[MB][NDB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    mc[mb] = a.m_c[crow[mb]];
+    lc[mb] = a.l_c[crow[mb]];
+    load_row<T, DH>(oc[mb], static_cast<const T *>(a.o_c) + crow[mb] * DH, g);
+  }
   const T *kbase = static_cast<const T *>(a.k) + (size_t)(off + bs) * kvstride + hk * DH;
   KStep<T, DH> kf[2];
   load_k_step<T, DH>(kf[0], kbase, kvstride, min(32, B), lane);
@@ -568,26 +580,32 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
   vtile_wait();
   lds_barrier();
 
-  AttnState<1, DH> st;
-  st.m[0] = mc * kLog2e;
-  st.l[0] = g == 0 ? lc : 0.f;
+  AttnState<MB, DH> st;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) st.o[0][db] = oc[db] * lc;
+  for (int mb = 0; mb < MB; ++mb) {
+    st.m[mb] = mc[mb] * kLog2e;
+    st.l[mb] = g == 0 ? lc[mb] : 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) st.o[mb][db] = oc[mb][db] * lc[mb];
+  }
 
   // Up to 4 steps (block <= 128 keys); the next step's keys load during this one.
   for (int c0 = 0; c0 < B; c0 += 64) {
     if (c0 + 32 < B) load_k_step<T, DH>(kf[1], kbase + (size_t)(c0 + 32) * kvstride, kvstride, min(32, B - c0 - 32), lane);
-    attend_step_pre<T, 1, DH, BMAX>(st, qf, kf[0], min(32, B - c0), vbuf, c0, a.scale_log2, lane);
+    attend_step_pre<T, MB, DH, BMAX>(st, qf, kf[0], min(32, B - c0), vbuf, c0, a.scale_log2, lane);
     if (c0 + 32 < B) {
       if (c0 + 64 < B) load_k_step<T, DH>(kf[0], kbase + (size_t)(c0 + 64) * kvstride, kvstride, min(32, B - c0 - 64), lane);
-      attend_step_pre<T, 1, DH, BMAX>(st, qf, kf[1], min(32, B - c0 - 32), vbuf, c0 + 32, a.scale_log2, lane);
+      attend_step_pre<T, MB, DH, BMAX>(st, qf, kf[1], min(32, B - c0 - 32), vbuf, c0 + 32, a.scale_log2, lane);
     }
   }
 
-  const float lt = group_sum(st.l[0]);
-  if (uvalid) {
-    store_row<TO, DH>(static_cast<TO *>(a.out) + crow * DH, st.o[0], 1.0f / lt, g);
-    if (a.lse && g == 0) a.lse[crow] = (st.m[0] + __log2f(lt)) * kLn2;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const float lt = group_sum(st.l[mb]);
+    if (uvalid[mb]) {
+      store_row<TO, DH>(static_cast<TO *>(a.out) + crow[mb] * DH, st.o[mb], 1.0f / lt, g);
+      if (a.lse && g == 0) a.lse[crow[mb]] = (st.m[mb] + __log2f(lt)) * kLn2;
+    }
   }
 }
 
@@ -804,20 +822,20 @@ __global__ __launch_bounds__(64) void invariant_stream_kernel(const SeqArgs sa, 
 // ---------------------------------------------------------------------------
 // Type A, streaming (16-bit caches): one workgroup of 4 waves per (sample,
 // head, 32 block rows, key chunk).  K and V of 64-key tiles go global -> LDS
-// row-wise through a 4-stage ring (up to three tiles in flight while one is
-// used); wave w takes row block w & 1 and keys 32 (w >> 1) .. +31 of every
+// row-wise through an NST-stage ring (up to NST-1 tiles in flight while one
+// is used); wave w takes row block w & 1 and keys 32 (w >> 1) .. +31 of every
 // tile.  The two waves of a row block merge through LDS at the end; the
 // chunk's state goes to the workspace, or, when a.direct (every chunk is a
 // whole sequence), O and LSE go out directly.
 // K tile: key c's 16-byte piece p in slot p ^ kslot(c); the 16 keys of one
 // A-operand read (8a + b + 4kb, a, b < 4) then hit distinct slots.
 // ---------------------------------------------------------------------------
-template <int DH> struct StreamA {
+template <int DH, int NST_> struct StreamA {
   static constexpr int ROWB = DH * 2, PPR = ROWB / 16, RPC = 1024 / ROWB;
   static constexpr int TK = 64;                                 // keys per tile
   static constexpr int KT = TK * ROWB;                          // bytes of a K (or V) tile
   static constexpr int STAGE = 2 * KT;
-  static constexpr int NST = 4;
+  static constexpr int NST = NST_;
   static constexpr int QB = kRowsA * ROWB;                      // the 32 query rows
   static constexpr int BYTES = QB + NST * STAGE;
   static constexpr int CPW = STAGE / 1024 / 4;                  // copies per wave per tile
@@ -826,10 +844,10 @@ __device__ __forceinline__ int kslot(int c, int ppr) {
   return ppr == 16 ? (((c >> 1) & 12) | (c & 3)) : (((c >> 1) & 4) | (c & 3));
 }
 
-template <typename TO, int DH>
+template <typename TO, int DH, int NST>
 __global__ __launch_bounds__(256) void block_rows_stream_kernel(const SeqArgs sa, const AttnArgs a) {
   using T = f16_t;
-  using S = StreamA<DH>;
+  using S = StreamA<DH, NST>;
   using QT = QTile<T, DH>;
   constexpr int NDB = DH / 16, HDB = NDB / 2;
   extern __shared__ __align__(16) char smem[];
@@ -878,16 +896,15 @@ __global__ __launch_bounds__(256) void block_rows_stream_kernel(const SeqArgs sa
             lbase + q * 1024);
     }
   }
-  // All four stages start filling; the queries and tile 0 are waited for.
-  issue(0);
-  if (ntiles > 1) issue(1);
-  if (ntiles > 2) issue(2);
-  if (ntiles > 3) issue(3);
+  // All stages start filling; the queries and tile 0 are waited for.
+#pragma unroll
+  for (int j = 0; j < S::NST; ++j)
+    if (j < ntiles) issue(j);
   {
-    const int behind = min(3, ntiles - 1);
-    if (behind == 3) vmcnt_wait<3 * S::CPW>();
-    else if (behind == 2) vmcnt_wait<2 * S::CPW>();
-    else if (behind == 1) vmcnt_wait<S::CPW>();
+    const int behind = min(S::NST - 1, ntiles - 1);
+    if (S::NST > 3 && behind == 3) vmcnt_wait<3 * S::CPW>();
+    else if (S::NST > 2 && behind == 2) vmcnt_wait<2 * S::CPW>();
+    else if (S::NST > 1 && behind == 1) vmcnt_wait<S::CPW>();
     else vmcnt_wait<0>();
   }
   lds_barrier();
@@ -920,15 +937,15 @@ __global__ __launch_bounds__(256) void block_rows_stream_kernel(const SeqArgs sa
       softmax_pv<T, 1, DH, S::TK>(st, sc, nv, reinterpret_cast<const T *>(stg + S::KT), 32 * kh, a.scale_log2, lane);
     }
     if (tt + 1 < ntiles) {
-      // This wave's copies of tile tt+1 landed (those of tt+2, tt+3 may not
-      // have); the barrier publishes it and frees stage tt for tile tt+4
-      // (tiles 0-3 were issued before the loop).
-      const int behind = min(2, ntiles - 2 - tt);
-      if (behind == 2) vmcnt_wait<2 * S::CPW>();
-      else if (behind == 1) vmcnt_wait<S::CPW>();
+      // This wave's copies of tile tt+1 landed (later tiles may not have);
+      // the barrier publishes it and frees stage tt for tile tt+NST (tiles
+      // 0..NST-1 were issued before the loop).
+      const int behind = min(S::NST - 2, ntiles - 2 - tt);
+      if (S::NST > 3 && behind == 2) vmcnt_wait<2 * S::CPW>();
+      else if (S::NST > 2 && behind == 1) vmcnt_wait<S::CPW>();
       else vmcnt_wait<0>();
       lds_barrier();
-      if (tt + 4 < ntiles) issue(tt + 4);
+      if (tt + S::NST < ntiles) issue(tt + S::NST);
     }
   }
 
@@ -1070,7 +1087,7 @@ __global__ __launch_bounds__(256) void attn_ab_kernel(const SeqArgs sa, const At
     return;
   }
   const int j = blockIdx.x - nA;
-  invariant_rows<T, TO, DH, BMAX>(sa, a, j / a.H, j % a.H, smem);
+  invariant_rows<T, TO, DH, BMAX, 1>(sa, a, j / a.H, j % a.H, smem);
 }
 
 // DualCache: the merge alone, 4 (row, head) pairs per workgroup.
@@ -1092,7 +1109,7 @@ __global__ __launch_bounds__(256) void invariant_rows_kernel(const SeqArgs sa, c
     return;
   }
   const int j = blockIdx.x - nmw;
-  invariant_rows<T, TO, DH, BMAX>(sa, a, j / a.H, j % a.H, smem);
+  invariant_rows<T, TO, DH, BMAX, 1>(sa, a, j / a.H, j % a.H, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1193,12 +1210,34 @@ template <typename T, int DH> constexpr size_t refresh_smem() {
     }                                                                                    \
   } while (0)
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
                              const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
   if (dt == kBF16 && a.direct) {
-    if (dh == 128) lc_launch(block_rows_stream_kernel<bf16_t, 128>, dim3(n_blocks), dim3(256), StreamA<128>::BYTES, s, ev, sa, a);
-    else lc_launch(block_rows_stream_kernel<bf16_t, 64>, dim3(n_blocks), dim3(256), StreamA<64>::BYTES, s, ev, sa, a);
+    // A 4-stage ring (three tiles of lookahead) holds one workgroup per CU.
+    // When the launch fits on the chip at two per CU but not at one, a
+    // 2-stage ring runs it in one round instead of two.
+    const int cus = device_cus();
+    const bool two = n_blocks > cus && n_blocks <= 2 * cus;
+    if (dh == 128) {
+      if (two) lc_launch(block_rows_stream_kernel<bf16_t, 128, 2>, dim3(n_blocks), dim3(256), StreamA<128, 2>::BYTES, s, ev, sa, a);
+      else lc_launch(block_rows_stream_kernel<bf16_t, 128, 4>, dim3(n_blocks), dim3(256), StreamA<128, 4>::BYTES, s, ev, sa, a);
+    } else {
+      if (two) lc_launch(block_rows_stream_kernel<bf16_t, 64, 2>, dim3(n_blocks), dim3(256), StreamA<64, 2>::BYTES, s, ev, sa, a);
+      else lc_launch(block_rows_stream_kernel<bf16_t, 64, 4>, dim3(n_blocks), dim3(256), StreamA<64, 4>::BYTES, s, ev, sa, a);
+    }
     return hipGetLastError();
   }
   LC_DISPATCH(dt, dh, (lc_launch(block_rows_kernel<T, TO, DH>, dim3(n_blocks), dim3(256), block_rows_smem<T, DH>(), s, ev, sa, a)));
@@ -1210,11 +1249,42 @@ template <typename T, int DH, int BM> constexpr size_t attn_ab_smem() {
                                                                      : invariant_rows_smem<T, DH, BM>();
 }
 
+namespace {
+int block_max(const SeqArgs &sa) {
+  int bmax = 0;
+  for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
+  return bmax;
+}
+// Workgroups of one combined launch resident on one CU (occupancy query, cached).
+template <typename K> int resident_per_cu(K kernel, size_t smem) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(kernel), 256, smem) !=
+          hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+}  // namespace
+
+// Workgroups of a combined launch resident on the whole chip at once.
+int attn_ab_capacity(DType dt, int dh, const SeqArgs &sa) {
+  const int bmax = block_max(sa);
+  static int cap[2][2][3] = {};                      // [fp32][dh == 128][block size class]
+  const int fi = dt != kBF16, di = dh == 128, bi = bmax <= 32 ? 0 : bmax <= 64 ? 1 : 2;
+  int &c = cap[fi][di][bi];
+  if (c == 0) {
+#define LC_CAP(BM) LC_DISPATCH(dt, dh, (c = resident_per_cu(attn_ab_kernel<T, TO, DH, BM>, attn_ab_smem<T, DH, BM>())))
+    if (bi == 0) LC_CAP(32);
+    else if (bi == 1) LC_CAP(64);
+    else LC_CAP(128);
+#undef LC_CAP
+  }
+  return c * device_cus();
+}
+
 hipError_t launch_attn_ab(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int nA, int nB, hipStream_t s,
                           const LaunchEvents &ev) {
   if (nA + nB <= 0) return hipSuccess;
-  int bmax = 0;
-  for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
+  const int bmax = block_max(sa);
 #define LC_AB(BM) \
   LC_DISPATCH(dt, dh, (lc_launch(attn_ab_kernel<T, TO, DH, BM>, dim3(nA + nB), dim3(256), attn_ab_smem<T, DH, BM>(), s, ev, sa, a, nA)))
   if (bmax <= 32) LC_AB(32);
@@ -1223,6 +1293,7 @@ hipError_t launch_attn_ab(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a
 #undef LC_AB
   return hipGetLastError();
 }
+
 
 hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                                    hipStream_t s, const LaunchEvents &ev) {
@@ -1306,8 +1377,10 @@ hipError_t setup_kernel_attributes() {
   LC_ATTR((refresh_attn_kernel<f16_t, bf16_t, 64>), (refresh_smem<f16_t, 64>()));
   LC_ATTR((refresh_attn_kernel<float, float, 128>), (refresh_smem<float, 128>()));
   LC_ATTR((refresh_attn_kernel<float, float, 64>), (refresh_smem<float, 64>()));
-  LC_ATTR((block_rows_stream_kernel<bf16_t, 128>), (StreamA<128>::BYTES));
-  LC_ATTR((block_rows_stream_kernel<bf16_t, 64>), (StreamA<64>::BYTES));
+  LC_ATTR((block_rows_stream_kernel<bf16_t, 128, 4>), (StreamA<128, 4>::BYTES));
+  LC_ATTR((block_rows_stream_kernel<bf16_t, 64, 4>), (StreamA<64, 4>::BYTES));
+  LC_ATTR((block_rows_stream_kernel<bf16_t, 128, 2>), (StreamA<128, 2>::BYTES));
+  LC_ATTR((block_rows_stream_kernel<bf16_t, 64, 2>), (StreamA<64, 2>::BYTES));
 #undef LC_ATTR
   return e;
 }

@@ -138,16 +138,35 @@ __device__ __forceinline__ void mma16(f32x4_t &acc, const Frag<float> &a, const 
   for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
 }
 
-// Reductions across the four lane groups (lanes l, l^16, l^32, l^48).
+// Lane exchanges by the gfx950 lane-swap instructions (one VALU step, no LDS
+// permute): swapping x with itself leaves in every lane l the values of lanes
+// l & ~16 and l | 16 (swap16), or of l & ~32 and l | 32 (swap32), i.e. the
+// lane's own value and that of its partner l ^ 16 (l ^ 32) in lane order.
+__device__ __forceinline__ void swap16(float x, float &lo, float &hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float x, float &lo, float &hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+// Reductions across the four lane groups (lanes l, l^16, l^32, l^48).  The
+// sum adds the pair (x_l, x_{l^16}), then the pair across l^32: the same
+// rounding in every lane of a group (addition is commutative).
 __device__ __forceinline__ float group_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  float a, b;
+  swap16(x, a, b);
+  swap32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float group_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  float a, b;
+  swap16(x, a, b);
+  swap32(a + b, a, b);
+  return a + b;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -111,12 +111,15 @@ bool skinny_supported(int M, int D);      // the packed-weight projection for <=
 int prep_rows(int M, int D, bool packed); // rows the prep kernel writes (zero rows past M included)
 hipError_t launch_pack_qkv_weight(const void *W, void *Wp, int D, int F, int dh, hipStream_t s);
 hipError_t setup_gemm_attributes();
+int device_cus();                         // compute units of the current device (cached; 256 if unknown)
 hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                              hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_invariant_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, int M,
                                  hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int M, hipStream_t s,
                         const LaunchEvents &ev);
+// Workgroups of a combined (type A + type B) launch resident on the chip at once.
+int attn_ab_capacity(DType dt, int dh, const SeqArgs &sa);
 hipError_t launch_attn_ab(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int nA, int nB, hipStream_t s,
                           const LaunchEvents &ev);
 constexpr int kStreamMaxBlock = 64;   // largest block the streaming type-B kernel serves
