@@ -132,12 +132,16 @@ def step_accounting(wl):
             "invariant_rows": dict(bytes=b_bytes, flops=4 * d * pairs_b),
             # small steps run both in one launch
             "attn": dict(bytes=a_bytes + b_bytes, flops=4 * d * (pairs_a + pairs_b))}
-    skinny = 1 <= M <= 64 and D // 512 in (1, 2, 4, 8, 16)
-    if wl.dtype == "bf16" and D % 512 == 0 and (M >= 128 or skinny):
+    skinny = 1 <= M <= 64 and D // 512 in (1, 2, 4, 8, 16) and wl.vocab * D * 2 < 2 ** 32
+    if wl.dtype == "bf16" and D % 512 == 0 and skinny:
+        # At most 64 tokens: one launch streams the packed fp16 weight,
+        # gathers the embedding rows, writes the EmbedCache rows and Q/K/V
+        # (bound by the weight's HBM stream).
+        kern["qkv_gemm"] = dict(bytes=F * D * 2 + 2 * M * D * s + D * s + M * F * c, flops=2 * M * F * D)
+    elif wl.dtype == "bf16" and D % 512 == 0 and M >= 128:
         # Prep (embedding rows in, EmbedCache rows and the fp16 activations
-        # out) and the GEMM over the packed fp16 weight (activations in,
-        # Q/K/V out): many tokens (matrix-core bound), or at most 64 tokens
-        # (the skinny GEMM, bound by the weight's HBM stream).
+        # out), then the GEMM over the packed fp16 weight (activations in,
+        # Q/K/V out; the matrix cores bound it).
         kern["qkv_prep"] = dict(bytes=2 * M * D * s + D * s + M * D * 2 + M * 4, flops=0)
         kern["qkv_gemm"] = dict(bytes=F * D * 2 + M * D * 2 + M * F * c, flops=2 * M * F * D)
     else:

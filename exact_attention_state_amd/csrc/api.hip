@@ -442,8 +442,11 @@ hipError_t run_qkv_gemm(lacache_ctx *ctx, const lacache_weights *w, const lacach
   pa.D = ctx->cfg.d_model;
   pa.dh = ctx->cfg.head_dim;
   pa.eps = ctx->cfg.rms_eps;
-  hipError_t e = timed(ctx, LACACHE_KERNEL_QKV_PREP, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv_prep(sa, pa, s, ev); });
-  if (e != hipSuccess) return e;
+  const bool fused = w->w_qkv_packed && lc::skinny_fused_supported(M, ctx->cfg.d_model, ctx->cfg.vocab);
+  if (!fused) {
+    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV_PREP, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv_prep(sa, pa, s, ev); });
+    if (e != hipSuccess) return e;
+  }
   lc::GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
   ga.A = gw.A;
@@ -460,6 +463,10 @@ hipError_t run_qkv_gemm(lacache_ctx *ctx, const lacache_weights *w, const lacach
   ga.F = features(ctx);
   ga.H = ctx->cfg.n_heads;
   ga.Hkv = ctx->cfg.n_kv_heads;
+  if (fused)
+    return timed(ctx, LACACHE_KERNEL_QKV_GEMM, s, [&](const lc::LaunchEvents &ev) {
+      return lc::launch_qkv_skinny_fused(ctx->cfg.head_dim, sa, pa, ga, s, ev);
+    });
   return timed(ctx, LACACHE_KERNEL_QKV_GEMM, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv_gemm(ctx->cfg.head_dim, ga, s, ev); });
 }
 

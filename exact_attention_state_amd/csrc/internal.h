@@ -105,6 +105,12 @@ inline void lc_launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_qkv_prep(const SeqArgs &sa, const PrepArgs &a, hipStream_t s, const LaunchEvents &ev);
+// At most 64 tokens with the packed weight and an embedding table below 4 GB.
+bool skinny_fused_supported(int M, int D, int vocab);
+// At most 64 tokens with the packed weight: prep folded into the skinny GEMM
+// (p.M == a.M, p.D == a.D; p.A, p.map, p.cs unused).
+hipError_t launch_qkv_skinny_fused(int dh, const SeqArgs &sa, const PrepArgs &p, const GemmArgs &a, hipStream_t s,
+                                   const LaunchEvents &ev);
 hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const LaunchEvents &ev);
 size_t packed_qkv_weight_bytes(int D, int F);
 bool skinny_supported(int M, int D);      // the packed-weight projection for <= 64 tokens
