@@ -51,6 +51,7 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="time eager launches only")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--refresh-reps", type=int, default=8, help="timed refresh calls (0: skip the refresh timing)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device copy (3 times): the reference for FETCH_SIZE/WRITE_SIZE")
     return p.parse_args()
@@ -148,6 +149,59 @@ def step_accounting(wl):
         kern["qkv"] = dict(bytes=qkv_bytes, flops=2 * M * F * D)
     return dict(M=M, pairs_computed=pairs_c, pairs_equiv=pairs_e, kernels=kern,
                 qkv_bytes=qkv_bytes, attn_bytes=a_bytes + b_bytes)
+
+
+def refresh_accounting(wl):
+    """Work of one refresh (lacache_prefill_cache): the projection of every
+    row and full bidirectional attention per sample (4 d flops per
+    query-key pair), plus the FACache written for the invariant rows."""
+    D, H, Hk, d, F = wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.n_features
+    T = sum(n for (_, n, _, _) in wl.table())
+    pairs = sum(H * n * n for (_, n, _, _) in wl.table())
+    return {"rows": T, "attn_flops": 4 * d * pairs, "proj_flops": 2 * T * F * D, "pairs": pairs}
+
+
+def measure_refresh(ctx, sets, base, stream, dev, reps, acc, wl):
+    """Time lacache_prefill_cache (the block-boundary refresh) on the rotating
+    sets: whole calls with events on the launch stream, then the same calls
+    with every kernel bracketed by events (per-kernel averages)."""
+    import torch
+    from exact_attention_state_amd import lacache
+    ids_dev = base.upload_ids(base.ids_host)
+    ws = ctx.alloc_workspace(lacache.OP_PREFILL, base.table, dev)
+
+    def call(r):
+        s = sets[r % len(sets)]
+        ctx.prefill_cache(s.weights, ids_dev, base.table, s.ct, workspace=ws, stream=stream)
+
+    call(0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for r in range(reps):
+        evs[r][0].record(stream)
+        call(r + 1)
+        evs[r][1].record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    ctx.profile(True)
+    ctx.profile_read()
+    for r in range(reps):
+        call(r + 1)
+    torch.cuda.synchronize()
+    prof = ctx.profile_read()
+    ctx.profile(False)
+    kern = {k: v[0] * 1e3 / v[1] for k, v in prof.items() if v[1]}
+    ra = refresh_accounting(wl)
+    peak = (MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS) * 1e12
+    t_attn = kern.get("refresh_attn")
+    out = {"us_per_refresh": us[len(us) // 2], "us_per_refresh_min": us[0], "calls": reps,
+           "kernels_us_avg_per_call": {k: v * prof[k][1] / reps for k, v in kern.items()},
+           "attn_flops": ra["attn_flops"],
+           "attn_mfma_frac": None if not t_attn else ra["attn_flops"] / (t_attn * prof["refresh_attn"][1] / reps * 1e-6) / peak}
+    log(f"[bench] refresh: {out['us_per_refresh']:.1f} us per call; kernels per call "
+        + ", ".join(f"{k} {v:.1f} us" for k, v in out["kernels_us_avg_per_call"].items())
+        + (f"; attention at {out['attn_mfma_frac']:.3f} of MFMA peak" if out["attn_mfma_frac"] else ""))
+    return out
 
 
 def cpu_baseline(wl, budget_s):
@@ -323,12 +377,17 @@ def main():
             for k, v in prof.items() if v[1]}
     log(f"[bench] per-kernel: " + ", ".join(f"{k} {v['us_avg']:.2f} us" for k, v in kern.items()))
 
+    refresh = measure_refresh(ctx, sets, base, stream, dev, args.refresh_reps, acc, wl) if args.refresh_reps > 0 else None
+
     # Parity spot check of the last step against the oracle would need its
     # caches; the tests do that.  Here only a sanity check of finiteness.
     assert torch.isfinite(base.ct.out.float()).all()
 
     ms = ms_graph if ms_graph is not None else ms_eager
     steps_timed = graph_steps if ms_graph is not None else args.steps
+    if refresh is not None:
+        # One block: its refresh, then the workload's inner steps.
+        refresh["us_per_step_amortized"] = (refresh["us_per_refresh"] + wl.steps * ms * 1e3) / (wl.steps + 1)
     value = acc["pairs_computed"] / (ms * 1e-3)
 
     # Roofline of the dominant kernel.
@@ -383,6 +442,7 @@ def main():
                               for k, v in kern.items() if k in acc["kernels"] and acc["kernels"][k]["flops"]},
         "kernel_source_sha256": {k: kernel_source_hash(k) for k in kern},
         "roofline": roof,
+        "refresh": refresh,
         "cpu_baseline": cpu,
         "host": platform.node(),
         "graph_error": graph_err,

@@ -18,6 +18,9 @@ ARCH = os.environ.get("LACACHE_OFFLOAD_ARCH", "gfx950")
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: accumulators that VALU code also
+    # touches (the online-softmax rescale) are not moved through AGPRs.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-result",
 ]
 
@@ -26,17 +29,38 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose=False):
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
+    return r.returncode, r.stdout + r.stderr
+
+
+def build(verbose=False):
+    """Compiles each source to an object in parallel, then links the library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.basename(f)[:-4] + ".o") for f in srcs]
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    cmds = [[hipcc, *compile_flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", f, "-o", o]
+            for f, o in zip(srcs, objs)]
+    with ThreadPoolExecutor(max_workers=min(len(cmds), 4)) as ex:
+        results = list(ex.map(lambda c: _run(c, verbose), cmds))
+    log = "\n".join(out for _, out in results)
+    if any(rc != 0 for rc, _ in results):
+        sys.stderr.write(log)
         raise RuntimeError("hipcc failed building liblacache.so")
-    warn = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+    tmp = LIB + ".tmp"
+    rc, out = _run([hipcc, *HIPCC_FLAGS, *objs, "-o", tmp], verbose)
+    log += "\n" + out
+    if rc != 0:
+        sys.stderr.write(log)
+        raise RuntimeError("hipcc failed linking liblacache.so")
+    warn = "\n".join(l for l in log.splitlines() if "packed-fp32-ops" not in l)
     if verbose and warn.strip():
         print(warn)
     os.replace(tmp, LIB)

@@ -492,12 +492,15 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
   const lc::DType dt = dtype_of(ctx);
   const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads;
 
+  // bf16 contexts (16-bit caches) run the streaming refresh.
+  const bool streaming = dt == lc::kBF16;
+  const int rows_item = streaming ? lc::kRowsRS : lc::kRowsR;
   for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
     const int ns = std::min(kMaxInline, batch - s0);
     lc::SeqArgs sa = slice_args(seqs, s0, ns);
     for (int i = 0; i < ns; ++i) {
       sa.pre[0][i + 1] = sa.pre[0][i] + sa.len[i];
-      sa.pre[1][i + 1] = sa.pre[1][i] + (sa.len[i] + lc::kRowsR - 1) / lc::kRowsR;
+      sa.pre[1][i + 1] = sa.pre[1][i] + (sa.len[i] + rows_item - 1) / rows_item;
     }
     hipError_t e = hipSuccess;
     if (gemm) {
@@ -528,8 +531,10 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
     aa.H = H;
     aa.Hkv = ctx->cfg.n_kv_heads;
     aa.scale_log2 = scale_log2(ctx);
-    e = timed(ctx, LACACHE_KERNEL_REFRESH_ATTN, s,
-              [&](const lc::LaunchEvents &ev) { return lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev); });
+    e = timed(ctx, LACACHE_KERNEL_REFRESH_ATTN, s, [&](const lc::LaunchEvents &ev) {
+      return streaming ? lc::launch_refresh_stream(dh, sa, aa, sa.pre[1][ns] * H, s, ev)
+                    : lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
+    });
     if (e != hipSuccess) return hip_fail(ctx, "refresh attention launch", e);
   }
   return LACACHE_OK;

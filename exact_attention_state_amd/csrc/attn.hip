@@ -319,8 +319,14 @@ __device__ __forceinline__ void softmax_pv(AttnState<MB, DH> &st, const f32x4_t 
       frag_set(pf[mb], j, p);
     }
     st.l[mb] = fmaf(st.l[mb], alpha, ps);
+    // Once the running maxima stop moving, alpha is exactly 1 in every lane
+    // and the rescale (a multiply per accumulator, plus moving accumulators
+    // held in AGPRs through VGPRs) is skipped; multiplying by 1 is exact, so
+    // the result does not depend on the branch.
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-    for (int db = 0; db < DH / 16; ++db) st.o[mb][db] *= alpha;
+      for (int db = 0; db < DH / 16; ++db) st.o[mb][db] *= alpha;
+    }
   }
 #pragma unroll
   for (int db = 0; db < DH / 16; ++db) {
@@ -1182,6 +1188,171 @@ __global__ __launch_bounds__(256) void refresh_attn_kernel(const SeqArgs sa, con
 }
 
 // ---------------------------------------------------------------------------
+// Refresh, streaming (16-bit caches): one workgroup of 4 waves per (sample,
+// head, 64 * MB rows); wave w owns MB row blocks (rows 16 MB w ..) and takes
+// every key, so each K or V fragment read from LDS feeds MB matrix products.
+// K and V of 64-key tiles arrive row-wise (the load unit's full-rate
+// pattern) through an NST-stage ring, as in block_rows_stream_kernel.  Key
+// order: the invariant keys [0, bs) and [be, N), then the block's [bs, be)
+// (each segment in its own tiles, the last one ragged); the state after the
+// last invariant tile is the FACache snapshot of the invariant rows
+// (LaCache Section 3.3.3: the cache holds the online-softmax state over the
+// invariant keys only).
+// ---------------------------------------------------------------------------
+template <int DH, int NST_> struct StreamR {
+  static constexpr int ROWB = DH * 2, PPR = ROWB / 16, RPC = 1024 / ROWB;
+  static constexpr int TK = 64;                                 // keys per tile
+  static constexpr int KT = TK * ROWB;                          // bytes of a K (or V) tile
+  static constexpr int STAGE = 2 * KT;
+  static constexpr int NST = NST_;
+  static constexpr int BYTES = NST * STAGE;
+  static constexpr int CPW = STAGE / 1024 / 4;                  // copies per wave per tile
+};
+
+template <typename TO, int DH, int MB, int NST>
+__global__ __launch_bounds__(256) void refresh_stream_kernel(const SeqArgs sa, const AttnArgs a) {
+  using T = f16_t;
+  using S = StreamR<DH, NST>;
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int item = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int b = find_sample(sa.pre[1], sa.n, item);
+  const int tile = item - sa.pre[1][b];
+  const int bs = sa.bs[b], be = sa.be[b], N = sa.len[b], off = sa.off[b];
+  const int hk = h / (a.H / a.Hkv);
+  const size_t kvstride = (size_t)a.Hkv * DH;
+  const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  const T *kb = static_cast<const T *>(a.k) + (size_t)off * kvstride + hk * DH;
+  const T *vb = static_cast<const T *>(a.v) + (size_t)off * kvstride + hk * DH;
+  const int rr = lane / S::PPR, slot = lane % S::PPR;             // row-wise lane: row rr (+ RPC q), slot
+
+  // Tiles of the three key segments; tile tt covers keys k0 .. k0 + nk - 1.
+  const int nt0 = (bs + S::TK - 1) / S::TK, nt1 = (N - be + S::TK - 1) / S::TK;
+  const int ntU = nt0 + nt1, ntiles = ntU + (be - bs + S::TK - 1) / S::TK;
+  // (Values selected, not references: a choice between references to the
+  // bounds would be compiled as pointers into scratch memory.)
+  auto tile_keys = [=](int tt, int &k0, int &nk) {
+    const int seg_base = tt < nt0 ? 0 : (tt < ntU ? be : bs);
+    const int seg_end = tt < nt0 ? bs : (tt < ntU ? N : be);
+    const int seg_t0 = tt < nt0 ? 0 : (tt < ntU ? nt0 : ntU);
+    k0 = seg_base + (tt - seg_t0) * S::TK;
+    nk = min(S::TK, seg_end - k0);
+  };
+  // Tile tt into stage tt % NST: wave w does copies q = w, w+4, .. of the
+  // tile's K then V rows (keys past the tile repeat its last key).
+  auto issue = [&](int tt) {
+    int k0, nk;
+    tile_keys(tt, k0, nk);
+    const uint32_t st = lbase + (tt % S::NST) * S::STAGE;
+#pragma unroll
+    for (int j = 0; j < S::CPW / 2; ++j) {
+      const int q = j * 4 + w;
+      const int c = q * S::RPC + rr;
+      const size_t key = (size_t)(k0 + min(c, nk - 1)) * kvstride;
+      dma16(kb + key + ((slot ^ kslot(c, S::PPR)) << 3), st + q * 1024);
+      dma16(vb + key + ((slot ^ (c & 3)) << 3), st + S::KT + q * 1024);
+    }
+  };
+
+  // This wave's query rows (rows past the sample repeat its last row; their
+  // results are dropped).
+  const T *qrow[MB];
+  int trow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    trow[mb] = tile * (64 * MB) + (w * MB + mb) * 16 + r16;
+    qrow[mb] = static_cast<const T *>(a.q) + ((size_t)(off + min(trow[mb], N - 1)) * a.H + h) * DH;
+  }
+  Frag<T> qf[MB][DH / 32];
+  load_q<T, MB, DH>(qf, qrow, g);
+  // All stages start filling; the queries and tile 0 are waited for.
+#pragma unroll
+  for (int j = 0; j < S::NST; ++j)
+    if (j < ntiles) issue(j);
+  {
+    const int behind = min(S::NST - 1, ntiles - 1);
+    if (S::NST > 3 && behind == 3) vmcnt_wait<3 * S::CPW>();
+    else if (S::NST > 2 && behind == 2) vmcnt_wait<2 * S::CPW>();
+    else if (S::NST > 1 && behind == 1) vmcnt_wait<S::CPW>();
+    else vmcnt_wait<0>();
+  }
+  lds_barrier();
+
+  AttnState<MB, DH> st;
+  state_init_empty(st);
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const char *stg = smem + (tt % S::NST) * S::STAGE;
+    int k0, nk;
+    tile_keys(tt, k0, nk);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int nv = min(32, nk - 32 * ks);
+      if (nv <= 0) continue;
+      // S^T = K Q^T over keys 32 ks ..: A row r16 of key block kb is key
+      // 32 ks + 8 (r16 >> 2) + 4 kb + (r16 & 3) of the tile.
+      f32x4_t sc[2][MB];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) sc[kb2][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int c = 32 * ks + 8 * (r16 >> 2) + 4 * kb2 + (r16 & 3);
+#pragma unroll
+        for (int kd = 0; kd < DH / 32; ++kd) {
+          const int e0 = 64 * (kd >> 1) + 16 * g + 8 * (kd & 1);
+          Frag<T> kfr;
+          frag_load(kfr, reinterpret_cast<const T *>(stg + c * S::ROWB + (((e0 >> 3) ^ kslot(c, S::PPR)) << 4)));
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) mma16(sc[kb2][mb], kfr, qf[mb][kd]);
+        }
+      }
+      softmax_pv<T, MB, DH, S::TK>(st, sc, nv, reinterpret_cast<const T *>(stg + S::KT), 32 * ks, a.scale_log2,
+                                   lane);
+    }
+    if (tt == ntU - 1) {
+      // FACache snapshot of the invariant rows: (m, l, O~/l) over the
+      // invariant keys.  Its stores join the copies in flight; vector memory
+      // operations complete in issue order, so the waits below (which count
+      // copies only) wait at most a little longer, once.
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int t = trow[mb];
+        const size_t crow = (size_t)(off + min(t, N - 1)) * a.H + h;
+        const float ls = group_sum(st.l[mb]);
+        if (t < N && (t < bs || t >= be)) {
+          if (g == 0) {
+            a.m_w[crow] = st.m[mb] * kLn2;
+            a.l_w[crow] = ls;
+          }
+          store_row<T, DH>(static_cast<T *>(a.o_w) + crow * DH, st.o[mb], 1.0f / ls, g);
+        }
+      }
+    }
+    if (tt + 1 < ntiles) {
+      // This wave's copies of tile tt+1 landed (later tiles may not have);
+      // the barrier publishes it and frees stage tt for tile tt+NST.
+      const int behind = min(S::NST - 2, ntiles - 2 - tt);
+      if (S::NST > 3 && behind == 2) vmcnt_wait<2 * S::CPW>();
+      else if (S::NST > 2 && behind == 1) vmcnt_wait<S::CPW>();
+      else vmcnt_wait<0>();
+      lds_barrier();
+      if (tt + S::NST < ntiles) issue(tt + S::NST);
+    }
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int t = trow[mb];
+    const size_t crow = (size_t)(off + min(t, N - 1)) * a.H + h;
+    const float lt = group_sum(st.l[mb]);
+    if (t < N) {
+      store_row<TO, DH>(static_cast<TO *>(a.out) + crow * DH, st.o[mb], 1.0f / lt, g);
+      if (a.lse && g == 0) a.lse[crow] = (st.m[mb] + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 // type A: query rows + key tile, then the state merge
@@ -1338,6 +1509,20 @@ hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, 
   return hipGetLastError();
 }
 
+hipError_t launch_refresh_stream(int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
+                                 const LaunchEvents &ev) {
+  if (n_blocks <= 0) return hipSuccess;
+  if (dh == 128)
+    lc_launch(refresh_stream_kernel<bf16_t, 128, kRefreshMB, 2>, dim3(n_blocks), dim3(256), StreamR<128, 2>::BYTES, s, ev,
+              sa, a);
+  else if (dh == 64)
+    lc_launch(refresh_stream_kernel<bf16_t, 64, kRefreshMB, 2>, dim3(n_blocks), dim3(256), StreamR<64, 2>::BYTES, s, ev,
+              sa, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                                hipStream_t s, const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
@@ -1377,6 +1562,8 @@ hipError_t setup_kernel_attributes() {
   LC_ATTR((refresh_attn_kernel<f16_t, bf16_t, 64>), (refresh_smem<f16_t, 64>()));
   LC_ATTR((refresh_attn_kernel<float, float, 128>), (refresh_smem<float, 128>()));
   LC_ATTR((refresh_attn_kernel<float, float, 64>), (refresh_smem<float, 64>()));
+  LC_ATTR((refresh_stream_kernel<bf16_t, 128, kRefreshMB, 2>), (StreamR<128, 2>::BYTES));
+  LC_ATTR((refresh_stream_kernel<bf16_t, 64, kRefreshMB, 2>), (StreamR<64, 2>::BYTES));
   LC_ATTR((block_rows_stream_kernel<bf16_t, 128, 4>), (StreamA<128, 4>::BYTES));
   LC_ATTR((block_rows_stream_kernel<bf16_t, 64, 4>), (StreamA<64, 4>::BYTES));
   LC_ATTR((block_rows_stream_kernel<bf16_t, 128, 2>), (StreamA<128, 2>::BYTES));
