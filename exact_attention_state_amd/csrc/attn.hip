@@ -292,7 +292,11 @@ __device__ __forceinline__ void load_k_step(KStep<T, DH> &kf, const T *kbase, si
 // Online-softmax update and P*V of one step of up to 32 keys, from its
 // scores S^T (s[kb][mb]: key block kb, row block mb).  V of the step is keys
 // c0 .. c0+31 of the staged tile `vbuf`.  Keys >= nvalid are masked; their
-// staged V must be finite (the stager copies a valid key).
+// staged V must be finite (the stager copies a valid key).  The scale
+// (> 0, log2 units) enters through the exponent's fma: the row max is taken
+// on raw scores (max(c s) = c max(s) for c > 0, bit for bit, as rounding is
+// monotone), and p = 2^(c s - m) is one fused operation.  Steps with all 32
+// keys valid skip the masking.
 template <typename T, int MB, int DH, int MAXC>
 __device__ __forceinline__ void softmax_pv(AttnState<MB, DH> &st, const f32x4_t (&s)[2][MB], int nvalid,
                                            const T *vbuf, int c0, float scale_log2, int lane) {
@@ -301,20 +305,22 @@ __device__ __forceinline__ void softmax_pv(AttnState<MB, DH> &st, const f32x4_t 
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     float x[8];
-    float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      x[j] = (8 * g + j < nvalid) ? s[j >> 2][mb][j & 3] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, x[j]);
+    for (int j = 0; j < 8; ++j) x[j] = s[j >> 2][mb][j & 3];
+    if (nvalid < 32) {                          // wave-uniform
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (8 * g + j >= nvalid) x[j] = -INFINITY;
     }
-    mx = group_max(mx);
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = group_max(mx) * scale_log2;
     const float mnew = fmaxf(st.m[mb], mx);
     const float alpha = fast_exp2(st.m[mb] - mnew);
     st.m[mb] = mnew;
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = fast_exp2(x[j] - mnew);
+      const float p = fast_exp2(fmaf(x[j], scale_log2, -mnew));   // masked: 2^-inf = 0
       ps += p;
       frag_set(pf[mb], j, p);
     }
@@ -334,6 +340,59 @@ __device__ __forceinline__ void softmax_pv(AttnState<MB, DH> &st, const f32x4_t 
     vtile_frag<T, DH, MAXC>(vf, vbuf, c0, db, lane);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) mma16(st.o[mb][db], vf, pf[mb]);
+  }
+}
+
+// The same update over one 64-key tile at once (two 32-key halves: sc[h]
+// are the S^T blocks of keys 32h ..; nvalid in [1, 64]): one row max, one
+// rescale and one normaliser update per tile, and the P*V products of both
+// halves.  V of the tile is keys 0 .. 63 of `vbuf`.
+template <typename T, int MB, int DH, int MAXC>
+__device__ __forceinline__ void softmax_pv64(AttnState<MB, DH> &st, const f32x4_t (&sc)[2][2][MB], int nvalid,
+                                             const T *vbuf, float scale_log2, int lane) {
+  const int g = lane >> 4;
+  Frag<T> pf[2][MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = sc[j >> 3][(j >> 2) & 1][mb][j & 3];
+    if (nvalid < 64) {                          // wave-uniform
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (32 * (j >> 3) + 8 * g + (j & 7) >= nvalid) x[j] = -INFINITY;
+    }
+    float m8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m8[j] = fmaxf(x[j], x[j + 8]);
+    float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])), fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+    mx = group_max(mx) * scale_log2;
+    const float mnew = fmaxf(st.m[mb], mx);
+    const float alpha = fast_exp2(st.m[mb] - mnew);
+    st.m[mb] = mnew;
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float p = fast_exp2(fmaf(x[j], scale_log2, -mnew));   // masked: 2^-inf = 0
+      ps += p;
+      frag_set(pf[j >> 3][mb], j & 7, p);
+    }
+    st.l[mb] = fmaf(st.l[mb], alpha, ps);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < DH / 16; ++db) st.o[mb][db] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (32 * h >= nvalid) break;                // wave-uniform: the second half holds no key
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db) {
+      Frag<T> vf;
+      vtile_frag<T, DH, MAXC>(vf, vbuf, 32 * h, db, lane);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) mma16(st.o[mb][db], vf, pf[h][mb]);
+    }
   }
 }
 
@@ -1285,17 +1344,17 @@ __global__ __launch_bounds__(256) void refresh_stream_kernel(const SeqArgs sa, c
     const char *stg = smem + (tt % S::NST) * S::STAGE;
     int k0, nk;
     tile_keys(tt, k0, nk);
+    // S^T = K Q^T over the tile's 64 keys (both halves before the softmax:
+    // eight independent accumulation chains): A row r16 of key block kb of
+    // half ks is key 32 ks + 8 (r16 >> 2) + 4 kb + (r16 & 3) of the tile
+    // (keys past nk are copies of its last key, masked in the softmax).
+    f32x4_t sc[2][2][MB];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int nv = min(32, nk - 32 * ks);
-      if (nv <= 0) continue;
-      // S^T = K Q^T over keys 32 ks ..: A row r16 of key block kb is key
-      // 32 ks + 8 (r16 >> 2) + 4 kb + (r16 & 3) of the tile.
-      f32x4_t sc[2][MB];
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) sc[kb2][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mb = 0; mb < MB; ++mb) sc[ks][kb2][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const int c = 32 * ks + 8 * (r16 >> 2) + 4 * kb2 + (r16 & 3);
 #pragma unroll
         for (int kd = 0; kd < DH / 32; ++kd) {
@@ -1303,12 +1362,10 @@ __global__ __launch_bounds__(256) void refresh_stream_kernel(const SeqArgs sa, c
           Frag<T> kfr;
           frag_load(kfr, reinterpret_cast<const T *>(stg + c * S::ROWB + (((e0 >> 3) ^ kslot(c, S::PPR)) << 4)));
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) mma16(sc[kb2][mb], kfr, qf[mb][kd]);
+          for (int mb = 0; mb < MB; ++mb) mma16(sc[ks][kb2][mb], kfr, qf[mb][kd]);
         }
       }
-      softmax_pv<T, MB, DH, S::TK>(st, sc, nv, reinterpret_cast<const T *>(stg + S::KT), 32 * ks, a.scale_log2,
-                                   lane);
-    }
+    softmax_pv64<T, MB, DH, S::TK>(st, sc, nk, reinterpret_cast<const T *>(stg + S::KT), a.scale_log2, lane);
     if (tt == ntU - 1) {
       // FACache snapshot of the invariant rows: (m, l, O~/l) over the
       // invariant keys.  Its stores join the copies in flight; vector memory
