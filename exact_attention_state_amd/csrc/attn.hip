@@ -225,6 +225,31 @@ __device__ __forceinline__ void vtile_stage(T *buf, const T *vbase, size_t vstri
   }
 }
 
+// K of up to MAXC keys staged in LDS (16-bit types), key rows of DH
+// elements: key c's 16-byte piece p sits in slot p ^ kslot(c) (ppr pieces
+// per row), so the 16 keys of one A-operand read (8a + b + 4kb, a, b < 4)
+// hit distinct slots.  Copied global -> LDS by the load unit, row-wise;
+// keys >= nvalid (>= 1) get a copy of key nvalid-1.
+__device__ __forceinline__ int kslot(int c, int ppr) {
+  return ppr == 16 ? (((c >> 1) & 12) | (c & 3)) : (((c >> 1) & 4) | (c & 3));
+}
+template <typename T, int DH, int MAXC, int NTHR>
+__device__ __forceinline__ void ktile_stage(T *buf, const T *kbase, size_t kstride, int nvalid, int t) {
+  static_assert(sizeof(T) == 2, "16-bit K tiles");
+  constexpr int CPK = DH / 8;                    // 16-byte pieces per key row
+  static_assert((MAXC * CPK) % NTHR == 0, "staging threads must tile the buffer");
+  constexpr int ITER = MAXC * CPK / NTHR;
+  const int lane = t & 63, w = t >> 6;
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int base = (it * (NTHR / 64) + w) * 64;        // first LDS slot of this wave's instruction
+    const int idx = base + lane;
+    const int c = idx / CPK, slot = idx % CPK;
+    const T *src = kbase + (size_t)min(c, nvalid - 1) * kstride + ((slot ^ kslot(c, CPK)) << 3);
+    load_lds16(src, buf + (size_t)base * 8);
+  }
+}
+
 // Completes this wave's global->LDS copies (and every other global load it
 // has in flight); a barrier must follow before other waves read the tile.
 __device__ __forceinline__ void vtile_wait() {
@@ -286,6 +311,22 @@ __device__ __forceinline__ void load_k_step(KStep<T, DH> &kf, const T *kbase, si
 #pragma unroll
     for (int p = 0; p < DH / 64; ++p)
       frag_load2(kf.f[kb][2 * p], kf.f[kb][2 * p + 1], kbase + (size_t)key * kstride + 64 * p + 16 * g);
+  }
+}
+
+// The same fragments from a K tile staged in LDS (ktile_stage), keys c0 ..
+// c0+31 of the tile (keys past the valid ones are copies: masked later).
+template <typename T, int DH>
+__device__ __forceinline__ void load_k_step_lds(KStep<T, DH> &kf, const T *kbuf, int c0, int lane) {
+  const int g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int c = c0 + 8 * (r16 >> 2) + 4 * kb + (r16 & 3);
+#pragma unroll
+    for (int kd = 0; kd < DH / 32; ++kd) {
+      const int e0 = 64 * (kd >> 1) + 16 * g + 8 * (kd & 1);
+      frag_load(kf.f[kb][kd], kbuf + (size_t)c * DH + (((e0 >> 3) ^ kslot(c, DH / 8)) << 3));
+    }
   }
 }
 
@@ -488,8 +529,10 @@ __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int ite
   // row; their results are dropped); each wave reads the fragments of one
   // head-dim step at a time.
   using QT = QTile<T, DH>;
+  constexpr bool kLdsK = sizeof(T) == 2;     // 16-bit caches: K staged row-wise in LDS too
   T *qbuf = reinterpret_cast<T *>(smem);
   T *vbuf = qbuf + kRowsA * DH;
+  T *kbuf = vbuf + VTile<T, DH, kTileA>::kBytes / sizeof(T);
   {
     const int qrow0 = a.qmode == 0 ? sa.off[b] + sa.bs[b] : a.row_base + sa.pre[0][b];
 #pragma unroll
@@ -514,11 +557,14 @@ __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int ite
     const int nv = max(0, min(32, nk - c0));
     // A step past the tile's end reads the tile's first keys (and is skipped).
     KStep<T, DH> kf;
-    load_k_step<T, DH>(kf, kbase0 + (size_t)(t0 + (nv > 0 ? c0 : 0)) * kvstride, kvstride, max(nv, 1), lane);
-    if (t0 > 0) lds_barrier();                 // the previous tile's V reads are done
+    if constexpr (!kLdsK)
+      load_k_step<T, DH>(kf, kbase0 + (size_t)(t0 + (nv > 0 ? c0 : 0)) * kvstride, kvstride, max(nv, 1), lane);
+    if (t0 > 0) lds_barrier();                 // the previous tile's K and V reads are done
+    if constexpr (kLdsK) ktile_stage<T, DH, kTileA, 256>(kbuf, kbase0 + (size_t)t0 * kvstride, kvstride, nk, tid);
     vtile_stage<T, DH, kTileA, 256>(vbuf, vbase0 + (size_t)t0 * kvstride, kvstride, nk, tid);
     vtile_wait();
     lds_barrier();
+    if constexpr (kLdsK) load_k_step_lds<T, DH>(kf, kbuf, nv > 0 ? c0 : 0, lane);
     if (nv > 0) {
       f32x4_t sc[2][MB];
 #pragma unroll
@@ -636,10 +682,15 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
     load_row<T, DH>(oc[mb], static_cast<const T *>(a.o_c) + crow[mb] * DH, g);
   }
   const T *kbase = static_cast<const T *>(a.k) + (size_t)(off + bs) * kvstride + hk * DH;
+  // 16-bit caches: the block's K is staged row-wise in LDS once per
+  // workgroup (one copy instead of one fragment load per wave).
+  constexpr bool kLds = sizeof(T) == 2;
   KStep<T, DH> kf[2];
-  load_k_step<T, DH>(kf[0], kbase, kvstride, min(32, B), lane);
-
   T *vbuf = reinterpret_cast<T *>(smem);
+  T *kbuf = vbuf + VTile<T, DH, BMAX>::kBytes / sizeof(T);
+  if constexpr (kLds) ktile_stage<T, DH, BMAX, 256>(kbuf, kbase, kvstride, B, tid);
+  else load_k_step<T, DH>(kf[0], kbase, kvstride, min(32, B), lane);
+
   vtile_stage<T, DH, BMAX, 256>(vbuf, static_cast<const T *>(a.v) + (size_t)(off + bs) * kvstride + hk * DH, kvstride,
                                 B, tid);
   vtile_wait();
@@ -654,6 +705,12 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
     for (int db = 0; db < NDB; ++db) st.o[mb][db] = oc[mb][db] * lc[mb];
   }
 
+  if constexpr (kLds) {
+    for (int c0 = 0; c0 < B; c0 += 32) {
+      load_k_step_lds<T, DH>(kf[0], kbuf, c0, lane);
+      attend_step_pre<T, MB, DH, BMAX>(st, qf, kf[0], min(32, B - c0), vbuf, c0, a.scale_log2, lane);
+    }
+  } else
   // Up to 4 steps (block <= 128 keys); the next step's keys load during this one.
   for (int c0 = 0; c0 < B; c0 += 64) {
     if (c0 + 32 < B) load_k_step<T, DH>(kf[1], kbase + (size_t)(c0 + 32) * kvstride, kvstride, min(32, B - c0 - 32), lane);
@@ -905,9 +962,6 @@ template <int DH, int NST_> struct StreamA {
   static constexpr int BYTES = QB + NST * STAGE;
   static constexpr int CPW = STAGE / 1024 / 4;                  // copies per wave per tile
 };
-__device__ __forceinline__ int kslot(int c, int ppr) {
-  return ppr == 16 ? (((c >> 1) & 12) | (c & 3)) : (((c >> 1) & 4) | (c & 3));
-}
 
 template <typename TO, int DH, int NST>
 __global__ __launch_bounds__(256) void block_rows_stream_kernel(const SeqArgs sa, const AttnArgs a) {
@@ -1414,13 +1468,15 @@ __global__ __launch_bounds__(256) void refresh_stream_kernel(const SeqArgs sa, c
 // ---------------------------------------------------------------------------
 // type A: query rows + key tile, then the state merge
 template <typename T, int DH> constexpr size_t block_rows_smem() {
-  constexpr size_t tile_a = (size_t)kRowsA * DH * sizeof(T) + VTile<T, DH, kTileA>::kBytes;
+  constexpr size_t tile_a = (size_t)kRowsA * DH * sizeof(T) + VTile<T, DH, kTileA>::kBytes +
+                            (sizeof(T) == 2 ? (size_t)kTileA * DH * sizeof(T) : 0);
   constexpr size_t merge_a = merge_a_bytes<DH>();
   return tile_a > merge_a ? tile_a : merge_a;
 }
 // type B: the block's keys
+// type B: the block's V (and, 16-bit, its K)
 template <typename T, int DH, int BMAX> constexpr size_t invariant_rows_smem() {
-  return VTile<T, DH, BMAX>::kBytes;
+  return VTile<T, DH, BMAX>::kBytes + (sizeof(T) == 2 ? (size_t)BMAX * DH * sizeof(T) : 0);
 }
 template <typename T, int DH> constexpr size_t refresh_smem() {
   return VTile<T, DH, 128>::kBytes;
