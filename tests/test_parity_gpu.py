@@ -96,6 +96,19 @@ def test_small_bf16_ragged_batch(packed):
     _run_full(wl, 3, packed=packed)
 
 
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_refresh_segment_edges(head_dim):
+    # The refresh streams the invariant keys in two segments, then the block's
+    # keys, each segment in 64-key tiles: a block at position 0 (empty first
+    # segment), blocks at the very end (empty second segment), a 40-key block
+    # (ragged block tile), and a sample spanning four 128-row items (420 rows);
+    # grouped KV heads.  Every row and every FACache pair is compared.
+    wl = synth.custom(f"refresh_edges_h{head_dim}", dtype="bf16", d_model=512, n_heads=4, n_kv_heads=2,
+                      head_dim=head_dim, vocab=1200, prompt_lens=(0, 130, 61, 300), gen_len=120, block_size=40,
+                      block_idx=(0, 2, 2, 1), steps=1, seed=51)
+    _run_full(wl, 1)
+
+
 def test_small_fp32_head64_multi_tile():
     wl = synth.custom("small_fp32_h64", dtype="f32", d_model=256, n_heads=4, head_dim=64, vocab=700,
                       prompt_lens=(300, 77), gen_len=96, block_size=32, block_idx=(1, 2), steps=2,
