@@ -531,9 +531,26 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
     aa.H = H;
     aa.Hkv = ctx->cfg.n_kv_heads;
     aa.scale_log2 = scale_log2(ctx);
+    // Every refresh item of a sample streams all of its keys: the streaming
+    // launch takes the samples longest first (workgroups start in order), so
+    // no long item starts last.  Items write their own sample's rows only.
+    lc::SeqArgs sr = sa;
+    if (streaming) {
+      int idx[kMaxInline];
+      for (int i = 0; i < ns; ++i) idx[i] = i;
+      std::stable_sort(idx, idx + ns, [&](int x, int y) { return sa.len[x] > sa.len[y]; });
+      for (int i = 0; i < ns; ++i) {
+        const int j = idx[i];
+        sr.off[i] = sa.off[j];
+        sr.len[i] = sa.len[j];
+        sr.bs[i] = sa.bs[j];
+        sr.be[i] = sa.be[j];
+        sr.pre[1][i + 1] = sr.pre[1][i] + (sa.pre[1][j + 1] - sa.pre[1][j]);
+      }
+    }
     e = timed(ctx, LACACHE_KERNEL_REFRESH_ATTN, s, [&](const lc::LaunchEvents &ev) {
-      return streaming ? lc::launch_refresh_stream(dh, sa, aa, sa.pre[1][ns] * H, s, ev)
-                    : lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
+      return streaming ? lc::launch_refresh_stream(dh, sr, aa, sr.pre[1][ns] * H, s, ev)
+                       : lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
     });
     if (e != hipSuccess) return hip_fail(ctx, "refresh attention launch", e);
   }
@@ -688,8 +705,26 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
       part_base += sa.pre[3][ns];
       continue;
     }
+    // Whole-sequence items cost in proportion to their sample's length: the
+    // launch takes them longest first (the dispatcher starts workgroups in
+    // order), so no long item starts last.  Each item writes its sample's
+    // own rows, so the order does not change the results.
+    lc::SeqArgs sb = sa;
+    if (direct) {
+      int idx[kMaxInline];
+      for (int i = 0; i < ns; ++i) idx[i] = i;
+      std::stable_sort(idx, idx + ns, [&](int x, int y) { return sa.len[x] > sa.len[y]; });
+      for (int i = 0; i < ns; ++i) {
+        const int j = idx[i];
+        sb.off[i] = sa.off[j];
+        sb.len[i] = sa.len[j];
+        sb.bs[i] = sa.bs[j];
+        sb.be[i] = sa.be[j];
+        sb.pre[1][i + 1] = sb.pre[1][i] + (sa.pre[1][j + 1] - sa.pre[1][j]);
+      }
+    }
     e = timed(ctx, LACACHE_KERNEL_BLOCK_ROWS, s, [&](const lc::LaunchEvents &ev) {
-      return lc::launch_block_rows(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
+      return lc::launch_block_rows(dt, dh, sb, aa, sb.pre[1][ns] * H, s, ev);
     });
     if (e != hipSuccess) return hip_fail(ctx, "block-step block-rows launch", e);
     if (seg_rows) {
