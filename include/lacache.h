@@ -160,7 +160,11 @@ typedef enum {
 /* Creates a context on the current HIP device: validates the configuration,
  * builds the RoPE cos/sin table (computed in double on the host, stored as
  * fp32 [max_seq_len, head_dim/2] pairs) and a device status word.  The
- * context must be used on that device only.  *out is NULL on failure. */
+ * context must be used on that device only.  *out is NULL on failure.
+ * Diagnostics: the environment variable LACACHE_SPLIT_KEYS (a multiple of
+ * 32), read here, fixes the key chunk of the block rows' split-KV partials
+ * for the context's lifetime instead of the per-call choice; results stay
+ * within the parity tolerances, not bit-identical. */
 LACACHE_API lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out);
 
 /* Frees the context's device memory (synchronises the device first).
