@@ -472,6 +472,31 @@ hipError_t run_qkv_gemm(lacache_ctx *ctx, const lacache_weights *w, const lacach
 
 }  // namespace
 
+namespace {
+// The launch's samples reordered longest first, every prefix array rebuilt
+// from the samples' own counts in the new order.  A launch whose items cost
+// in proportion to their sample's length finishes sooner when the long ones
+// start first (the dispatcher starts workgroups in index order).  Only for
+// launches that address rows through each sample's seq_offset and block
+// (qmode = omode = 0): pre[0] then no longer follows the caller's sample
+// order of q_block / out_block.
+lc::SeqArgs longest_first(const lc::SeqArgs &sa) {
+  int idx[kMaxInline];
+  for (int i = 0; i < sa.n; ++i) idx[i] = i;
+  std::stable_sort(idx, idx + sa.n, [&](int x, int y) { return sa.len[x] > sa.len[y]; });
+  lc::SeqArgs r = sa;
+  for (int i = 0; i < sa.n; ++i) {
+    const int j = idx[i];
+    r.off[i] = sa.off[j];
+    r.len[i] = sa.len[j];
+    r.bs[i] = sa.bs[j];
+    r.be[i] = sa.be[j];
+    for (int k = 0; k < 4; ++k) r.pre[k][i + 1] = r.pre[k][i] + (sa.pre[k][j + 1] - sa.pre[k][j]);
+  }
+  return r;
+}
+}  // namespace
+
 lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w, const int32_t *ids,
                                      const lacache_seq *seqs, int32_t batch, const lacache_cache *cache, void *out,
                                      float *lse, void *workspace, size_t workspace_bytes, void *stream) {
@@ -532,22 +557,8 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
     aa.Hkv = ctx->cfg.n_kv_heads;
     aa.scale_log2 = scale_log2(ctx);
     // Every refresh item of a sample streams all of its keys: the streaming
-    // launch takes the samples longest first (workgroups start in order), so
-    // no long item starts last.  Items write their own sample's rows only.
-    lc::SeqArgs sr = sa;
-    if (streaming) {
-      int idx[kMaxInline];
-      for (int i = 0; i < ns; ++i) idx[i] = i;
-      std::stable_sort(idx, idx + ns, [&](int x, int y) { return sa.len[x] > sa.len[y]; });
-      for (int i = 0; i < ns; ++i) {
-        const int j = idx[i];
-        sr.off[i] = sa.off[j];
-        sr.len[i] = sa.len[j];
-        sr.bs[i] = sa.bs[j];
-        sr.be[i] = sa.be[j];
-        sr.pre[1][i + 1] = sr.pre[1][i] + (sa.pre[1][j + 1] - sa.pre[1][j]);
-      }
-    }
+    // launch takes the samples longest first.
+    const lc::SeqArgs sr = streaming ? longest_first(sa) : sa;
     e = timed(ctx, LACACHE_KERNEL_REFRESH_ATTN, s, [&](const lc::LaunchEvents &ev) {
       return streaming ? lc::launch_refresh_stream(dh, sr, aa, sr.pre[1][ns] * H, s, ev)
                        : lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
@@ -706,23 +717,9 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
       continue;
     }
     // Whole-sequence items cost in proportion to their sample's length: the
-    // launch takes them longest first (the dispatcher starts workgroups in
-    // order), so no long item starts last.  Each item writes its sample's
-    // own rows, so the order does not change the results.
-    lc::SeqArgs sb = sa;
-    if (direct) {
-      int idx[kMaxInline];
-      for (int i = 0; i < ns; ++i) idx[i] = i;
-      std::stable_sort(idx, idx + ns, [&](int x, int y) { return sa.len[x] > sa.len[y]; });
-      for (int i = 0; i < ns; ++i) {
-        const int j = idx[i];
-        sb.off[i] = sa.off[j];
-        sb.len[i] = sa.len[j];
-        sb.bs[i] = sa.bs[j];
-        sb.be[i] = sa.be[j];
-        sb.pre[1][i + 1] = sb.pre[1][i] + (sa.pre[1][j + 1] - sa.pre[1][j]);
-      }
-    }
+    // launch takes them longest first (it writes O and LSE at each sample's
+    // own rows, qmode = omode = 0).
+    const lc::SeqArgs sb = direct ? longest_first(sa) : sa;
     e = timed(ctx, LACACHE_KERNEL_BLOCK_ROWS, s, [&](const lc::LaunchEvents &ev) {
       return lc::launch_block_rows(dt, dh, sb, aa, sb.pre[1][ns] * H, s, ev);
     });
