@@ -10,13 +10,16 @@
 //   O^T += V^T P^T    A = V^T read from LDS, B = P^T straight from the
 //                     softmax registers; the result keeps each query row in
 //                     one lane, so the per-row rescale is lane-local.
-// K fragments are read straight from HBM; only V goes through LDS.  Every
-// work item issues all of its global loads before its first wait, and its
-// workgroup barriers order LDS traffic only, so one item costs one memory
-// round trip per key tile.
+// With 16-bit caches K and V tiles go through LDS, copied row-wise by the
+// load unit (its full-rate access pattern); with fp32 caches K fragments are
+// read straight from memory and only V is staged.  Every work item issues
+// all of its global loads before its first wait, and its workgroup barriers
+// order LDS traffic only, so one item costs one memory round trip per key
+// tile.  The streaming kernels further down (block rows, invariant rows,
+// refresh) instead keep a ring of tiles in flight.
 //
-// Work items (one workgroup of 4 waves each, times the head count); the
-// block step runs type A, then type B together with the merge:
+// Work items of the one-tile kernels (one workgroup of 4 waves each, times
+// the head count):
 //   type A  block rows (<= 32) of one sample against one chunk of its keys
 //           [prefix | fresh block | suffix]; wave w takes the w-th 32-key step
 //           of every 128-key tile for all 32 rows, and the 4 waves merge their
@@ -25,8 +28,9 @@
 //   type B  64 invariant rows of one sample: the state starts from FACache and
 //           streams only the block's keys, then O = O~/l and LSE = m + ln l.
 //   merge   combines the type-A chunks of every block row into O and LSE.
-//   refresh 64 rows of one sample against every key: invariant keys first,
-//           a snapshot of (m, l, O~/l) into FACache for invariant rows, then
+//   refresh 64 rows of one sample against every key (fp32 caches; 16-bit
+//           caches use refresh_stream_kernel): invariant keys first, a
+//           snapshot of (m, l, O~/l) into FACache for invariant rows, then
 //           the block's keys, then O and LSE.
 //
 // FACache and the partials hold O~/l (the state's output, normalised) in the
@@ -367,9 +371,8 @@ __device__ __forceinline__ void softmax_pv(AttnState<MB, DH> &st, const f32x4_t 
     }
     st.l[mb] = fmaf(st.l[mb], alpha, ps);
     // Once the running maxima stop moving, alpha is exactly 1 in every lane
-    // and the rescale (a multiply per accumulator, plus moving accumulators
-    // held in AGPRs through VGPRs) is skipped; multiplying by 1 is exact, so
-    // the result does not depend on the branch.
+    // and the rescale (a multiply per accumulator) is skipped; multiplying
+    // by 1 is exact, so the result does not depend on the branch.
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
       for (int db = 0; db < DH / 16; ++db) st.o[mb][db] *= alpha;
