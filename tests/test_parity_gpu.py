@@ -109,6 +109,19 @@ def test_refresh_segment_edges(head_dim):
     _run_full(wl, 1)
 
 
+def test_batch_beyond_one_launch_slice():
+    # 70 samples: the library launches at most 64 samples' block table per
+    # kernel, so the refresh and every step run as two slices (64 + 6) with
+    # different kernel paths (the first slice has enough items for the
+    # whole-sequence streaming block-row kernel, the second does not).
+    # Ragged prompt lengths 0..40, blocks of 16, random block positions.
+    rng = np.random.default_rng([20261202, 70])
+    prompts = tuple(int(x) for x in rng.integers(0, 41, size=70))
+    wl = synth.custom("batch70", dtype="bf16", d_model=512, n_heads=4, head_dim=128, vocab=900,
+                      prompt_lens=prompts, gen_len=32, block_size=16, steps=2, seed=61)
+    _run_full(wl, 2)
+
+
 def test_small_fp32_head64_multi_tile():
     wl = synth.custom("small_fp32_h64", dtype="f32", d_model=256, n_heads=4, head_dim=64, vocab=700,
                       prompt_lens=(300, 77), gen_len=96, block_size=32, block_idx=(1, 2), steps=2,
