@@ -412,6 +412,10 @@ lacache_status lacache_workspace_size(const lacache_ctx *cctx, int32_t op, const
     case LACACHE_OP_DUALCACHE_ATTN:
       *bytes = partial_bytes(ctx, partial_rows(split_keys(ctx, seqs, batch), seqs, batch));
       return LACACHE_OK;
+    case LACACHE_OP_REFRESH_BLOCK:
+      // seqs: the table of the rows to re-project (lacache_refresh_block's proj)
+      *bytes = gemm_capable(ctx) ? gemm_bytes(ctx, block_tokens(seqs, batch)) : 0;
+      return LACACHE_OK;
   }
   return fail(ctx, LACACHE_ERR_INVALID_ARG, "unknown op %d", op);
 }
@@ -495,6 +499,56 @@ lc::SeqArgs longest_first(const lc::SeqArgs &sa) {
   }
   return r;
 }
+// The refresh attention of one slice (block table sa, rows by seq_offset):
+// every row against every key of its sample, invariant keys first, with the
+// FACache snapshot of the invariant rows; O and LSE of every row.
+hipError_t refresh_attention(lacache_ctx *ctx, const lacache_cache *cache, const lc::SeqArgs &slice, void *out,
+                             float *lse, hipStream_t s) {
+  const lc::DType dt = dtype_of(ctx);
+  const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads, ns = slice.n;
+  // bf16 contexts (16-bit caches) run the streaming refresh.
+  const bool streaming = dt == lc::kBF16;
+  const int rows_item = streaming ? lc::kRowsRS : lc::kRowsR;
+  lc::SeqArgs sa = slice;
+  for (int i = 0; i < ns; ++i) sa.pre[1][i + 1] = sa.pre[1][i] + (sa.len[i] + rows_item - 1) / rows_item;
+  lc::AttnArgs aa;
+  std::memset(&aa, 0, sizeof(aa));
+  aa.q = cache->q;
+  aa.k = cache->k;
+  aa.v = cache->v;
+  aa.out = out;
+  aa.lse = lse;
+  aa.m_w = cache->m;
+  aa.l_w = cache->l;
+  aa.o_w = cache->o;
+  aa.H = H;
+  aa.Hkv = ctx->cfg.n_kv_heads;
+  aa.scale_log2 = scale_log2(ctx);
+  // Every refresh item of a sample streams all of its keys: the streaming
+  // launch takes the samples longest first.
+  const lc::SeqArgs sr = streaming ? longest_first(sa) : sa;
+  return timed(ctx, LACACHE_KERNEL_REFRESH_ATTN, s, [&](const lc::LaunchEvents &ev) {
+    return streaming ? lc::launch_refresh_stream(dh, sr, aa, sr.pre[1][ns] * H, s, ev)
+                     : lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
+  });
+}
+
+// The projection of the block rows of one slice (block table sa with pre[0]
+// the prefix sums of its block lengths): embedding gather, RMSNorm, QKV,
+// RoPE and the cache write of rows [block_start, block_end) of each sample;
+// block_ids[row_base ..] are the slice's block ids.
+hipError_t project_block_rows(lacache_ctx *ctx, const lacache_weights *w, const lacache_cache *cache,
+                              const int32_t *block_ids, const lc::SeqArgs &sa, int row_base, bool gemm, char *gemm_ws,
+                              hipStream_t s) {
+  const int M = sa.pre[0][sa.n];
+  if (gemm) return run_qkv_gemm(ctx, w, cache, block_ids, sa, 0, 0, row_base, M, gemm_layout(ctx, gemm_ws, M), s);
+  lc::QkvArgs qa = qkv_args(ctx, w, cache, block_ids, 0);
+  qa.M = M;
+  qa.ids_base = row_base;
+  const lc::DType dt = dtype_of(ctx);
+  return timed(ctx, LACACHE_KERNEL_QKV, s,
+               [&](const lc::LaunchEvents &ev) { return lc::launch_qkv(dt, sa, qa, features(ctx), s, ev); });
+}
 }  // namespace
 
 lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w, const int32_t *ids,
@@ -517,16 +571,10 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
   const lc::DType dt = dtype_of(ctx);
   const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads;
 
-  // bf16 contexts (16-bit caches) run the streaming refresh.
-  const bool streaming = dt == lc::kBF16;
-  const int rows_item = streaming ? lc::kRowsRS : lc::kRowsR;
   for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
     const int ns = std::min(kMaxInline, batch - s0);
     lc::SeqArgs sa = slice_args(seqs, s0, ns);
-    for (int i = 0; i < ns; ++i) {
-      sa.pre[0][i + 1] = sa.pre[0][i] + sa.len[i];
-      sa.pre[1][i + 1] = sa.pre[1][i] + (sa.len[i] + rows_item - 1) / rows_item;
-    }
+    for (int i = 0; i < ns; ++i) sa.pre[0][i + 1] = sa.pre[0][i] + sa.len[i];
     hipError_t e = hipSuccess;
     if (gemm) {
       // Rows of the slice in passes of at most kPrefillChunk tokens.
@@ -543,26 +591,7 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
       if (e != hipSuccess) return hip_fail(ctx, "prefill qkv launch", e);
     }
 
-    lc::AttnArgs aa;
-    std::memset(&aa, 0, sizeof(aa));
-    aa.q = cache->q;
-    aa.k = cache->k;
-    aa.v = cache->v;
-    aa.out = out;
-    aa.lse = lse;
-    aa.m_w = cache->m;
-    aa.l_w = cache->l;
-    aa.o_w = cache->o;
-    aa.H = H;
-    aa.Hkv = ctx->cfg.n_kv_heads;
-    aa.scale_log2 = scale_log2(ctx);
-    // Every refresh item of a sample streams all of its keys: the streaming
-    // launch takes the samples longest first.
-    const lc::SeqArgs sr = streaming ? longest_first(sa) : sa;
-    e = timed(ctx, LACACHE_KERNEL_REFRESH_ATTN, s, [&](const lc::LaunchEvents &ev) {
-      return streaming ? lc::launch_refresh_stream(dh, sr, aa, sr.pre[1][ns] * H, s, ev)
-                       : lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
-    });
+    e = refresh_attention(ctx, cache, sa, out, lse, s);
     if (e != hipSuccess) return hip_fail(ctx, "refresh attention launch", e);
   }
   return LACACHE_OK;
@@ -670,15 +699,7 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     }
     const int M = sa.pre[0][ns];
 
-    hipError_t e = hipSuccess;
-    if (gemm) {
-      e = run_qkv_gemm(ctx, w, cache, block_ids, sa, 0, 0, row_base, M, gemm_layout(ctx, gemm_ws, M), s);
-    } else {
-      lc::QkvArgs qa = qkv_args(ctx, w, cache, block_ids, 0);
-      qa.M = M;
-      qa.ids_base = row_base;
-      e = timed(ctx, LACACHE_KERNEL_QKV, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv(dt, sa, qa, features(ctx), s, ev); });
-    }
+    hipError_t e = project_block_rows(ctx, w, cache, block_ids, sa, row_base, gemm, gemm_ws, s);
     if (e != hipSuccess) return hip_fail(ctx, "block-step qkv launch", e);
 
     lc::AttnArgs aa;
@@ -743,6 +764,43 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     if (e != hipSuccess) return hip_fail(ctx, "block-step invariant-rows launch", e);
     row_base += M;
     part_base += sa.pre[3][ns];
+  }
+  return LACACHE_OK;
+}
+
+lacache_status lacache_refresh_block(lacache_ctx *ctx, const lacache_weights *w, const int32_t *proj_ids,
+                                     const lacache_seq *proj, const lacache_seq *seqs, int32_t batch,
+                                     const lacache_cache *cache, void *out, float *lse, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if ((st = check_weights(ctx, w)) != LACACHE_OK) return st;
+  if ((st = check_cache(ctx, cache, true)) != LACACHE_OK) return st;
+  if (!proj_ids) return fail(ctx, LACACHE_ERR_INVALID_ARG, "proj_ids is NULL");
+  if (!out || !aligned16(out)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
+  if ((st = check_table(ctx, proj, batch, cache->n_rows)) != LACACHE_OK) return st;
+  if ((st = check_table(ctx, seqs, batch, cache->n_rows)) != LACACHE_OK) return st;
+  for (int i = 0; i < batch; ++i)
+    if (proj[i].seq_offset != seqs[i].seq_offset || proj[i].seq_len != seqs[i].seq_len)
+      return fail(ctx, LACACHE_ERR_INVALID_ARG, "sample %d: proj and seqs differ in seq_offset or seq_len", i);
+  const int64_t Mall = block_tokens(proj, batch);
+  const bool gemm = step_uses_prep(ctx, w, Mall);
+  const size_t need = gemm ? gemm_bytes(ctx, Mall) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
+                workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int row_base = 0;
+  for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
+    const int ns = std::min(kMaxInline, batch - s0);
+    lc::SeqArgs sp = slice_args(proj, s0, ns);
+    for (int i = 0; i < ns; ++i) sp.pre[0][i + 1] = sp.pre[0][i] + (sp.be[i] - sp.bs[i]);
+    hipError_t e = project_block_rows(ctx, w, cache, proj_ids, sp, row_base, gemm, static_cast<char *>(workspace), s);
+    if (e != hipSuccess) return hip_fail(ctx, "block-refresh qkv launch", e);
+    row_base += sp.pre[0][ns];
+    e = refresh_attention(ctx, cache, slice_args(seqs, s0, ns), out, lse, s);
+    if (e != hipSuccess) return hip_fail(ctx, "block-refresh attention launch", e);
   }
   return LACACHE_OK;
 }

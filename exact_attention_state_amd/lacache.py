@@ -19,12 +19,12 @@ LIB_PATH = os.path.join(_HERE, "liblacache.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
-OP_PREFILL, OP_BLOCK_STEP, OP_DUALCACHE_ATTN = 0, 1, 2
+OP_PREFILL, OP_BLOCK_STEP, OP_DUALCACHE_ATTN, OP_REFRESH_BLOCK = 0, 1, 2, 3
 DEVFLAG_BAD_TOKEN_ID = 1
 DEVFLAG_CACHE_RANGE = 2
 
 EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "lacache_prefill_cache",
-            "lacache_block_step", "lacache_dualcache_attn", "lacache_read_device_status",
+            "lacache_block_step", "lacache_refresh_block", "lacache_dualcache_attn", "lacache_read_device_status",
             "lacache_profile_enable", "lacache_profile_read", "lacache_status_string", "lacache_last_error",
             "lacache_packed_weight_size", "lacache_pack_qkv_weight")
 (KERNEL_QKV, KERNEL_BLOCK_ROWS, KERNEL_INVARIANT_ROWS, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_QKV_PREP,
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
                                        ctypes.POINTER(Cache), P, P, P, SZ, P]),
         "lacache_block_step": (st, [P, ctypes.POINTER(Weights), P, ctypes.POINTER(Seq), I32,
                                     ctypes.POINTER(Cache), P, P, P, SZ, P]),
+        "lacache_refresh_block": (st, [P, ctypes.POINTER(Weights), P, ctypes.POINTER(Seq), ctypes.POINTER(Seq), I32,
+                                       ctypes.POINTER(Cache), P, P, P, SZ, P]),
         "lacache_dualcache_attn": (st, [P, P, P, P, I64, ctypes.POINTER(Seq), I32, P, P, P, SZ, P]),
         "lacache_packed_weight_size": (st, [P, ctypes.POINTER(SZ)]),
         "lacache_pack_qkv_weight": (st, [P, P, P, SZ, P]),
@@ -258,6 +260,20 @@ class Context:
                                          _ptr(ct.lse) if lse else None, _ptr(workspace),
                                          0 if workspace is None else workspace.numel(), _stream(stream))
         self._check(st, "lacache_block_step")
+
+    def refresh_block(self, weights, proj_ids, proj_table, table, ct: CacheTensors, workspace=None, stream=None,
+                      lse=True):
+        """Block-boundary refresh: re-project the rows of proj_table's blocks (ids proj_ids), then the full
+        refresh attention for the block table `table`."""
+        if len(proj_table) != len(table):
+            raise ValueError("proj_table and table must have one row per sample each")
+        w = self._weights(*weights)
+        cache = self._cache(ct)
+        st = self.lib.lacache_refresh_block(self.handle, ctypes.byref(w), _ptr(self._ids(proj_ids)), _seqs(proj_table),
+                                            _seqs(table), len(table), ctypes.byref(cache), _ptr(ct.out),
+                                            _ptr(ct.lse) if lse else None, _ptr(workspace),
+                                            0 if workspace is None else workspace.numel(), _stream(stream))
+        self._check(st, "lacache_refresh_block")
 
     def dualcache_attn(self, q_block, k, v, table, out_block, lse_block=None, workspace=None, stream=None):
         for name, t, dt in (("q_block", q_block, self.cache_dtype), ("k", k, self.cache_dtype),

@@ -154,7 +154,8 @@ typedef struct lacache_ctx lacache_ctx;
 typedef enum {
   LACACHE_OP_PREFILL = 0,
   LACACHE_OP_BLOCK_STEP = 1,
-  LACACHE_OP_DUALCACHE_ATTN = 2
+  LACACHE_OP_DUALCACHE_ATTN = 2,
+  LACACHE_OP_REFRESH_BLOCK = 3     /* seqs: the table of the rows to re-project (proj) */
 } lacache_op;
 
 /* Creates a context on the current HIP device: validates the configuration,
@@ -210,6 +211,30 @@ LACACHE_API lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_we
                                   int32_t batch, const lacache_cache *cache,
                                   void *out, float *lse, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* Refresh at a block boundary when only some rows' ids changed since their
+ * last projection (normally the block just finished: its final ids are
+ * chosen after its last inner step).  Layer-0 q, k, v of a row depend only on
+ * its id and position (Section 3.3.2, EmbedCache and RoPECache), so only the
+ * rows of proj are re-projected; the attention is the full refresh of
+ * lacache_prefill_cache for the new block table seqs (the invariant set
+ * changes at the boundary and keys cannot leave an online-softmax state).
+ *   proj_ids device int32 [sum_b (proj[b].block_end - proj[b].block_start)]:
+ *            the ids of the rows to re-project, concatenated in sample order.
+ *   proj     host [batch]: per sample, the same seq_offset and seq_len as
+ *            seqs, and as block the rows [block_start, block_end) to
+ *            re-project (non-empty, at most 128 rows).
+ *   seqs     host [batch]: the block table from now on (the new block).
+ * Writes h, q, k, v of the proj rows; m, l, o for every row of the new U;
+ * out and lse (lse may be NULL) for every row.  The result equals
+ * lacache_prefill_cache on the full new ids up to rounding, provided the
+ * other rows' cache entries are those of their current ids.  Workspace:
+ * lacache_workspace_size(LACACHE_OP_REFRESH_BLOCK, proj, batch). */
+LACACHE_API lacache_status lacache_refresh_block(lacache_ctx *ctx, const lacache_weights *w,
+                                     const int32_t *proj_ids, const lacache_seq *proj,
+                                     const lacache_seq *seqs, int32_t batch,
+                                     const lacache_cache *cache, void *out, float *lse,
+                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Block-query attention over [prefix | fresh block | suffix] keys: the
  * attention of Fast-dLLM's DualCache inner step (decode_block), exact at

@@ -109,6 +109,37 @@ def test_refresh_segment_edges(head_dim):
     _run_full(wl, 1)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_boundary_refresh(dtype):
+    # At a block boundary the finished block's ids change (its final ids) and
+    # the block table moves to the next block.  lacache_refresh_block
+    # re-projects only the finished block's rows and recomputes the attention
+    # with the new table; the result must equal the oracle's refresh of the new
+    # ids on the new table (every row, every cache entry, every FACache pair).
+    d_model, head_dim = (512, 128) if dtype == "bf16" else (256, 64)
+    wl = synth.custom(f"block_refresh_{dtype}", dtype=dtype, d_model=d_model, n_heads=4, n_kv_heads=2,
+                      head_dim=head_dim, vocab=1500, prompt_lens=(37, 100, 0), gen_len=96, block_size=32,
+                      block_idx=(0, 1, 1), steps=1, seed=71)
+    _say(f"[parity] {wl.name}: table {wl.table()}")
+    dw = DeviceWorkload(wl)
+    cfg = cfg_of(wl)
+    dw.prefill()
+    rng = np.random.default_rng([20261202, 71])
+    ids_new = np.array(dw.ids_host, copy=True)
+    proj = dw.table
+    for (off, n, bs, be) in proj:
+        ids_new[off + bs:off + be] = rng.integers(0, wl.vocab, size=be - bs)
+    proj_ids = np.concatenate([ids_new[off + bs:off + be] for (off, n, bs, be) in proj]).astype(np.int32)
+    new_table = [(off, n, be, be + (be - bs)) for (off, n, bs, be) in proj]
+    ws = dw.ctx.alloc_workspace(lacache.OP_REFRESH_BLOCK, proj)
+    dw.ctx.refresh_block(dw.weights, torch.from_numpy(proj_ids).cuda(), proj, new_table, dw.ct, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.refresh(dw.params, cfg, ids_new, new_table)
+    dw.table = new_table
+    st = _compare_refresh(dw, ref, f"{wl.name} block refresh")
+    _say(f"[parity] {wl.name} block refresh ok {st}")
+
+
 def test_batch_beyond_one_launch_slice():
     # 70 samples: the library launches at most 64 samples' block table per
     # kernel, so the refresh and every step run as two slices (64 + 6) with
@@ -397,5 +428,10 @@ def test_invalid_arguments_are_rejected_before_any_launch():
     assert ei.value.status == lacache.ERR_WORKSPACE
     with pytest.raises(lacache.LaCacheError) as ei:
         dw.ctx.block_step(dw.weights, blk, [(0, 160, 0, 160)], dw.ct, dw.ws)
+    # Block-boundary refresh: proj and seqs must describe the same samples.
+    for proj, seqs in (([(0, 100, 80, 96)], [(0, 128, 96, 112)]), ([(8, 120, 80, 96)], [(0, 128, 96, 112)])):
+        with pytest.raises(lacache.LaCacheError) as ei:
+            dw.ctx.refresh_block(dw.weights, blk, proj, seqs, dw.ct, workspace=dw.ws)
+        assert ei.value.status == lacache.ERR_INVALID_ARG, (proj, seqs)
     torch.cuda.synchronize()
     assert torch.equal(before, dw.ct.out), "a rejected call wrote the output"
