@@ -13,7 +13,10 @@
 //
 // Operand tiles: 128 tokens x 64 contraction elements of A (16 KB) and 192
 // GEMM columns x 64 elements of W (24 KB) per stage of a 4-stage LDS ring,
-// filled global -> LDS by the load unit (global_load_lds_dwordx4).  A tile
+// filled global -> LDS by the load unit (global_load_lds_dwordx4).  (The
+// packed GEMM can also take half of the 192 columns per workgroup, with a
+// 5-stage ring of 28 KB stages, when whole tiles would leave half of the
+// chip idle.)  A tile
 // row is 128 bytes; its 16-byte piece p sits in slot p ^ ((r >> 1) & 7), so
 // the 16 rows of one MFMA operand read hit all 64 banks once.  prep writes A
 // in exactly that tile order ([row tile][contraction tile][128 x 64],
@@ -23,7 +26,7 @@
 //   packed  W converted once to fp16 in the same tile order (see
 //           pack_qkv_weight_kernel): contiguous copies, no conversion in the
 //           loop.  The contraction is split over two groups of four waves
-//           (64 tokens x 96 columns per wave); the kernel computes C^T so a
+//           (64 or 32 tokens x 96 columns per wave); the kernel computes C^T so a
 //           lane's four accumulator values are four GEMM columns of one token,
 //           and the column order puts both members of two RoPE pairs in one
 //           lane: RoPE needs no lane exchange.
@@ -42,6 +45,7 @@
 // streaming the weights.
 
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -370,14 +374,18 @@ __global__ __launch_bounds__(64 * kGWaves) void qkv_gemm_bf16_kernel(const GemmA
 }
 
 // ---------------------------------------------------------------------------
-// packed GEMM.  The 8 waves form two groups of 2 x 2; both groups cover the
-// whole 128 x 192 tile (64 tokens x 96 columns per wave, 6 x 4 accumulator
-// blocks), group 0 on the first 32 of each tile's 64 contraction elements
-// and group 1 on the second.  Per contraction tile a wave reads 10 operand
-// fragments for 24 MFMAs; the fragments of tile kt+1 are read right after
-// the barrier that publishes it, interleaved with the MFMAs of tile kt.
-// At the end each wave hands half of its blocks to its partner in the other
-// group through LDS, and each finishes the half it keeps.
+// packed GEMM.  A workgroup takes CT halves (96 GEMM columns each) of one
+// packed 192-column tile: CT = 2, the whole tile, or CT = 1, one half, for
+// launches whose whole tiles would leave at least half of the compute units
+// without a workgroup (twice the workgroups, each with half the work).  The
+// 8 waves form two groups of four; both groups cover the whole tile, group 0
+// on the first 32 of each tile's 64 contraction elements and group 1 on the
+// second.  A wave owns 16*RB tokens x 96 columns (6 x RB accumulator blocks;
+// RB = 2 CT): per contraction tile it reads 6 + RB operand fragments for
+// 6 RB MFMAs.  The fragments of tile kt+1 are read right after the barrier
+// that publishes it, interleaved with the MFMAs of tile kt.  At the end each
+// wave hands half of its blocks to its partner in the other group through
+// LDS, and each finishes the half it keeps.
 //
 // Column order inside a 16-column block cb of head hh (pairs p0..p0+7,
 // p0 = 8 * (cb mod d_h/16)): column 4g + v is feature p0 + 2g + (v >> 1)
@@ -385,8 +393,20 @@ __global__ __launch_bounds__(64 * kGWaves) void qkv_gemm_bf16_kernel(const GemmA
 // half for odd v.  With C^T on the matrix core, lane (g, t) holds columns
 // 4g..4g+3 of token t: two complete pairs.
 // ---------------------------------------------------------------------------
-constexpr int kPRB = 4, kPCB = 6;                     // token blocks x column blocks per wave
-constexpr int kPRedBytes = kGWaves * kPCB * 2 * 1024;  // blocks handed over: 96 KB
+constexpr int kPCB = 6;                               // column blocks per wave
+
+template <int CT> struct PackedTile {
+  static_assert(CT == 1 || CT == 2, "one or two column halves");
+  static constexpr int BN = 96 * CT;                  // GEMM columns per workgroup
+  static constexpr int RB = 2 * CT;                   // 16-token blocks per wave
+  static constexpr int StW = kGStageW / 2 * CT;       // W bytes per stage
+  static constexpr int Stage = kGStageA + StW;
+  static constexpr int NST = CT == 2 ? 4 : 5;         // ring stages: 160 KB or 140 KB
+  static constexpr int Smem = NST * Stage;
+  static constexpr int CopiesW = StW / 1024;          // 1 KB copies of W per stage: 24 or 12
+  static constexpr int RedBytes = kGWaves * kPCB * (RB / 2) * 1024;   // blocks handed over
+};
+
 
 __device__ __forceinline__ int packed_weight_row(int gc, int F, int dh) {
   const int ncb = F / 16, cbh = dh / 16;
@@ -417,86 +437,103 @@ __global__ __launch_bounds__(256) void pack_qkv_weight_kernel(const bf16_t *W, u
                        f16pair(__uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u)));
 }
 
-template <int DH>
+template <int DH, int CT>
 __global__ __launch_bounds__(512) void qkv_gemm_packed_kernel(const GemmArgs a) {
+  using T = PackedTile<CT>;
+  constexpr int RB = T::RB, HB = RB / 2, NST = T::NST;
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int kg = w >> 2, wq = w & 3, wm = wq >> 1, wn = wq & 1;
+  const int kg = w >> 2, wq = w & 3;
+  const int wm = CT == 2 ? wq >> 1 : wq, wn = CT == 2 ? (wq & 1) : 0;
   const int D = a.D, nk = D / kGBK;                  // nk: a multiple of 8
   const int cbh = DH / 16, ncb = a.F / 16;
-  const int n0 = blockIdx.x * kGBN, m0 = blockIdx.y * kGBM;
+  const int n0 = blockIdx.x * T::BN, m0 = blockIdx.y * kGBM;
+  const int ntile = CT == 2 ? blockIdx.x : blockIdx.x >> 1, half = CT == 2 ? 0 : blockIdx.x & 1;
   const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
   // Cache row of tile row tid, for the stores; its latency hides behind the loop.
   const int my_dst = tid < kGBM ? a.map[min(m0 + tid, a.M - 1)].x : 0;
 
-  // Copy j of wave w moves pieces [(j*8 + w)*64, +64) of a stage: 1 KB at
-  // byte j*8192 + w*1024 of both the tiled source and the LDS tile.
+  // Copy j of wave w moves pieces [(j*8 + w)*64, +64) of an operand's
+  // stage: 1 KB at byte j*8192 + w*1024 of both the tiled source and the
+  // LDS tile.  With CT = 1 a stage holds 12 KB of W: waves 0-3 copy two of
+  // them, waves 4-7 one.
   const uint32_t lw = __builtin_amdgcn_readfirstlane(w * 1024);
   const char *asrc = static_cast<const char *>(a.A) + (size_t)blockIdx.y * nk * kGStageA + (size_t)(w * 64 + lane) * 16;
-  const char *wsrc = static_cast<const char *>(a.Wp) + (size_t)blockIdx.x * nk * kGStageW + (size_t)(w * 64 + lane) * 16;
+  const char *wsrc = static_cast<const char *>(a.Wp) + (size_t)ntile * nk * kGStageW + (size_t)half * T::StW +
+                     (size_t)(w * 64 + lane) * 16;
   auto issue = [&](int kt) {
-    const uint32_t st = smem_lds + (kt % kGStages) * kGStage + lw;
+    const uint32_t st = smem_lds + (kt % NST) * T::Stage + lw;
     const char *as = asrc + (size_t)kt * kGStageA, *ws = wsrc + (size_t)kt * kGStageW;
 #pragma unroll
     for (int j = 0; j < kGCopyA; ++j) dma16(as + j * 8192, st + j * 8192);
 #pragma unroll
-    for (int j = 0; j < kGCopyW; ++j) dma16(ws + j * 8192, st + kGStageA + j * 8192);
+    for (int j = 0; j < (T::CopiesW + 7) / 8; ++j)
+      if (j * 8 + w < T::CopiesW) dma16(ws + j * 8192, st + kGStageA + j * 8192);
   };
-  auto frags = [&](int kt, Frag<f16_t> (&fa)[kPRB], Frag<f16_t> (&fw)[kPCB]) {
-    const char *st = smem + (kt % kGStages) * kGStage;
+  // Wait until at most `t` (0..3) later tiles' copies of this wave are in
+  // flight.
+  auto wait_tiles = [&](int t) {
+    constexpr int C = kGCopyA + (T::CopiesW + 7) / 8, C4 = kGCopyA + T::CopiesW / 8;   // waves 0-3, 4-7
+    auto wait = [&](auto CC) {
+      constexpr int c = decltype(CC)::value;
+      if (t >= 3) vmcnt_wait<3 * c>();
+      else if (t == 2) vmcnt_wait<2 * c>();
+      else if (t == 1) vmcnt_wait<c>();
+      else vmcnt_wait<0>();
+    };
+    if (C4 != C && w >= 4) wait(std::integral_constant<int, C4>{});
+    else wait(std::integral_constant<int, C>{});
+  };
+  auto frags = [&](int kt, Frag<f16_t> (&fa)[RB], Frag<f16_t> (&fw)[kPCB]) {
+    const char *st = smem + (kt % NST) * T::Stage;
 #pragma unroll
-    for (int i = 0; i < kPRB; ++i)
-      fa[i].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + frag_off(wm * kPRB + i, kg) + lane * 16));
+    for (int i = 0; i < RB; ++i)
+      fa[i].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + frag_off(wm * RB + i, kg) + lane * 16));
 #pragma unroll
     for (int j = 0; j < kPCB; ++j)
       fw[j].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + kGStageA + frag_off(wn * kPCB + j, kg) + lane * 16));
   };
 
-  f32x4_t acc[kPCB][kPRB];                           // C^T blocks: lane (g, t) holds columns 4g..4g+3 of token t
+  f32x4_t acc[kPCB][RB];                             // C^T blocks: lane (g, t) holds columns 4g..4g+3 of token t
 #pragma unroll
   for (int j = 0; j < kPCB; ++j)
 #pragma unroll
-    for (int i = 0; i < kPRB; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < RB; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // One contraction tile (kt + 1 < nk): tile kt+1 published (this wave's
   // copies landed, then the barrier), the fragments of tile kt+1 read, the
-  // MFMAs of tile kt, and the copy of tile kt+3 issued into the stage tile
-  // kt-1 left (its fragments were consumed before the barrier).  Copies in
-  // flight on entry: tiles kt+1 and kt+2.
-  auto step = [&](int kt, const Frag<f16_t> (&ca)[kPRB], const Frag<f16_t> (&cw)[kPCB],
-                  Frag<f16_t> (&na)[kPRB], Frag<f16_t> (&nw)[kPCB]) {
-    if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | kGCopies);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  // MFMAs of tile kt, and the copy of tile kt+NST-1 issued into the stage
+  // tile kt-1 left (its fragments were consumed before the barrier).
+  // Copies in flight on entry: tiles kt+1 .. kt+NST-2 (those below nk).
+  constexpr int NM = kPCB * RB, R = RB + kPCB;       // MFMAs, fragment reads per tile
+  constexpr int F1 = CT == 2 ? NM / 2 : R;           // MFMAs before the copy goes out
+  static_assert(F1 >= R && F1 <= NM, "reads fit before the copy");
+  auto step = [&](int kt, const Frag<f16_t> (&ca)[RB], const Frag<f16_t> (&cw)[kPCB],
+                  Frag<f16_t> (&na)[RB], Frag<f16_t> (&nw)[kPCB]) {
+    wait_tiles(min(NST - 3, nk - 2 - kt));
     lds_barrier();
     frags(kt + 1, na, nw);
-    // Fragment reads first, interleaved with the first half of the MFMAs;
-    // the copy of tile kt+3 goes out after them, so its LDS writes do not
-    // compete with this wave's reads.
-    constexpr int H1 = kPCB / 2, F1 = kPRB * H1, R = kPRB + kPCB;
-    static_assert(F1 >= R, "reads fit in the first half");
+    // Fragment reads first, interleaved with the first MFMAs; the copy of
+    // tile kt+NST-1 goes out after them, so its LDS writes do not compete
+    // with this wave's reads.
 #pragma unroll
-    for (int j = 0; j < H1; ++j)
-#pragma unroll
-      for (int i = 0; i < kPRB; ++i) mma16(acc[j][i], cw[j], ca[i]);
+    for (int q = 0; q < F1; ++q) mma16(acc[q / RB][q % RB], cw[q / RB], ca[q % RB]);
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, F1 - R, 0);
-    if (kt + kGStages - 1 < nk) issue(kt + kGStages - 1);
+    if constexpr (F1 > R) __builtin_amdgcn_sched_group_barrier(0x008, F1 - R, 0);
+    if (kt + NST - 1 < nk) issue(kt + NST - 1);
 #pragma unroll
-    for (int j = H1; j < kPCB; ++j)
-#pragma unroll
-      for (int i = 0; i < kPRB; ++i) mma16(acc[j][i], cw[j], ca[i]);
+    for (int q = F1; q < NM; ++q) mma16(acc[q / RB][q % RB], cw[q / RB], ca[q % RB]);
   };
-  issue(0);
-  issue(1);
-  issue(2);
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kGCopies));
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t) issue(t);
+  wait_tiles(NST - 2);
   lds_barrier();
-  Frag<f16_t> fa0[kPRB], fw0[kPCB], fa1[kPRB], fw1[kPCB];
+  Frag<f16_t> fa0[RB], fw0[kPCB], fa1[RB], fw1[kPCB];
   frags(0, fa0, fw0);
   // No branch around the fragment reads inside the loop: the wait before the
   // MFMAs then covers only the previous tile's reads.
@@ -508,32 +545,32 @@ __global__ __launch_bounds__(512) void qkv_gemm_packed_kernel(const GemmArgs a) 
 #pragma unroll
   for (int j = 0; j < kPCB; ++j)
 #pragma unroll
-    for (int i = 0; i < kPRB; ++i) mma16(acc[j][i], fw1[j], fa1[i]);
+    for (int i = 0; i < RB; ++i) mma16(acc[j][i], fw1[j], fa1[i]);
 
-  // Epilogue.  Group kg keeps token blocks 2kg, 2kg+1 of its wave's four and
-  // hands the other two to its partner (wave w ^ 4, same region, other half
-  // of the contraction).  Then RoPE per lane into an fp16 output tile [128
-  // tokens][192 columns in run order: per block the 8 first-half features,
-  // then their 8 partners], which all waves store as 16-byte runs.
-  constexpr int OST = kGBN + 8;                      // fp16 elements per output row (pad: banks)
+  // Epilogue.  Group kg keeps token blocks kg*HB .. kg*HB+HB-1 of its wave's
+  // RB and hands the others to its partner (wave w ^ 4, same region, other
+  // half of the contraction).  Then RoPE per lane into an fp16 output tile
+  // [128 tokens][BN columns in run order: per block the 8 first-half
+  // features, then their 8 partners], which all waves store as 16-byte runs.
+  constexpr int OST = T::BN + 8;                     // fp16 elements per output row (pad: banks)
   constexpr int OT_BYTES = kGBM * OST * 2;
-  static_assert(OT_BYTES + kGBM * 4 <= kPRedBytes && kPRedBytes <= kGemmSmem, "epilogue fits the ring");
+  static_assert(OT_BYTES + kGBM * 4 <= T::Smem && T::RedBytes <= T::Smem, "epilogue fits the ring");
   f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
   _Float16 *otile = reinterpret_cast<_Float16 *>(smem);
   int *s_dst = reinterpret_cast<int *>(smem + OT_BYTES);
   const int nrot = (a.H + a.Hkv) * DH;
   bool range = true;
   auto finish = [&](auto KG) {
-    constexpr int own = 2 * decltype(KG)::value, other = 2 - own;
+    constexpr int own = HB * decltype(KG)::value, other = HB - own;
     // (cos, sin) of pairs p0+2g and p0+2g+1 for each kept block's token.
-    uint4 csv[kPCB][2];
+    uint4 csv[kPCB][HB];
 #pragma unroll
     for (int j = 0; j < kPCB; ++j) {
       const int cb = min((n0 >> 4) + wn * kPCB + j, ncb - 1);
       const int hh = cb / cbh, p0 = (cb % cbh) * 8;
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int t = (wm * kPRB + own + ii) * 16 + r16;
+      for (int ii = 0; ii < HB; ++ii) {
+        const int t = (wm * RB + own + ii) * 16 + r16;
         csv[j][ii] = hh * DH < nrot ? *reinterpret_cast<const uint4 *>(a.cs + (size_t)(m0 + t) * (DH / 2) + p0 + 2 * g)
                                     : make_uint4(0, 0, 0, 0);
       }
@@ -542,12 +579,12 @@ __global__ __launch_bounds__(512) void qkv_gemm_packed_kernel(const GemmArgs a) 
 #pragma unroll
     for (int j = 0; j < kPCB; ++j)
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) red[(w * kPCB * 2 + j * 2 + ii) * 64 + lane] = acc[j][other + ii];
+      for (int ii = 0; ii < HB; ++ii) red[(w * kPCB * HB + j * HB + ii) * 64 + lane] = acc[j][other + ii];
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < kPCB; ++j)
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) acc[j][own + ii] += red[((w ^ 4) * kPCB * 2 + j * 2 + ii) * 64 + lane];
+      for (int ii = 0; ii < HB; ++ii) acc[j][own + ii] += red[((w ^ 4) * kPCB * HB + j * HB + ii) * 64 + lane];
     lds_barrier();                                   // hand-over area free for the output tile
 #pragma unroll
     for (int j = 0; j < kPCB; ++j) {
@@ -555,8 +592,8 @@ __global__ __launch_bounds__(512) void qkv_gemm_packed_kernel(const GemmArgs a) 
       const int cb = min((n0 >> 4) + jb, ncb - 1);
       const bool rot = cb / cbh * DH < nrot;
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int t = (wm * kPRB + own + ii) * 16 + r16;
+      for (int ii = 0; ii < HB; ++ii) {
+        const int t = (wm * RB + own + ii) * 16 + r16;
         const f32x4_t y = acc[j][own + ii];
         float o0 = y[0], o1 = y[1], o2 = y[2], o3 = y[3];
         if (rot) {
@@ -574,16 +611,16 @@ __global__ __launch_bounds__(512) void qkv_gemm_packed_kernel(const GemmArgs a) 
       }
     }
   };
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  vmcnt_wait<0>();
   if (kg == 0) finish(std::integral_constant<int, 0>{});
   else finish(std::integral_constant<int, 1>{});
   if (tid < kGBM) s_dst[tid] = my_dst;
   if (!range) atomicOr(a.flags, 2u);
   lds_barrier();
-  // 128 rows x 24 runs of 8 features per tile.
+  // 128 rows x BN/8 runs of 8 features per tile.
   const int qf = a.H * DH, kf = a.Hkv * DH;
-  for (int t = tid; t < kGBM * (kGBN / 8); t += 64 * kGWaves) {
-    const int row = t / (kGBN / 8), run = t % (kGBN / 8);
+  for (int t = tid; t < kGBM * (T::BN / 8); t += 64 * kGWaves) {
+    const int row = t / (T::BN / 8), run = t % (T::BN / 8);
     const int m = m0 + row;
     const int cb = (n0 >> 4) + (run >> 1);
     if (m >= a.M || cb >= ncb) continue;
@@ -1084,8 +1121,15 @@ hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const Launc
   }
   dim3 grid((a.F + kGBN - 1) / kGBN, (a.M + kGBM - 1) / kGBM);
   if (a.Wp) {
-    if (dh == 128) lc_launch(qkv_gemm_packed_kernel<128>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
-    else lc_launch(qkv_gemm_packed_kernel<64>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
+    // Half-width tiles when whole ones would leave half of the chip idle.
+    if (2 * grid.x * grid.y <= (unsigned)device_cus()) {
+      grid.x = (a.F + PackedTile<1>::BN - 1) / PackedTile<1>::BN;
+      if (dh == 128) lc_launch(qkv_gemm_packed_kernel<128, 1>, grid, dim3(64 * kGWaves), PackedTile<1>::Smem, s, ev, a);
+      else lc_launch(qkv_gemm_packed_kernel<64, 1>, grid, dim3(64 * kGWaves), PackedTile<1>::Smem, s, ev, a);
+    } else {
+      if (dh == 128) lc_launch(qkv_gemm_packed_kernel<128, 2>, grid, dim3(64 * kGWaves), PackedTile<2>::Smem, s, ev, a);
+      else lc_launch(qkv_gemm_packed_kernel<64, 2>, grid, dim3(64 * kGWaves), PackedTile<2>::Smem, s, ev, a);
+    }
   } else {
     if (dh == 128) lc_launch(qkv_gemm_bf16_kernel<128>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
     else lc_launch(qkv_gemm_bf16_kernel<64>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
@@ -1094,12 +1138,15 @@ hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const Launc
 }
 
 hipError_t setup_gemm_attributes() {
-  const void *kernels[] = {reinterpret_cast<const void *>(qkv_gemm_bf16_kernel<128>),
-                           reinterpret_cast<const void *>(qkv_gemm_bf16_kernel<64>),
-                           reinterpret_cast<const void *>(qkv_gemm_packed_kernel<128>),
-                           reinterpret_cast<const void *>(qkv_gemm_packed_kernel<64>)};
-  for (const void *k : kernels) {
-    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmSmem);
+  const std::pair<const void *, int> kernels[] = {
+      {reinterpret_cast<const void *>(qkv_gemm_bf16_kernel<128>), kGemmSmem},
+      {reinterpret_cast<const void *>(qkv_gemm_bf16_kernel<64>), kGemmSmem},
+      {reinterpret_cast<const void *>(qkv_gemm_packed_kernel<128, 2>), PackedTile<2>::Smem},
+      {reinterpret_cast<const void *>(qkv_gemm_packed_kernel<64, 2>), PackedTile<2>::Smem},
+      {reinterpret_cast<const void *>(qkv_gemm_packed_kernel<128, 1>), PackedTile<1>::Smem},
+      {reinterpret_cast<const void *>(qkv_gemm_packed_kernel<64, 1>), PackedTile<1>::Smem}};
+  for (const auto &k : kernels) {
+    const hipError_t e = hipFuncSetAttribute(k.first, hipFuncAttributeMaxDynamicSharedMemorySize, k.second);
     if (e != hipSuccess) return e;
   }
 #define LC_SKA(DHV, NPWV)                                                                                    \
