@@ -24,6 +24,7 @@ struct lacache_ctx {
   float2 *rope;
   unsigned *flags;
   int split_keys;          // keys per type-A chunk if fixed by LACACHE_SPLIT_KEYS, else 0 (per call)
+  int gemm_tile;           // packed GEMM tile fixed by LACACHE_GEMM_TILE (lc::GemmTile), else automatic
   std::string last_error;
   // Diagnostics: event pairs stamped by each launch while profiling is on.
   bool profiling = false;
@@ -347,6 +348,12 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
     const int v = std::atoi(env);
     if (v >= 32 && v % 32 == 0) ctx->split_keys = v;
   }
+  ctx->gemm_tile = lc::kGemmTileAuto;
+  if (const char *env = std::getenv("LACACHE_GEMM_TILE")) {
+    if (!std::strcmp(env, "whole")) ctx->gemm_tile = lc::kGemmTileWhole;
+    else if (!std::strcmp(env, "half")) ctx->gemm_tile = lc::kGemmTileHalf;
+    else if (!std::strcmp(env, "wide")) ctx->gemm_tile = lc::kGemmTileWide;
+  }
   hipError_t e = hipGetDevice(&ctx->device);
   // RoPE angles in double on the host: position * theta^(-2i/d_h), stored as fp32 (cos, sin).
   const int half = c.head_dim / 2;
@@ -471,7 +478,7 @@ hipError_t run_qkv_gemm(lacache_ctx *ctx, const lacache_weights *w, const lacach
     return timed(ctx, LACACHE_KERNEL_QKV_GEMM, s, [&](const lc::LaunchEvents &ev) {
       return lc::launch_qkv_skinny_fused(ctx->cfg.head_dim, sa, pa, ga, s, ev);
     });
-  return timed(ctx, LACACHE_KERNEL_QKV_GEMM, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv_gemm(ctx->cfg.head_dim, ga, s, ev); });
+  return timed(ctx, LACACHE_KERNEL_QKV_GEMM, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv_gemm(ctx->cfg.head_dim, ga, ctx->gemm_tile, s, ev); });
 }
 
 }  // namespace

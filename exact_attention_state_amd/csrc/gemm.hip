@@ -14,9 +14,10 @@
 // Operand tiles: 128 tokens x 64 contraction elements of A (16 KB) and 192
 // GEMM columns x 64 elements of W (24 KB) per stage of a 4-stage LDS ring,
 // filled global -> LDS by the load unit (global_load_lds_dwordx4).  (The
-// packed GEMM can also take half of the 192 columns per workgroup, with a
-// 5-stage ring of 28 KB stages, when whole tiles would leave half of the
-// chip idle.)  A tile
+// packed GEMM can also take half of the 192 columns per workgroup when whole
+// tiles would leave half of the chip idle, or 256 tokens x 192 columns in
+// 32-wide contraction stages for large launches; both with a 5-stage ring
+// of 28 KB stages.)  A tile
 // row is 128 bytes; its 16-byte piece p sits in slot p ^ ((r >> 1) & 7), so
 // the 16 rows of one MFMA operand read hit all 64 banks once.  prep writes A
 // in exactly that tile order ([row tile][contraction tile][128 x 64],
@@ -636,6 +637,208 @@ __global__ __launch_bounds__(512) void qkv_gemm_packed_kernel(const GemmArgs a) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide packed GEMM, for launches with at least one full round of 256 x 192
+// tiles: per CU 1.43x fewer operand bytes per flop than 128 x 192.  A stage
+// is one 32-wide half of a 64-wide contraction tile: the 16 A fragments of
+// the two 128-token row tiles (16 KB) and the 12 W fragments of the column
+// tile (12 KB), each a contiguous KB of the tiled operands; a 5-stage ring
+// (140 KB).  Wave w owns tokens 64 (w & 3) .. +63 and columns 96 (w >> 2)
+// .. +95 over the whole contraction (no hand-over): per stage 10 fragment
+// reads and 24 MFMAs.  A second row tile past the launch repeats the last
+// one (its rows are not stored).  Epilogue as in the packed GEMM.
+// ---------------------------------------------------------------------------
+struct WideTile {
+  static constexpr int BM = 256, BN = 192, RB = 4;
+  static constexpr int StA = 16 * 1024, StW = 12 * 1024, Stage = StA + StW, NST = 5;
+  static constexpr int Smem = NST * Stage;            // 140 KB
+  static constexpr int Copies = Stage / 1024;         // 28: waves 0-3 issue four, waves 4-7 three
+};
+
+template <int DH>
+__global__ __launch_bounds__(512) void qkv_gemm_packed_wide_kernel(const GemmArgs a) {
+  using T = WideTile;
+  constexpr int RB = T::RB, NST = T::NST;
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wm = w & 3, wn = w >> 2;
+  const int D = a.D, nk = D / kGBK, ns = 2 * nk;     // ns: 32-wide stages
+  const int cbh = DH / 16, ncb = a.F / 16;
+  const int n0 = blockIdx.x * T::BN, m0 = blockIdx.y * T::BM;
+  const int mt_last = (a.M + kGBM - 1) / kGBM - 1;
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  // Cache row of tile row tid, for the stores; its latency hides behind the loop.
+  const int my_dst = tid < T::BM ? a.map[min(m0 + tid, a.M - 1)].x : 0;
+
+  // Copy j of wave w is fragment c = 8 j + w of the stage (c < 16: A
+  // fragment c, c >= 16: W fragment c - 16), 1 KB to LDS byte c * 1024.
+  const char *src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = min(8 * j + w, T::Copies - 1);
+    if (c < 16) {
+      const int mt = min(2 * (int)blockIdx.y + (c >> 3), mt_last);
+      src[j] = static_cast<const char *>(a.A) + (size_t)mt * nk * kGStageA + (size_t)((c & 7) * 2) * 1024;
+    } else {
+      src[j] = static_cast<const char *>(a.Wp) + (size_t)blockIdx.x * nk * kGStageW + (size_t)((c - 16) * 2) * 1024;
+    }
+    src[j] += lane * 16;
+  }
+  auto issue = [&](int sg) {
+    const uint32_t st = smem_lds + (sg % NST) * T::Stage;
+    const int kt = sg >> 1, ks = sg & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 8 * j + w;
+      if (c < T::Copies) {
+        const size_t step = c < 16 ? (size_t)kGStageA : (size_t)kGStageW;
+        dma16(src[j] + (size_t)kt * step + ks * 1024, st + c * 1024);
+      }
+    }
+  };
+  // Wait until at most `t` (0..3) later stages' copies of this wave are in flight.
+  auto wait_stages = [&](int t) {
+    auto wait = [&](auto CC) {
+      constexpr int c = decltype(CC)::value;
+      if (t >= 3) vmcnt_wait<3 * c>();
+      else if (t == 2) vmcnt_wait<2 * c>();
+      else if (t == 1) vmcnt_wait<c>();
+      else vmcnt_wait<0>();
+    };
+    if (w >= 4) wait(std::integral_constant<int, 3>{});
+    else wait(std::integral_constant<int, 4>{});
+  };
+  auto frags = [&](int sg, Frag<f16_t> (&fa)[RB], Frag<f16_t> (&fw)[kPCB]) {
+    const char *st = smem + (sg % NST) * T::Stage;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      fa[i].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + ((wm * RB + i) << 10) + lane * 16));
+#pragma unroll
+    for (int j = 0; j < kPCB; ++j)
+      fw[j].v = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4 *>(st + T::StA + ((wn * kPCB + j) << 10) + lane * 16));
+  };
+
+  f32x4_t acc[kPCB][RB];                             // C^T blocks: lane (g, t) holds columns 4g..4g+3 of token t
+#pragma unroll
+  for (int j = 0; j < kPCB; ++j)
+#pragma unroll
+    for (int i = 0; i < RB; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // One stage (sg + 1 < ns): stage sg+1 published, its fragments read, the
+  // MFMAs of stage sg, and the copy of stage sg+NST-1 issued into the ring
+  // slot stage sg-1 left.  Copies in flight on entry: stages sg+1 .. sg+3.
+  constexpr int NM = kPCB * RB, R = RB + kPCB, F1 = NM / 2;
+  static_assert(F1 >= R, "reads fit before the copy");
+  auto step = [&](int sg, const Frag<f16_t> (&ca)[RB], const Frag<f16_t> (&cw)[kPCB],
+                  Frag<f16_t> (&na)[RB], Frag<f16_t> (&nw)[kPCB]) {
+    wait_stages(min(NST - 3, ns - 2 - sg));
+    lds_barrier();
+    frags(sg + 1, na, nw);
+#pragma unroll
+    for (int q = 0; q < F1; ++q) mma16(acc[q / RB][q % RB], cw[q / RB], ca[q % RB]);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, F1 - R, 0);
+    if (sg + NST - 1 < ns) issue(sg + NST - 1);
+#pragma unroll
+    for (int q = F1; q < NM; ++q) mma16(acc[q / RB][q % RB], cw[q / RB], ca[q % RB]);
+  };
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t) issue(t);
+  wait_stages(NST - 2);
+  lds_barrier();
+  Frag<f16_t> fa0[RB], fw0[kPCB], fa1[RB], fw1[kPCB];
+  frags(0, fa0, fw0);
+  for (int sg = 0; sg < ns - 2; sg += 2) {
+    step(sg, fa0, fw0, fa1, fw1);
+    step(sg + 1, fa1, fw1, fa0, fw0);
+  }
+  step(ns - 2, fa0, fw0, fa1, fw1);
+#pragma unroll
+  for (int j = 0; j < kPCB; ++j)
+#pragma unroll
+    for (int i = 0; i < RB; ++i) mma16(acc[j][i], fw1[j], fa1[i]);
+
+  // Epilogue: RoPE per lane into an fp16 output tile [256 tokens][192
+  // columns in run order], two row blocks at a time (their (cos, sin) rows
+  // loaded together), then 16-byte stores by all waves.
+  constexpr int OST = T::BN + 8;                     // fp16 elements per output row (pad: banks)
+  constexpr int OT_BYTES = T::BM * OST * 2;
+  static_assert(OT_BYTES + T::BM * 4 <= T::Smem, "epilogue fits the ring");
+  _Float16 *otile = reinterpret_cast<_Float16 *>(smem);
+  int *s_dst = reinterpret_cast<int *>(smem + OT_BYTES);
+  const int nrot = (a.H + a.Hkv) * DH;
+  bool range = true;
+  vmcnt_wait<0>();
+  lds_barrier();                                     // every wave is past its last ring reads
+  auto rope_half = [&](auto HC) {
+    constexpr int i0 = 2 * decltype(HC)::value;
+    uint4 csv[kPCB][2];
+#pragma unroll
+    for (int j = 0; j < kPCB; ++j) {
+      const int cb = min((n0 >> 4) + wn * kPCB + j, ncb - 1);
+      const int hh = cb / cbh, p0 = (cb % cbh) * 8;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int t = (wm * RB + i0 + ii) * 16 + r16;
+        const int row = min(m0 + t, a.M - 1);
+        csv[j][ii] = hh * DH < nrot ? *reinterpret_cast<const uint4 *>(a.cs + (size_t)row * (DH / 2) + p0 + 2 * g)
+                                    : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kPCB; ++j) {
+      const int jb = wn * kPCB + j;
+      const int cb = min((n0 >> 4) + jb, ncb - 1);
+      const bool rot = cb / cbh * DH < nrot;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int t = (wm * RB + i0 + ii) * 16 + r16;
+        const f32x4_t y = acc[j][i0 + ii];
+        float o0 = y[0], o1 = y[1], o2 = y[2], o3 = y[3];
+        if (rot) {
+          const uint4 c = csv[j][ii];
+          const float c0 = __uint_as_float(c.x), s0 = __uint_as_float(c.y);
+          const float c1 = __uint_as_float(c.z), s1 = __uint_as_float(c.w);
+          o0 = y[0] * c0 - y[1] * s0;
+          o1 = y[1] * c0 + y[0] * s0;
+          o2 = y[2] * c1 - y[3] * s1;
+          o3 = y[3] * c1 + y[2] * s1;
+        }
+        range = range && fabsf(o0) <= kF16Max && fabsf(o1) <= kF16Max && fabsf(o2) <= kF16Max && fabsf(o3) <= kF16Max;
+        *reinterpret_cast<uint32_t *>(otile + t * OST + jb * 16 + 2 * g) = f16pair(o0, o2);
+        *reinterpret_cast<uint32_t *>(otile + t * OST + jb * 16 + 8 + 2 * g) = f16pair(o1, o3);
+      }
+    }
+  };
+  rope_half(std::integral_constant<int, 0>{});
+  rope_half(std::integral_constant<int, 1>{});
+  if (tid < T::BM) s_dst[tid] = my_dst;
+  if (!range) atomicOr(a.flags, 2u);
+  lds_barrier();
+  // 256 rows x 24 runs of 8 features per tile.
+  const int qf = a.H * DH, kf = a.Hkv * DH;
+  for (int t = tid; t < T::BM * (T::BN / 8); t += 64 * kGWaves) {
+    const int row = t / (T::BN / 8), run = t % (T::BN / 8);
+    const int m = m0 + row;
+    const int cb = (n0 >> 4) + (run >> 1);
+    if (m >= a.M || cb >= ncb) continue;
+    const int hh = cb / cbh, p0 = (cb % cbh) * 8;
+    const int feat = hh * DH + ((run & 1) ? DH / 2 + p0 : p0);
+    const int dst = s_dst[row];
+    const uint4 val = *reinterpret_cast<const uint4 *>(otile + row * OST + run * 8);
+    f16_t *out;
+    if (feat < qf) out = static_cast<f16_t *>(a.q) + (size_t)dst * qf + feat;
+    else if (feat < qf + kf) out = static_cast<f16_t *>(a.k) + (size_t)dst * kf + (feat - qf);
+    else out = static_cast<f16_t *>(a.v) + (size_t)dst * kf + (feat - qf - kf);
+    *reinterpret_cast<uint4 *>(out) = val;
+  }
+}
+
 int gemm_rows_padded(int M) { return (M + kGBM - 1) / kGBM * kGBM; }
 
 hipError_t launch_qkv_prep(const SeqArgs &sa, const PrepArgs &a, hipStream_t s, const LaunchEvents &ev) {
@@ -1096,7 +1299,7 @@ hipError_t launch_pack_qkv_weight(const void *W, void *Wp, int D, int F, int dh,
   return hipGetLastError();
 }
 
-hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const LaunchEvents &ev) {
+hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, int tile, hipStream_t s, const LaunchEvents &ev) {
   if (a.M <= 0) return hipSuccess;
   if (a.Wp && skinny_supported(a.M, a.D)) {
     const dim3 grid(4 * ((a.F + kGBN - 1) / kGBN));
@@ -1121,8 +1324,17 @@ hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const Launc
   }
   dim3 grid((a.F + kGBN - 1) / kGBN, (a.M + kGBM - 1) / kGBM);
   if (a.Wp) {
-    // Half-width tiles when whole ones would leave half of the chip idle.
-    if (2 * grid.x * grid.y <= (unsigned)device_cus()) {
+    const unsigned cus = (unsigned)device_cus();
+    const dim3 wgrid(grid.x, (a.M + WideTile::BM - 1) / WideTile::BM);
+    if (tile == kGemmTileAuto) {
+      // Wide tiles for at least one full round of them; half-width ones when
+      // whole ones would leave half of the chip idle.
+      tile = wgrid.x * wgrid.y >= cus ? kGemmTileWide : 2 * grid.x * grid.y <= cus ? kGemmTileHalf : kGemmTileWhole;
+    }
+    if (tile == kGemmTileWide) {
+      if (dh == 128) lc_launch(qkv_gemm_packed_wide_kernel<128>, wgrid, dim3(64 * kGWaves), WideTile::Smem, s, ev, a);
+      else lc_launch(qkv_gemm_packed_wide_kernel<64>, wgrid, dim3(64 * kGWaves), WideTile::Smem, s, ev, a);
+    } else if (tile == kGemmTileHalf) {
       grid.x = (a.F + PackedTile<1>::BN - 1) / PackedTile<1>::BN;
       if (dh == 128) lc_launch(qkv_gemm_packed_kernel<128, 1>, grid, dim3(64 * kGWaves), PackedTile<1>::Smem, s, ev, a);
       else lc_launch(qkv_gemm_packed_kernel<64, 1>, grid, dim3(64 * kGWaves), PackedTile<1>::Smem, s, ev, a);
@@ -1144,7 +1356,9 @@ hipError_t setup_gemm_attributes() {
       {reinterpret_cast<const void *>(qkv_gemm_packed_kernel<128, 2>), PackedTile<2>::Smem},
       {reinterpret_cast<const void *>(qkv_gemm_packed_kernel<64, 2>), PackedTile<2>::Smem},
       {reinterpret_cast<const void *>(qkv_gemm_packed_kernel<128, 1>), PackedTile<1>::Smem},
-      {reinterpret_cast<const void *>(qkv_gemm_packed_kernel<64, 1>), PackedTile<1>::Smem}};
+      {reinterpret_cast<const void *>(qkv_gemm_packed_kernel<64, 1>), PackedTile<1>::Smem},
+      {reinterpret_cast<const void *>(qkv_gemm_packed_wide_kernel<128>), WideTile::Smem},
+      {reinterpret_cast<const void *>(qkv_gemm_packed_wide_kernel<64>), WideTile::Smem}};
   for (const auto &k : kernels) {
     const hipError_t e = hipFuncSetAttribute(k.first, hipFuncAttributeMaxDynamicSharedMemorySize, k.second);
     if (e != hipSuccess) return e;

@@ -111,7 +111,10 @@ bool skinny_fused_supported(int M, int D, int vocab);
 // (p.M == a.M, p.D == a.D; p.A, p.map, p.cs unused).
 hipError_t launch_qkv_skinny_fused(int dh, const SeqArgs &sa, const PrepArgs &p, const GemmArgs &a, hipStream_t s,
                                    const LaunchEvents &ev);
-hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, hipStream_t s, const LaunchEvents &ev);
+// Tile of the packed-weight GEMM (>= 128 tokens): automatic by launch size,
+// or fixed (diagnostics): whole 128 x 192, half-width 128 x 96, wide 256 x 192.
+enum GemmTile { kGemmTileAuto = 0, kGemmTileWhole = 1, kGemmTileHalf = 2, kGemmTileWide = 3 };
+hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, int tile, hipStream_t s, const LaunchEvents &ev);
 size_t packed_qkv_weight_bytes(int D, int F);
 bool skinny_supported(int M, int D);      // the packed-weight projection for <= 64 tokens
 int prep_rows(int M, int D, bool packed); // rows the prep kernel writes (zero rows past M included)

@@ -165,7 +165,12 @@ typedef enum {
  * Diagnostics: the environment variable LACACHE_SPLIT_KEYS (a multiple of
  * 32), read here, fixes the key chunk of the block rows' split-KV partials
  * for the context's lifetime instead of the per-call choice; results stay
- * within the parity tolerances, not bit-identical. */
+ * within the parity tolerances, not bit-identical.  LACACHE_GEMM_TILE
+ * ("whole", "half" or "wide"), also read here, fixes the tile of the
+ * packed-weight projection GEMM used for 128 or more tokens (128 x 192,
+ * 128 x 96 or 256 x 192 tokens x columns per workgroup) instead of the
+ * choice by launch size; the results are the same up to fp32 summation
+ * order (within the parity tolerances). */
 LACACHE_API lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out);
 
 /* Frees the context's device memory (synchronises the device first).

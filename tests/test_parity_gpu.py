@@ -160,13 +160,20 @@ def test_small_fp32_head64_multi_tile():
     _run_full(wl, 2)
 
 
-@pytest.mark.parametrize("packed", [True, False])
+@pytest.mark.parametrize("packed,tile", [(True, None), (True, "whole"), (True, "half"), (True, "wide"),
+                                         (False, None)])
 @pytest.mark.parametrize("shape", ["h128_gqa", "h64"])
-def test_many_token_projection_every_row(shape, packed):
+def test_many_token_projection_every_row(shape, packed, tile, monkeypatch):
     """Block steps of >= 128 tokens run the MFMA GEMM projection (and so does
-    every refresh): both weight forms, every row against the oracle.  h128_gqa:
-    F = 2048 is not a multiple of the 192-column tile (a partial last tile) and
-    K/V head boundaries fall inside tiles; 320 block tokens are 2.5 row tiles."""
+    every refresh): both weight forms, every row against the oracle, and each
+    tile of the packed-weight GEMM (chosen by launch size, or fixed through
+    LACACHE_GEMM_TILE): 128 x 192, 128 x 96 and 256 x 192.  h128_gqa:
+    F = 2048 is not a multiple of the 192-column tile (a partial last tile,
+    and an empty last half-width tile) and K/V head boundaries fall inside
+    tiles; 320 block tokens are 2.5 row tiles (1.25 wide ones: the second
+    row tile of the last wide tile lies past the launch)."""
+    if tile is not None:
+        monkeypatch.setenv("LACACHE_GEMM_TILE", tile)
     if shape == "h128_gqa":
         wl = synth.custom("gemm_h128_gqa", dtype="bf16", d_model=1024, n_heads=8, n_kv_heads=4, head_dim=128,
                           vocab=2000, prompt_lens=(40, 7, 96, 130, 3, 64, 21, 50, 77, 12), gen_len=64,
@@ -176,6 +183,7 @@ def test_many_token_projection_every_row(shape, packed):
                           prompt_lens=(20, 33, 48, 9, 60, 17, 40, 28), gen_len=32, block_size=16,
                           block_idx=(0, 1, 1, 0, 0, 1, 0, 1), steps=2, seed=42)
     assert wl.block_tokens >= 128
+    _say(f"[parity] GEMM tile {tile or 'by launch size'}")
     _run_full(wl, 2, packed=packed)
 
 
