@@ -153,6 +153,23 @@ def test_batch_beyond_one_launch_slice():
     _run_full(wl, 2)
 
 
+@pytest.mark.parametrize("lengths", ["equal", "ragged"])
+def test_streaming_kernels_head64_every_row(lengths):
+    """A batch large enough for the streaming block-row kernel (whole-sequence
+    chunks: 16 samples x 16 heads = 256 items) and the streaming invariant-row
+    kernel (more than 2048 (64-row tile, head) items) at head_dim 64, every row
+    against the oracle.  equal: every sample's invariant rows split into equal
+    segments; ragged: 128-row segments."""
+    if lengths == "equal":
+        prompts = (600,) * 16
+    else:
+        rng = np.random.default_rng([20261202, 72])
+        prompts = tuple(int(x) for x in rng.integers(500, 701, size=16))
+    wl = synth.custom(f"stream_h64_{lengths}", dtype="bf16", d_model=1024, n_heads=16, head_dim=64, vocab=3000,
+                      prompt_lens=prompts, gen_len=64, block_size=32, steps=1, seed=72)
+    _run_full(wl, 1)
+
+
 def test_small_fp32_head64_multi_tile():
     wl = synth.custom("small_fp32_h64", dtype="f32", d_model=256, n_heads=4, head_dim=64, vocab=700,
                       prompt_lens=(300, 77), gen_len=96, block_size=32, block_idx=(1, 2), steps=2,
