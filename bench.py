@@ -397,6 +397,30 @@ def main():
             for k, v in prof.items() if v[1]}
     log(f"[bench] per-kernel: " + ", ".join(f"{k} {v['us_avg']:.2f} us" for k, v in kern.items()))
 
+    # Per-step distribution: every step bracketed by events on the launch
+    # stream, enqueued behind a bounded matmul as above (GPU time of each step,
+    # host submission excluded).
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    big = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    with torch.cuda.stream(stream):
+        for _ in range(8):
+            big = (big @ big).clamp_(-1, 1)
+        for i in range(args.steps):
+            step_ev[i][0].record(stream)
+            run_step(i, sh)
+            step_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    del big
+    per_step = sorted(a.elapsed_time(b) * 1e3 for a, b in step_ev)
+
+    def pct(q):
+        return per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
+
+    step_pct = {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9), "steps": len(per_step)}
+    log(f"[bench] per step (events, eager): p10 {step_pct['p10']:.2f} us, median {step_pct['median']:.2f} us, "
+        f"p90 {step_pct['p90']:.2f} us")
+
     refresh = (measure_refresh(ctx, sets, base, stream, dev, args.refresh_reps, acc, wl, blk_ids[0])
                if args.refresh_reps > 0 else None)
 
@@ -455,6 +479,7 @@ def main():
         "pairs_computed_per_step": acc["pairs_computed"],
         "pairs_equiv_per_s": acc["pairs_equiv"] / (ms * 1e-3),
         "us_per_step_eager": ms_eager * 1e3,
+        "us_per_step_events": step_pct,
         "us_per_step_graph": None if ms_graph is None else ms_graph * 1e3,
         "us_per_step_warm_eager": ms_warm * 1e3,
         "kernels_us_avg": {k: v["us_avg"] for k, v in kern.items()},
