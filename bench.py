@@ -103,6 +103,25 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
+def stream_copy_gbs(dev, reps=5):
+    """STREAM-style device copy of 512 MiB (read + write bytes per second, GB/s): the
+    achievable bandwidth that the HBM-bound kernels are also compared with."""
+    import torch
+    n = 512 * 1024 * 1024
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    del src, dst
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
 def step_accounting(wl):
     """Work and algorithmic HBM bytes of one block step of workload `wl`, per kernel.
 
@@ -447,6 +466,10 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": peak_flops / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if roof["bound"] == "hbm":
+        # Beside the nominal peak: the fraction of what a plain device copy reaches.
+        roof["stream_copy_GBps"] = stream_copy_gbs(dev)
+        roof["frac_of_copy"] = roof["achieved"] / roof["stream_copy_GBps"]
     roof["traffic"] = measured_traffic(dom, wl.name)
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = nbytes
