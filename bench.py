@@ -122,6 +122,33 @@ def stream_copy_gbs(dev, reps=5):
     return 2 * n / (ms * 1e-3) / 1e9
 
 
+def attention_summary(acc, kern):
+    """The step's attention (block rows and invariant rows, with the merge of the
+    block rows' partials where it runs) as one unit: algorithmic bytes over the
+    summed average durations of its launches, against the HBM peak."""
+    names = [k for k in ("attn", "block_rows", "invariant_rows", "merge") if k in kern]
+    us = sum(kern[k]["us_avg"] for k in names)
+    nbytes = acc["kernels"]["attn"]["bytes"]
+    return {"kernels": names, "us": us, "algorithmic_bytes": nbytes,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS if us else None}
+
+
+def projection_summary(acc, kern, peak_flops):
+    """The step's projection (prep and GEMM, or the single fused launch): flops
+    over the summed average durations, against the bf16 MFMA peak and against
+    the attainable roofline min(peak, AI x HBM peak)."""
+    names = [k for k in ("qkv", "qkv_prep", "qkv_gemm") if k in kern]
+    us = sum(kern[k]["us_avg"] for k in names)
+    flops = sum(acc["kernels"][k]["flops"] for k in names)
+    nbytes = sum(acc["kernels"][k]["bytes"] for k in names)
+    if not us:
+        return None
+    rate = flops / (us * 1e-6)
+    attainable = min(peak_flops, flops / nbytes * HBM_PEAK_GBS * 1e9)
+    return {"kernels": names, "us": us, "flops": flops, "algorithmic_bytes": nbytes,
+            "mfma_frac": rate / peak_flops, "attainable_frac": rate / attainable}
+
+
 def step_accounting(wl):
     """Work and algorithmic HBM bytes of one block step of workload `wl`, per kernel.
 
@@ -511,6 +538,8 @@ def main():
         "kernels_mfma_frac": {k: acc["kernels"][k]["flops"] / (v["us_avg"] * 1e-6) / peak_flops
                               for k, v in kern.items() if k in acc["kernels"] and acc["kernels"][k]["flops"]},
         "kernel_source_sha256": {k: kernel_source_hash(k) for k in kern},
+        "attention": attention_summary(acc, kern),
+        "projection": projection_summary(acc, kern, peak_flops),
         "roofline": roof,
         "refresh": refresh,
         "cpu_baseline": cpu,
