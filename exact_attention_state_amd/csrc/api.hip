@@ -25,6 +25,7 @@ struct lacache_ctx {
   unsigned *flags;
   int split_keys;          // keys per type-A chunk if fixed by LACACHE_SPLIT_KEYS, else 0 (per call)
   int gemm_tile;           // packed GEMM tile fixed by LACACHE_GEMM_TILE (lc::GemmTile), else automatic
+  int refresh_rows;        // streaming refresh item rows fixed by LACACHE_REFRESH_ROWS (64 or 128), else 0
   std::string last_error;
   // Diagnostics: event pairs stamped by each launch while profiling is on.
   bool profiling = false;
@@ -348,6 +349,11 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
     const int v = std::atoi(env);
     if (v >= 32 && v % 32 == 0) ctx->split_keys = v;
   }
+  ctx->refresh_rows = 0;
+  if (const char *env = std::getenv("LACACHE_REFRESH_ROWS")) {
+    const int v = std::atoi(env);
+    if (v == 64 || v == 128) ctx->refresh_rows = v;
+  }
   ctx->gemm_tile = lc::kGemmTileAuto;
   if (const char *env = std::getenv("LACACHE_GEMM_TILE")) {
     if (!std::strcmp(env, "whole")) ctx->gemm_tile = lc::kGemmTileWhole;
@@ -513,9 +519,21 @@ hipError_t refresh_attention(lacache_ctx *ctx, const lacache_cache *cache, const
                              float *lse, hipStream_t s) {
   const lc::DType dt = dtype_of(ctx);
   const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads, ns = slice.n;
-  // bf16 contexts (16-bit caches) run the streaming refresh.
+  // bf16 contexts (16-bit caches) run the streaming refresh: 128-row items
+  // (two row blocks per wave), or 64-row items when 128-row ones would leave
+  // compute units without a workgroup.
   const bool streaming = dt == lc::kBF16;
-  const int rows_item = streaming ? lc::kRowsRS : lc::kRowsR;
+  auto items = [&](int rows) {
+    int64_t n = 0;
+    for (int i = 0; i < ns; ++i) n += (slice.len[i] + rows - 1) / rows;
+    return n * H;
+  };
+  int mb = lc::kRefreshMB;
+  if (streaming) {
+    if (ctx->refresh_rows) mb = ctx->refresh_rows / 64;
+    else if (items(64 * lc::kRefreshMB) < lc::device_cus()) mb = 1;
+  }
+  const int rows_item = streaming ? 64 * mb : lc::kRowsR;
   lc::SeqArgs sa = slice;
   for (int i = 0; i < ns; ++i) sa.pre[1][i + 1] = sa.pre[1][i] + (sa.len[i] + rows_item - 1) / rows_item;
   lc::AttnArgs aa;
@@ -535,7 +553,7 @@ hipError_t refresh_attention(lacache_ctx *ctx, const lacache_cache *cache, const
   // launch takes the samples longest first.
   const lc::SeqArgs sr = streaming ? longest_first(sa) : sa;
   return timed(ctx, LACACHE_KERNEL_REFRESH_ATTN, s, [&](const lc::LaunchEvents &ev) {
-    return streaming ? lc::launch_refresh_stream(dh, sr, aa, sr.pre[1][ns] * H, s, ev)
+    return streaming ? lc::launch_refresh_stream(dh, mb, sr, aa, sr.pre[1][ns] * H, s, ev)
                      : lc::launch_refresh_attn(dt, dh, sa, aa, sa.pre[1][ns] * H, s, ev);
   });
 }

@@ -1625,17 +1625,22 @@ hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, 
   return hipGetLastError();
 }
 
-hipError_t launch_refresh_stream(int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
+hipError_t launch_refresh_stream(int dh, int mb, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
                                  const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
-  if (dh == 128)
-    lc_launch(refresh_stream_kernel<bf16_t, 128, kRefreshMB, 2>, dim3(n_blocks), dim3(256), StreamR<128, 2>::BYTES, s, ev,
-              sa, a);
-  else if (dh == 64)
-    lc_launch(refresh_stream_kernel<bf16_t, 64, kRefreshMB, 2>, dim3(n_blocks), dim3(256), StreamR<64, 2>::BYTES, s, ev,
-              sa, a);
-  else
+  if (mb != 1 && mb != 2) return hipErrorInvalidValue;
+#define LC_RS(DHV, MBV) \
+  lc_launch(refresh_stream_kernel<bf16_t, DHV, MBV, 2>, dim3(n_blocks), dim3(256), StreamR<DHV, 2>::BYTES, s, ev, sa, a)
+  if (dh == 128) {
+    if (mb == 2) LC_RS(128, 2);
+    else LC_RS(128, 1);
+  } else if (dh == 64) {
+    if (mb == 2) LC_RS(64, 2);
+    else LC_RS(64, 1);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef LC_RS
   return hipGetLastError();
 }
 
@@ -1678,8 +1683,10 @@ hipError_t setup_kernel_attributes() {
   LC_ATTR((refresh_attn_kernel<f16_t, bf16_t, 64>), (refresh_smem<f16_t, 64>()));
   LC_ATTR((refresh_attn_kernel<float, float, 128>), (refresh_smem<float, 128>()));
   LC_ATTR((refresh_attn_kernel<float, float, 64>), (refresh_smem<float, 64>()));
-  LC_ATTR((refresh_stream_kernel<bf16_t, 128, kRefreshMB, 2>), (StreamR<128, 2>::BYTES));
-  LC_ATTR((refresh_stream_kernel<bf16_t, 64, kRefreshMB, 2>), (StreamR<64, 2>::BYTES));
+  LC_ATTR((refresh_stream_kernel<bf16_t, 128, 2, 2>), (StreamR<128, 2>::BYTES));
+  LC_ATTR((refresh_stream_kernel<bf16_t, 64, 2, 2>), (StreamR<64, 2>::BYTES));
+  LC_ATTR((refresh_stream_kernel<bf16_t, 128, 1, 2>), (StreamR<128, 2>::BYTES));
+  LC_ATTR((refresh_stream_kernel<bf16_t, 64, 1, 2>), (StreamR<64, 2>::BYTES));
   LC_ATTR((block_rows_stream_kernel<bf16_t, 128, 4>), (StreamA<128, 4>::BYTES));
   LC_ATTR((block_rows_stream_kernel<bf16_t, 64, 4>), (StreamA<64, 4>::BYTES));
   LC_ATTR((block_rows_stream_kernel<bf16_t, 128, 2>), (StreamA<128, 2>::BYTES));

@@ -136,9 +136,10 @@ hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const At
                                    hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                                hipStream_t s, const LaunchEvents &ev);
-// Streaming refresh (bf16 parameters, 16-bit caches): items of kRowsRS rows,
-// a 2-stage ring of 64-key tiles (two workgroups per CU).
-hipError_t launch_refresh_stream(int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
+// Streaming refresh (bf16 parameters, 16-bit caches): items of 64 * mb rows
+// (mb = 1 or 2 row blocks of 16 per wave), a 2-stage ring of 64-key tiles
+// (two workgroups per CU).
+hipError_t launch_refresh_stream(int dh, int mb, const SeqArgs &sa, const AttnArgs &a, int n_blocks, hipStream_t s,
                                  const LaunchEvents &ev);
 hipError_t setup_kernel_attributes();
 
@@ -146,8 +147,7 @@ hipError_t setup_kernel_attributes();
 constexpr int kRowsA = 32;     // block rows per type-A item
 constexpr int kRowsB = 64;     // invariant rows per type-B item
 constexpr int kRowsR = 64;     // rows per refresh item (fp32)
-constexpr int kRefreshMB = 2;  // row blocks of 16 per wave in the streaming refresh
-constexpr int kRowsRS = 64 * kRefreshMB;   // rows per streaming refresh item (bf16)
+constexpr int kRefreshMB = 2;  // row blocks of 16 per wave in the streaming refresh (1 for small launches)
 constexpr int kQkvRows = 32;   // token rows per QKV tile
 constexpr int kQkvNB = 3;      // 16-feature column blocks per QKV tile
 constexpr int kQkvWaves = 8;   // waves splitting the contraction

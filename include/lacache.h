@@ -170,7 +170,10 @@ typedef enum {
  * packed-weight projection GEMM used for 128 or more tokens (128 x 192,
  * 128 x 96 or 256 x 192 tokens x columns per workgroup) instead of the
  * choice by launch size; the results are the same up to fp32 summation
- * order (within the parity tolerances). */
+ * order (within the parity tolerances).  LACACHE_REFRESH_ROWS (64 or 128),
+ * also read here, fixes the rows per workgroup of the bf16 refresh attention
+ * instead of the choice by launch size (bit-identical results: the rows per
+ * workgroup do not change any row's arithmetic). */
 LACACHE_API lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out);
 
 /* Frees the context's device memory (synchronises the device first).

@@ -96,17 +96,39 @@ def test_small_bf16_ragged_batch(packed):
     _run_full(wl, 3, packed=packed)
 
 
+@pytest.mark.parametrize("rows", [64, 128])
 @pytest.mark.parametrize("head_dim", [64, 128])
-def test_refresh_segment_edges(head_dim):
+def test_refresh_segment_edges(head_dim, rows, monkeypatch):
     # The refresh streams the invariant keys in two segments, then the block's
     # keys, each segment in 64-key tiles: a block at position 0 (empty first
     # segment), blocks at the very end (empty second segment), a 40-key block
     # (ragged block tile), and a sample spanning four 128-row items (420 rows);
-    # grouped KV heads.  Every row and every FACache pair is compared.
+    # grouped KV heads.  Every row and every FACache pair is compared, with
+    # 64-row and 128-row refresh workgroups (fixed through LACACHE_REFRESH_ROWS).
+    monkeypatch.setenv("LACACHE_REFRESH_ROWS", str(rows))
     wl = synth.custom(f"refresh_edges_h{head_dim}", dtype="bf16", d_model=512, n_heads=4, n_kv_heads=2,
                       head_dim=head_dim, vocab=1200, prompt_lens=(0, 130, 61, 300), gen_len=120, block_size=40,
                       block_idx=(0, 2, 2, 1), steps=1, seed=51)
     _run_full(wl, 1)
+
+
+def test_refresh_rows_per_workgroup_bitwise(monkeypatch):
+    """The rows per refresh workgroup (64 or 128) change no row's arithmetic:
+    both launches give bit-identical outputs, LSE and FACache."""
+    wl = synth.custom("refresh_rows", dtype="bf16", d_model=512, n_heads=4, head_dim=128, vocab=900,
+                      prompt_lens=(100, 7, 250), gen_len=64, block_size=32, block_idx=(1, 0, 1), steps=1, seed=53)
+    res = {}
+    for rows in (64, 128):
+        monkeypatch.setenv("LACACHE_REFRESH_ROWS", str(rows))
+        dw = DeviceWorkload(wl)
+        dw.prefill()
+        torch.cuda.synchronize()
+        res[rows] = {k: getattr(dw.ct, k).clone() for k in ("out", "lse", "m", "l", "o")}
+    urows = torch.from_numpy(np.concatenate([off + np.r_[0:bs, be:n] for (off, n, bs, be) in wl.table()])).to("cuda")
+    for k in ("out", "lse"):
+        assert torch.equal(res[64][k], res[128][k]), k
+    for k in ("m", "l", "o"):
+        assert torch.equal(res[64][k].index_select(0, urows), res[128][k].index_select(0, urows)), k
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
