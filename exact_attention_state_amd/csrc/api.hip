@@ -7,6 +7,7 @@
 // than lc::kMaxInline samples are launched in slices.
 
 #include <algorithm>
+#include <cxxabi.h>
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
@@ -35,6 +36,31 @@ struct lacache_ctx {
   double prof_ms[LACACHE_KERNEL_COUNT] = {};
   int64_t prof_n[LACACHE_KERNEL_COUNT] = {};
 };
+
+namespace lc {
+namespace {
+bool g_launch_log = false;
+}
+void set_launch_log(bool on) { g_launch_log = on; }
+bool launch_log_enabled() { return g_launch_log; }
+void log_launch(const void *kernel, hipStream_t s, unsigned grid) {
+  // The runtime's (mangled) name of the kernel, demangled:
+  // "void lc::name<args>(params)" -> "lc::name<args>".
+  const char *mangled = hipKernelNameRefByPtr(kernel, s);
+  std::string m = mangled ? mangled : "?";
+  // _Float16 is mangled DF16_, which the host demangler may not know: read it
+  // as the half type (Dh).
+  for (size_t p = m.find("DF16_"); p != std::string::npos; p = m.find("DF16_", p)) m.replace(p, 5, "Dh");
+  int status = -1;
+  char *dem = abi::__cxa_demangle(m.c_str(), nullptr, nullptr, &status);
+  std::string name = status == 0 && dem ? dem : m;
+  std::free(dem);
+  if (name.compare(0, 5, "void ") == 0) name.erase(0, 5);
+  const size_t args = name.rfind(">(");
+  if (args != std::string::npos) name.erase(args + 1);
+  std::fprintf(stderr, "lacache launch: %s grid %u\n", name.c_str(), grid);
+}
+}  // namespace lc
 
 namespace {
 
@@ -88,6 +114,10 @@ lacache_status check_table(lacache_ctx *ctx, const lacache_seq *seqs, int32_t ba
       return fail(ctx, LACACHE_ERR_UNSUPPORTED, "sample %d: block of %d tokens (at most 128 supported)", i,
                   s.block_end - s.block_start);
     const int64_t end = (int64_t)s.seq_offset + s.seq_len;
+    // Kernels index rows in 32 bits (offsets into the buffers are 64-bit).
+    if (end > INT32_MAX)
+      return fail(ctx, LACACHE_ERR_INVALID_ARG, "sample %d: rows [%d, %lld) end past row 2^31 - 1", i, s.seq_offset,
+                  (long long)end);
     if (n_rows >= 0 && end > n_rows)
       return fail(ctx, LACACHE_ERR_INVALID_ARG, "sample %d: rows [%d, %lld) exceed the %lld rows of the buffers", i,
                   s.seq_offset, (long long)end, (long long)n_rows);
@@ -353,6 +383,10 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   if (const char *env = std::getenv("LACACHE_REFRESH_ROWS")) {
     const int v = std::atoi(env);
     if (v == 64 || v == 128) ctx->refresh_rows = v;
+  }
+  {
+    const char *env = std::getenv("LACACHE_LOG");
+    lc::set_launch_log(env && env[0] != 0 && std::strcmp(env, "0") != 0);
   }
   ctx->gemm_tile = lc::kGemmTileAuto;
   if (const char *env = std::getenv("LACACHE_GEMM_TILE")) {
@@ -658,6 +692,14 @@ int stream_segment_rows(const lc::SeqArgs &sa, int H, lc::DType dt) {
   return ((nu0 + nseg - 1) / nseg + 15) / 16 * 16;
 }
 
+// Workspace of one block step with these weights (the packed weight decides
+// the projection path) and block table.
+size_t block_step_bytes(const lacache_ctx *ctx, const lacache_weights *w, const lacache_seq *seqs, int32_t batch) {
+  const int64_t M = block_tokens(seqs, batch);
+  return partial_bytes(ctx, partial_rows(split_keys(ctx, seqs, batch), seqs, batch)) +
+         (step_uses_prep(ctx, w, M) ? gemm_bytes(ctx, M) : 0);
+}
+
 void plan_block_rows(int split, lc::SeqArgs &sa) {
   for (int i = 0; i < sa.n; ++i) {
     const int B = sa.be[i] - sa.bs[i];
@@ -686,7 +728,7 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
   const int64_t P = partial_rows(split, seqs, batch);
   const int64_t Mall = block_tokens(seqs, batch);
   const bool gemm = step_uses_prep(ctx, w, Mall);
-  const size_t need = partial_bytes(ctx, P) + (gemm ? gemm_bytes(ctx, Mall) : 0);
+  const size_t need = block_step_bytes(ctx, w, seqs, batch);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
                 workspace);

@@ -1519,15 +1519,15 @@ hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs
     const int cus = device_cus();
     const bool two = n_blocks > cus && n_blocks <= 2 * cus;
     if (dh == 128) {
-      if (two) lc_launch(block_rows_stream_kernel<bf16_t, 128, 2>, dim3(n_blocks), dim3(256), StreamA<128, 2>::BYTES, s, ev, sa, a);
-      else lc_launch(block_rows_stream_kernel<bf16_t, 128, 4>, dim3(n_blocks), dim3(256), StreamA<128, 4>::BYTES, s, ev, sa, a);
+      if (two) lc_launch<block_rows_stream_kernel<bf16_t, 128, 2>>(dim3(n_blocks), dim3(256), StreamA<128, 2>::BYTES, s, ev, sa, a);
+      else lc_launch<block_rows_stream_kernel<bf16_t, 128, 4>>(dim3(n_blocks), dim3(256), StreamA<128, 4>::BYTES, s, ev, sa, a);
     } else {
-      if (two) lc_launch(block_rows_stream_kernel<bf16_t, 64, 2>, dim3(n_blocks), dim3(256), StreamA<64, 2>::BYTES, s, ev, sa, a);
-      else lc_launch(block_rows_stream_kernel<bf16_t, 64, 4>, dim3(n_blocks), dim3(256), StreamA<64, 4>::BYTES, s, ev, sa, a);
+      if (two) lc_launch<block_rows_stream_kernel<bf16_t, 64, 2>>(dim3(n_blocks), dim3(256), StreamA<64, 2>::BYTES, s, ev, sa, a);
+      else lc_launch<block_rows_stream_kernel<bf16_t, 64, 4>>(dim3(n_blocks), dim3(256), StreamA<64, 4>::BYTES, s, ev, sa, a);
     }
     return hipGetLastError();
   }
-  LC_DISPATCH(dt, dh, (lc_launch(block_rows_kernel<T, TO, DH>, dim3(n_blocks), dim3(256), block_rows_smem<T, DH>(), s, ev, sa, a)));
+  LC_DISPATCH(dt, dh, (lc_launch<block_rows_kernel<T, TO, DH>>(dim3(n_blocks), dim3(256), block_rows_smem<T, DH>(), s, ev, sa, a)));
   return hipGetLastError();
 }
 
@@ -1573,7 +1573,7 @@ hipError_t launch_attn_ab(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a
   if (nA + nB <= 0) return hipSuccess;
   const int bmax = block_max(sa);
 #define LC_AB(BM) \
-  LC_DISPATCH(dt, dh, (lc_launch(attn_ab_kernel<T, TO, DH, BM>, dim3(nA + nB), dim3(256), attn_ab_smem<T, DH, BM>(), s, ev, sa, a, nA)))
+  LC_DISPATCH(dt, dh, (lc_launch<attn_ab_kernel<T, TO, DH, BM>>(dim3(nA + nB), dim3(256), attn_ab_smem<T, DH, BM>(), s, ev, sa, a, nA)))
   if (bmax <= 32) LC_AB(32);
   else if (bmax <= 64) LC_AB(64);
   else LC_AB(128);
@@ -1590,7 +1590,7 @@ hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const At
   if (bmax > kStreamMaxBlock) return hipErrorInvalidValue;
   if (dt != kBF16) return hipErrorInvalidValue;
 #define LC_STR(DH, NK) \
-  lc_launch(invariant_stream_kernel<bf16_t, DH, NK>, dim3(n_blocks), dim3(64), StreamLds<DH, NK>::BYTES, s, ev, sa, a)
+  lc_launch<invariant_stream_kernel<bf16_t, DH, NK>>(dim3(n_blocks), dim3(64), StreamLds<DH, NK>::BYTES, s, ev, sa, a)
   if (dh == 128) {
     if (bmax <= 32) LC_STR(128, 1);
     else LC_STR(128, 2);
@@ -1609,7 +1609,7 @@ hipError_t launch_invariant_rows(DType dt, int dh, const SeqArgs &sa, const Attn
   int bmax = 0;
   for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
 #define LC_INV(BM) \
-  LC_DISPATCH(dt, dh, (lc_launch(invariant_rows_kernel<T, TO, DH, BM>, dim3(grid), dim3(256), invariant_rows_smem<T, DH, BM>(), s, ev, sa, a, M)))
+  LC_DISPATCH(dt, dh, (lc_launch<invariant_rows_kernel<T, TO, DH, BM>>(dim3(grid), dim3(256), invariant_rows_smem<T, DH, BM>(), s, ev, sa, a, M)))
   if (bmax <= 32) LC_INV(32);
   else if (bmax <= 64) LC_INV(64);
   else LC_INV(128);
@@ -1621,7 +1621,7 @@ hipError_t launch_merge(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, 
                         const LaunchEvents &ev) {
   const int waves = M * a.H;
   if (waves <= 0) return hipSuccess;
-  LC_DISPATCH(dt, dh, (lc_launch(merge_kernel<T, TO, DH>, dim3((waves + 3) / 4), dim3(256), 0, s, ev, sa, a, M)));
+  LC_DISPATCH(dt, dh, (lc_launch<merge_kernel<T, TO, DH>>(dim3((waves + 3) / 4), dim3(256), 0, s, ev, sa, a, M)));
   return hipGetLastError();
 }
 
@@ -1630,7 +1630,7 @@ hipError_t launch_refresh_stream(int dh, int mb, const SeqArgs &sa, const AttnAr
   if (n_blocks <= 0) return hipSuccess;
   if (mb != 1 && mb != 2) return hipErrorInvalidValue;
 #define LC_RS(DHV, MBV) \
-  lc_launch(refresh_stream_kernel<bf16_t, DHV, MBV, 2>, dim3(n_blocks), dim3(256), StreamR<DHV, 2>::BYTES, s, ev, sa, a)
+  lc_launch<refresh_stream_kernel<bf16_t, DHV, MBV, 2>>(dim3(n_blocks), dim3(256), StreamR<DHV, 2>::BYTES, s, ev, sa, a)
   if (dh == 128) {
     if (mb == 2) LC_RS(128, 2);
     else LC_RS(128, 1);
@@ -1647,7 +1647,7 @@ hipError_t launch_refresh_stream(int dh, int mb, const SeqArgs &sa, const AttnAr
 hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                                hipStream_t s, const LaunchEvents &ev) {
   if (n_blocks <= 0) return hipSuccess;
-  LC_DISPATCH(dt, dh, (lc_launch(refresh_attn_kernel<T, TO, DH>, dim3(n_blocks), dim3(256), refresh_smem<T, DH>(), s, ev, sa, a)));
+  LC_DISPATCH(dt, dh, (lc_launch<refresh_attn_kernel<T, TO, DH>>(dim3(n_blocks), dim3(256), refresh_smem<T, DH>(), s, ev, sa, a)));
   return hipGetLastError();
 }
 

@@ -846,7 +846,7 @@ hipError_t launch_qkv_prep(const SeqArgs &sa, const PrepArgs &a, hipStream_t s, 
   const dim3 grid((a.M_pad + 3) / 4);
   switch (a.D / 512) {
 #define LC_PREP(NPV) \
-  case NPV: lc_launch(qkv_prep_kernel<NPV>, grid, dim3(256), 0, s, ev, sa, a); break;
+  case NPV: lc_launch<qkv_prep_kernel<NPV>>(grid, dim3(256), 0, s, ev, sa, a); break;
     LC_PREP(1) LC_PREP(2) LC_PREP(3) LC_PREP(4) LC_PREP(5) LC_PREP(6) LC_PREP(7) LC_PREP(8)
     LC_PREP(9) LC_PREP(10) LC_PREP(11) LC_PREP(12) LC_PREP(13) LC_PREP(14) LC_PREP(15) LC_PREP(16)
 #undef LC_PREP
@@ -968,10 +968,10 @@ __global__ __launch_bounds__(512) void qkv_skinny_kernel(const GemmArgs a) {
     const int dst = a.map[tok].x;
     const int fa = hh * DH + p0 + 2 * g, fbf = fa + DH / 2;   // first-half pair, partners
     f16_t *base;
-    int off;
-    if (fa < qf) { base = static_cast<f16_t *>(a.q); off = dst * qf + fa; }
-    else if (fa < qf + kf) { base = static_cast<f16_t *>(a.k); off = dst * kf + (fa - qf); }
-    else { base = static_cast<f16_t *>(a.v); off = dst * kf + (fa - qf - kf); }
+    size_t off;                                              // cache rows reach 2^31 / (H d_h) and beyond
+    if (fa < qf) { base = static_cast<f16_t *>(a.q); off = (size_t)dst * qf + fa; }
+    else if (fa < qf + kf) { base = static_cast<f16_t *>(a.k); off = (size_t)dst * kf + (fa - qf); }
+    else { base = static_cast<f16_t *>(a.v); off = (size_t)dst * kf + (fa - qf - kf); }
     *reinterpret_cast<uint32_t *>(base + off) = f16pair(o0, o2);
     *reinterpret_cast<uint32_t *>(base + off + (fbf - fa)) = f16pair(o1, o3);
   }
@@ -1240,10 +1240,10 @@ __global__ __launch_bounds__(512) void qkv_skinny_fused_kernel(const SeqArgs sa,
     range = range && fabsf(o0) <= kF16Max && fabsf(o1) <= kF16Max && fabsf(o2) <= kF16Max && fabsf(o3) <= kF16Max;
     const int fa = hh * DH + p0 + 2 * g, fbf = fa + DH / 2;   // first-half pair, partners
     f16_t *base;
-    int off;
-    if (fa < qf) { base = static_cast<f16_t *>(a.q); off = dst * qf + fa; }
-    else if (fa < qf + kf) { base = static_cast<f16_t *>(a.k); off = dst * kf + (fa - qf); }
-    else { base = static_cast<f16_t *>(a.v); off = dst * kf + (fa - qf - kf); }
+    size_t off;                                              // cache rows reach 2^31 / (H d_h) and beyond
+    if (fa < qf) { base = static_cast<f16_t *>(a.q); off = (size_t)dst * qf + fa; }
+    else if (fa < qf + kf) { base = static_cast<f16_t *>(a.k); off = (size_t)dst * kf + (fa - qf); }
+    else { base = static_cast<f16_t *>(a.v); off = (size_t)dst * kf + (fa - qf - kf); }
     *reinterpret_cast<uint32_t *>(base + off) = f16pair(o0, o2);
     *reinterpret_cast<uint32_t *>(base + off + (fbf - fa)) = f16pair(o1, o3);
   }
@@ -1260,7 +1260,7 @@ hipError_t launch_qkv_skinny_fused(int dh, const SeqArgs &sa, const PrepArgs &p,
   if (!skinny_fused_supported(a.M, a.D, p.vocab) || !a.Wp || a.M != p.M || a.D != p.D) return hipErrorInvalidValue;
   const dim3 grid(4 * ((a.F + kGBN - 1) / kGBN));
 #define LC_SF(DHV, TBV, NPWV) \
-  lc_launch(qkv_skinny_fused_kernel<DHV, TBV, NPWV>, grid, dim3(512), skinny_fused_smem<TBV, NPWV>(), s, ev, sa, p, a)
+  lc_launch<qkv_skinny_fused_kernel<DHV, TBV, NPWV>>(grid, dim3(512), skinny_fused_smem<TBV, NPWV>(), s, ev, sa, p, a)
 #define LC_SF_NPW(DHV, TBV)                       \
   switch (a.D / 512) {                             \
     case 1: LC_SF(DHV, TBV, 1); break;             \
@@ -1304,7 +1304,7 @@ hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, int tile, hipStream_t s, c
   if (a.Wp && skinny_supported(a.M, a.D)) {
     const dim3 grid(4 * ((a.F + kGBN - 1) / kGBN));
 #define LC_SK(DHV, TBV, NPWV) \
-  lc_launch(qkv_skinny_kernel<DHV, TBV, NPWV>, grid, dim3(512), skinny_smem<TBV>(), s, ev, a)
+  lc_launch<qkv_skinny_kernel<DHV, TBV, NPWV>>(grid, dim3(512), skinny_smem<TBV>(), s, ev, a)
 #define LC_SK_NPW(DHV, TBV)                       \
   switch (a.D / 512) {                             \
     case 1: LC_SK(DHV, TBV, 1); break;             \
@@ -1332,19 +1332,19 @@ hipError_t launch_qkv_gemm(int dh, const GemmArgs &a, int tile, hipStream_t s, c
       tile = wgrid.x * wgrid.y >= cus ? kGemmTileWide : 2 * grid.x * grid.y <= cus ? kGemmTileHalf : kGemmTileWhole;
     }
     if (tile == kGemmTileWide) {
-      if (dh == 128) lc_launch(qkv_gemm_packed_wide_kernel<128>, wgrid, dim3(64 * kGWaves), WideTile::Smem, s, ev, a);
-      else lc_launch(qkv_gemm_packed_wide_kernel<64>, wgrid, dim3(64 * kGWaves), WideTile::Smem, s, ev, a);
+      if (dh == 128) lc_launch<qkv_gemm_packed_wide_kernel<128>>(wgrid, dim3(64 * kGWaves), WideTile::Smem, s, ev, a);
+      else lc_launch<qkv_gemm_packed_wide_kernel<64>>(wgrid, dim3(64 * kGWaves), WideTile::Smem, s, ev, a);
     } else if (tile == kGemmTileHalf) {
       grid.x = (a.F + PackedTile<1>::BN - 1) / PackedTile<1>::BN;
-      if (dh == 128) lc_launch(qkv_gemm_packed_kernel<128, 1>, grid, dim3(64 * kGWaves), PackedTile<1>::Smem, s, ev, a);
-      else lc_launch(qkv_gemm_packed_kernel<64, 1>, grid, dim3(64 * kGWaves), PackedTile<1>::Smem, s, ev, a);
+      if (dh == 128) lc_launch<qkv_gemm_packed_kernel<128, 1>>(grid, dim3(64 * kGWaves), PackedTile<1>::Smem, s, ev, a);
+      else lc_launch<qkv_gemm_packed_kernel<64, 1>>(grid, dim3(64 * kGWaves), PackedTile<1>::Smem, s, ev, a);
     } else {
-      if (dh == 128) lc_launch(qkv_gemm_packed_kernel<128, 2>, grid, dim3(64 * kGWaves), PackedTile<2>::Smem, s, ev, a);
-      else lc_launch(qkv_gemm_packed_kernel<64, 2>, grid, dim3(64 * kGWaves), PackedTile<2>::Smem, s, ev, a);
+      if (dh == 128) lc_launch<qkv_gemm_packed_kernel<128, 2>>(grid, dim3(64 * kGWaves), PackedTile<2>::Smem, s, ev, a);
+      else lc_launch<qkv_gemm_packed_kernel<64, 2>>(grid, dim3(64 * kGWaves), PackedTile<2>::Smem, s, ev, a);
     }
   } else {
-    if (dh == 128) lc_launch(qkv_gemm_bf16_kernel<128>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
-    else lc_launch(qkv_gemm_bf16_kernel<64>, grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
+    if (dh == 128) lc_launch<qkv_gemm_bf16_kernel<128>>(grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
+    else lc_launch<qkv_gemm_bf16_kernel<64>>(grid, dim3(64 * kGWaves), kGemmSmem, s, ev, a);
   }
   return hipGetLastError();
 }

@@ -92,14 +92,22 @@ struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 
-// Launch one kernel on stream s, with events if requested.
-template <typename... KArgs, typename... Args>
-inline void lc_launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned shmem, hipStream_t s,
-                      const LaunchEvents &ev, Args... args) {
+// Launch log (diagnostics): when on, every launch prints its kernel
+// instantiation and grid size to stderr.  Switched on by lacache_create when
+// the environment variable LACACHE_LOG is set to a non-empty value other than
+// "0"; process-wide.
+void set_launch_log(bool on);
+bool launch_log_enabled();
+void log_launch(const void *kernel, hipStream_t s, unsigned grid);
+
+// Launch kernel K on stream s, with events if requested.
+template <auto K, typename... Args>
+inline void lc_launch(dim3 grid, dim3 block, unsigned shmem, hipStream_t s, const LaunchEvents &ev, Args... args) {
+  if (launch_log_enabled()) log_launch(reinterpret_cast<const void *>(K), s, grid.x * grid.y * grid.z);
   if (ev.start)
-    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0, args...);
+    hipExtLaunchKernelGGL(K, grid, block, shmem, s, ev.start, ev.stop, 0, args...);
   else
-    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+    hipLaunchKernelGGL(K, grid, block, shmem, s, args...);
 }
 
 // Launchers: return hipSuccess or the launch error.

@@ -300,7 +300,7 @@ hipError_t launch_qkv(DType dt, const SeqArgs &sa, const QkvArgs &a, int F, hipS
   dim3 block(64 * kQkvWaves);
   const int steps_per_wave = a.D / kQkvWaves / 32;
 #define LC_QKV(TP, TC, SPLIT, U, NG) \
-  lc_launch(qkv_fused_kernel<TP, TC, kQkvNB, kQkvWaves, SPLIT, U, NG>, grid, block, 0, s, ev, sa, a)
+  lc_launch<qkv_fused_kernel<TP, TC, kQkvNB, kQkvWaves, SPLIT, U, NG>>(grid, block, 0, s, ev, sa, a)
   if (dt == kBF16) {
     switch (steps_per_wave) {
       case 2: LC_QKV(bf16_t, f16_t, true, 2, 1); break;

@@ -140,7 +140,9 @@ typedef struct {
  * [block_start, block_end) in positions of the sample.  Rules:
  * 0 <= block_start < block_end <= seq_len <= max_seq_len,
  * block_end - block_start <= 128, row ranges of different samples disjoint
- * and inside [0, n_rows). */
+ * and inside [0, n_rows), seq_offset + seq_len <= 2^31 - 1 (rows are indexed
+ * in 32 bits; byte offsets into the buffers are 64-bit, so a buffer may hold
+ * any number of bytes). */
 typedef struct {
   int32_t seq_offset;
   int32_t seq_len;
@@ -173,7 +175,10 @@ typedef enum {
  * order (within the parity tolerances).  LACACHE_REFRESH_ROWS (64 or 128),
  * also read here, fixes the rows per workgroup of the bf16 refresh attention
  * instead of the choice by launch size (bit-identical results: the rows per
- * workgroup do not change any row's arithmetic). */
+ * workgroup do not change any row's arithmetic).  LACACHE_LOG (non-empty and
+ * not "0"), also read here, makes every later kernel launch of the process
+ * print one line "lacache launch: <kernel instantiation> grid <workgroups>"
+ * to stderr; unset or "0" by the next lacache_create switches it off. */
 LACACHE_API lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out);
 
 /* Frees the context's device memory (synchronises the device first).

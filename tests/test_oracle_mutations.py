@@ -1,0 +1,180 @@
+"""Planted mistakes in the oracle must fail its pins.
+
+Each mutation below replaces one oracle function with a plausibly wrong
+version (a dropped term, a wrong sign, index, base or operand order); with it
+in place, at least one pin of tests/test_oracle_pins.py other than the
+regression fixture (which the oracle itself wrote) must fail.  The mistakes
+are planted in the oracle on the CPU only; no GPU is used.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.lacache_ref as ref
+import test_oracle_pins as pins
+
+
+def _pin_calls():
+    """Every pin as a zero-argument call (parametrized pins expanded)."""
+    calls = []
+    for name in sorted(dir(pins)):
+        fn = getattr(pins, name)
+        if not name.startswith("test_") or not callable(fn) or name == "test_oracle_regression_fixture":
+            continue
+        params = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+        if not params:
+            calls.append((name, fn, {}))
+            continue
+        combos = [{}]
+        for m in params:
+            argnames = [a.strip() for a in m.args[0].split(",")] if isinstance(m.args[0], str) else list(m.args[0])
+            new = []
+            for c in combos:
+                for vals in m.args[1]:
+                    vals = vals if len(argnames) > 1 else (vals,)
+                    new.append({**c, **dict(zip(argnames, vals))})
+            combos = new
+        calls.extend((f"{name}{c}", fn, c) for c in combos)
+    return calls
+
+
+# ---------------------------------------------------------------- mutants ---
+
+def _rms_no_gamma(H, gamma, eps):
+    H = np.asarray(H, np.float64)
+    return H / np.sqrt(np.mean(H * H, axis=-1, keepdims=True) + eps)
+
+
+def _rms_eps_outside(H, gamma, eps):
+    H = np.asarray(H, np.float64)
+    return np.asarray(gamma, np.float64) * H / (np.sqrt(np.mean(H * H, axis=-1, keepdims=True)) + eps)
+
+
+def _qkv_k_v_swapped(Hhat, W, cfg):
+    q, k, v = ref.__dict__["_orig_qkv_project"](Hhat, W, cfg)
+    return q, v, k
+
+
+def _qkv_heads_feature_major(Hhat, W, cfg):
+    y = np.asarray(Hhat, np.float64) @ np.asarray(W, np.float64).T
+    H, Hk, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    q = y[:, : H * d].reshape(-1, d, H).transpose(0, 2, 1)
+    k = y[:, H * d: (H + Hk) * d].reshape(-1, Hk, d)
+    v = y[:, (H + Hk) * d:].reshape(-1, Hk, d)
+    return q, k, v
+
+
+def _rope_angles_half_freq(pos, head_dim, theta):
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.asarray(pos, np.float64)[:, None] * np.power(float(theta), -1.0 * i / head_dim)[None, :]
+
+
+def _rope_wrong_sign(x, pos, theta):
+    x = np.asarray(x, np.float64)
+    half = x.shape[-1] // 2
+    ang = ref.rope_angles(pos, x.shape[-1], theta)[:, None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c + b * s, -a * s + b * c], axis=-1)
+
+
+def _finalize_log2(state):
+    m, l, O = state
+    return O / l[:, None], m + np.log2(l)
+
+
+def _online_alpha_inverted(state, q, k_tile, v_tile, scale):
+    m, l, O = state
+    S = scale * (np.asarray(q, np.float64) @ np.asarray(k_tile, np.float64).T)
+    m_new = np.maximum(m, S.max(axis=1))
+    with np.errstate(invalid="ignore", over="ignore"):
+        alpha = np.where(np.isneginf(m), 0.0, np.exp(m_new - m))
+    P = np.exp(S - m_new[:, None])
+    return m_new, alpha * l + P.sum(axis=1), alpha[:, None] * O + P @ np.asarray(v_tile, np.float64)
+
+
+def _merge_unscaled_second(s1, s2):
+    m1, l1, O1 = s1
+    m2, l2, O2 = s2
+    m = np.maximum(m1, m2)
+    with np.errstate(invalid="ignore"):
+        a1 = np.where(np.isneginf(m1), 0.0, np.exp(m1 - m))
+    return m, a1 * l1 + l2, a1[:, None] * O1 + O2
+
+
+def _facache_all_keys(q, k, v, U, cfg):
+    H, d = cfg.n_heads, cfg.head_dim
+    n = len(q)
+    m = np.empty((len(U), H)); l = np.empty((len(U), H)); O = np.empty((len(U), H, d))
+    for hd in range(H):
+        kh = ref._kv_head(hd, cfg)
+        m[:, hd], l[:, hd], O[:, hd] = ref.state_over_keys(q[U, hd], k[np.arange(n), kh], v[np.arange(n), kh],
+                                                           cfg.scale)
+    return (m, l, O), (O / l[..., None], m + np.log(l))
+
+
+def _kv_head_modulo(h, cfg):
+    return h % cfg.n_kv_heads
+
+
+def _attention_unscaled(q, k, v, scale):
+    return ref.__dict__["_orig_attention"](q, k, v, 1.0)
+
+
+def _cached_step_block_at_zero(params, cfg, cache, block_ids, seqs, kv_tile=16):
+    # RoPE of the block computed at positions 0..B-1 instead of block_start..
+    orig_rope = ref.rope
+
+    def rope_from_zero(x, pos, theta):
+        pos = np.asarray(pos)
+        if len(pos) and len(pos) == len(x) and pos[0] > 0 and np.all(np.diff(pos) == 1) and len(pos) < 64:
+            pos = pos - pos[0]
+        return orig_rope(x, pos, theta)
+
+    ref.rope = rope_from_zero
+    try:
+        return ref.__dict__["_orig_cached_step"](params, cfg, cache, block_ids, seqs, kv_tile)
+    finally:
+        ref.rope = orig_rope
+
+
+MUTATIONS = {
+    "rms_norm drops gamma": ("rms_norm", _rms_no_gamma),
+    "rms_norm eps outside the root": ("rms_norm", _rms_eps_outside),
+    "qkv_project swaps k and v": ("qkv_project", _qkv_k_v_swapped),
+    "qkv_project reads heads feature-major": ("qkv_project", _qkv_heads_feature_major),
+    "rope frequency theta^(-i/d)": ("rope_angles", _rope_angles_half_freq),
+    "rope rotates the wrong way": ("rope", _rope_wrong_sign),
+    "lse in log base 2": ("finalize", _finalize_log2),
+    "online update alpha inverted": ("online_update", _online_alpha_inverted),
+    "merge leaves the second state unscaled": ("merge_states", _merge_unscaled_second),
+    "FACache over all keys": ("facache_canonical", _facache_all_keys),
+    "grouped KV head by modulo": ("_kv_head", _kv_head_modulo),
+    "attention without the scale": ("attention", _attention_unscaled),
+    "cached step ropes the block from position 0": ("cached_step", _cached_step_block_at_zero),
+}
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_planted_mutation_fails_a_pin(mutation, monkeypatch):
+    fname, fn = MUTATIONS[mutation]
+    orig = getattr(ref, fname)
+    monkeypatch.setitem(ref.__dict__, f"_orig_{fname}", orig)
+    monkeypatch.setattr(ref, fname, fn)
+    if hasattr(oracle, fname):
+        monkeypatch.setattr(oracle, fname, fn)
+    failed = []
+    for name, pin, kwargs in _pin_calls():
+        try:
+            pin(**kwargs)
+        except AssertionError:
+            failed.append(name)
+    print(f"{mutation}: fails {failed}")
+    assert failed, f"mutation '{mutation}' passed every pin"
+
+
+def test_pins_pass_without_mutation():
+    for name, pin, kwargs in _pin_calls():
+        pin(**kwargs)

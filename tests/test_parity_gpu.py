@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import attn_check
 import oracle
 from exact_attention_state_amd import lacache, synth
 from exact_attention_state_amd.workload import DeviceWorkload
@@ -60,23 +61,31 @@ def _compare_step(dw, ref, what):
     return stats
 
 
-def _run_full(wl, steps, packed=True):
+def _run_full(wl, steps, packed=True, dw=None):
+    """Refresh, then `steps` inner steps, every row against the oracle (the
+    layer's output bar) and against the attention over the GPU's own cache
+    values (tests/attn_check.py); the device status word must stay clear (no
+    fp16 range overflow, no bad id)."""
     _say(f"[parity] {wl.name}: dtype {wl.dtype} D {wl.d_model} H {wl.n_heads}x{wl.head_dim} "
          f"batch {wl.batch} seq_lens {wl.seq_lens[:4]}... block {wl.block_size} seed {wl.seed} packed {packed}")
-    dw = DeviceWorkload(wl, packed=packed)
+    dw = dw or DeviceWorkload(wl, packed=packed)
     cfg = cfg_of(wl)
     dw.prefill()
     torch.cuda.synchronize()
     ref = oracle.refresh(dw.params, cfg, dw.ids_host, dw.table)
     st = _compare_refresh(dw, ref, f"{wl.name} refresh")
-    _say(f"[parity] {wl.name} refresh ok {st}")
+    at = attn_check.check_all(dw.ct, dw.table, cfg, "refresh", f"{wl.name} refresh", wl.dtype)
+    _say(f"[parity] {wl.name} refresh ok {st} attention-only {at}")
     for s in range(1, steps + 1):
         blk = dw.next_block_ids()
         dw.block_step(blk)
         torch.cuda.synchronize()
         ref = oracle.full_recompute(dw.params, cfg, dw.ids_host, dw.table)
         st = _compare_step(dw, ref, f"{wl.name} step {s}")
-        _say(f"[parity] {wl.name} step {s} ok {st}")
+        at = attn_check.check_all(dw.ct, dw.table, cfg, "step", f"{wl.name} step {s}", wl.dtype)
+        _say(f"[parity] {wl.name} step {s} ok {st} attention-only {at}")
+    flags = dw.ctx.read_device_status()
+    assert flags == 0, f"{wl.name}: device status flags {flags:#x} after the run"
     return dw
 
 
@@ -265,21 +274,29 @@ def _sample_rows(rng, n, bs, be, k):
     return sorted(set(int(r) for r in fixed + rand if 0 <= r < n))
 
 
-def _check_sampled(dw, rng, n_samples, heads, what, k_rows=12):
+def _check_sampled(dw, rng, n_samples, heads, what, k_rows=12, kind="step", tight_rows=64):
+    """Sampled (sample, row, head) outputs against the oracle's layer0_rows; on
+    the same samples, `tight_rows` random rows (plus the block's edges) against
+    the attention over the GPU's own cache values."""
     wl = dw.wl
     cfg = cfg_of(wl)
-    out, lse = host(dw.ct.out), host(dw.ct.lse)
     samples = rng.choice(len(dw.table), size=min(n_samples, len(dw.table)), replace=False)
     worst = {}
+    rep = attn_check.Report()
     for b in samples:
         off, n, bs, be = dw.table[b]
         rows = _sample_rows(rng, n, bs, be, k_rows)
         ref = oracle.layer0_rows(dw.params, cfg, dw.ids_host[off:off + n], rows, heads)
-        got_o = out[off + np.asarray(rows)][:, heads]
-        got_l = lse[off + np.asarray(rows)][:, heads]
+        idx = torch.from_numpy(off + np.asarray(rows)).to(dw.ct.out.device)
+        got_o = host(dw.ct.out.index_select(0, idx))[:, heads]
+        got_l = host(dw.ct.lse.index_select(0, idx))[:, heads]
         st = check_output(got_o, ref["out"], wl.dtype, f"{what} sample {b}")
         check_lse(got_l, ref["lse"], wl.dtype, f"{what} sample {b}")
         worst = {k: max(worst.get(k, 0.0), v) for k, v in st.items()}
+        trows = sorted(set(_sample_rows(rng, n, bs, be, tight_rows)) | {bs, be - 1})
+        attn_check.check_sample(rep, dw.ct, off, n, bs, be, cfg.n_heads, cfg.n_kv_heads, cfg.scale, kind,
+                                rows=trows, heads=heads, what=f"{what} sample {b}")
+    worst["attention_only"] = rep.summary()
     return worst
 
 
@@ -294,21 +311,22 @@ def test_full_size_configs_sampled(name):
     dw = DeviceWorkload(wl)
     dw.prefill()
     torch.cuda.synchronize()
-    _say(f"[parity] {name} refresh {_check_sampled(dw, rng, 3, heads, name + ' refresh')}")
+    _say(f"[parity] {name} refresh {_check_sampled(dw, rng, 3, heads, name + ' refresh', kind='refresh')}")
     for s in range(1, wl.steps + 1):
         blk = dw.next_block_ids()
         dw.block_step(blk)
         if s in (1, wl.steps):
             torch.cuda.synchronize()
             _say(f"[parity] {name} step {s} {_check_sampled(dw, rng, 3, heads, f'{name} step {s}')}")
+    assert dw.ctx.read_device_status() == 0
 
 
-def test_varlen32_dualcache_attention_sampled():
-    """DualCache block-query attention on the variable-length batch (block rows only)."""
-    wl = synth.WORKLOADS["varlen32"]
-    _say(f"[parity] varlen32 dualcache: batch {wl.batch}")
-    dw = DeviceWorkload(wl)
-    dw.prefill()
+def _dualcache_sampled(dw, rng, heads, what, n_samples=4):
+    """DualCache block-query attention over the current caches: sampled samples
+    against the oracle (every block row, `heads`) and against the attention over
+    the GPU's own q/k/v values."""
+    wl = dw.wl
+    cfg = cfg_of(wl)
     crow = np.concatenate([off + np.arange(bs, be) for (off, n, bs, be) in dw.table])
     q_block = dw.ct.q.index_select(0, torch.from_numpy(crow).to("cuda")).contiguous()
     out_block = torch.empty(q_block.shape, dtype=dw.ctx.torch_dtype, device="cuda")
@@ -316,20 +334,73 @@ def test_varlen32_dualcache_attention_sampled():
     ws = dw.ctx.alloc_workspace(lacache.OP_DUALCACHE_ATTN, dw.table)
     dw.ctx.dualcache_attn(q_block, dw.ct.k, dw.ct.v, dw.table, out_block, lse_block, ws)
     torch.cuda.synchronize()
-    # The block rows of the refresh output are the same quantity, computed by another kernel;
-    # the oracle pins both on sampled samples.
-    cfg = cfg_of(wl)
-    rng = np.random.default_rng(5)
-    heads = [1, 16, 30]
     got_o, got_l = host(out_block), host(lse_block)
     row0 = np.cumsum([0] + [be - bs for (_, _, bs, be) in dw.table])
-    for b in rng.choice(len(dw.table), size=4, replace=False):
+    samples = rng.choice(len(dw.table), size=n_samples, replace=False)
+    for b in samples:
         off, n, bs, be = dw.table[b]
-        rows = list(range(bs, be))
-        ref = oracle.layer0_rows(dw.params, cfg, dw.ids_host[off:off + n], rows, heads)
+        ref = oracle.layer0_rows(dw.params, cfg, dw.ids_host[off:off + n], list(range(bs, be)), heads)
         sl = slice(row0[b], row0[b + 1])
-        check_output(got_o[sl][:, heads], ref["out"], wl.dtype, f"dualcache sample {b}")
-        check_lse(got_l[sl][:, heads], ref["lse"], wl.dtype, f"dualcache sample {b}")
+        check_output(got_o[sl][:, heads], ref["out"], wl.dtype, f"{what} sample {b}")
+        check_lse(got_l[sl][:, heads], ref["lse"], wl.dtype, f"{what} sample {b}")
+    at = attn_check.check_block_query(q_block, dw.ct.k, dw.ct.v, dw.table, out_block, lse_block, cfg, what,
+                                      wl.dtype, samples=samples)
+    _say(f"[parity] {what}: samples {sorted(int(x) for x in samples)} ok, attention-only {at}")
+
+
+def test_varlen32_dualcache_attention_sampled():
+    """DualCache block-query attention on the variable-length batch (block rows
+    only) after the refresh, after step 1 and after step 20: the caches the
+    DualCache reads are the block step's, so its output must equal the oracle
+    on the current ids."""
+    wl = synth.WORKLOADS["varlen32"]
+    _say(f"[parity] varlen32 dualcache: batch {wl.batch}")
+    dw = DeviceWorkload(wl)
+    dw.prefill()
+    rng = np.random.default_rng(5)
+    heads = [1, 16, 30]
+    _dualcache_sampled(dw, rng, heads, "varlen32 dualcache after refresh")
+    for s in range(1, wl.steps + 1):
+        dw.block_step(dw.next_block_ids())
+        if s in (1, wl.steps):
+            _dualcache_sampled(dw, rng, heads, f"varlen32 dualcache after step {s}")
+    assert dw.ctx.read_device_status() == 0
+
+
+def test_varlen32_batched_equals_per_sample_within_tolerance():
+    """Each sample of the variable-length batch alone (its own launches, hence
+    its own kernel paths and key chunks) against the same sample inside the
+    32-sample batch, after the refresh and one step: equal within the output
+    bar (the key chunks follow the launch's size, so the two can round
+    differently; identical launches are bitwise equal, tested on small
+    batches)."""
+    wl = synth.WORKLOADS["varlen32"]
+    _say(f"[parity] varlen32 batched vs alone: batch {wl.batch}")
+    dw = DeviceWorkload(wl)
+    dw.prefill()
+    blk = dw.next_block_ids()
+    dw.block_step(blk)
+    torch.cuda.synchronize()
+    worst = {}
+    crow0 = 0
+    # One more cache over the same weights; each sample alone runs in it.
+    one = DeviceWorkload.__new__(DeviceWorkload)
+    one.__dict__.update(dw.__dict__)
+    one.ct = dw.ctx.alloc_cache(dw.n_rows)
+    for b, (off, n, bs, be) in enumerate(dw.table):
+        B = be - bs
+        one.table = [(off, n, bs, be)]
+        one.ids_host = synth.initial_ids(wl)
+        one.prefill()
+        one.ctx.block_step(one.weights, blk[crow0:crow0 + B].contiguous(), one.table, one.ct,
+                           one.ctx.alloc_workspace(lacache.OP_BLOCK_STEP, one.table))
+        torch.cuda.synchronize()
+        rows = slice(off, off + n)
+        st = check_output(host(one.ct.out[rows]), host(dw.ct.out[rows]), wl.dtype, f"sample {b} out")
+        check_lse(host(one.ct.lse[rows]), host(dw.ct.lse[rows]), wl.dtype, f"sample {b} lse")
+        worst = {k: max(worst.get(k, 0.0), v) for k, v in st.items()}
+        crow0 += B
+    _say(f"[parity] varlen32 batched vs alone ok, worst {worst}")
 
 
 # ---------------------------------------------------------------------------
