@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -27,6 +28,7 @@ struct lacache_ctx {
   int split_keys;          // keys per type-A chunk if fixed by LACACHE_SPLIT_KEYS, else 0 (per call)
   int gemm_tile;           // packed GEMM tile fixed by LACACHE_GEMM_TILE (lc::GemmTile), else automatic
   int refresh_rows;        // streaming refresh item rows fixed by LACACHE_REFRESH_ROWS (64 or 128), else 0
+  void *scratch;           // device address of this device's static scratch (lacache_block_step_noalloc)
   std::string last_error;
   // Diagnostics: event pairs stamped by each launch while profiling is on.
   bool profiling = false;
@@ -61,6 +63,34 @@ void log_launch(const void *kernel, hipStream_t s, unsigned grid) {
   std::fprintf(stderr, "lacache launch: %s grid %u\n", name.c_str(), grid);
 }
 }  // namespace lc
+
+// Scratch of lacache_block_step_noalloc (callers that cannot allocate): one
+// array per device, which every GPU the library runs on holds until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device.
+namespace {
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) __attribute__((used)) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on device `dev` (the current device), looked
+// up on the first request for that device.
+hipError_t static_scratch_address(int dev, void **out) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!addr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+}  // namespace
 
 namespace {
 
@@ -407,6 +437,8 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   if (e == hipSuccess) e = hipMemcpy(ctx->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMalloc(&ctx->flags, 256);
   if (e == hipSuccess) e = hipMemset(ctx->flags, 0, 256);
+  ctx->scratch = nullptr;
+  if (e == hipSuccess) e = static_scratch_address(ctx->device, &ctx->scratch);
   if (e == hipSuccess) e = lc::setup_kernel_attributes();
   if (e == hipSuccess) e = lc::setup_gemm_attributes();
   if (e != hipSuccess) {
@@ -833,6 +865,29 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     part_base += sa.pre[3][ns];
   }
   return LACACHE_OK;
+}
+
+lacache_status lacache_block_step_noalloc(lacache_ctx *ctx, const lacache_weights *w, const int32_t *block_ids,
+                                          const lacache_seq *seqs, int32_t batch, const lacache_cache *cache,
+                                          void *out, float *lse, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if (ctx->profiling)
+    return fail(ctx, LACACHE_ERR_INVALID_ARG,
+                "per-kernel profiling is on (it creates events on demand): switch it off for the no-allocation step");
+  if (!ctx->scratch) return fail(ctx, LACACHE_ERR_HIP, "no static scratch on device %d", ctx->device);
+  if ((st = check_weights(ctx, w)) != LACACHE_OK) return st;
+  if ((st = check_cache(ctx, cache, true)) != LACACHE_OK) return st;
+  if ((st = check_table(ctx, seqs, batch, cache->n_rows)) != LACACHE_OK) return st;
+  const size_t need = block_step_bytes(ctx, w, seqs, batch);
+  if (need > kStaticScratchBytes)
+    return fail(ctx, LACACHE_ERR_UNSUPPORTED,
+                "this block table needs %zu bytes of scratch, the static scratch holds %zu: "
+                "use lacache_block_step with a workspace",
+                need, kStaticScratchBytes);
+  return lacache_block_step(ctx, w, block_ids, seqs, batch, cache, out, lse, ctx->scratch, kStaticScratchBytes,
+                            stream);
 }
 
 lacache_status lacache_refresh_block(lacache_ctx *ctx, const lacache_weights *w, const int32_t *proj_ids,

@@ -26,7 +26,7 @@ DEVFLAG_CACHE_RANGE = 2
 EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "lacache_prefill_cache",
             "lacache_block_step", "lacache_refresh_block", "lacache_dualcache_attn", "lacache_read_device_status",
             "lacache_profile_enable", "lacache_profile_read", "lacache_status_string", "lacache_last_error",
-            "lacache_packed_weight_size", "lacache_pack_qkv_weight")
+            "lacache_packed_weight_size", "lacache_pack_qkv_weight", "lacache_block_step_noalloc")
 (KERNEL_QKV, KERNEL_BLOCK_ROWS, KERNEL_INVARIANT_ROWS, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_QKV_PREP,
  KERNEL_QKV_GEMM, KERNEL_ATTN) = range(8)
 KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn", "qkv_prep", "qkv_gemm", "attn")
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
                                        ctypes.POINTER(Cache), P, P, P, SZ, P]),
         "lacache_block_step": (st, [P, ctypes.POINTER(Weights), P, ctypes.POINTER(Seq), I32,
                                     ctypes.POINTER(Cache), P, P, P, SZ, P]),
+        "lacache_block_step_noalloc": (st, [P, ctypes.POINTER(Weights), P, ctypes.POINTER(Seq), I32,
+                                            ctypes.POINTER(Cache), P, P, P]),
         "lacache_refresh_block": (st, [P, ctypes.POINTER(Weights), P, ctypes.POINTER(Seq), ctypes.POINTER(Seq), I32,
                                        ctypes.POINTER(Cache), P, P, P, SZ, P]),
         "lacache_dualcache_attn": (st, [P, P, P, P, I64, ctypes.POINTER(Seq), I32, P, P, P, SZ, P]),
@@ -260,6 +262,16 @@ class Context:
                                          _ptr(ct.lse) if lse else None, _ptr(workspace),
                                          0 if workspace is None else workspace.numel(), _stream(stream))
         self._check(st, "lacache_block_step")
+
+    def block_step_noalloc(self, weights, block_ids, table, ct: CacheTensors, stream=None, lse=True):
+        """lacache_block_step_noalloc: the block step on the library's static scratch (no workspace)."""
+        w = self._weights(*weights)
+        seqs = _seqs(table)
+        cache = self._cache(ct)
+        st = self.lib.lacache_block_step_noalloc(self.handle, ctypes.byref(w), _ptr(self._ids(block_ids)), seqs,
+                                                 len(table), ctypes.byref(cache), _ptr(ct.out),
+                                                 _ptr(ct.lse) if lse else None, _stream(stream))
+        self._check(st, "lacache_block_step_noalloc")
 
     def refresh_block(self, weights, proj_ids, proj_table, table, ct: CacheTensors, workspace=None, stream=None,
                       lse=True):

@@ -225,6 +225,27 @@ LACACHE_API lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_we
                                   void *out, float *lse, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* lacache_block_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Its scratch (the split-KV partial states
+ * and the projection's activation tiles) is a static device array of
+ * 32 MiB (33554432 bytes) that each GPU the library runs on holds from its
+ * first lacache_create on that GPU until the process ends; the call itself
+ * allocates nothing.  Arguments, results and the other errors are those of
+ * lacache_block_step.  Returns LACACHE_ERR_UNSUPPORTED, with nothing
+ * launched, when the block table needs more scratch than that (the message
+ * gives both sizes; lacache_workspace_size(LACACHE_OP_BLOCK_STEP) bounds the
+ * need from above), and LACACHE_ERR_INVALID_ARG while per-kernel profiling is
+ * enabled on the context (its events are created on demand).  Every call on
+ * one GPU shares that GPU's scratch, which keeps the last call's contents (no
+ * kernel needs it cleared: every partial state and activation tile is written
+ * before it is read): calls that overlap on one GPU (other streams, other
+ * threads, other contexts) race and must be serialised by the caller. */
+LACACHE_API lacache_status lacache_block_step_noalloc(lacache_ctx *ctx, const lacache_weights *w,
+                                                      const int32_t *block_ids, const lacache_seq *seqs,
+                                                      int32_t batch, const lacache_cache *cache, void *out,
+                                                      float *lse, void *stream);
+
 /* Refresh at a block boundary when only some rows' ids changed since their
  * last projection (normally the block just finished: its final ids are
  * chosen after its last inner step).  Layer-0 q, k, v of a row depend only on
