@@ -1,9 +1,10 @@
 """Planted mistakes in the oracle must fail its pins.
 
 Each mutation below replaces one oracle function with a plausibly wrong
-version (a dropped term, a wrong sign, index, base or operand order); with it
-in place, at least one pin of tests/test_oracle_pins.py other than the
-regression fixture (which the oracle itself wrote) must fail.  The mistakes
+version (a dropped term, a wrong sign, index, base, rounding or operand
+order); with it in place, at least one pin of tests/test_oracle_pins.py or
+tests/test_fp8_oracle_pins.py other than the regression fixture (which the
+oracle itself wrote) must fail.  The mistakes
 are planted in the oracle on the CPU only; no GPU is used.
 """
 
@@ -11,15 +12,17 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.fp8_ref as q8
 import oracle.lacache_ref as ref
+import test_fp8_oracle_pins as fp8_pins
 import test_oracle_pins as pins
 
 
 def _pin_calls():
     """Every pin as a zero-argument call (parametrized pins expanded)."""
     calls = []
-    for name in sorted(dir(pins)):
-        fn = getattr(pins, name)
+    for mod, name in sorted([(p, n) for p in (pins, fp8_pins) for n in dir(p)], key=lambda x: x[1]):
+        fn = getattr(mod, name)
         if not name.startswith("test_") or not callable(fn) or name == "test_oracle_regression_fixture":
             continue
         params = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
@@ -139,6 +142,49 @@ def _cached_step_block_at_zero(params, cfg, cache, block_ids, seqs, kv_tile=16):
         ref.rope = orig_rope
 
 
+def _round_e4m3_toward_zero(v):
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    idx = np.searchsorted(q8._POS, a, side="right") - 1
+    return np.copysign(q8._POS[idx], v)
+
+
+def _round_e4m3_ties_away(v):
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    hi = np.minimum(np.searchsorted(q8._POS, a, side="left"), len(q8._POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    pick_hi = (q8._POS[hi] - a) <= (a - q8._POS[lo])
+    return np.copysign(np.where(pick_hi, q8._POS[hi], q8._POS[lo]), v)
+
+
+def _quantize_group_scale_times(x32, amax32):
+    # scale = amax * Q_max instead of amax / Q_max
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scale = (amax32 * np.float32(q8.E4M3_MAX)).astype(np.float32)
+        v = np.where(scale == 0, 0, x32 / scale)
+    return q8.round_e4m3(np.clip(v, -448, 448)), scale
+
+
+def _quantize_weight_row_stripes(w, group=128):
+    # one scale per 128 rows over the whole contraction, not per 128 x 128 block
+    w32 = np.asarray(w, np.float64).astype(np.float32)
+    N, K = w32.shape
+    b = w32.reshape(N // group, group, K)
+    amax = np.max(np.abs(b), axis=(1, 2), keepdims=True)
+    q, scale = q8._quantize_group_values(b, amax)
+    return q.reshape(N, K), np.repeat(scale[:, 0, :].astype(np.float64), K // group, axis=1)
+
+
+def _swiglu_swapped(gate, up):
+    return q8.silu(up) * np.asarray(gate, np.float64)
+
+
+def _add_norm_unrounded_residual(h, a, gamma, eps):
+    r = np.asarray(h, np.float64) + np.asarray(a, np.float64)
+    return r, np.asarray(gamma, np.float64) * r / np.sqrt(np.mean(r * r, axis=-1, keepdims=True) + eps)
+
+
 MUTATIONS = {
     "rms_norm drops gamma": ("rms_norm", _rms_no_gamma),
     "rms_norm eps outside the root": ("rms_norm", _rms_eps_outside),
@@ -153,6 +199,12 @@ MUTATIONS = {
     "grouped KV head by modulo": ("_kv_head", _kv_head_modulo),
     "attention without the scale": ("attention", _attention_unscaled),
     "cached step ropes the block from position 0": ("cached_step", _cached_step_block_at_zero),
+    "fp8 rounds toward zero": ("fp8:round_e4m3", _round_e4m3_toward_zero),
+    "fp8 ties away from zero": ("fp8:round_e4m3", _round_e4m3_ties_away),
+    "fp8 scale amax * Q_max": ("fp8:_quantize_group_values", _quantize_group_scale_times),
+    "fp8 weight scale per row stripe": ("fp8:quantize_weight", _quantize_weight_row_stripes),
+    "swiglu gate and up swapped": ("fp8:swiglu", _swiglu_swapped),
+    "residual not rounded to bf16": ("fp8:add_norm", _add_norm_unrounded_residual),
 }
 
 
@@ -160,10 +212,13 @@ MUTATIONS = {
 @pytest.mark.parametrize("mutation", sorted(MUTATIONS))
 def test_planted_mutation_fails_a_pin(mutation, monkeypatch):
     fname, fn = MUTATIONS[mutation]
-    orig = getattr(ref, fname)
-    monkeypatch.setitem(ref.__dict__, f"_orig_{fname}", orig)
-    monkeypatch.setattr(ref, fname, fn)
-    if hasattr(oracle, fname):
+    mod = ref
+    if fname.startswith("fp8:"):
+        mod, fname = q8, fname[4:]
+    orig = getattr(mod, fname)
+    monkeypatch.setitem(mod.__dict__, f"_orig_{fname}", orig)
+    monkeypatch.setattr(mod, fname, fn)
+    if mod is ref and hasattr(oracle, fname):
         monkeypatch.setattr(oracle, fname, fn)
     failed = []
     for name, pin, kwargs in _pin_calls():
