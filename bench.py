@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 MFMA_FP32_PEAK_TFLOPS = 157.3
 
 
@@ -54,6 +55,9 @@ def parse():
     p.add_argument("--refresh-reps", type=int, default=8, help="timed refresh calls (0: skip the refresh timing)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device copy (3 times): the reference for FETCH_SIZE/WRITE_SIZE")
+    p.add_argument("--ffn-rows", default="768,8192",
+                   help="rows of the per-group FP8 FFN measurement (LLaDA-8B FFN shape); empty: skip it")
+    p.add_argument("--ffn-only", action="store_true", help="only the FP8 FFN measurement (its JSON object)")
     return p.parse_args()
 
 
@@ -270,6 +274,90 @@ def measure_refresh(ctx, sets, base, stream, dev, reps, acc, wl, blk):
     return out
 
 
+def ffn_accounting(T, D, F):
+    """Work and algorithmic HBM bytes of one FP8 FFN call per kernel: the
+    AddNorm reads h and the attention output and writes r, the x codes and
+    scales; the gate-up GEMM reads its FP8 weight once plus the x codes and
+    writes the y codes and scales; the down GEMM reads its weight, the y
+    codes, r, and writes out."""
+    Mp = -(-T // 256) * 256
+    return {"ffn_norm": dict(bytes=3 * T * D * 2 + D * 2 + Mp * D + Mp * D // 128 * 4, flops=0),
+            "ffn_gate_up": dict(bytes=2 * F * D + Mp * D + Mp * D // 128 * 4 + Mp * F + Mp * F // 128 * 4,
+                                flops=2 * T * D * 2 * F),
+            "ffn_down": dict(bytes=D * F + Mp * F + Mp * F // 128 * 4 + 2 * T * D * 2, flops=2 * T * F * D)}
+
+
+def measure_ffn(dev, rows_list, reps=20, n_sets=3):
+    """The per-group FP8 FFN of a layer after the first at LLaDA-8B's shape
+    (d_model 4096, d_ff 12288), for each row count: median time per call over
+    `reps` calls cycling `n_sets` independent packed weight sets (150 MB each,
+    so the set a call reads is not left in the 256 MB memory-side cache by the
+    previous call), per-kernel averages from event-bracketed calls, and each
+    GEMM's fraction of the dense FP8 matrix-core peak."""
+    import numpy as np
+    import torch
+    from exact_attention_state_amd import lacache, synth
+    D, F = 4096, synth.LLADA_D_FF
+    ctx = lacache.Context(D, 32, 32, 128, 1000, 64, 5e5, 1e-5, 0.0, "bf16")
+    p = synth.ffn_params(D, F, 2)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).to(dev)
+    g = bf(p["gamma"])
+    sets = []
+    for i in range(n_sets):
+        wg, wu, wd = bf(p["w_gate"]), bf(p["w_up"]), bf(p["w_down"])
+        sets.append(ctx.ffn_pack_weights(F, wg, wu, wd))
+        del wg, wu, wd
+    stream = torch.cuda.Stream(device=dev)
+    res = {"shape": {"d_model": D, "d_ff": F}, "protocol": f"cold ({n_sets} rotating packed weight sets)", "rows": {}}
+    for T in rows_list:
+        h, a = synth.ffn_inputs(T, D, 7)
+        hd, ad = bf(h), bf(a)
+        out, r = torch.empty_like(hd), torch.empty_like(hd)
+        ws = ctx.ffn_workspace(F, T, True, dev)
+
+        def call(i):
+            ctx.ffn_fp8(F, g, sets[i % n_sets], hd, ad, out, r_out=r, workspace=ws, stream=stream)
+
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            ev[i][0].record(stream)
+            call(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = sorted(x.elapsed_time(y) * 1e3 for x, y in ev)[reps // 2]
+        ctx.profile(True)
+        ctx.profile_read()
+        for i in range(reps):
+            call(i)
+        torch.cuda.synchronize()
+        prof = ctx.profile_read()
+        ctx.profile(False)
+        acc = ffn_accounting(T, D, F)
+        kern = {}
+        for k in ("ffn_norm", "ffn_gate_up", "ffn_down"):
+            ms, n = prof[k]
+            t = ms * 1e3 / n
+            e = {"us_avg": t, "hbm_frac": acc[k]["bytes"] / (t * 1e-6) / 1e9 / HBM_PEAK_GBS}
+            if acc[k]["flops"]:
+                e["fp8_mfma_frac"] = acc[k]["flops"] / (t * 1e-6) / (MFMA_FP8_PEAK_TFLOPS * 1e12)
+                e["tflops"] = acc[k]["flops"] / (t * 1e-6) / 1e12
+            kern[k] = e
+        flops = sum(v["flops"] for v in acc.values())
+        res["rows"][str(T)] = {"us_per_call": us, "tflops": flops / (us * 1e-6) / 1e12,
+                               "fp8_mfma_frac": flops / (us * 1e-6) / (MFMA_FP8_PEAK_TFLOPS * 1e12),
+                               "kernels": kern, "algorithmic_bytes": {k: v["bytes"] for k, v in acc.items()},
+                               "flops": {k: v["flops"] for k, v in acc.items()}}
+        log(f"[bench] FP8 FFN rows {T}: {us:.1f} us per call ({flops / (us * 1e-6) / 1e12:.0f} TFLOP/s); "
+            + ", ".join(f"{k} {v['us_avg']:.1f} us" + (f" ({v['fp8_mfma_frac']:.3f} of FP8 peak)" if 'fp8_mfma_frac' in v else "")
+                        for k, v in kern.items()))
+        del hd, ad, out, r, ws
+    assert ctx.read_device_status() == 0
+    return res
+
+
 def host_info():
     """The host the oracle baseline runs on: CPU model, cores, NumPy and its BLAS."""
     import numpy as np
@@ -368,6 +456,11 @@ def main():
     from exact_attention_state_amd import lacache, synth
     from exact_attention_state_amd.workload import DeviceWorkload, to_device_array
 
+    ffn_rows = [int(x) for x in args.ffn_rows.split(",") if x.strip()]
+    if args.ffn_only:
+        torch.cuda.init()
+        print(json.dumps({"ffn_fp8": measure_ffn(torch.device("cuda:0"), ffn_rows)}), flush=True)
+        return
     wl = synth.WORKLOADS[args.workload]
     acc = step_accounting(wl)
     log(f"[bench] workload {wl.name}: batch {wl.batch} N {wl.seq_lens[:4]} block {wl.block_size} "
@@ -554,6 +647,8 @@ def main():
     roof["algorithmic_bytes"] = nbytes
     roof["flops"] = flops
 
+    ffn = measure_ffn(dev, ffn_rows) if ffn_rows else None
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] oracle CPU baseline ...")
@@ -601,6 +696,7 @@ def main():
         "projection": projection_summary(acc, kern, peak_flops),
         "roofline": roof,
         "refresh": refresh,
+        "ffn_fp8": ffn,
         "cpu_baseline": cpu,
         "host": platform.node(),
         "graph_error": graph_err,

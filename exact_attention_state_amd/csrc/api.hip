@@ -29,6 +29,7 @@ struct lacache_ctx {
   int gemm_tile;           // packed GEMM tile fixed by LACACHE_GEMM_TILE (lc::GemmTile), else automatic
   int refresh_rows;        // streaming refresh item rows fixed by LACACHE_REFRESH_ROWS (64 or 128), else 0
   void *scratch;           // device address of this device's static scratch (lacache_block_step_noalloc)
+  int fp8_tile;            // down-projection FP8 GEMM tile fixed by LACACHE_FP8_TILE (1: 256, 2: 128), else 0
   std::string last_error;
   // Diagnostics: event pairs stamped by each launch while profiling is on.
   bool profiling = false;
@@ -419,6 +420,11 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
     lc::set_launch_log(env && env[0] != 0 && std::strcmp(env, "0") != 0);
   }
   ctx->gemm_tile = lc::kGemmTileAuto;
+  ctx->fp8_tile = 0;
+  if (const char *env = std::getenv("LACACHE_FP8_TILE")) {
+    if (!std::strcmp(env, "256")) ctx->fp8_tile = 1;
+    else if (!std::strcmp(env, "128")) ctx->fp8_tile = 2;
+  }
   if (const char *env = std::getenv("LACACHE_GEMM_TILE")) {
     if (!std::strcmp(env, "whole")) ctx->gemm_tile = lc::kGemmTileWhole;
     else if (!std::strcmp(env, "half")) ctx->gemm_tile = lc::kGemmTileHalf;
@@ -441,6 +447,7 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   if (e == hipSuccess) e = static_scratch_address(ctx->device, &ctx->scratch);
   if (e == hipSuccess) e = lc::setup_kernel_attributes();
   if (e == hipSuccess) e = lc::setup_gemm_attributes();
+  if (e == hipSuccess) e = lc::setup_fp8_attributes();
   if (e != hipSuccess) {
     if (ctx->rope) (void)hipFree(ctx->rope);
     if (ctx->flags) (void)hipFree(ctx->flags);
@@ -986,6 +993,152 @@ lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *q_block, con
     row_base += M;
     part_base += sa.pre[3][ns];
   }
+  return LACACHE_OK;
+}
+
+namespace {
+bool ffn_capable(const lacache_ctx *ctx, int32_t d_ff) {
+  return ctx->cfg.dtype == LACACHE_BF16 && ctx->cfg.d_model % 512 == 0 && d_ff >= 128 && d_ff % 128 == 0;
+}
+int64_t ffn_rows_padded(int64_t n) { return (n + 255) / 256 * 256; }
+struct FfnWs {
+  void *xq, *yq, *r;
+  float *sx, *sy;
+};
+// Workspace of one FFN call: x codes [M_pad, D], their scales, y codes
+// [M_pad, F], their scales, and the residual r when the caller keeps none.
+size_t ffn_ws_layout(const lacache_ctx *ctx, int32_t d_ff, int64_t n_rows, bool own_r, void *base, FfnWs *out) {
+  const size_t D = ctx->cfg.d_model, F = d_ff, Mp = (size_t)ffn_rows_padded(n_rows);
+  const size_t sizes[5] = {align256(Mp * D), align256(D / 128 * Mp * 4), align256(Mp * F), align256(F / 128 * Mp * 4),
+                           own_r ? align256((size_t)n_rows * D * 2) : 0};
+  char *p = static_cast<char *>(base);
+  size_t off = 0;
+  void *ptrs[5];
+  for (int i = 0; i < 5; ++i) {
+    ptrs[i] = p ? p + off : nullptr;
+    off += sizes[i];
+  }
+  if (out) {
+    out->xq = ptrs[0];
+    out->sx = static_cast<float *>(ptrs[1]);
+    out->yq = ptrs[2];
+    out->sy = static_cast<float *>(ptrs[3]);
+    out->r = ptrs[4];
+  }
+  return off;
+}
+}  // namespace
+
+lacache_status lacache_ffn_weight_bytes(const lacache_ctx *ctx, int32_t d_ff, size_t *gate_up_bytes,
+                                        size_t *gate_up_scale_bytes, size_t *down_bytes, size_t *down_scale_bytes) {
+  if (!ctx || !gate_up_bytes || !gate_up_scale_bytes || !down_bytes || !down_scale_bytes) return LACACHE_ERR_INVALID_ARG;
+  if (!ffn_capable(ctx, d_ff))
+    return fail(ctx, LACACHE_ERR_UNSUPPORTED, "the FP8 FFN needs bf16, d_model a multiple of 512, d_ff a multiple of 128");
+  const int D = ctx->cfg.d_model;
+  *gate_up_bytes = lc::fp8_packed_bytes(2 * d_ff, D);
+  *gate_up_scale_bytes = (size_t)(D / 128) * (2 * d_ff / 128) * sizeof(float);
+  *down_bytes = lc::fp8_packed_bytes(D, d_ff);
+  *down_scale_bytes = (size_t)(d_ff / 128) * (D / 128) * sizeof(float);
+  return LACACHE_OK;
+}
+
+lacache_status lacache_ffn_pack_weights(lacache_ctx *ctx, int32_t d_ff, const void *w_gate, const void *w_up,
+                                        const void *w_down, void *gate_up, float *s_gate_up, void *down, float *s_down,
+                                        void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if (!ffn_capable(ctx, d_ff))
+    return fail(ctx, LACACHE_ERR_UNSUPPORTED, "the FP8 FFN needs bf16, d_model a multiple of 512, d_ff a multiple of 128");
+  const void *ptrs[7] = {w_gate, w_up, w_down, gate_up, s_gate_up, down, s_down};
+  for (const void *p : ptrs)
+    if (!p || !aligned16(p)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "a weight pointer is NULL or not 16-byte aligned");
+  const int D = ctx->cfg.d_model;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = lc::launch_fp8_pack_weight(w_gate, d_ff, D, 1, gate_up, s_gate_up, 2 * d_ff, s);
+  if (e == hipSuccess) e = lc::launch_fp8_pack_weight(w_up, d_ff, D, 2, gate_up, s_gate_up, 2 * d_ff, s);
+  if (e == hipSuccess) e = lc::launch_fp8_pack_weight(w_down, D, d_ff, 0, down, s_down, D, s);
+  if (e != hipSuccess) return hip_fail(ctx, "FP8 weight packing launch", e);
+  return LACACHE_OK;
+}
+
+lacache_status lacache_ffn_workspace_size(const lacache_ctx *ctx, int32_t d_ff, int64_t n_rows, int32_t keeps_residual,
+                                          size_t *bytes) {
+  if (!ctx || !bytes) return LACACHE_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (!ffn_capable(ctx, d_ff))
+    return fail(ctx, LACACHE_ERR_UNSUPPORTED, "the FP8 FFN needs bf16, d_model a multiple of 512, d_ff a multiple of 128");
+  if (n_rows < 1 || n_rows > (int64_t)1 << 24)
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "n_rows must be in [1, 2^24] (got %lld)", (long long)n_rows);
+  *bytes = ffn_ws_layout(ctx, d_ff, n_rows, !keeps_residual, nullptr, nullptr);
+  return LACACHE_OK;
+}
+
+lacache_status lacache_ffn_fp8(lacache_ctx *ctx, int32_t d_ff, const lacache_ffn_weights *w, const void *h,
+                               const void *attn_out, int64_t n_rows, void *r_out, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if (!ffn_capable(ctx, d_ff))
+    return fail(ctx, LACACHE_ERR_UNSUPPORTED, "the FP8 FFN needs bf16, d_model a multiple of 512, d_ff a multiple of 128");
+  if (!w || !w->gamma || !w->gate_up || !w->s_gate_up || !w->down || !w->s_down)
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "FFN weights or a weight pointer is NULL");
+  const void *ptrs[8] = {w->gamma, w->gate_up, w->s_gate_up, w->down, w->s_down, h, attn_out, out};
+  for (const void *p : ptrs)
+    if (!p || !aligned16(p)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "a pointer is NULL or not 16-byte aligned");
+  if (r_out && !aligned16(r_out)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "r_out is not 16-byte aligned");
+  if (n_rows < 1 || n_rows > (int64_t)1 << 24)
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "n_rows must be in [1, 2^24] (got %lld)", (long long)n_rows);
+  const size_t need = ffn_ws_layout(ctx, d_ff, n_rows, r_out == nullptr, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
+                workspace);
+  FfnWs ws;
+  ffn_ws_layout(ctx, d_ff, n_rows, r_out == nullptr, workspace, &ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = ctx->cfg.d_model, M = (int)n_rows, Mp = (int)ffn_rows_padded(n_rows);
+  lc::Fp8NormArgs na;
+  na.h = h;
+  na.a = attn_out;
+  na.gamma = w->gamma;
+  na.r = r_out ? r_out : ws.r;
+  na.xq = ws.xq;
+  na.sx = ws.sx;
+  na.M = M;
+  na.M_pad = Mp;
+  na.D = D;
+  na.eps = ctx->cfg.rms_eps;
+  hipError_t e = timed(ctx, LACACHE_KERNEL_FFN_NORM, s, [&](const lc::LaunchEvents &ev) { return lc::launch_fp8_addnorm_quant(na, s, ev); });
+  if (e != hipSuccess) return hip_fail(ctx, "FFN AddNorm launch", e);
+  lc::Fp8GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.A = ws.xq;
+  ga.sa = ws.sx;
+  ga.B = w->gate_up;
+  ga.sw = w->s_gate_up;
+  ga.M = M;
+  ga.M_pad = Mp;
+  ga.N = 2 * d_ff;
+  ga.K = D;
+  ga.yq = ws.yq;
+  ga.sy = ws.sy;
+  e = timed(ctx, LACACHE_KERNEL_FFN_GATE_UP, s, [&](const lc::LaunchEvents &ev) { return lc::launch_fp8_gemm_swiglu(ga, s, ev); });
+  if (e != hipSuccess) return hip_fail(ctx, "FFN gate-up launch", e);
+  lc::Fp8GemmArgs gd;
+  std::memset(&gd, 0, sizeof(gd));
+  gd.A = ws.yq;
+  gd.sa = ws.sy;
+  gd.B = w->down;
+  gd.sw = w->s_down;
+  gd.M = M;
+  gd.M_pad = Mp;
+  gd.N = D;
+  gd.K = d_ff;
+  gd.res = na.r;
+  gd.out = out;
+  e = timed(ctx, LACACHE_KERNEL_FFN_DOWN, s, [&](const lc::LaunchEvents &ev) { return lc::launch_fp8_gemm_resid(gd, ctx->fp8_tile, s, ev); });
+  if (e != hipSuccess) return hip_fail(ctx, "FFN down launch", e);
   return LACACHE_OK;
 }
 

@@ -1,0 +1,510 @@
+// Per-group FP8 FFN of the layers after the first (LaCache Section 3.4,
+// "Mixed precision strategy", Eqs. (7)-(8); Figure 2): the feed-forward
+// AddNorm with the quantization of its output fused in, the gate-up linear on
+// FP8 operands with SwiGLU and the quantization of its output fused into the
+// epilogue, and the ffout (down) linear on FP8 operands with the residual add
+// in its epilogue.
+//
+// Quantization (Eqs. (7)-(8)): a group g of 128 activations of one token, or
+// a 128 x 128 block of a weight, gets scale_g = max|x| / 448 and codes
+// E4M3(clip(x / scale_g, -448, 448)), rounded to nearest even by the
+// hardware conversion (OCP E4M3, the FP8 format the gfx950 matrix cores
+// take); scale and x / scale are fp32 (correctly rounded division).
+//
+// FP8 GEMM y = A W^T: one v_mfma 16x16x128 (E4M3 x E4M3, unit block scales)
+// per 16 x 16 output tile and 128-wide group, so every MFMA result is one
+// group's partial product; it is scaled by sa[row, g] * sw[col block, g] and
+// added to fp32 accumulators.  The matrix core's own sum of its 128 products
+// is not exact fp32 (measured: up to 2^-12.4 of sum |a_k b_k|), so the groups
+// are combined in fp32 outside it.
+//
+// Operand layout in memory ("packed", written by the quantization kernels):
+// 256-row tiles (rows of A, or columns of the output = rows of W), then
+// 128-wide groups of the contraction, then 16-row fragments of 2 KB.  In a
+// fragment, lane l (row l % 16, contraction bytes 32 (l / 16) .. +31 of the
+// group) owns 32 bytes, split into two 1 KB halves (its bytes 0-15 at
+// 16 l, 16-31 at 1024 + 16 l), so each half is one full-rate 1 KB copy and
+// one conflict-free 16-byte LDS read per lane.  A 256-row tile's group is a
+// contiguous 32 KB stage.  Activation scales are stored group-major
+// ([K/128][M_pad]) so a stage's row scales are contiguous.
+
+#include "internal.h"
+
+namespace lc {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kF8Frag = 2048;                 // one 16 x 128 FP8 operand fragment
+constexpr int kF8Tile = 16 * kF8Frag;         // 256 rows x one 128-wide group
+constexpr float kE4M3Max = 448.0f;
+
+__host__ __device__ inline size_t fp8_pack_offset(int i, int k, int KG) {
+  const int kk = k & 127;
+  const int lane = ((kk >> 5) << 4) | (i & 15);
+  return ((size_t)(i >> 8) * KG + (k >> 7)) * kF8Tile + ((i >> 4) & 15) * kF8Frag + ((kk >> 4) & 1) * 1024 +
+         lane * 16 + (kk & 15);
+}
+
+// E4M3 code of v (already divided by its scale), clipped to the format's range.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  v = fminf(fmaxf(v, -kE4M3Max), kE4M3Max);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xffu;
+}
+// Codes of four values, packed little-endian in a 32-bit word.
+__device__ __forceinline__ uint32_t e4m3_code4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -kE4M3Max), kE4M3Max);
+  b = fminf(fmaxf(b, -kE4M3Max), kE4M3Max);
+  c = fminf(fmaxf(c, -kE4M3Max), kE4M3Max);
+  d = fminf(fmaxf(d, -kE4M3Max), kE4M3Max);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// Global -> LDS copies with a wave-uniform base address (scalar registers) and
+// a per-lane 32-bit byte offset: lane l moves 16 (4) bytes from base + voff
+// to LDS byte address lds + 16 l (4 l).  One offset register serves every
+// copy of a stage.  Waited for by the caller (vmcnt_wait); M0 is clobbered.
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_s(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
+// In-wave LDS ordering: this wave's LDS writes complete before its later reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" : : : "memory");
+}
+
+__device__ __forceinline__ float wave_max16(float x) {    // max over the 16 lanes of a lane group
+  x = fmaxf(x, __shfl_xor(x, 1));
+  x = fmaxf(x, __shfl_xor(x, 2));
+  x = fmaxf(x, __shfl_xor(x, 4));
+  return fmaxf(x, __shfl_xor(x, 8));
+}
+
+// ---------------------------------------------------------------------------
+// Weight quantization: one workgroup per 128 x 128 block (Eq. (8) over the
+// block), codes written in the packed layout at output row n' = remap(n).
+// mode 0: n' = n; mode 1 / 2: the gate / up half of a gate-up weight, whose
+// 256-row packed tiles hold 128 gate rows then the 128 up rows of the same
+// output features (so one GEMM tile sees both halves of its SwiGLU inputs).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fp8_pack_weight_kernel(const bf16_t *W, int N, int K, int mode, uint8_t *Wp,
+                                                              float *sw, int Np) {
+  __shared__ float s_max[4];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int nb = blockIdx.x, g = blockIdx.y;
+  const int n = nb * 128 + (t >> 1), k0 = g * 128 + 64 * (t & 1);
+  const uint4 *src = reinterpret_cast<const uint4 *>(W + (size_t)n * K + k0);
+  uint4 raw[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) raw[j] = src[j];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t u[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(u[q] << 16)), fabsf(__uint_as_float(u[q] & 0xffff0000u))));
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if (lane == 0) s_max[w] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const float scale = amax / kE4M3Max;
+  const int np = mode == 0 ? n : 256 * (n >> 7) + (mode == 2 ? 128 : 0) + (n & 127);
+  const int KG = K / 128;
+#pragma unroll
+  for (int u4 = 0; u4 < 4; ++u4) {
+    // 16 consecutive contraction elements: one contiguous 16-byte run of the packed layout.
+    uint32_t word[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 r2 = raw[2 * u4 + (q >> 1)];
+      const uint32_t a = (q & 1) ? r2.z : r2.x, b = (q & 1) ? r2.w : r2.y;
+      const float x0 = __uint_as_float(a << 16), x1 = __uint_as_float(a & 0xffff0000u);
+      const float x2 = __uint_as_float(b << 16), x3 = __uint_as_float(b & 0xffff0000u);
+      word[q] = scale > 0.f ? e4m3_code4(x0 / scale, x1 / scale, x2 / scale, x3 / scale) : 0u;
+    }
+    *reinterpret_cast<uint4 *>(Wp + fp8_pack_offset(np, k0 + 16 * u4, KG)) = make_uint4(word[0], word[1], word[2], word[3]);
+  }
+  if (t == 0) sw[(size_t)g * (Np / 128) + np / 128] = scale;
+}
+
+// ---------------------------------------------------------------------------
+// AddNorm + quantization: one wave per token row.  r = bf16(h + a) (the
+// residual stream), x = gamma * r / sqrt(mean(r^2) + eps), then every group of
+// 128 features of x quantized (Eqs. (7)-(8)).  Lane l holds features
+// 512 j + 8 l .. +7; a group is 16 lanes of one 512-feature chunk.  Rows in
+// [M, M_pad) get zero codes and scale 0.
+// ---------------------------------------------------------------------------
+template <int NCH>
+__global__ __launch_bounds__(256) void fp8_addnorm_quant_kernel(const Fp8NormArgs a) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = blockIdx.x * 4 + w;
+  constexpr int D = NCH * 512, KG = D / 128, nch = NCH;
+  const int gl = lane >> 4;                                     // group within the chunk
+  uint8_t *xq = static_cast<uint8_t *>(a.xq);
+  // byte offset of this lane's 8 codes of chunk j
+  auto code_off = [&](int j) {
+    const int k = 512 * j + 8 * lane;
+    return fp8_pack_offset(m, k, KG);
+  };
+  if (m >= a.M) {
+    for (int j = 0; j < nch; ++j) {
+      *reinterpret_cast<uint2 *>(xq + code_off(j)) = make_uint2(0u, 0u);
+      if ((lane & 15) == 0) a.sx[(size_t)(4 * j + gl) * a.M_pad + m] = 0.f;
+    }
+    return;
+  }
+  const bf16_t *h = static_cast<const bf16_t *>(a.h) + (size_t)m * D;
+  const bf16_t *ad = static_cast<const bf16_t *>(a.a) + (size_t)m * D;
+  const bf16_t *gm = static_cast<const bf16_t *>(a.gamma);
+  bf16_t *r = static_cast<bf16_t *>(a.r) + (size_t)m * D;
+  float rv[NCH][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const uint4 hu = *reinterpret_cast<const uint4 *>(h + 512 * j + 8 * lane);
+    const uint4 au = *reinterpret_cast<const uint4 *>(ad + 512 * j + 8 * lane);
+    const uint32_t hw[4] = {hu.x, hu.y, hu.z, hu.w}, aw[4] = {au.x, au.y, au.z, au.w};
+    uint32_t ow[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float s0 = __uint_as_float(hw[q] << 16) + __uint_as_float(aw[q] << 16);
+      const float s1 = __uint_as_float(hw[q] & 0xffff0000u) + __uint_as_float(aw[q] & 0xffff0000u);
+      const bf16_t b0 = f2bf(s0), b1 = f2bf(s1);
+      rv[j][2 * q] = bf2f(b0);
+      rv[j][2 * q + 1] = bf2f(b1);
+      ss = fmaf(rv[j][2 * q], rv[j][2 * q], ss);
+      ss = fmaf(rv[j][2 * q + 1], rv[j][2 * q + 1], ss);
+      ow[q] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+    }
+    *reinterpret_cast<uint4 *>(r + 512 * j + 8 * lane) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o);
+  const float inv = 1.0f / __fsqrt_rn(ss / (float)D + a.eps);
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const uint4 gu = *reinterpret_cast<const uint4 *>(gm + 512 * j + 8 * lane);
+    const uint32_t gw[4] = {gu.x, gu.y, gu.z, gu.w};
+    float x[8], amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x[2 * q] = __uint_as_float(gw[q] << 16) * rv[j][2 * q] * inv;
+      x[2 * q + 1] = __uint_as_float(gw[q] & 0xffff0000u) * rv[j][2 * q + 1] * inv;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = wave_max16(amax);
+    const float scale = amax / kE4M3Max;
+    uint2 c = make_uint2(0u, 0u);
+    if (scale > 0.f) {
+      c.x = e4m3_code4(x[0] / scale, x[1] / scale, x[2] / scale, x[3] / scale);
+      c.y = e4m3_code4(x[4] / scale, x[5] / scale, x[6] / scale, x[7] / scale);
+    }
+    *reinterpret_cast<uint2 *>(xq + code_off(j)) = c;
+    if ((lane & 15) == 0) a.sx[(size_t)(4 * j + gl) * a.M_pad + m] = scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 GEMM: one workgroup of 8 waves per TM x TN output tile; wave w owns rows
+// (w & 1) * TM/2 .. and its WCB column blocks (EPI_RESID: the (w >> 1)-th
+// quarter of the tile's columns; EPI_SWIGLU: gate blocks 2 wn, 2 wn + 1 and
+// the up blocks 8 + 2 wn, 9 + 2 wn of the same output features).  Groups of
+// 128 pass through an NST-stage LDS ring of direct-to-LDS copies.
+// ---------------------------------------------------------------------------
+template <int TM, int TN> struct F8T {
+  static constexpr int RB = TM / 16, CB = TN / 16;
+  static constexpr int A_BYTES = RB * kF8Frag, B_BYTES = CB * kF8Frag, SA_BYTES = TM * 4, SW_BYTES = 256;
+  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SW_BYTES;
+  static constexpr int COPIES = (A_BYTES + B_BYTES) / 1024 / 8;  // 1 KB copies per wave per stage
+  static constexpr int SA_COPIES = SA_BYTES / 256;               // 256-byte row-scale copies (waves 0 ..)
+  // The tile's weight scales of the group (TN / 128 values) are one more
+  // 256-byte copy, by wave 7.
+  static constexpr int WRB = RB / 2, WCB = CB / 4;               // fragments per wave
+  static_assert(COPIES * 8 * 1024 == A_BYTES + B_BYTES, "copies must tile the stage");
+  static_assert(SA_COPIES <= 8, "scale copies");
+};
+
+template <int N> __device__ __forceinline__ void vmcnt_wait_rt(int n) {   // n in [0, N]: runtime -> constant
+  if constexpr (N == 0) {
+    vmcnt_wait<0>();
+  } else {
+    if (n >= N) vmcnt_wait<N>();
+    else vmcnt_wait_rt<N - 1>(n);
+  }
+}
+
+enum { kEpiResid = 0, kEpiSwiglu = 1 };
+
+template <int TM, int TN, int NST, int EPI>
+__global__ __launch_bounds__(512) void fp8_gemm_kernel(const Fp8GemmArgs a) {
+  using L = F8T<TM, TN>;
+  static_assert(EPI != kEpiSwiglu || (TM == 256 && TN == 256), "SwiGLU tiles hold 128 features of both halves");
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w & 1, wn = w >> 1;
+  // Tile order: workgroup wg runs on compute-die wg % 8 (the dispatcher deals
+  // workgroups round-robin over the 8 dies); each die takes a contiguous run
+  // of the tile sequence, which walks groups of kGM row tiles column tile by
+  // column tile.  The ~32 workgroups a die runs at once then share 4 weight
+  // tiles and 8 activation tiles through its L2.
+  const int NX = a.N / TN, MY = a.M_pad / TM, ntiles = NX * MY;
+  const int per_die = (ntiles + 7) / 8;
+  const int wg = blockIdx.x;
+  const int u = (wg & 7) * per_die + (wg >> 3);
+  if (u >= ntiles) return;                                     // whole workgroup: no barrier is skipped by part of it
+  constexpr int kGM = 8;
+  const int grp = u / (kGM * NX), within = u % (kGM * NX);
+  const int gm = min(kGM, MY - grp * kGM);                     // row tiles in this (last, maybe partial) group
+  const int m0 = (grp * kGM + within % gm) * TM, n0 = (within / gm) * TN;
+  const int KG = a.K / 128, NB = a.N / 128;
+  const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  const char *Ab = static_cast<const char *>(a.A) + (size_t)(m0 >> 8) * KG * kF8Tile + ((m0 & 255) >> 4) * kF8Frag;
+  const char *Bb = static_cast<const char *>(a.B) + (size_t)(n0 >> 8) * KG * kF8Tile + ((n0 & 255) >> 4) * kF8Frag;
+  const int my_copies = L::COPIES + (w < L::SA_COPIES ? 1 : 0) + (w == 7 ? 1 : 0);
+
+  const uint32_t voff16 = lane * 16, voff4 = lane * 4, voff_sw = min(lane, TN / 128 - 1) * 4;
+  auto issue = [&](int g) {
+    const uint32_t st = lbase + (g % NST) * L::STAGE;
+    const char *ag = Ab + (size_t)g * kF8Tile, *bg = Bb + (size_t)g * kF8Tile;
+#pragma unroll
+    for (int j = 0; j < L::COPIES; ++j) {
+      const int c = w * L::COPIES + j;
+      const char *src = c < 2 * L::RB ? ag + c * 1024 : bg + (c - 2 * L::RB) * 1024;
+      dma16_s(src, voff16, st + c * 1024);
+    }
+    if (w < L::SA_COPIES) dma4_s(a.sa + (size_t)g * a.M_pad + m0 + w * 64, voff4, st + L::A_BYTES + L::B_BYTES + w * 256);
+    if (w == 7) dma4_s(a.sw + (size_t)g * NB + n0 / 128, voff_sw, st + L::A_BYTES + L::B_BYTES + L::SA_BYTES);
+  };
+  // The wave's column blocks within the tile.
+  auto cb_of = [&](int j) {
+    if constexpr (EPI == kEpiSwiglu) return (j < 2 ? 0 : 8) + 2 * wn + (j & 1);
+    else return wn * L::WCB + j;
+  };
+
+  f32x4_t acc[L::WRB][L::WCB];
+#pragma unroll
+  for (int i = 0; i < L::WRB; ++i)
+#pragma unroll
+    for (int j = 0; j < L::WCB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int pro = KG < NST ? KG : NST;
+  for (int s = 0; s < pro; ++s) issue(s);
+  vmcnt_wait_rt<NST * (L::COPIES + 2)>((pro - 1) * my_copies);
+  lds_barrier();
+
+  for (int g = 0; g < KG; ++g) {
+    const char *st = smem + (g % NST) * L::STAGE;
+    i32x8_t bfr[L::WCB];
+    float swv[L::WCB];
+#pragma unroll
+    for (int j = 0; j < L::WCB; ++j) {
+      const int cb = cb_of(j);
+      const uint4 lo = *reinterpret_cast<const uint4 *>(st + L::A_BYTES + cb * kF8Frag + lane * 16);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(st + L::A_BYTES + cb * kF8Frag + 1024 + lane * 16);
+      bfr[j] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      // wave-uniform: kept in a scalar register
+      swv[j] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                   int, *reinterpret_cast<const float *>(st + L::A_BYTES + L::B_BYTES + L::SA_BYTES + 4 * (cb / 8)))));
+    }
+#pragma unroll
+    for (int i = 0; i < L::WRB; ++i) {
+      const int rb = wm * L::WRB + i;
+      const uint4 lo = *reinterpret_cast<const uint4 *>(st + rb * kF8Frag + lane * 16);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(st + rb * kF8Frag + 1024 + lane * 16);
+      const i32x8_t afr = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const f32x4_t sa4 = *reinterpret_cast<const f32x4_t *>(st + L::A_BYTES + L::B_BYTES + (rb * 16 + 4 * (lane >> 4)) * 4);
+      // The wave's column blocks span one (EPI_RESID with 64 columns, or 32)
+      // or two (EPI_SWIGLU: gate and up) 128-column weight blocks.
+      constexpr int NSW = EPI == kEpiSwiglu ? 2 : 1;
+      f32x4_t sc[NSW];
+#pragma unroll
+      for (int q = 0; q < NSW; ++q) sc[q] = sa4 * swv[q * (L::WCB / NSW)];
+#pragma unroll
+      for (int j = 0; j < L::WCB; ++j) {
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4_t t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0, 127, 0, 127);
+        const f32x4_t s4 = sc[j / (L::WCB / NSW)];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(t[v], s4[v], acc[i][j][v]);
+      }
+      // One row fragment at a time: overlapping the next one's reads would
+      // need registers the 128 x 64 accumulator tile does not leave.
+      if constexpr (L::WRB * L::WCB >= 32) __builtin_amdgcn_sched_barrier(0);
+    }
+    if (g + 1 < KG) {
+      // This wave's copies of group g + 1 landed (later ones may not have);
+      // the barrier publishes the stage and frees stage g for group g + NST.
+      const int behind = (KG - 2 - g) < (NST - 2) ? (KG - 2 - g) : (NST - 2);
+      vmcnt_wait_rt<NST * (L::COPIES + 2)>(behind * my_copies);
+      lds_barrier();
+      if (g + NST < KG) issue(g + NST);
+    }
+  }
+  __syncthreads();                                             // the ring's LDS is free
+
+  if constexpr (EPI == kEpiResid) {
+    // out = bf16(res + acc), staged per 16-row fragment through this wave's
+    // LDS area so global traffic is row-wise 16-byte pieces.
+    constexpr int COLS = 16 * L::WCB, STRIDE = COLS + 4, CPL = COLS / 4;   // CPL columns per lane (8 or 16)
+    float *ws = reinterpret_cast<float *>(smem) + w * 16 * STRIDE;
+    const int rr = lane >> 2, c0 = (lane & 3) * CPL;
+    const int ncol = n0 + wn * COLS + c0;
+#pragma unroll
+    for (int i = 0; i < L::WRB; ++i) {
+#pragma unroll
+      for (int j = 0; j < L::WCB; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ws[(4 * (lane >> 4) + v) * STRIDE + 16 * j + (lane & 15)] = acc[i][j][v];
+      wave_lds_sync();
+      const int m = m0 + (wm * L::WRB + i) * 16 + rr;
+      if (m < a.M) {
+        const bf16_t *res = static_cast<const bf16_t *>(a.res) + (size_t)m * a.N + ncol;
+        bf16_t *out = static_cast<bf16_t *>(a.out) + (size_t)m * a.N + ncol;
+#pragma unroll
+        for (int p = 0; p < CPL / 8; ++p) {
+          const uint4 ru = *reinterpret_cast<const uint4 *>(res + 8 * p);
+          const uint32_t rw[4] = {ru.x, ru.y, ru.z, ru.w};
+          uint32_t ow[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float y0 = ws[rr * STRIDE + c0 + 8 * p + 2 * q] + __uint_as_float(rw[q] << 16);
+            const float y1 = ws[rr * STRIDE + c0 + 8 * p + 2 * q + 1] + __uint_as_float(rw[q] & 0xffff0000u);
+            ow[q] = (uint32_t)f2bf(y0) | ((uint32_t)f2bf(y1) << 16);
+          }
+          *reinterpret_cast<uint4 *>(out + 8 * p) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        }
+      }
+      wave_lds_sync();
+    }
+  } else {
+    // SwiGLU: acc[i][0..1] are gate and acc[i][2..3] up of the same 32
+    // output features of this wave (features 32 wn + 16 jj + lane % 16 of the
+    // tile's 128).  y = silu(gate) * up, one 128-feature group per row over
+    // the 4 waves of a row half: maxima meet in LDS, then codes go to LDS in
+    // the packed layout of the down projection's operand and leave as one
+    // contiguous 32 KB block (rows m0.., group n0 / 256 of the down projection).
+    float *s_amax = reinterpret_cast<float *>(smem);                       // [4 wn][256 rows]
+    uint8_t *s_codes = reinterpret_cast<uint8_t *>(smem) + 4 * 256 * 4;    // 32 KB
+#pragma unroll
+    for (int i = 0; i < L::WRB; ++i) {
+      float pm[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const float gt = acc[i][jj][v], up = acc[i][2 + jj][v];
+          acc[i][jj][v] = gt / (1.0f + fast_exp2(-gt * kLog2e)) * up;
+        }
+        pm[v] = wave_max16(fmaxf(fabsf(acc[i][0][v]), fabsf(acc[i][1][v])));
+      }
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s_amax[wn * 256 + wm * 128 + i * 16 + 4 * (lane >> 4) + v] = pm[v];
+      }
+    }
+    __syncthreads();
+    const int KG2 = a.N / 256;                                 // groups of the down projection's operand
+#pragma unroll
+    for (int i = 0; i < L::WRB; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = wm * 128 + i * 16 + 4 * (lane >> 4) + v;
+        const float amax = fmaxf(fmaxf(s_amax[row], s_amax[256 + row]), fmaxf(s_amax[512 + row], s_amax[768 + row]));
+        const float scale = amax / kE4M3Max;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const uint32_t c = scale > 0.f ? e4m3_code(acc[i][jj][v] / scale) : 0u;
+          s_codes[(wm * 8 + i) * kF8Frag + jj * 1024 + (16 * wn + 4 * (lane >> 4) + v) * 16 + (lane & 15)] = (uint8_t)c;
+        }
+        if (wn == 0 && (lane & 15) == 0) a.sy[(size_t)(n0 / TN) * a.M_pad + m0 + row] = scale;
+      }
+    }
+    __syncthreads();
+    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.yq) + ((size_t)(m0 >> 8) * KG2 + n0 / TN) * kF8Tile);
+    const uint4 *srcl = reinterpret_cast<const uint4 *>(s_codes);
+#pragma unroll
+    for (int p = 0; p < kF8Tile / 16 / 512; ++p) dst[p * 512 + tid] = srcl[p * 512 + tid];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+size_t fp8_packed_bytes(int N, int K) { return (size_t)((N + 255) / 256) * (K / 128) * kF8Tile; }
+
+hipError_t launch_fp8_pack_weight(const void *W, int N, int K, int mode, void *Wp, float *sw, int Np, hipStream_t s) {
+  if (N % 128 || K % 128 || N <= 0 || K <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fp8_pack_weight_kernel, dim3(N / 128, K / 128), dim3(256), 0, s, static_cast<const bf16_t *>(W),
+                     N, K, mode, static_cast<uint8_t *>(Wp), sw, Np);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_addnorm_quant(const Fp8NormArgs &a, hipStream_t s, const LaunchEvents &ev) {
+  if (a.M_pad <= 0) return hipSuccess;
+  if (a.M_pad % 256) return hipErrorInvalidValue;
+  switch (a.D) {
+    case 512: lc_launch<fp8_addnorm_quant_kernel<1>>(dim3(a.M_pad / 4), dim3(256), 0, s, ev, a); break;
+    case 1024: lc_launch<fp8_addnorm_quant_kernel<2>>(dim3(a.M_pad / 4), dim3(256), 0, s, ev, a); break;
+    case 2048: lc_launch<fp8_addnorm_quant_kernel<4>>(dim3(a.M_pad / 4), dim3(256), 0, s, ev, a); break;
+    case 4096: lc_launch<fp8_addnorm_quant_kernel<8>>(dim3(a.M_pad / 4), dim3(256), 0, s, ev, a); break;
+    case 8192: lc_launch<fp8_addnorm_quant_kernel<16>>(dim3(a.M_pad / 4), dim3(256), 0, s, ev, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int TM, int TN, int NST> constexpr int fp8_gemm_smem() { return NST * F8T<TM, TN>::STAGE; }
+// Workgroups for `tiles` output tiles: a multiple of the 8 compute dies (the
+// kernel's tile order gives each die a contiguous run; surplus workgroups exit).
+inline unsigned fp8_grid(int tiles) { return (unsigned)((tiles + 7) / 8 * 8); }
+
+hipError_t launch_fp8_gemm_swiglu(const Fp8GemmArgs &a, hipStream_t s, const LaunchEvents &ev) {
+  if (a.M_pad <= 0) return hipSuccess;
+  if (a.N % 256 || a.K % 128 || a.M_pad % 256) return hipErrorInvalidValue;
+  lc_launch<fp8_gemm_kernel<256, 256, 2, kEpiSwiglu>>(dim3(fp8_grid(a.N / 256 * (a.M_pad / 256))), dim3(512),
+                                                      fp8_gemm_smem<256, 256, 2>(), s, ev, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm_resid(const Fp8GemmArgs &a, int tile, hipStream_t s, const LaunchEvents &ev) {
+  if (a.M_pad <= 0) return hipSuccess;
+  if (a.N % 256 || a.K % 128 || a.M_pad % 256) return hipErrorInvalidValue;
+  // 256 x 256 tiles when they give every compute unit a workgroup, else 128 x 128.
+  const bool big = tile == 1 || (tile == 0 && (a.N / 256) * (a.M_pad / 256) >= device_cus());
+  if (big)
+    lc_launch<fp8_gemm_kernel<256, 256, 2, kEpiResid>>(dim3(fp8_grid(a.N / 256 * (a.M_pad / 256))), dim3(512),
+                                                       fp8_gemm_smem<256, 256, 2>(), s, ev, a);
+  else
+    lc_launch<fp8_gemm_kernel<128, 128, 4, kEpiResid>>(dim3(fp8_grid(a.N / 128 * (a.M_pad / 128))), dim3(512),
+                                                       fp8_gemm_smem<128, 128, 4>(), s, ev, a);
+  return hipGetLastError();
+}
+
+hipError_t setup_fp8_attributes() {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fp8_gemm_kernel<256, 256, 2, kEpiSwiglu>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, fp8_gemm_smem<256, 256, 2>());
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(fp8_gemm_kernel<256, 256, 2, kEpiResid>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, fp8_gemm_smem<256, 256, 2>());
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(fp8_gemm_kernel<128, 128, 4, kEpiResid>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, fp8_gemm_smem<128, 128, 4>());
+  return e;
+}
+
+}  // namespace lc

@@ -151,6 +151,36 @@ hipError_t launch_refresh_stream(int dh, int mb, const SeqArgs &sa, const AttnAr
                                  const LaunchEvents &ev);
 hipError_t setup_kernel_attributes();
 
+// Per-group FP8 FFN (layers after the first): AddNorm + quantization, FP8
+// GEMMs with SwiGLU + quantization or residual epilogues, weight packing.
+struct Fp8NormArgs {
+  const void *h, *a;       // [M, D] bf16: residual stream and the attention block's output
+  const void *gamma;       // [D] bf16
+  void *r;                 // [M, D] bf16: r = bf16(h + a)
+  void *xq;                // packed FP8 codes of RMSNorm(r) (M_pad rows)
+  float *sx;               // [D/128][M_pad] scales
+  int M, M_pad, D;
+  float eps;
+};
+struct Fp8GemmArgs {
+  const void *A;           // packed FP8 activations (M_pad rows, K contraction)
+  const float *sa;         // [K/128][M_pad]
+  const void *B;           // packed FP8 weight (N rows, K contraction)
+  const float *sw;         // [K/128][N/128]
+  int M, M_pad, N, K;
+  void *yq;                // SwiGLU epilogue: packed FP8 of silu(gate) * up (M_pad rows, N/2 contraction)
+  float *sy;               //   [N/256][M_pad]
+  const void *res;         // residual epilogue: out = bf16(res + A W^T), [M, N] bf16
+  void *out;
+};
+size_t fp8_packed_bytes(int N, int K);                     // bytes of a packed FP8 operand of N rows
+hipError_t launch_fp8_pack_weight(const void *W, int N, int K, int mode, void *Wp, float *sw, int Np, hipStream_t s);
+hipError_t launch_fp8_addnorm_quant(const Fp8NormArgs &a, hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_fp8_gemm_swiglu(const Fp8GemmArgs &a, hipStream_t s, const LaunchEvents &ev);
+// tile: 0 automatic, 1 = 256 x 256, 2 = 128 x 128
+hipError_t launch_fp8_gemm_resid(const Fp8GemmArgs &a, int tile, hipStream_t s, const LaunchEvents &ev);
+hipError_t setup_fp8_attributes();
+
 // Work decomposition shared by the planner and the kernels.
 constexpr int kRowsA = 32;     // block rows per type-A item
 constexpr int kRowsB = 64;     // invariant rows per type-B item

@@ -26,10 +26,12 @@ DEVFLAG_CACHE_RANGE = 2
 EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "lacache_prefill_cache",
             "lacache_block_step", "lacache_refresh_block", "lacache_dualcache_attn", "lacache_read_device_status",
             "lacache_profile_enable", "lacache_profile_read", "lacache_status_string", "lacache_last_error",
-            "lacache_packed_weight_size", "lacache_pack_qkv_weight", "lacache_block_step_noalloc")
+            "lacache_packed_weight_size", "lacache_pack_qkv_weight", "lacache_block_step_noalloc",
+            "lacache_ffn_weight_bytes", "lacache_ffn_pack_weights", "lacache_ffn_workspace_size", "lacache_ffn_fp8")
 (KERNEL_QKV, KERNEL_BLOCK_ROWS, KERNEL_INVARIANT_ROWS, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_QKV_PREP,
- KERNEL_QKV_GEMM, KERNEL_ATTN) = range(8)
-KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn", "qkv_prep", "qkv_gemm", "attn")
+ KERNEL_QKV_GEMM, KERNEL_ATTN, KERNEL_FFN_NORM, KERNEL_FFN_GATE_UP, KERNEL_FFN_DOWN) = range(11)
+KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn", "qkv_prep", "qkv_gemm", "attn",
+                "ffn_norm", "ffn_gate_up", "ffn_down")
 
 
 class Config(ctypes.Structure):
@@ -48,6 +50,11 @@ class Cache(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("m", ctypes.c_void_p), ("l", ctypes.c_void_p), ("o", ctypes.c_void_p),
                 ("n_rows", ctypes.c_int64)]
+
+
+class FfnWeights(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_void_p), ("gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
+                ("down", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
 
 
 class Seq(ctypes.Structure):
@@ -89,6 +96,11 @@ def load_library(path: str = LIB_PATH):
         "lacache_dualcache_attn": (st, [P, P, P, P, I64, ctypes.POINTER(Seq), I32, P, P, P, SZ, P]),
         "lacache_packed_weight_size": (st, [P, ctypes.POINTER(SZ)]),
         "lacache_pack_qkv_weight": (st, [P, P, P, SZ, P]),
+        "lacache_ffn_weight_bytes": (st, [P, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ),
+                                          ctypes.POINTER(SZ)]),
+        "lacache_ffn_pack_weights": (st, [P, I32, P, P, P, P, P, P, P, P]),
+        "lacache_ffn_workspace_size": (st, [P, I32, I64, I32, ctypes.POINTER(SZ)]),
+        "lacache_ffn_fp8": (st, [P, I32, ctypes.POINTER(FfnWeights), P, P, I64, P, P, P, SZ, P]),
         "lacache_read_device_status": (st, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
         "lacache_profile_enable": (st, [P, ctypes.c_int]),
         "lacache_profile_read": (st, [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
@@ -297,6 +309,49 @@ class Context:
                                              len(table), _ptr(out_block), _ptr(lse_block), _ptr(workspace),
                                              0 if workspace is None else workspace.numel(), _stream(stream))
         self._check(st, "lacache_dualcache_attn")
+
+    # ------------------------------------------------------------------
+    # Per-group FP8 FFN of the layers after the first
+    def ffn_pack_weights(self, d_ff, w_gate, w_up, w_down, stream=None):
+        """Quantize a layer's FFN weights (bf16 CUDA tensors) to the packed FP8 form:
+        returns (gate_up uint8, s_gate_up float32, down uint8, s_down float32) CUDA tensors."""
+        n = [ctypes.c_size_t() for _ in range(4)]
+        self._check(self.lib.lacache_ffn_weight_bytes(self.handle, d_ff, *[ctypes.byref(x) for x in n]),
+                    "lacache_ffn_weight_bytes")
+        D = self.cfg.d_model
+        for name, t, shape in (("w_gate", w_gate, (d_ff, D)), ("w_up", w_up, (d_ff, D)), ("w_down", w_down, (D, d_ff))):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor of shape {shape}")
+        dev = w_gate.device
+        gu = torch.empty(n[0].value, dtype=torch.uint8, device=dev)
+        sgu = torch.empty(n[1].value // 4, dtype=torch.float32, device=dev)
+        dn = torch.empty(n[2].value, dtype=torch.uint8, device=dev)
+        sdn = torch.empty(n[3].value // 4, dtype=torch.float32, device=dev)
+        self._check(self.lib.lacache_ffn_pack_weights(self.handle, d_ff, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                                      _ptr(gu), _ptr(sgu), _ptr(dn), _ptr(sdn), _stream(stream)),
+                    "lacache_ffn_pack_weights")
+        return gu, sgu, dn, sdn
+
+    def ffn_workspace(self, d_ff, n_rows, keeps_residual=True, device="cuda"):
+        n = ctypes.c_size_t()
+        self._check(self.lib.lacache_ffn_workspace_size(self.handle, d_ff, n_rows, int(bool(keeps_residual)),
+                                                        ctypes.byref(n)), "lacache_ffn_workspace_size")
+        return torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+
+    def ffn_fp8(self, d_ff, gamma, packed, h, attn_out, out, r_out=None, workspace=None, stream=None):
+        """One FP8 FFN sub-block: out = bf16(r + down(swiglu(gate_up(RMSNorm(r))))) with r = bf16(h + attn_out)."""
+        gu, sgu, dn, sdn = packed
+        for name, t in (("gamma", gamma), ("h", h), ("attn_out", attn_out), ("out", out)):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+        if h.shape != attn_out.shape or h.shape != out.shape or (r_out is not None and r_out.shape != h.shape):
+            raise ValueError("h, attn_out, out (and r_out) must have the same shape [n_rows, d_model]")
+        w = FfnWeights(gamma.data_ptr(), gu.data_ptr(), sgu.data_ptr(), dn.data_ptr(), sdn.data_ptr())
+        ws = workspace if workspace is not None else self.ffn_workspace(d_ff, h.shape[0], r_out is not None, h.device)
+        st = self.lib.lacache_ffn_fp8(self.handle, d_ff, ctypes.byref(w), _ptr(h), _ptr(attn_out), h.shape[0],
+                                      _ptr(r_out), _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+        self._check(st, "lacache_ffn_fp8")
+        return ws
 
     def profile(self, enable: bool):
         """Bracket every launch with HIP events (diagnostics)."""

@@ -241,3 +241,32 @@ def block_ids_of(wl: Workload, ids: np.ndarray) -> np.ndarray:
 
 def with_steps(wl: Workload, steps: int) -> Workload:
     return replace(wl, steps=steps)
+
+
+# ----------------------------------------------------------------------------
+# The FFN of a layer after the first (per-group FP8): weights and inputs
+# ----------------------------------------------------------------------------
+
+# LLaDA-8B's feed-forward width (SwiGLU, d_model 4096).
+LLADA_D_FF = 12288
+_S_FFN_W, _S_FFN_X = 6, 7
+
+
+def ffn_params(d_model: int, d_ff: int, family: int = 0) -> dict:
+    """RMSNorm gain gamma [D] ~ 1 + N(0, 0.1), w_gate, w_up [F, D] and w_down
+    [D, F] ~ N(0, 0.02), drawn in fp32 and rounded to bf16 (float32 arrays)."""
+    rng = np.random.default_rng([BASE_SEED, 50 + family, _S_FFN_W, d_model, d_ff])
+    gamma = round_to_bf16(1.0 + rng.standard_normal(d_model, dtype=np.float32) * np.float32(0.1))
+    w_gate = round_to_bf16(rng.standard_normal((d_ff, d_model), dtype=np.float32) * np.float32(0.02))
+    w_up = round_to_bf16(rng.standard_normal((d_ff, d_model), dtype=np.float32) * np.float32(0.02))
+    w_down = round_to_bf16(rng.standard_normal((d_model, d_ff), dtype=np.float32) * np.float32(0.02))
+    return {"gamma": gamma, "w_gate": w_gate, "w_up": w_up, "w_down": w_down}
+
+
+def ffn_inputs(n_rows: int, d_model: int, seed: int = 0):
+    """The residual stream h [T, D] ~ N(0, 1) and the attention block's output
+    a [T, D] ~ N(0, 0.5^2), bf16 values (float32 arrays)."""
+    rng = np.random.default_rng([BASE_SEED, 60 + seed, _S_FFN_X, n_rows, d_model])
+    h = round_to_bf16(rng.standard_normal((n_rows, d_model), dtype=np.float32))
+    a = round_to_bf16(rng.standard_normal((n_rows, d_model), dtype=np.float32) * np.float32(0.5))
+    return h, a

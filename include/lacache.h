@@ -287,6 +287,73 @@ LACACHE_API lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *
                                       void *workspace, size_t workspace_bytes,
                                       void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Per-group FP8 FFN of the layers after the first (LaCache Section 3.4,
+ * "Mixed precision strategy", Eqs. (7)-(8), and Figure 2): per-group FP8
+ * quantization before the gate-up and ffout linears, fused with the
+ * feed-forward AddNorm and with SwiGLU, and both linears on FP8 operands.
+ *   Quantization: groups of 128 consecutive features of one token
+ *   (activations) or 128 x 128 blocks (weights); scale = max |x| / 448 and
+ *   code = E4M3(clip(x / scale, -448, 448)), OCP E4M3, round to nearest
+ *   even, scale and x / scale in fp32; an all-zero group has scale 0.
+ *   Layer: r = bf16(h + attn_out); x = RMSNorm(r) with gamma and the
+ *   context's rms_eps; [gate; up] = Q(x) Q(W_gate_up)^T; y = silu(gate) * up;
+ *   out = bf16(r + Q(y) Q(W_down)^T), every product of quantized operands
+ *   dequantized group by group in fp32.
+ * The context must be bf16 with d_model a multiple of 512; d_ff a multiple of
+ * 128.  Shapes: w_gate, w_up [d_ff, d_model] bf16, w_down [d_model, d_ff]
+ * bf16 (row-major, out-features major), gamma [d_model] bf16; h, attn_out,
+ * r_out, out [n_rows, d_model] bf16.  The FFN runs on whole sequences: the
+ * rows of the layer (no block table). */
+typedef struct {
+  const void *gamma;         /* feed-forward RMSNorm gain, [d_model] bf16               */
+  const void *gate_up;       /* packed FP8 [w_gate; w_up] (lacache_ffn_pack_weights)    */
+  const float *s_gate_up;    /* its block scales                                        */
+  const void *down;          /* packed FP8 w_down                                       */
+  const float *s_down;       /* its block scales                                        */
+} lacache_ffn_weights;
+
+/* Bytes of the packed FP8 weights and of their block scales for d_ff. */
+LACACHE_API lacache_status lacache_ffn_weight_bytes(const lacache_ctx *ctx, int32_t d_ff, size_t *gate_up_bytes,
+                                                    size_t *gate_up_scale_bytes, size_t *down_bytes,
+                                                    size_t *down_scale_bytes);
+
+/* Enqueues the one-time quantization of a layer's FFN weights (device, bf16)
+ * into the packed FP8 form lacache_ffn_fp8 reads (device, caller-owned, at
+ * least the sizes above), with one fp32 scale per 128 x 128 block. */
+LACACHE_API lacache_status lacache_ffn_pack_weights(lacache_ctx *ctx, int32_t d_ff, const void *w_gate,
+                                                    const void *w_up, const void *w_down, void *gate_up,
+                                                    float *s_gate_up, void *down, float *s_down, void *stream);
+
+/* Workspace bytes of lacache_ffn_fp8 for n_rows rows (1 <= n_rows <= 2^24);
+ * keeps_residual: whether the call will be given r_out (else r lives in the
+ * workspace). */
+LACACHE_API lacache_status lacache_ffn_workspace_size(const lacache_ctx *ctx, int32_t d_ff, int64_t n_rows,
+                                                      int32_t keeps_residual, size_t *bytes);
+
+/* One FFN sub-block: writes out (and r_out unless NULL) for every row.  The
+ * diagnostic environment variable LACACHE_FP8_TILE ("256" or "128"), read by
+ * lacache_create, fixes the down projection's output tile instead of the
+ * choice by launch size.
+ * Packed FP8 layout (the weights, and the quantized activations in the
+ * workspace): element (i, k) of an [N rows, K] operand (i: a row of the
+ * activations or an output feature of the weight, k: the contraction index)
+ * is byte ((i/256) (K/128) + k/128) 32768 + ((i/16) % 16) 2048 +
+ * ((k/16) % 2) 1024 + (16 ((k % 128)/32) + i % 16) 16 + k % 16 (N padded to a
+ * multiple of 256 with zero codes).  The packed gate-up weight holds, in its
+ * 256-row tile j, rows 128 j .. 128 j + 127 of w_gate then the same rows of
+ * w_up; its scales are [d_model/128][2 d_ff/128] with column 2 j for the gate
+ * block and 2 j + 1 for the up block of tile j; the down weight's scales are
+ * [d_ff/128][d_model/128].
+ * Workspace after the call (M_pad = n_rows rounded up to 256; each part
+ * starts at a multiple of 256 bytes, in this order): the packed codes of
+ * x = RMSNorm(r) [M_pad, d_model]; their scales [d_model/128][M_pad] fp32;
+ * the packed codes of y = silu(gate) * up [M_pad, d_ff]; their scales
+ * [d_ff/128][M_pad] fp32; r [n_rows, d_model] bf16 when r_out is NULL. */
+LACACHE_API lacache_status lacache_ffn_fp8(lacache_ctx *ctx, int32_t d_ff, const lacache_ffn_weights *w,
+                                           const void *h, const void *attn_out, int64_t n_rows, void *r_out,
+                                           void *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of the packed projection weight for this context: 0 where the
  * configuration has no many-token projection (fp32, or d_model not a
  * multiple of 512). */
@@ -326,7 +393,10 @@ typedef enum {
   LACACHE_KERNEL_QKV_GEMM = 6,       /* prep'd tokens: QKV GEMM + RoPE + cache write */
   LACACHE_KERNEL_ATTN = 7,           /* small block steps: block-row partials and
                                         invariant rows in one launch               */
-  LACACHE_KERNEL_COUNT = 8
+  LACACHE_KERNEL_FFN_NORM = 8,       /* FP8 FFN: AddNorm + quantization             */
+  LACACHE_KERNEL_FFN_GATE_UP = 9,    /* FP8 FFN: gate-up GEMM + SwiGLU + quantization */
+  LACACHE_KERNEL_FFN_DOWN = 10,      /* FP8 FFN: down GEMM + residual               */
+  LACACHE_KERNEL_COUNT = 11
 } lacache_kernel;
 
 LACACHE_API lacache_status lacache_profile_enable(lacache_ctx *ctx, int enable);
