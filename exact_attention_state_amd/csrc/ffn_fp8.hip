@@ -77,6 +77,19 @@ __device__ __forceinline__ void dma4_s(const void *base, uint32_t voff, uint32_t
                : "memory", "m0");
 }
 
+// x << sh, recomputed where it is used: a loop holding every copy offset in
+// its own register across the main loop runs out of registers.
+__device__ __forceinline__ uint32_t lane_bytes(int x, int sh) {
+  uint32_t r;
+  asm volatile("v_lshlrev_b32 %0, %1, %2" : "=v"(r) : "i"(sh), "v"(x));
+  return r;
+}
+
+// Value of lane 4 (l / 4) + v in lane l (a DPP quad permutation).
+template <int V> __device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), V * 0x55, 0xf, 0xf, false));
+}
+
 // In-wave LDS ordering: this wave's LDS writes complete before its later reads.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0)
@@ -277,7 +290,6 @@ __global__ __launch_bounds__(512) void fp8_gemm_kernel(const Fp8GemmArgs a) {
   const char *Bb = static_cast<const char *>(a.B) + (size_t)(n0 >> 8) * KG * kF8Tile + ((n0 & 255) >> 4) * kF8Frag;
   const int my_copies = L::COPIES + (w < L::SA_COPIES ? 1 : 0) + (w == 7 ? 1 : 0);
 
-  const uint32_t voff16 = lane * 16, voff4 = lane * 4, voff_sw = min(lane, TN / 128 - 1) * 4;
   auto issue = [&](int g) {
     const uint32_t st = lbase + (g % NST) * L::STAGE;
     const char *ag = Ab + (size_t)g * kF8Tile, *bg = Bb + (size_t)g * kF8Tile;
@@ -285,10 +297,10 @@ __global__ __launch_bounds__(512) void fp8_gemm_kernel(const Fp8GemmArgs a) {
     for (int j = 0; j < L::COPIES; ++j) {
       const int c = w * L::COPIES + j;
       const char *src = c < 2 * L::RB ? ag + c * 1024 : bg + (c - 2 * L::RB) * 1024;
-      dma16_s(src, voff16, st + c * 1024);
+      dma16_s(src, lane_bytes(lane, 4), st + c * 1024);
     }
-    if (w < L::SA_COPIES) dma4_s(a.sa + (size_t)g * a.M_pad + m0 + w * 64, voff4, st + L::A_BYTES + L::B_BYTES + w * 256);
-    if (w == 7) dma4_s(a.sw + (size_t)g * NB + n0 / 128, voff_sw, st + L::A_BYTES + L::B_BYTES + L::SA_BYTES);
+    if (w < L::SA_COPIES) dma4_s(a.sa + (size_t)g * a.M_pad + m0 + w * 64, lane_bytes(lane, 2), st + L::A_BYTES + L::B_BYTES + w * 256);
+    if (w == 7) dma4_s(a.sw + (size_t)g * NB + n0 / 128, lane_bytes(min(lane, TN / 128 - 1), 2), st + L::A_BYTES + L::B_BYTES + L::SA_BYTES);
   };
   // The wave's column blocks within the tile.
   auto cb_of = [&](int j) {
@@ -309,6 +321,16 @@ __global__ __launch_bounds__(512) void fp8_gemm_kernel(const Fp8GemmArgs a) {
 
   for (int g = 0; g < KG; ++g) {
     const char *st = smem + (g % NST) * L::STAGE;
+    // Operands of the first MFMA first: row fragment 0, then the column
+    // fragments, then the row scales.
+    i32x8_t afr[2];
+    auto load_a = [&](int i) {
+      const int rb = wm * L::WRB + i;
+      const uint4 lo = *reinterpret_cast<const uint4 *>(st + rb * kF8Frag + lane * 16);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(st + rb * kF8Frag + 1024 + lane * 16);
+      afr[i & 1] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    load_a(0);
     i32x8_t bfr[L::WCB];
     float swv[L::WCB];
 #pragma unroll
@@ -321,31 +343,72 @@ __global__ __launch_bounds__(512) void fp8_gemm_kernel(const Fp8GemmArgs a) {
       swv[j] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                    int, *reinterpret_cast<const float *>(st + L::A_BYTES + L::B_BYTES + L::SA_BYTES + 4 * (cb / 8)))));
     }
+    // Row scales: an MFMA result's lane l holds rows 4 (l / 16) + v, v < 4,
+    // of its 16-row block.  Lane l reads the scale of row 4 (l / 16) + l % 4,
+    // so the four lanes of each quad hold exactly the four rows their
+    // results need; a quad broadcast hands value v to every lane of the quad.
+    // One 4-byte read per lane and row block instead of a replicated 16-byte one.
+    float sar[L::WRB];
 #pragma unroll
-    for (int i = 0; i < L::WRB; ++i) {
-      const int rb = wm * L::WRB + i;
-      const uint4 lo = *reinterpret_cast<const uint4 *>(st + rb * kF8Frag + lane * 16);
-      const uint4 hi = *reinterpret_cast<const uint4 *>(st + rb * kF8Frag + 1024 + lane * 16);
-      const i32x8_t afr = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const f32x4_t sa4 = *reinterpret_cast<const f32x4_t *>(st + L::A_BYTES + L::B_BYTES + (rb * 16 + 4 * (lane >> 4)) * 4);
-      // The wave's column blocks span one (EPI_RESID with 64 columns, or 32)
-      // or two (EPI_SWIGLU: gate and up) 128-column weight blocks.
-      constexpr int NSW = EPI == kEpiSwiglu ? 2 : 1;
-      f32x4_t sc[NSW];
+    for (int i = 0; i < L::WRB; ++i)
+      sar[i] = *reinterpret_cast<const float *>(st + L::A_BYTES + L::B_BYTES +
+                                                ((wm * L::WRB + i) * 16 + 4 * (lane >> 4) + (lane & 3)) * 4);
+    // The wave's column blocks span one (EPI_RESID with 64 columns, or 32)
+    // or two (EPI_SWIGLU: gate and up) 128-column weight blocks.
+    constexpr int NSW = EPI == kEpiSwiglu ? 2 : 1, PER = L::WCB / NSW;
+    // Scale of each lane's four result rows times the weight block's scale,
+    // prepared one row block ahead of its FMAs.
+    f32x4_t sc[2][NSW];
+    auto prep = [&](int i) {
 #pragma unroll
-      for (int q = 0; q < NSW; ++q) sc[q] = sa4 * swv[q * (L::WCB / NSW)];
-#pragma unroll
-      for (int j = 0; j < L::WCB; ++j) {
-        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4_t t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0, 127, 0, 127);
-        const f32x4_t s4 = sc[j / (L::WCB / NSW)];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(t[v], s4[v], acc[i][j][v]);
+      for (int u = 0; u < NSW; ++u) {
+        const float s1 = sar[i] * swv[u * PER];
+        sc[i & 1][u] = f32x4_t{quad_bcast<0>(s1), quad_bcast<1>(s1), quad_bcast<2>(s1), quad_bcast<3>(s1)};
       }
-      // One row fragment at a time: overlapping the next one's reads would
-      // need registers the 128 x 64 accumulator tile does not leave.
-      if constexpr (L::WRB * L::WCB >= 32) __builtin_amdgcn_sched_barrier(0);
+    };
+    prep(0);
+    // Each MFMA's product is scaled and added one MFMA later, so a wave
+    // issues the next MFMA before it waits for the previous result.
+    f32x4_t tq[2];
+    constexpr int NQ = L::WRB * L::WCB;
+#pragma unroll
+    for (int q = 0; q <= NQ; ++q) {
+      const int i = q / L::WCB, j = q % L::WCB;
+      if (q < NQ) {
+        if (j == 0) {
+          // Row block i + 1's fragment is read while row block i computes;
+          // later ones stay unloaded (hoisted, they would need registers the
+          // accumulators hold).
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+          if (i + 1 < L::WRB) load_a(i + 1);
+        }
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        tq[q & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr[i & 1], bfr[j], zero, 0, 0, 0, 127, 0, 127);
+      }
+      if (q > 0) {
+        const int pi = (q - 1) / L::WCB, pj = (q - 1) % L::WCB;
+        const f32x4_t t = tq[(q - 1) & 1], s4 = sc[pi & 1][pj / PER];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[pi][pj][v] = fmaf(t[v], s4[v], acc[pi][pj][v]);
+      }
+      if (q < NQ && j == L::WCB - 1 && i + 1 < L::WRB) prep(i + 1);
+      // Issue order within a row block: each MFMA, then the previous
+      // product's FMAs; the next row fragment's reads after the first MFMA,
+      // the next row block's scales after the last.
+      if (q < NQ) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (j == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (q > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        if (j == L::WCB - 1 && i + 1 < L::WRB) __builtin_amdgcn_sched_group_barrier(0x002, 5 * NSW, 0);
+      }
     }
+    // The group's products are complete here, before the wait and barrier
+    // below (sunk past them, every fragment of the group would be live at once).
+#pragma unroll
+    for (int i = 0; i < L::WRB; ++i)
+#pragma unroll
+      for (int j = 0; j < L::WCB; ++j) asm volatile("" : "+v"(acc[i][j]));
     if (g + 1 < KG) {
       // This wave's copies of group g + 1 landed (later ones may not have);
       // the barrier publishes the stage and frees stage g for group g + NST.
