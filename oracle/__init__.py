@@ -1,5 +1,6 @@
 """fp64 CPU oracles: LaCache's exact layer-0 step (lacache_ref, re-exported
-here) and the per-group FP8 FFN of the later layers (fp8_ref).
+here), the per-group FP8 FFN of the later layers (fp8_ref), and the rest of
+layer 0 with the sampler cut (layer_ref).
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py``; never by the product path.

@@ -2,9 +2,9 @@
 
 Each mutation below replaces one oracle function with a plausibly wrong
 version (a dropped term, a wrong sign, index, base, rounding or operand
-order); with it in place, at least one pin of tests/test_oracle_pins.py or
-tests/test_fp8_oracle_pins.py other than the regression fixture (which the
-oracle itself wrote) must fail.  The mistakes
+order); with it in place, at least one pin of tests/test_oracle_pins.py,
+tests/test_fp8_oracle_pins.py or tests/test_layer_oracle_pins.py other than
+the regression fixture (which the oracle itself wrote) must fail.  The mistakes
 are planted in the oracle on the CPU only; no GPU is used.
 """
 
@@ -14,14 +14,16 @@ import pytest
 import oracle
 import oracle.fp8_ref as q8
 import oracle.lacache_ref as ref
+import oracle.layer_ref as lay
 import test_fp8_oracle_pins as fp8_pins
+import test_layer_oracle_pins as layer_pins
 import test_oracle_pins as pins
 
 
 def _pin_calls():
     """Every pin as a zero-argument call (parametrized pins expanded)."""
     calls = []
-    for mod, name in sorted([(p, n) for p in (pins, fp8_pins) for n in dir(p)], key=lambda x: x[1]):
+    for mod, name in sorted([(p, n) for p in (pins, fp8_pins, layer_pins) for n in dir(p)], key=lambda x: x[1]):
         fn = getattr(mod, name)
         if not name.startswith("test_") or not callable(fn) or name == "test_oracle_regression_fixture":
             continue
@@ -185,6 +187,37 @@ def _add_norm_unrounded_residual(h, a, gamma, eps):
     return r, np.asarray(gamma, np.float64) * r / np.sqrt(np.mean(r * r, axis=-1, keepdims=True) + eps)
 
 
+def _o_proj_unrounded_a(h, o, w_o):
+    a = lay.linear(o, w_o)
+    return q8.round_bf16(a), q8.round_bf16(np.asarray(h, np.float64) + a)
+
+
+def _ffn_gate_up_swapped(r, gamma, w_gate, w_up, w_down, eps):
+    return lay.__dict__["_orig_ffn_bf16"](r, gamma, w_up, w_gate, w_down, eps)
+
+
+def _final_norm_no_gamma(rows, gamma_f, eps):
+    return q8.round_bf16(lay.rms_norm_rows(rows, np.ones_like(np.asarray(gamma_f, np.float64)), eps))
+
+
+def _block_rows_shifted(seqs):
+    return np.concatenate([np.arange(s[0] + s[2] + 1, s[0] + s[3] + 1) for s in seqs]).astype(np.int64)
+
+
+def _softmax_columns(logits):
+    l = np.asarray(logits, np.float64)
+    e = np.exp(l - l.max(axis=0, keepdims=True))
+    return e / e.sum(axis=0, keepdims=True)
+
+
+def _sample_rows_last_max(hidden_rows, gamma_f, w_lm, eps):
+    out = lay.__dict__["_orig_sample_rows"](hidden_rows, gamma_f, w_lm, eps)
+    lg = out["logits"]
+    out["token"] = lg.shape[-1] - 1 - np.argmax(lg[:, ::-1], axis=-1)
+    out["confidence"] = out["probs"][np.arange(len(lg)), out["token"]]
+    return out
+
+
 MUTATIONS = {
     "rms_norm drops gamma": ("rms_norm", _rms_no_gamma),
     "rms_norm eps outside the root": ("rms_norm", _rms_eps_outside),
@@ -205,6 +238,12 @@ MUTATIONS = {
     "fp8 weight scale per row stripe": ("fp8:quantize_weight", _quantize_weight_row_stripes),
     "swiglu gate and up swapped": ("fp8:swiglu", _swiglu_swapped),
     "residual not rounded to bf16": ("fp8:add_norm", _add_norm_unrounded_residual),
+    "layer residual adds the unrounded projection": ("layer:o_proj_residual", _o_proj_unrounded_a),
+    "layer ffn gate and up swapped": ("layer:ffn_bf16", _ffn_gate_up_swapped),
+    "final norm drops gamma": ("layer:final_norm", _final_norm_no_gamma),
+    "sampler cut one row late": ("layer:block_rows", _block_rows_shifted),
+    "softmax over the wrong axis": ("layer:softmax_rows", _softmax_columns),
+    "argmax takes the last of equal maxima": ("layer:sample_rows", _sample_rows_last_max),
 }
 
 
@@ -215,6 +254,8 @@ def test_planted_mutation_fails_a_pin(mutation, monkeypatch):
     mod = ref
     if fname.startswith("fp8:"):
         mod, fname = q8, fname[4:]
+    elif fname.startswith("layer:"):
+        mod, fname = lay, fname[6:]
     orig = getattr(mod, fname)
     monkeypatch.setitem(mod.__dict__, f"_orig_{fname}", orig)
     monkeypatch.setattr(mod, fname, fn)
@@ -224,7 +265,7 @@ def test_planted_mutation_fails_a_pin(mutation, monkeypatch):
     for name, pin, kwargs in _pin_calls():
         try:
             pin(**kwargs)
-        except AssertionError:
+        except Exception:          # a wrong value, or a mutant that breaks the pin's indexing
             failed.append(name)
     print(f"{mutation}: fails {failed}")
     assert failed, f"mutation '{mutation}' passed every pin"
