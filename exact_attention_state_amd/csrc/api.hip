@@ -30,6 +30,7 @@ struct lacache_ctx {
   int refresh_rows;        // streaming refresh item rows fixed by LACACHE_REFRESH_ROWS (64 or 128), else 0
   void *scratch;           // device address of this device's static scratch (lacache_block_step_noalloc)
   int fp8_tile;            // down-projection FP8 GEMM tile fixed by LACACHE_FP8_TILE (1: 256, 2: 128), else 0
+  int layer_tile;          // bf16 layer GEMM tile fixed by LACACHE_LAYER_TILE (1: 256, 2: 128, 3: 64 x 256), else 0
   std::string last_error;
   // Diagnostics: event pairs stamped by each launch while profiling is on.
   bool profiling = false;
@@ -96,6 +97,7 @@ hipError_t static_scratch_address(int dev, void **out) {
 namespace {
 
 using lc::kMaxInline;
+using lc::bf16_t;
 
 lacache_status fail(const lacache_ctx *ctx, lacache_status st, const char *fmt, ...)
     __attribute__((format(printf, 3, 4)));
@@ -125,7 +127,8 @@ lacache_status check_device(lacache_ctx *ctx) {
 }
 
 // Block-table checks shared by every call.  n_rows < 0: no row bound.
-lacache_status check_table(lacache_ctx *ctx, const lacache_seq *seqs, int32_t batch, int64_t n_rows) {
+lacache_status check_table(lacache_ctx *ctx, const lacache_seq *seqs, int32_t batch, int64_t n_rows,
+                           int max_block = 128) {
   if (!seqs) return fail(ctx, LACACHE_ERR_INVALID_ARG, "seqs is NULL");
   if (batch < 1) return fail(ctx, LACACHE_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
   std::vector<std::pair<int64_t, int64_t>> ranges;
@@ -141,9 +144,9 @@ lacache_status check_table(lacache_ctx *ctx, const lacache_seq *seqs, int32_t ba
     if (!(0 <= s.block_start && s.block_start < s.block_end && s.block_end <= s.seq_len))
       return fail(ctx, LACACHE_ERR_INVALID_ARG, "sample %d: block [%d, %d) not inside [0, %d) or empty", i,
                   s.block_start, s.block_end, s.seq_len);
-    if (s.block_end - s.block_start > 128)
-      return fail(ctx, LACACHE_ERR_UNSUPPORTED, "sample %d: block of %d tokens (at most 128 supported)", i,
-                  s.block_end - s.block_start);
+    if (s.block_end - s.block_start > max_block)
+      return fail(ctx, LACACHE_ERR_UNSUPPORTED, "sample %d: block of %d tokens (at most %d supported)", i,
+                  s.block_end - s.block_start, max_block);
     const int64_t end = (int64_t)s.seq_offset + s.seq_len;
     // Kernels index rows in 32 bits (offsets into the buffers are 64-bit).
     if (end > INT32_MAX)
@@ -425,6 +428,12 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
     if (!std::strcmp(env, "256")) ctx->fp8_tile = 1;
     else if (!std::strcmp(env, "128")) ctx->fp8_tile = 2;
   }
+  ctx->layer_tile = 0;
+  if (const char *env = std::getenv("LACACHE_LAYER_TILE")) {
+    if (!std::strcmp(env, "256")) ctx->layer_tile = 1;
+    else if (!std::strcmp(env, "128")) ctx->layer_tile = 2;
+    else if (!std::strcmp(env, "64")) ctx->layer_tile = 3;
+  }
   if (const char *env = std::getenv("LACACHE_GEMM_TILE")) {
     if (!std::strcmp(env, "whole")) ctx->gemm_tile = lc::kGemmTileWhole;
     else if (!std::strcmp(env, "half")) ctx->gemm_tile = lc::kGemmTileHalf;
@@ -448,6 +457,7 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   if (e == hipSuccess) e = lc::setup_kernel_attributes();
   if (e == hipSuccess) e = lc::setup_gemm_attributes();
   if (e == hipSuccess) e = lc::setup_fp8_attributes();
+  if (e == hipSuccess) e = lc::setup_layer_attributes();
   if (e != hipSuccess) {
     if (ctx->rope) (void)hipFree(ctx->rope);
     if (ctx->flags) (void)hipFree(ctx->flags);
@@ -1139,6 +1149,243 @@ lacache_status lacache_ffn_fp8(lacache_ctx *ctx, int32_t d_ff, const lacache_ffn
   gd.out = out;
   e = timed(ctx, LACACHE_KERNEL_FFN_DOWN, s, [&](const lc::LaunchEvents &ev) { return lc::launch_fp8_gemm_resid(gd, ctx->fp8_tile, s, ev); });
   if (e != hipSuccess) return hip_fail(ctx, "FFN down launch", e);
+  return LACACHE_OK;
+}
+
+namespace {
+bool layer_capable(const lacache_ctx *ctx, int32_t d_ff) {
+  const int D = ctx->cfg.d_model;
+  return ctx->cfg.dtype == LACACHE_BF16 && (D == 512 || D == 1024 || D == 2048 || D == 4096 || D == 8192) &&
+         d_ff >= 128 && d_ff % 128 == 0 && (ctx->cfg.n_heads * ctx->cfg.head_dim) % 64 == 0;
+}
+const char *kLayerNeeds = "the layer finish needs bf16, d_model in {512, 1024, 2048, 4096, 8192}, d_ff a multiple "
+                          "of 128 and n_heads * head_dim a multiple of 64";
+struct LayerWs {
+  void *r, *x, *y;
+};
+// r [n, D] (when the caller keeps none), x [n, D], y [n, F], all bf16.
+size_t layer_ws_layout(const lacache_ctx *ctx, int32_t d_ff, int64_t n, bool own_r, void *base, LayerWs *out) {
+  const size_t D = ctx->cfg.d_model;
+  const size_t sizes[3] = {own_r ? align256((size_t)n * D * 2) : 0, align256((size_t)n * D * 2),
+                           align256((size_t)n * d_ff * 2)};
+  char *p = static_cast<char *>(base);
+  size_t off = 0;
+  void *ptrs[3];
+  for (int i = 0; i < 3; ++i) {
+    ptrs[i] = p ? p + off : nullptr;
+    off += sizes[i];
+  }
+  if (out) *out = LayerWs{ptrs[0], ptrs[1], ptrs[2]};
+  return off;
+}
+}  // namespace
+
+lacache_status lacache_layer_finish_workspace_size(const lacache_ctx *ctx, int32_t d_ff, int64_t n_rows,
+                                                   int32_t keeps_residual, size_t *bytes) {
+  if (!ctx || !bytes) return LACACHE_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (!layer_capable(ctx, d_ff)) return fail(ctx, LACACHE_ERR_UNSUPPORTED, "%s", kLayerNeeds);
+  if (n_rows < 1 || n_rows > (int64_t)1 << 24)
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "n_rows must be in [1, 2^24] (got %lld)", (long long)n_rows);
+  *bytes = layer_ws_layout(ctx, d_ff, n_rows, !keeps_residual, nullptr, nullptr);
+  return LACACHE_OK;
+}
+
+lacache_status lacache_layer_finish(lacache_ctx *ctx, int32_t d_ff, const lacache_layer_weights *w, const void *h,
+                                    const void *attn_out, int64_t n_rows, void *r_out, void *out, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if (!layer_capable(ctx, d_ff)) return fail(ctx, LACACHE_ERR_UNSUPPORTED, "%s", kLayerNeeds);
+  if (!w) return fail(ctx, LACACHE_ERR_INVALID_ARG, "layer weights are NULL");
+  const void *ptrs[8] = {w->w_o, w->gamma, w->w_gate, w->w_up, w->w_down, h, attn_out, out};
+  for (const void *p : ptrs)
+    if (!p || !aligned16(p)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "a pointer is NULL or not 16-byte aligned");
+  if (r_out && !aligned16(r_out)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "r_out is not 16-byte aligned");
+  if (n_rows < 1 || n_rows > (int64_t)1 << 24)
+    return fail(ctx, LACACHE_ERR_INVALID_ARG, "n_rows must be in [1, 2^24] (got %lld)", (long long)n_rows);
+  const size_t need = layer_ws_layout(ctx, d_ff, n_rows, r_out == nullptr, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
+                workspace);
+  LayerWs ws;
+  layer_ws_layout(ctx, d_ff, n_rows, r_out == nullptr, workspace, &ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = ctx->cfg.d_model, HD = ctx->cfg.n_heads * ctx->cfg.head_dim, M = (int)n_rows;
+  bf16_t *r = static_cast<bf16_t *>(r_out ? r_out : ws.r);
+  // r = bf16(h + bf16(O W_o^T))
+  lc::Bf16GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.A = static_cast<const bf16_t *>(attn_out);
+  g.lda = HD;
+  g.B = static_cast<const bf16_t *>(w->w_o);
+  g.ldb = HD;
+  g.res = static_cast<const bf16_t *>(h);
+  g.ldr = D;
+  g.out = r;
+  g.ldo = D;
+  g.M = M;
+  g.N = D;
+  g.K = HD;
+  hipError_t e = timed(ctx, LACACHE_KERNEL_LAYER_OPROJ, s, [&](const lc::LaunchEvents &ev) {
+    return lc::launch_bf16_gemm(g, lc::kGemmOutBf16, ctx->layer_tile, s, ev);
+  });
+  if (e != hipSuccess) return hip_fail(ctx, "layer output projection launch", e);
+  // x = bf16(RMSNorm(r))
+  lc::RowNormArgs na;
+  std::memset(&na, 0, sizeof(na));
+  na.src = r;
+  na.lds = D;
+  na.gamma = static_cast<const bf16_t *>(w->gamma);
+  na.out = static_cast<bf16_t *>(ws.x);
+  na.M = M;
+  na.D = D;
+  na.eps = ctx->cfg.rms_eps;
+  e = timed(ctx, LACACHE_KERNEL_LAYER_NORM, s, [&](const lc::LaunchEvents &ev) { return lc::launch_rmsnorm_rows(na, s, ev); });
+  if (e != hipSuccess) return hip_fail(ctx, "layer RMSNorm launch", e);
+  // y = bf16(silu(bf16(x W_g^T)) bf16(x W_u^T))
+  std::memset(&g, 0, sizeof(g));
+  g.A = static_cast<const bf16_t *>(ws.x);
+  g.lda = D;
+  g.B = static_cast<const bf16_t *>(w->w_gate);
+  g.B2 = static_cast<const bf16_t *>(w->w_up);
+  g.ldb = D;
+  g.out = ws.y;
+  g.ldo = d_ff;
+  g.M = M;
+  g.N = d_ff;
+  g.K = D;
+  e = timed(ctx, LACACHE_KERNEL_LAYER_GATE_UP, s, [&](const lc::LaunchEvents &ev) {
+    return lc::launch_bf16_gemm(g, lc::kGemmOutSwiglu, ctx->layer_tile == 2 ? 3 : ctx->layer_tile, s, ev);
+  });
+  if (e != hipSuccess) return hip_fail(ctx, "layer gate-up launch", e);
+  // out = bf16(r + bf16(y W_d^T))
+  std::memset(&g, 0, sizeof(g));
+  g.A = static_cast<const bf16_t *>(ws.y);
+  g.lda = d_ff;
+  g.B = static_cast<const bf16_t *>(w->w_down);
+  g.ldb = d_ff;
+  g.res = r;
+  g.ldr = D;
+  g.out = out;
+  g.ldo = D;
+  g.M = M;
+  g.N = D;
+  g.K = d_ff;
+  e = timed(ctx, LACACHE_KERNEL_LAYER_DOWN, s, [&](const lc::LaunchEvents &ev) {
+    return lc::launch_bf16_gemm(g, lc::kGemmOutBf16, ctx->layer_tile, s, ev);
+  });
+  if (e != hipSuccess) return hip_fail(ctx, "layer down launch", e);
+  return LACACHE_OK;
+}
+
+namespace {
+bool sampler_capable(const lacache_ctx *ctx, int32_t vocab) {
+  const int D = ctx->cfg.d_model;
+  return ctx->cfg.dtype == LACACHE_BF16 && (D == 512 || D == 1024 || D == 2048 || D == 4096 || D == 8192) &&
+         vocab >= 8 && vocab % 8 == 0;
+}
+const char *kSamplerNeeds = "the sampler needs bf16, d_model in {512, 1024, 2048, 4096, 8192} and a vocabulary "
+                            "that is a multiple of 8";
+// z [M, D] bf16 (final norm of the block rows), logits [M, V] fp32.
+size_t sampler_ws(const lacache_ctx *ctx, int64_t M, int32_t vocab, void *base, void **z, float **logits) {
+  const size_t zb = align256((size_t)M * ctx->cfg.d_model * 2), lb = align256((size_t)M * vocab * 4);
+  if (base) {
+    *z = base;
+    *logits = reinterpret_cast<float *>(static_cast<char *>(base) + zb);
+  }
+  return zb + lb;
+}
+}  // namespace
+
+lacache_status lacache_sampler_workspace_size(const lacache_ctx *cctx, int32_t vocab, const lacache_seq *seqs,
+                                              int32_t batch, size_t *bytes) {
+  lacache_ctx *ctx = const_cast<lacache_ctx *>(cctx);
+  if (!ctx || !bytes) return LACACHE_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (!sampler_capable(ctx, vocab)) return fail(ctx, LACACHE_ERR_UNSUPPORTED, "%s", kSamplerNeeds);
+  lacache_status st = check_table(ctx, seqs, batch, -1, INT32_MAX);
+  if (st != LACACHE_OK) return st;
+  *bytes = sampler_ws(ctx, block_tokens(seqs, batch), vocab, nullptr, nullptr, nullptr);
+  return LACACHE_OK;
+}
+
+lacache_status lacache_sampler_cut(lacache_ctx *ctx, const void *hidden, int64_t n_rows, const lacache_seq *seqs,
+                                   int32_t batch, const void *gamma_final, const void *w_lm, int32_t vocab,
+                                   int32_t *token, float *confidence, float *probs, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if (!sampler_capable(ctx, vocab)) return fail(ctx, LACACHE_ERR_UNSUPPORTED, "%s", kSamplerNeeds);
+  if ((st = check_table(ctx, seqs, batch, n_rows, INT32_MAX)) != LACACHE_OK) return st;
+  const void *ptrs[5] = {hidden, gamma_final, w_lm, token, confidence};
+  for (const void *p : ptrs)
+    if (!p || !aligned16(p)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "a pointer is NULL or not 16-byte aligned");
+  if (probs && !aligned16(probs)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "probs is not 16-byte aligned");
+  const int64_t M = block_tokens(seqs, batch);
+  if (M > (int64_t)1 << 24) return fail(ctx, LACACHE_ERR_UNSUPPORTED, "%lld block rows (at most 2^24)", (long long)M);
+  void *z = nullptr;
+  float *logits = nullptr;
+  const size_t need = sampler_ws(ctx, M, vocab, nullptr, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
+                workspace);
+  sampler_ws(ctx, M, vocab, workspace, &z, &logits);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = ctx->cfg.d_model;
+  // The cut: the final norm reads only the block rows (block-table order).
+  int64_t row_base = 0;
+  for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
+    const int ns = std::min(batch - s0, kMaxInline);
+    lc::RowNormArgs na;
+    std::memset(&na, 0, sizeof(na));
+    na.sa = slice_args(seqs, s0, ns);
+    na.sa.pre[0][0] = 0;
+    for (int i = 0; i < ns; ++i) na.sa.pre[0][i + 1] = na.sa.pre[0][i] + (na.sa.be[i] - na.sa.bs[i]);
+    na.gather = 1;
+    na.src = static_cast<const bf16_t *>(hidden);
+    na.lds = D;
+    na.gamma = static_cast<const bf16_t *>(gamma_final);
+    na.out = static_cast<bf16_t *>(z) + row_base * D;
+    na.M = na.sa.pre[0][ns];
+    na.D = D;
+    na.eps = ctx->cfg.rms_eps;
+    hipError_t e = timed(ctx, LACACHE_KERNEL_SAMPLER_NORM, s, [&](const lc::LaunchEvents &ev) {
+      return lc::launch_rmsnorm_rows(na, s, ev);
+    });
+    if (e != hipSuccess) return hip_fail(ctx, "sampler final norm launch", e);
+    row_base += na.M;
+  }
+  lc::Bf16GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.A = static_cast<const bf16_t *>(z);
+  g.lda = D;
+  g.B = static_cast<const bf16_t *>(w_lm);
+  g.ldb = D;
+  g.out = logits;
+  g.ldo = vocab;
+  g.M = (int)M;
+  g.N = vocab;
+  g.K = D;
+  hipError_t e = timed(ctx, LACACHE_KERNEL_SAMPLER_LMHEAD, s, [&](const lc::LaunchEvents &ev) {
+    return lc::launch_bf16_gemm(g, lc::kGemmOutF32, ctx->layer_tile, s, ev);
+  });
+  if (e != hipSuccess) return hip_fail(ctx, "sampler lm-head launch", e);
+  lc::SoftmaxArgs sm;
+  sm.logits = logits;
+  sm.ld = vocab;
+  sm.token = token;
+  sm.conf = confidence;
+  sm.probs = probs;
+  sm.ldp = vocab;
+  sm.M = (int)M;
+  sm.V = vocab;
+  e = timed(ctx, LACACHE_KERNEL_SAMPLER_SOFTMAX, s, [&](const lc::LaunchEvents &ev) {
+    return lc::launch_softmax_argmax(sm, s, ev);
+  });
+  if (e != hipSuccess) return hip_fail(ctx, "sampler softmax launch", e);
   return LACACHE_OK;
 }
 

@@ -203,6 +203,49 @@ template <int N> __device__ __forceinline__ void vmcnt_wait() {
   asm volatile("" : : : "memory");
 }
 
+// Global -> LDS copies with a wave-uniform base address (scalar registers) and
+// a per-lane 32-bit byte offset: lane l moves 16 (4) bytes from base + voff
+// to LDS byte address lds + 16 l (4 l).  One offset register serves every
+// copy of a stage.  Waited for by the caller (vmcnt_wait); M0 is clobbered.
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_s(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
+// x << sh, recomputed where it is used: a loop holding every copy offset in
+// its own register across the main loop runs out of registers.
+__device__ __forceinline__ uint32_t lane_bytes(int x, int sh) {
+  uint32_t r;
+  asm volatile("v_lshlrev_b32 %0, %1, %2" : "=v"(r) : "i"(sh), "v"(x));
+  return r;
+}
+
+// s_waitcnt vmcnt(n) for a runtime n in [0, N].
+template <int N> __device__ __forceinline__ void vmcnt_wait_rt(int n) {   // n in [0, N]: runtime -> constant
+  if constexpr (N == 0) {
+    vmcnt_wait<0>();
+  } else {
+    if (n >= N) vmcnt_wait<N>();
+    else vmcnt_wait_rt<N - 1>(n);
+  }
+}
+
+
+// In-wave LDS ordering: this wave's LDS writes complete before its later reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" : : : "memory");
+}
+
 // Workgroup barrier that orders LDS traffic only: the waves meet, and LDS
 // stores issued before it are visible after it, while global loads issued
 // before it stay in flight (a full __syncthreads would wait for them).

@@ -60,41 +60,9 @@ __device__ __forceinline__ uint32_t e4m3_code4(float a, float b, float c, float 
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// Global -> LDS copies with a wave-uniform base address (scalar registers) and
-// a per-lane 32-bit byte offset: lane l moves 16 (4) bytes from base + voff
-// to LDS byte address lds + 16 l (4 l).  One offset register serves every
-// copy of a stage.  Waited for by the caller (vmcnt_wait); M0 is clobbered.
-__device__ __forceinline__ void dma16_s(const void *base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4_s(const void *base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base)
-               : "memory", "m0");
-}
-
-// x << sh, recomputed where it is used: a loop holding every copy offset in
-// its own register across the main loop runs out of registers.
-__device__ __forceinline__ uint32_t lane_bytes(int x, int sh) {
-  uint32_t r;
-  asm volatile("v_lshlrev_b32 %0, %1, %2" : "=v"(r) : "i"(sh), "v"(x));
-  return r;
-}
-
 // Value of lane 4 (l / 4) + v in lane l (a DPP quad permutation).
 template <int V> __device__ __forceinline__ float quad_bcast(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), V * 0x55, 0xf, 0xf, false));
-}
-
-// In-wave LDS ordering: this wave's LDS writes complete before its later reads.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("" : : : "memory");
 }
 
 __device__ __forceinline__ float wave_max16(float x) {    // max over the 16 lanes of a lane group
@@ -251,15 +219,6 @@ template <int TM, int TN> struct F8T {
   static_assert(COPIES * 8 * 1024 == A_BYTES + B_BYTES, "copies must tile the stage");
   static_assert(SA_COPIES <= 8, "scale copies");
 };
-
-template <int N> __device__ __forceinline__ void vmcnt_wait_rt(int n) {   // n in [0, N]: runtime -> constant
-  if constexpr (N == 0) {
-    vmcnt_wait<0>();
-  } else {
-    if (n >= N) vmcnt_wait<N>();
-    else vmcnt_wait_rt<N - 1>(n);
-  }
-}
 
 enum { kEpiResid = 0, kEpiSwiglu = 1 };
 

@@ -181,6 +181,39 @@ hipError_t launch_fp8_gemm_swiglu(const Fp8GemmArgs &a, hipStream_t s, const Lau
 hipError_t launch_fp8_gemm_resid(const Fp8GemmArgs &a, int tile, hipStream_t s, const LaunchEvents &ev);
 hipError_t setup_fp8_attributes();
 
+// The rest of layer 0 and the sampler cut (layer.hip).
+struct Bf16GemmArgs {
+  const bf16_t *A;         // [M, K] row-major, leading dimension lda (elements)
+  const bf16_t *B;         // [N, K] row-major (SwiGLU: the gate rows), leading dimension ldb
+  const bf16_t *B2;        // SwiGLU: the up rows [N, K]; else unused
+  const bf16_t *res;       // bf16 output: residual [M, N] (leading dimension ldr) added after rounding, or null
+  void *out;               // [M, N] bf16 or fp32 (SwiGLU: [M, N] bf16 with N the features), leading dimension ldo
+  int M, N, K;
+  int lda, ldb, ldr, ldo;
+};
+enum { kGemmOutBf16 = 0, kGemmOutF32 = 1, kGemmOutSwiglu = 2 };
+// tile: 0 automatic, 1 256 x 256, 2 128 x 128, 3 64 x 256 (rows x columns of the output)
+hipError_t launch_bf16_gemm(const Bf16GemmArgs &a, int out_kind, int tile, hipStream_t s, const LaunchEvents &ev);
+struct RowNormArgs {
+  const bf16_t *src;       // rows, leading dimension lds (elements)
+  const bf16_t *gamma;     // [D]
+  bf16_t *out;             // [M, D]
+  int lds, M, D;
+  float eps;
+  int gather;              // 1: output row m is block row m of sa (pre[0]: block-token prefix sums)
+  SeqArgs sa;
+};
+hipError_t launch_rmsnorm_rows(const RowNormArgs &a, hipStream_t s, const LaunchEvents &ev);
+struct SoftmaxArgs {
+  const float *logits;     // [M, V], leading dimension ld
+  int *token;              // [M] argmax (first index among equal maxima)
+  float *conf;             // [M] its probability
+  float *probs;            // [M, V] probabilities (leading dimension ldp), or null
+  int M, V, ld, ldp;
+};
+hipError_t launch_softmax_argmax(const SoftmaxArgs &a, hipStream_t s, const LaunchEvents &ev);
+hipError_t setup_layer_attributes();
+
 // Work decomposition shared by the planner and the kernels.
 constexpr int kRowsA = 32;     // block rows per type-A item
 constexpr int kRowsB = 64;     // invariant rows per type-B item

@@ -27,11 +27,16 @@ EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "laca
             "lacache_block_step", "lacache_refresh_block", "lacache_dualcache_attn", "lacache_read_device_status",
             "lacache_profile_enable", "lacache_profile_read", "lacache_status_string", "lacache_last_error",
             "lacache_packed_weight_size", "lacache_pack_qkv_weight", "lacache_block_step_noalloc",
-            "lacache_ffn_weight_bytes", "lacache_ffn_pack_weights", "lacache_ffn_workspace_size", "lacache_ffn_fp8")
+            "lacache_ffn_weight_bytes", "lacache_ffn_pack_weights", "lacache_ffn_workspace_size", "lacache_ffn_fp8",
+            "lacache_layer_finish_workspace_size", "lacache_layer_finish", "lacache_sampler_workspace_size",
+            "lacache_sampler_cut")
 (KERNEL_QKV, KERNEL_BLOCK_ROWS, KERNEL_INVARIANT_ROWS, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_QKV_PREP,
- KERNEL_QKV_GEMM, KERNEL_ATTN, KERNEL_FFN_NORM, KERNEL_FFN_GATE_UP, KERNEL_FFN_DOWN) = range(11)
+ KERNEL_QKV_GEMM, KERNEL_ATTN, KERNEL_FFN_NORM, KERNEL_FFN_GATE_UP, KERNEL_FFN_DOWN, KERNEL_LAYER_OPROJ,
+ KERNEL_LAYER_NORM, KERNEL_LAYER_GATE_UP, KERNEL_LAYER_DOWN, KERNEL_SAMPLER_NORM, KERNEL_SAMPLER_LMHEAD,
+ KERNEL_SAMPLER_SOFTMAX) = range(18)
 KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn", "qkv_prep", "qkv_gemm", "attn",
-                "ffn_norm", "ffn_gate_up", "ffn_down")
+                "ffn_norm", "ffn_gate_up", "ffn_down", "layer_oproj", "layer_norm", "layer_gate_up", "layer_down",
+                "sampler_norm", "sampler_lmhead", "sampler_softmax")
 
 
 class Config(ctypes.Structure):
@@ -55,6 +60,11 @@ class Cache(ctypes.Structure):
 class FfnWeights(ctypes.Structure):
     _fields_ = [("gamma", ctypes.c_void_p), ("gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
                 ("down", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [("w_o", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
 
 
 class Seq(ctypes.Structure):
@@ -101,6 +111,10 @@ def load_library(path: str = LIB_PATH):
         "lacache_ffn_pack_weights": (st, [P, I32, P, P, P, P, P, P, P, P]),
         "lacache_ffn_workspace_size": (st, [P, I32, I64, I32, ctypes.POINTER(SZ)]),
         "lacache_ffn_fp8": (st, [P, I32, ctypes.POINTER(FfnWeights), P, P, I64, P, P, P, SZ, P]),
+        "lacache_layer_finish_workspace_size": (st, [P, I32, I64, I32, ctypes.POINTER(SZ)]),
+        "lacache_layer_finish": (st, [P, I32, ctypes.POINTER(LayerWeights), P, P, I64, P, P, P, SZ, P]),
+        "lacache_sampler_workspace_size": (st, [P, I32, ctypes.POINTER(Seq), I32, ctypes.POINTER(SZ)]),
+        "lacache_sampler_cut": (st, [P, P, I64, ctypes.POINTER(Seq), I32, P, P, I32, P, P, P, P, SZ, P]),
         "lacache_read_device_status": (st, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
         "lacache_profile_enable": (st, [P, ctypes.c_int]),
         "lacache_profile_read": (st, [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
@@ -351,6 +365,56 @@ class Context:
         st = self.lib.lacache_ffn_fp8(self.handle, d_ff, ctypes.byref(w), _ptr(h), _ptr(attn_out), h.shape[0],
                                       _ptr(r_out), _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
         self._check(st, "lacache_ffn_fp8")
+        return ws
+
+    def layer_workspace(self, d_ff, n_rows, keeps_residual=True, device="cuda"):
+        n = ctypes.c_size_t()
+        self._check(self.lib.lacache_layer_finish_workspace_size(self.handle, d_ff, n_rows, int(bool(keeps_residual)),
+                                                                 ctypes.byref(n)), "lacache_layer_finish_workspace_size")
+        return torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+
+    def layer_finish(self, d_ff, weights, h, attn_out, out, r_out=None, workspace=None, stream=None):
+        """The rest of the layer in bf16: weights = (w_o, gamma, w_gate, w_up, w_down);
+        out = bf16(r + bf16(swiglu(...) W_down^T)) with r = bf16(h + bf16(attn_out W_o^T))."""
+        names = ("w_o", "gamma", "w_gate", "w_up", "w_down")
+        for name, t in list(zip(names, weights)) + [("h", h), ("attn_out", attn_out), ("out", out)]:
+            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+        n, D = h.shape
+        if out.shape != h.shape or attn_out.shape[0] != n or (r_out is not None and r_out.shape != h.shape):
+            raise ValueError("h, out (and r_out) must be [n_rows, d_model], attn_out [n_rows, n_heads head_dim]")
+        w = LayerWeights(*[t.data_ptr() for t in weights])
+        ws = workspace if workspace is not None else self.layer_workspace(d_ff, n, r_out is not None, h.device)
+        st = self.lib.lacache_layer_finish(self.handle, d_ff, ctypes.byref(w), _ptr(h), _ptr(attn_out), n,
+                                           _ptr(r_out), _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+        self._check(st, "lacache_layer_finish")
+        return ws
+
+    def sampler_workspace(self, vocab, table, device="cuda"):
+        n = ctypes.c_size_t()
+        seqs = _seqs(table)
+        self._check(self.lib.lacache_sampler_workspace_size(self.handle, vocab, seqs, len(table), ctypes.byref(n)),
+                    "lacache_sampler_workspace_size")
+        return torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+
+    def sampler_cut(self, hidden, table, gamma_f, w_lm, token, confidence, probs=None, workspace=None, stream=None):
+        """Final norm, lm-head and float softmax of the block rows of `table`:
+        token [M] int32 (argmax), confidence [M] fp32, probs [M, vocab] fp32 or None."""
+        for name, t in (("hidden", hidden), ("gamma_f", gamma_f), ("w_lm", w_lm)):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+        if token.dtype != torch.int32 or confidence.dtype != torch.float32:
+            raise ValueError("token must be int32 and confidence fp32")
+        vocab = w_lm.shape[0]
+        M = sum(be - bs for _, _, bs, be in table)
+        if token.numel() < M or confidence.numel() < M or (probs is not None and probs.numel() < M * vocab):
+            raise ValueError("token / confidence / probs are smaller than the block rows")
+        seqs = _seqs(table)
+        ws = workspace if workspace is not None else self.sampler_workspace(vocab, table, hidden.device)
+        st = self.lib.lacache_sampler_cut(self.handle, _ptr(hidden), hidden.shape[0], seqs, len(table), _ptr(gamma_f),
+                                          _ptr(w_lm), vocab, _ptr(token), _ptr(confidence), _ptr(probs), _ptr(ws),
+                                          ws.numel(), _stream(stream))
+        self._check(st, "lacache_sampler_cut")
         return ws
 
     def profile(self, enable: bool):

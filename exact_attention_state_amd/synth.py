@@ -250,6 +250,9 @@ def with_steps(wl: Workload, steps: int) -> Workload:
 # LLaDA-8B's feed-forward width (SwiGLU, d_model 4096).
 LLADA_D_FF = 12288
 _S_FFN_W, _S_FFN_X = 6, 7
+_S_LAYER_W, _S_LM = 8, 9
+# LLaDA-8B's vocabulary (the lm-head rows).
+LLADA_VOCAB = 126464
 
 
 def ffn_params(d_model: int, d_ff: int, family: int = 0) -> dict:
@@ -270,3 +273,27 @@ def ffn_inputs(n_rows: int, d_model: int, seed: int = 0):
     h = round_to_bf16(rng.standard_normal((n_rows, d_model), dtype=np.float32))
     a = round_to_bf16(rng.standard_normal((n_rows, d_model), dtype=np.float32) * np.float32(0.5))
     return h, a
+
+
+def layer_params(d_model: int, hd: int, d_ff: int, family: int = 0) -> dict:
+    """The rest of a layer: w_o [D, hd] ~ N(0, 0.02) and the FFN of ffn_params
+    (gamma, w_gate, w_up, w_down), bf16 values (float32 arrays)."""
+    rng = np.random.default_rng([BASE_SEED, 70 + family, _S_LAYER_W, d_model, hd])
+    w_o = round_to_bf16(rng.standard_normal((d_model, hd), dtype=np.float32) * np.float32(0.02))
+    p = ffn_params(d_model, d_ff, 100 + family)
+    p["w_o"] = w_o
+    return p
+
+
+def lm_head_params(d_model: int, vocab: int, family: int = 0) -> dict:
+    """Final norm gain gamma_f [D] ~ 1 + N(0, 0.1) and the lm-head w_lm
+    [vocab, D] ~ N(0, 0.02), drawn 8192 rows per generator stream (so rows can
+    be regenerated alone), bf16 values (float32 arrays)."""
+    rng = np.random.default_rng([BASE_SEED, 80 + family, _S_LM, d_model, vocab])
+    gamma_f = round_to_bf16(1.0 + rng.standard_normal(d_model, dtype=np.float32) * np.float32(0.1))
+    w = np.empty((vocab, d_model), np.float32)
+    for r0 in range(0, vocab, 8192):
+        g = np.random.default_rng([BASE_SEED, 80 + family, _S_LM, d_model, vocab, r0])
+        n = min(8192, vocab - r0)
+        w[r0:r0 + n] = g.standard_normal((n, d_model), dtype=np.float32) * np.float32(0.02)
+    return {"gamma_f": gamma_f, "w_lm": round_to_bf16(w)}

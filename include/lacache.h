@@ -354,6 +354,71 @@ LACACHE_API lacache_status lacache_ffn_fp8(lacache_ctx *ctx, int32_t d_ff, const
                                            const void *h, const void *attn_out, int64_t n_rows, void *r_out,
                                            void *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * The rest of layer 0 after its attention, and the sampler cut (LaCache
+ * Figure 2; Section 3.4: the first layer keeps the parameter precision, and
+ * at the sampling stage only the current block's rows of the transformer
+ * output go through the final norm, the lm-head and the float softmax).
+ * bf16 throughout, fp32 accumulation, every operator's output rounded to bf16
+ * (round to nearest even):
+ *   a = bf16(attn_out W_o^T); r = bf16(h + a);
+ *   x = bf16(gamma r / sqrt(mean(r^2) + rms_eps));
+ *   gate = bf16(x W_gate^T), up = bf16(x W_up^T), y = bf16(silu(gate) up);
+ *   out = bf16(r + bf16(y W_down^T)).
+ * Shapes (row-major, bf16): w_o [d_model, n_heads head_dim]; gamma
+ * [d_model]; w_gate, w_up [d_ff, d_model]; w_down [d_model, d_ff]; h, r_out,
+ * out [n_rows, d_model] (h: the layer's input rows, i.e. the EmbedCache at
+ * layer 0); attn_out [n_rows, n_heads head_dim] (the attention output, heads
+ * concatenated: the `out` rows of lacache_block_step).  Every row of the
+ * sequences is computed: each row's attention output changes with the
+ * block's keys.  The context must be bf16 with d_model in {512, 1024, 2048,
+ * 4096, 8192}, n_heads head_dim a multiple of 64; d_ff a multiple of 128. */
+typedef struct {
+  const void *w_o;           /* attention output projection                             */
+  const void *gamma;         /* feed-forward RMSNorm gain                               */
+  const void *w_gate;        /* gate linear                                             */
+  const void *w_up;          /* up linear                                               */
+  const void *w_down;        /* down (ffout) linear                                     */
+} lacache_layer_weights;
+
+/* Workspace bytes of lacache_layer_finish for n_rows rows (1 <= n_rows <=
+ * 2^24); keeps_residual: whether the call will be given r_out. */
+LACACHE_API lacache_status lacache_layer_finish_workspace_size(const lacache_ctx *ctx, int32_t d_ff, int64_t n_rows,
+                                                               int32_t keeps_residual, size_t *bytes);
+
+/* Enqueues the rest of the layer for n_rows rows: out (and r_out unless
+ * NULL).  The diagnostic environment variable LACACHE_LAYER_TILE ("256",
+ * "128" or "64"), read by lacache_create, fixes the output tile of the bf16
+ * GEMMs here and in lacache_sampler_cut (256 x 256, 128 x 128 or 64 x 256;
+ * the SwiGLU GEMM takes 64 x 256 for "128") instead of the choice by launch
+ * size.  Workspace after the call (each part at a multiple of 256 bytes, in
+ * this order): r [n_rows, d_model] when r_out is NULL; x [n_rows, d_model];
+ * y [n_rows, d_ff]. */
+LACACHE_API lacache_status lacache_layer_finish(lacache_ctx *ctx, int32_t d_ff, const lacache_layer_weights *w,
+                                                const void *h, const void *attn_out, int64_t n_rows, void *r_out,
+                                                void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of lacache_sampler_cut for this block table and vocabulary
+ * (a multiple of 8).  The table's blocks may be any size here (a block that
+ * spans a whole sequence gives the sampler without the cut). */
+LACACHE_API lacache_status lacache_sampler_workspace_size(const lacache_ctx *ctx, int32_t vocab,
+                                                          const lacache_seq *seqs, int32_t batch, size_t *bytes);
+
+/* The sampler on the block rows only.  For block row t of the table (rows
+ * seq_offset + [block_start, block_end), sample by sample; M rows in all) of
+ * hidden [n_rows, d_model] bf16: z = bf16(gamma_final row / sqrt(mean(row^2)
+ * + rms_eps)); logits = z w_lm^T in fp32 (w_lm [vocab, d_model] bf16);
+ * token[t] = the argmax (the first index among equal maxima), confidence[t]
+ * = its softmax probability 1 / sum_v exp(logit_v - max); probs [M, vocab]
+ * fp32, unless NULL, every probability.  Workspace after the call: z
+ * [M, d_model] bf16, then (at a multiple of 256 bytes) the logits [M, vocab]
+ * fp32. */
+LACACHE_API lacache_status lacache_sampler_cut(lacache_ctx *ctx, const void *hidden, int64_t n_rows,
+                                               const lacache_seq *seqs, int32_t batch, const void *gamma_final,
+                                               const void *w_lm, int32_t vocab, int32_t *token, float *confidence,
+                                               float *probs, void *workspace, size_t workspace_bytes,
+                                               void *stream);
+
 /* Bytes of the packed projection weight for this context: 0 where the
  * configuration has no many-token projection (fp32, or d_model not a
  * multiple of 512). */
@@ -396,7 +461,14 @@ typedef enum {
   LACACHE_KERNEL_FFN_NORM = 8,       /* FP8 FFN: AddNorm + quantization             */
   LACACHE_KERNEL_FFN_GATE_UP = 9,    /* FP8 FFN: gate-up GEMM + SwiGLU + quantization */
   LACACHE_KERNEL_FFN_DOWN = 10,      /* FP8 FFN: down GEMM + residual               */
-  LACACHE_KERNEL_COUNT = 11
+  LACACHE_KERNEL_LAYER_OPROJ = 11,   /* layer finish: W_o GEMM + residual           */
+  LACACHE_KERNEL_LAYER_NORM = 12,    /* layer finish: feed-forward RMSNorm          */
+  LACACHE_KERNEL_LAYER_GATE_UP = 13, /* layer finish: gate-up GEMM + SwiGLU         */
+  LACACHE_KERNEL_LAYER_DOWN = 14,    /* layer finish: down GEMM + residual          */
+  LACACHE_KERNEL_SAMPLER_NORM = 15,  /* sampler: final norm of the block rows       */
+  LACACHE_KERNEL_SAMPLER_LMHEAD = 16, /* sampler: lm-head GEMM (fp32 logits)        */
+  LACACHE_KERNEL_SAMPLER_SOFTMAX = 17, /* sampler: float softmax and argmax         */
+  LACACHE_KERNEL_COUNT = 18
 } lacache_kernel;
 
 LACACHE_API lacache_status lacache_profile_enable(lacache_ctx *ctx, int enable);
