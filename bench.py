@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--ffn-rows", default="768,8192",
                    help="rows of the per-group FP8 FFN measurement (LLaDA-8B FFN shape); empty: skip it")
     p.add_argument("--ffn-only", action="store_true", help="only the FP8 FFN measurement (its JSON object)")
+    p.add_argument("--no-layer", action="store_true", help="skip the layer-finish and sampler measurement")
+    p.add_argument("--layer-only", action="store_true", help="only the layer-finish and sampler measurement")
     return p.parse_args()
 
 
@@ -440,6 +442,112 @@ def cpu_baseline(wl, budget_s, t_step_s):
             "host": info}
 
 
+def layer_accounting(T, D, HD, F):
+    """Work and algorithmic HBM bytes of one layer finish call per kernel (bf16)."""
+    return {"layer_oproj": dict(flops=2 * T * HD * D, bytes=2 * (D * HD + T * HD + 2 * T * D)),
+            "layer_norm": dict(flops=0, bytes=2 * (2 * T * D + D)),
+            "layer_gate_up": dict(flops=2 * T * D * 2 * F, bytes=2 * (2 * F * D + T * D + T * F)),
+            "layer_down": dict(flops=2 * T * F * D, bytes=2 * (D * F + T * F + 2 * T * D))}
+
+
+def sampler_accounting(M, D, V):
+    return {"sampler_norm": dict(flops=0, bytes=2 * (2 * M * D + D)),
+            "sampler_lmhead": dict(flops=2 * M * V * D, bytes=2 * (V * D + M * D) + 4 * M * V),
+            "sampler_softmax": dict(flops=0, bytes=4 * M * V + 8 * M)}
+
+
+def _kernel_fracs(acc, prof):
+    out = {}
+    for k, a in acc.items():
+        ms, n = prof[k]
+        t = ms * 1e3 / max(n, 1)
+        e = {"us_avg": t, "hbm_frac": a["bytes"] / (t * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        if a["flops"]:
+            e["bf16_mfma_frac"] = a["flops"] / (t * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        out[k] = e
+    return out
+
+
+def measure_layer(dev, reps=20, n_sets=2):
+    """The rest of layer 0 (lacache_layer_finish) over llada8b's 768 rows at
+    LLaDA-8B's shape (d_model 4096, 32 x 128 heads, d_ff 12288), cycling
+    `n_sets` weight sets (335 MB each, beyond the 256 MB memory-side cache),
+    and the sampler (vocabulary 126464, a 1 GB lm-head) on the block's 32 rows
+    (the cut) and on all 768 rows (no cut): median time per call and
+    per-kernel averages from event-bracketed calls."""
+    import numpy as np
+    import torch
+    from exact_attention_state_amd import lacache, synth
+    wl = synth.WORKLOADS["llada8b"]
+    T, D, F, V = wl.total_tokens, wl.d_model, synth.LLADA_D_FF, synth.LLADA_VOCAB
+    HD = wl.n_heads * wl.head_dim
+    ctx = lacache.context_for(wl)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).to(dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def timed_calls(call):
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            ev[i][0].record(stream)
+            call(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = sorted(x.elapsed_time(y) * 1e3 for x, y in ev)[reps // 2]
+        ctx.profile(True)
+        ctx.profile_read()
+        for i in range(reps):
+            call(i)
+        torch.cuda.synchronize()
+        prof = ctx.profile_read()
+        ctx.profile(False)
+        return us, prof
+
+    sets = []
+    for i in range(n_sets):
+        p = synth.layer_params(D, HD, F, i)
+        sets.append([bf(p[k]) for k in ("w_o", "gamma", "w_gate", "w_up", "w_down")])
+    h, _ = synth.ffn_inputs(T, D, 11)
+    o = synth.ffn_inputs(T, HD, 12)[1]
+    hd, od = bf(h), bf(o)
+    out = torch.empty(T, D, dtype=torch.bfloat16, device=dev)
+    r = torch.empty_like(out)
+    ws = ctx.layer_workspace(F, T, True, dev)
+    us, prof = timed_calls(lambda i: ctx.layer_finish(F, sets[i % n_sets], hd, od, out, r_out=r, workspace=ws,
+                                                      stream=stream))
+    acc = layer_accounting(T, D, HD, F)
+    flops = sum(a["flops"] for a in acc.values())
+    layer = {"shape": {"rows": T, "d_model": D, "heads_x_head_dim": HD, "d_ff": F},
+             "protocol": f"cold ({n_sets} rotating weight sets)", "us_per_call": us,
+             "bf16_mfma_frac": flops / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+             "kernels": _kernel_fracs(acc, prof), "flops": {k: a["flops"] for k, a in acc.items()},
+             "algorithmic_bytes": {k: a["bytes"] for k, a in acc.items()}}
+    log(f"[bench] layer finish, {T} rows: {us:.1f} us per call ({layer['bf16_mfma_frac']:.3f} of the bf16 MFMA peak); "
+        + ", ".join(f"{k} {v['us_avg']:.1f} us" for k, v in layer["kernels"].items()))
+    del sets, ws, r
+    lm = synth.lm_head_params(D, V, 0)
+    gd, wd = bf(lm["gamma_f"]), bf(lm["w_lm"])
+    del lm
+    sampler = {"vocab": V, "protocol": "cold (the 1 GB lm-head exceeds the memory-side cache)"}
+    for name, table in (("cut", wl.table()), ("uncut", [(off, n, 0, n) for off, n, _, _ in wl.table()])):
+        M = sum(be - bs for _, _, bs, be in table)
+        token = torch.empty(M, dtype=torch.int32, device=dev)
+        conf = torch.empty(M, dtype=torch.float32, device=dev)
+        sws = ctx.sampler_workspace(V, table, dev)
+        us, prof = timed_calls(lambda i: ctx.sampler_cut(out, table, gd, wd, token, conf, workspace=sws, stream=stream))
+        acc = sampler_accounting(M, D, V)
+        sampler[name] = {"rows": M, "us_per_call": us, "kernels": _kernel_fracs(acc, prof),
+                         "algorithmic_bytes": {k: a["bytes"] for k, a in acc.items()}}
+        log(f"[bench] sampler {name}, {M} rows: {us:.1f} us per call; "
+            + ", ".join(f"{k} {v['us_avg']:.1f} us" for k, v in sampler[name]["kernels"].items()))
+        del sws
+    sampler["cut_speedup"] = sampler["uncut"]["us_per_call"] / sampler["cut"]["us_per_call"]
+    assert ctx.read_device_status() == 0
+    return {"layer0_finish": layer, "sampler": sampler}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -460,6 +568,10 @@ def main():
     if args.ffn_only:
         torch.cuda.init()
         print(json.dumps({"ffn_fp8": measure_ffn(torch.device("cuda:0"), ffn_rows)}), flush=True)
+        return
+    if args.layer_only:
+        torch.cuda.init()
+        print(json.dumps(measure_layer(torch.device("cuda:0"))), flush=True)
         return
     wl = synth.WORKLOADS[args.workload]
     acc = step_accounting(wl)
@@ -648,6 +760,7 @@ def main():
     roof["flops"] = flops
 
     ffn = measure_ffn(dev, ffn_rows) if ffn_rows else None
+    layer = None if args.no_layer else measure_layer(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -697,6 +810,8 @@ def main():
         "roofline": roof,
         "refresh": refresh,
         "ffn_fp8": ffn,
+        "layer0_finish": None if layer is None else layer["layer0_finish"],
+        "sampler": None if layer is None else layer["sampler"],
         "cpu_baseline": cpu,
         "host": platform.node(),
         "graph_error": graph_err,

@@ -1288,14 +1288,35 @@ bool sampler_capable(const lacache_ctx *ctx, int32_t vocab) {
 }
 const char *kSamplerNeeds = "the sampler needs bf16, d_model in {512, 1024, 2048, 4096, 8192} and a vocabulary "
                             "that is a multiple of 8";
-// z [M, D] bf16 (final norm of the block rows), logits [M, V] fp32.
-size_t sampler_ws(const lacache_ctx *ctx, int64_t M, int32_t vocab, void *base, void **z, float **logits) {
-  const size_t zb = align256((size_t)M * ctx->cfg.d_model * 2), lb = align256((size_t)M * vocab * 4);
-  if (base) {
-    *z = base;
-    *logits = reinterpret_cast<float *>(static_cast<char *>(base) + zb);
+// z [M, D] bf16 (final norm of the block rows), logits [M, V] fp32, the
+// softmax's chunk partials [M, C] float2 and [M, C] int32, and row (max, sum)
+// [M] float2, each at a multiple of 256 bytes.
+struct SamplerWs {
+  void *z;
+  float *logits;
+  float2 *part;
+  int *part_idx;
+  float2 *row_stat;
+};
+size_t sampler_ws(const lacache_ctx *ctx, int64_t M, int32_t vocab, void *base, SamplerWs *out) {
+  const size_t C = (size_t)lc::softmax_chunks(vocab);
+  const size_t sizes[5] = {align256((size_t)M * ctx->cfg.d_model * 2), align256((size_t)M * vocab * 4),
+                           align256((size_t)M * C * 8), align256((size_t)M * C * 4), align256((size_t)M * 8)};
+  char *p = static_cast<char *>(base);
+  size_t off = 0;
+  void *ptrs[5];
+  for (int i = 0; i < 5; ++i) {
+    ptrs[i] = p ? p + off : nullptr;
+    off += sizes[i];
   }
-  return zb + lb;
+  if (out) {
+    out->z = ptrs[0];
+    out->logits = static_cast<float *>(ptrs[1]);
+    out->part = static_cast<float2 *>(ptrs[2]);
+    out->part_idx = static_cast<int *>(ptrs[3]);
+    out->row_stat = static_cast<float2 *>(ptrs[4]);
+  }
+  return off;
 }
 }  // namespace
 
@@ -1307,7 +1328,7 @@ lacache_status lacache_sampler_workspace_size(const lacache_ctx *cctx, int32_t v
   if (!sampler_capable(ctx, vocab)) return fail(ctx, LACACHE_ERR_UNSUPPORTED, "%s", kSamplerNeeds);
   lacache_status st = check_table(ctx, seqs, batch, -1, INT32_MAX);
   if (st != LACACHE_OK) return st;
-  *bytes = sampler_ws(ctx, block_tokens(seqs, batch), vocab, nullptr, nullptr, nullptr);
+  *bytes = sampler_ws(ctx, block_tokens(seqs, batch), vocab, nullptr, nullptr);
   return LACACHE_OK;
 }
 
@@ -1326,13 +1347,14 @@ lacache_status lacache_sampler_cut(lacache_ctx *ctx, const void *hidden, int64_t
   if (probs && !aligned16(probs)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "probs is not 16-byte aligned");
   const int64_t M = block_tokens(seqs, batch);
   if (M > (int64_t)1 << 24) return fail(ctx, LACACHE_ERR_UNSUPPORTED, "%lld block rows (at most 2^24)", (long long)M);
-  void *z = nullptr;
-  float *logits = nullptr;
-  const size_t need = sampler_ws(ctx, M, vocab, nullptr, nullptr, nullptr);
+  const size_t need = sampler_ws(ctx, M, vocab, nullptr, nullptr);
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
                 workspace);
-  sampler_ws(ctx, M, vocab, workspace, &z, &logits);
+  SamplerWs sw;
+  sampler_ws(ctx, M, vocab, workspace, &sw);
+  void *z = sw.z;
+  float *logits = sw.logits;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = ctx->cfg.d_model;
   // The cut: the final norm reads only the block rows (block-table order).
@@ -1380,6 +1402,9 @@ lacache_status lacache_sampler_cut(lacache_ctx *ctx, const void *hidden, int64_t
   sm.conf = confidence;
   sm.probs = probs;
   sm.ldp = vocab;
+  sm.part = sw.part;
+  sm.part_idx = sw.part_idx;
+  sm.row_stat = sw.row_stat;
   sm.M = (int)M;
   sm.V = vocab;
   e = timed(ctx, LACACHE_KERNEL_SAMPLER_SOFTMAX, s, [&](const lc::LaunchEvents &ev) {

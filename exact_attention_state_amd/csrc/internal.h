@@ -104,7 +104,7 @@ void log_launch(const void *kernel, hipStream_t s, unsigned grid);
 template <auto K, typename... Args>
 inline void lc_launch(dim3 grid, dim3 block, unsigned shmem, hipStream_t s, const LaunchEvents &ev, Args... args) {
   if (launch_log_enabled()) log_launch(reinterpret_cast<const void *>(K), s, grid.x * grid.y * grid.z);
-  if (ev.start)
+  if (ev.start || ev.stop)                 // either stamp may be absent (launch sequences share one pair)
     hipExtLaunchKernelGGL(K, grid, block, shmem, s, ev.start, ev.stop, 0, args...);
   else
     hipLaunchKernelGGL(K, grid, block, shmem, s, args...);
@@ -209,8 +209,12 @@ struct SoftmaxArgs {
   int *token;              // [M] argmax (first index among equal maxima)
   float *conf;             // [M] its probability
   float *probs;            // [M, V] probabilities (leading dimension ldp), or null
+  float2 *part;            // [M, softmax_chunks(V)] chunk (max, sum exp(l - max)) (workspace)
+  int *part_idx;           // [M, softmax_chunks(V)] chunk argmax (workspace)
+  float2 *row_stat;        // [M] row (max, sum exp(l - max)) (workspace)
   int M, V, ld, ldp;
 };
+int softmax_chunks(int V);
 hipError_t launch_softmax_argmax(const SoftmaxArgs &a, hipStream_t s, const LaunchEvents &ev);
 hipError_t setup_layer_attributes();
 

@@ -11,7 +11,8 @@
 // * Row RMSNorm to bf16 (gamma r / sqrt(mean(r^2) + eps)), on every row or on
 //   the block rows of a block table.
 // * Float softmax of fp32 logit rows: argmax (first index among equal maxima),
-//   its probability, and optionally every probability.
+//   its probability, and optionally every probability (three launches: chunk
+//   partials, per-row combine, probabilities).
 //
 // Operand tiles move from HBM straight into LDS (global_load_lds_dwordx4).
 // A tile row of one 64-wide contraction step is 128 bytes = eight 16-byte
@@ -279,10 +280,15 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const RowNormArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// Float softmax of one logit row per workgroup (V a multiple of 4): the
-// maximum and its first index, the sum of exp(l - max), the argmax's
-// probability 1 / sum, and (if requested) every probability.
+// Float softmax of fp32 logit rows (V a multiple of 4), in three steps so a
+// row spreads over many workgroups: (1) per chunk of kSmChunk logits, the
+// chunk's maximum, its first index and sum exp(l - chunk max); (2) per row,
+// one wave combines the chunks: the row maximum, its first index and
+// sum = sum_c s_c exp(m_c - max); the argmax's probability is 1 / sum;
+// (3) if requested, every probability exp(l - max) / sum.
 // ---------------------------------------------------------------------------
+constexpr int kSmChunk = 4096;
+
 __device__ __forceinline__ void better(float &mx, int &ix, float m2, int i2) {
   if (m2 > mx || (m2 == mx && i2 < ix)) {
     mx = m2;
@@ -290,21 +296,26 @@ __device__ __forceinline__ void better(float &mx, int &ix, float m2, int i2) {
   }
 }
 
-__global__ __launch_bounds__(256) void softmax_argmax_kernel(const SoftmaxArgs a) {
-  __shared__ float s_m[4];
+__global__ __launch_bounds__(256) void softmax_partial_kernel(const SoftmaxArgs a) {
+  __shared__ float s_m[4], s_s[4];
   __shared__ int s_i[4];
-  __shared__ float s_s[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int row = blockIdx.x;
+  const int row = blockIdx.y, c = blockIdx.x, nch = gridDim.x;
   const float *l = a.logits + (size_t)row * a.ld;
+  const int v0 = c * kSmChunk, v1 = min(a.V, v0 + kSmChunk);
   float mx = -INFINITY;
   int ix = 0x7fffffff;
-  for (int i = 4 * tid; i < a.V; i += 1024) {
-    const float4 x = *reinterpret_cast<const float4 *>(l + i);
-    better(mx, ix, x.x, i);
-    better(mx, ix, x.y, i + 1);
-    better(mx, ix, x.z, i + 2);
-    better(mx, ix, x.w, i + 3);
+  float4 x[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {                                // 16 logits per thread
+    const int i = v0 + 4 * (tid + 256 * k);
+    x[k] = i < v1 ? *reinterpret_cast<const float4 *>(l + i) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (i < v1) {
+      better(mx, ix, x[k].x, i);
+      better(mx, ix, x[k].y, i + 1);
+      better(mx, ix, x[k].z, i + 2);
+      better(mx, ix, x[k].w, i + 3);
+    }
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) better(mx, ix, __shfl_xor(mx, o), __shfl_xor(ix, o));
@@ -318,28 +329,55 @@ __global__ __launch_bounds__(256) void softmax_argmax_kernel(const SoftmaxArgs a
 #pragma unroll
   for (int k = 1; k < 4; ++k) better(mx, ix, s_m[k], s_i[k]);
   float sum = 0.f;
-  for (int i = 4 * tid; i < a.V; i += 1024) {
-    const float4 x = *reinterpret_cast<const float4 *>(l + i);
-    sum += (expf(x.x - mx) + expf(x.y - mx)) + (expf(x.z - mx) + expf(x.w - mx));
-  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (v0 + 4 * (tid + 256 * k) < v1)
+      sum += (expf(x[k].x - mx) + expf(x[k].y - mx)) + (expf(x[k].z - mx) + expf(x[k].w - mx));
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o);
   if (lane == 0) s_s[w] = sum;
   __syncthreads();
-  sum = (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]);
   if (tid == 0) {
-    a.token[row] = ix;
-    a.conf[row] = 1.0f / sum;
-  }
-  if (a.probs) {
-    float *p = a.probs + (size_t)row * a.ldp;
-    for (int i = 4 * tid; i < a.V; i += 1024) {
-      const float4 x = *reinterpret_cast<const float4 *>(l + i);
-      *reinterpret_cast<float4 *>(p + i) =
-          make_float4(expf(x.x - mx) / sum, expf(x.y - mx) / sum, expf(x.z - mx) / sum, expf(x.w - mx) / sum);
-    }
+    const size_t p = (size_t)row * nch + c;
+    a.part[p] = make_float2(mx, (s_s[0] + s_s[1]) + (s_s[2] + s_s[3]));
+    a.part_idx[p] = ix;
   }
 }
+
+__global__ __launch_bounds__(256) void softmax_combine_kernel(const SoftmaxArgs a, int nch) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.M) return;                                      // whole wave
+  float mx = -INFINITY;
+  int ix = 0x7fffffff;
+  for (int c = lane; c < nch; c += 64) better(mx, ix, a.part[(size_t)row * nch + c].x, a.part_idx[(size_t)row * nch + c]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) better(mx, ix, __shfl_xor(mx, o), __shfl_xor(ix, o));
+  float sum = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    const float2 p = a.part[(size_t)row * nch + c];
+    sum += p.y * expf(p.x - mx);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o);
+  if (lane == 0) {
+    a.token[row] = ix;
+    a.conf[row] = 1.0f / sum;
+    a.row_stat[row] = make_float2(mx, sum);
+  }
+}
+
+__global__ __launch_bounds__(256) void softmax_probs_kernel(const SoftmaxArgs a) {
+  const int row = blockIdx.y;
+  const int i = 4 * (blockIdx.x * 256 + threadIdx.x);
+  if (i >= a.V) return;
+  const float2 st = a.row_stat[row];
+  const float4 x = *reinterpret_cast<const float4 *>(a.logits + (size_t)row * a.ld + i);
+  *reinterpret_cast<float4 *>(a.probs + (size_t)row * a.ldp + i) = make_float4(
+      expf(x.x - st.x) / st.y, expf(x.y - st.x) / st.y, expf(x.z - st.x) / st.y, expf(x.w - st.x) / st.y);
+}
+
+int softmax_chunks(int V) { return (V + kSmChunk - 1) / kSmChunk; }
 
 // ---------------------------------------------------------------------------
 // Launchers
@@ -404,8 +442,17 @@ hipError_t launch_rmsnorm_rows(const RowNormArgs &a, hipStream_t s, const Launch
 
 hipError_t launch_softmax_argmax(const SoftmaxArgs &a, hipStream_t s, const LaunchEvents &ev) {
   if (a.M <= 0) return hipSuccess;
-  if (a.V % 4 || a.ld % 4 || (a.probs && a.ldp % 4)) return hipErrorInvalidValue;
-  lc_launch<softmax_argmax_kernel>(dim3(a.M), dim3(256), 0, s, ev, a);
+  if (a.V % 4 || a.ld % 4 || (a.probs && a.ldp % 4) || !a.part || !a.part_idx || !a.row_stat) return hipErrorInvalidValue;
+  const int nch = softmax_chunks(a.V);
+  // The three launches share one event pair: the first stamps the start, the last the end.
+  const LaunchEvents first{ev.start, nullptr}, last{nullptr, ev.stop};
+  lc_launch<softmax_partial_kernel>(dim3(nch, a.M), dim3(256), 0, s, first, a);
+  if (a.probs) {
+    lc_launch<softmax_combine_kernel>(dim3((a.M + 3) / 4), dim3(256), 0, s, LaunchEvents{}, a, nch);
+    lc_launch<softmax_probs_kernel>(dim3((a.V / 4 + 255) / 256, a.M), dim3(256), 0, s, last, a);
+  } else {
+    lc_launch<softmax_combine_kernel>(dim3((a.M + 3) / 4), dim3(256), 0, s, last, a, nch);
+  }
   return hipGetLastError();
 }
 

@@ -410,9 +410,11 @@ LACACHE_API lacache_status lacache_sampler_workspace_size(const lacache_ctx *ctx
  * + rms_eps)); logits = z w_lm^T in fp32 (w_lm [vocab, d_model] bf16);
  * token[t] = the argmax (the first index among equal maxima), confidence[t]
  * = its softmax probability 1 / sum_v exp(logit_v - max); probs [M, vocab]
- * fp32, unless NULL, every probability.  Workspace after the call: z
- * [M, d_model] bf16, then (at a multiple of 256 bytes) the logits [M, vocab]
- * fp32. */
+ * fp32, unless NULL, every probability.  Workspace after the call (each
+ * part at a multiple of 256 bytes, in this order): z [M, d_model] bf16; the
+ * logits [M, vocab] fp32; the softmax's per-chunk (max, sum exp(l - max))
+ * [M, ceil(vocab / 4096)] float pairs and chunk argmaxes int32; the rows'
+ * (max, sum) [M] float pairs. */
 LACACHE_API lacache_status lacache_sampler_cut(lacache_ctx *ctx, const void *hidden, int64_t n_rows,
                                                const lacache_seq *seqs, int32_t batch, const void *gamma_final,
                                                const void *w_lm, int32_t vocab, int32_t *token, float *confidence,
