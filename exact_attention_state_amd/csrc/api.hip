@@ -512,6 +512,9 @@ lacache_status lacache_workspace_size(const lacache_ctx *cctx, int32_t op, const
       // seqs: the table of the rows to re-project (lacache_refresh_block's proj)
       *bytes = gemm_capable(ctx) ? gemm_bytes(ctx, block_tokens(seqs, batch)) : 0;
       return LACACHE_OK;
+    case LACACHE_OP_PROJECT_BLOCK:
+      *bytes = gemm_capable(ctx) ? gemm_bytes(ctx, block_tokens(seqs, batch)) : 0;
+      return LACACHE_OK;
   }
   return fail(ctx, LACACHE_ERR_INVALID_ARG, "unknown op %d", op);
 }
@@ -880,6 +883,35 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     if (e != hipSuccess) return hip_fail(ctx, "block-step invariant-rows launch", e);
     row_base += M;
     part_base += sa.pre[3][ns];
+  }
+  return LACACHE_OK;
+}
+
+lacache_status lacache_project_block(lacache_ctx *ctx, const lacache_weights *w, const int32_t *block_ids,
+                                     const lacache_seq *seqs, int32_t batch, const lacache_cache *cache,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if ((st = check_weights(ctx, w)) != LACACHE_OK) return st;
+  if ((st = check_cache(ctx, cache, false)) != LACACHE_OK) return st;
+  if (!block_ids) return fail(ctx, LACACHE_ERR_INVALID_ARG, "block_ids is NULL");
+  if ((st = check_table(ctx, seqs, batch, cache->n_rows)) != LACACHE_OK) return st;
+  const int64_t Mall = block_tokens(seqs, batch);
+  const bool gemm = step_uses_prep(ctx, w, Mall);
+  const size_t need = gemm ? gemm_bytes(ctx, Mall) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
+                workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int row_base = 0;
+  for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
+    const int ns = std::min(kMaxInline, batch - s0);
+    lc::SeqArgs sa = slice_args(seqs, s0, ns);
+    for (int i = 0; i < ns; ++i) sa.pre[0][i + 1] = sa.pre[0][i] + (sa.be[i] - sa.bs[i]);
+    hipError_t e = project_block_rows(ctx, w, cache, block_ids, sa, row_base, gemm, static_cast<char *>(workspace), s);
+    if (e != hipSuccess) return hip_fail(ctx, "block projection launch", e);
+    row_base += sa.pre[0][ns];
   }
   return LACACHE_OK;
 }

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "liblacache.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
-OP_PREFILL, OP_BLOCK_STEP, OP_DUALCACHE_ATTN, OP_REFRESH_BLOCK = 0, 1, 2, 3
+OP_PREFILL, OP_BLOCK_STEP, OP_DUALCACHE_ATTN, OP_REFRESH_BLOCK, OP_PROJECT_BLOCK = 0, 1, 2, 3, 4
 DEVFLAG_BAD_TOKEN_ID = 1
 DEVFLAG_CACHE_RANGE = 2
 
@@ -29,7 +29,7 @@ EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "laca
             "lacache_packed_weight_size", "lacache_pack_qkv_weight", "lacache_block_step_noalloc",
             "lacache_ffn_weight_bytes", "lacache_ffn_pack_weights", "lacache_ffn_workspace_size", "lacache_ffn_fp8",
             "lacache_layer_finish_workspace_size", "lacache_layer_finish", "lacache_sampler_workspace_size",
-            "lacache_sampler_cut")
+            "lacache_sampler_cut", "lacache_project_block")
 (KERNEL_QKV, KERNEL_BLOCK_ROWS, KERNEL_INVARIANT_ROWS, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_QKV_PREP,
  KERNEL_QKV_GEMM, KERNEL_ATTN, KERNEL_FFN_NORM, KERNEL_FFN_GATE_UP, KERNEL_FFN_DOWN, KERNEL_LAYER_OPROJ,
  KERNEL_LAYER_NORM, KERNEL_LAYER_GATE_UP, KERNEL_LAYER_DOWN, KERNEL_SAMPLER_NORM, KERNEL_SAMPLER_LMHEAD,
@@ -111,6 +111,8 @@ def load_library(path: str = LIB_PATH):
         "lacache_ffn_pack_weights": (st, [P, I32, P, P, P, P, P, P, P, P]),
         "lacache_ffn_workspace_size": (st, [P, I32, I64, I32, ctypes.POINTER(SZ)]),
         "lacache_ffn_fp8": (st, [P, I32, ctypes.POINTER(FfnWeights), P, P, I64, P, P, P, SZ, P]),
+        "lacache_project_block": (st, [P, ctypes.POINTER(Weights), P, ctypes.POINTER(Seq), I32,
+                                       ctypes.POINTER(Cache), P, SZ, P]),
         "lacache_layer_finish_workspace_size": (st, [P, I32, I64, I32, ctypes.POINTER(SZ)]),
         "lacache_layer_finish": (st, [P, I32, ctypes.POINTER(LayerWeights), P, P, I64, P, P, P, SZ, P]),
         "lacache_sampler_workspace_size": (st, [P, I32, ctypes.POINTER(Seq), I32, ctypes.POINTER(SZ)]),
@@ -288,6 +290,16 @@ class Context:
                                          _ptr(ct.lse) if lse else None, _ptr(workspace),
                                          0 if workspace is None else workspace.numel(), _stream(stream))
         self._check(st, "lacache_block_step")
+
+    def project_block(self, weights, block_ids, table, ct: CacheTensors, workspace=None, stream=None):
+        """lacache_project_block: a1-a5 for the block rows (RoPECache q, k, v and EmbedCache), no attention."""
+        w = self._weights(*weights)
+        seqs = _seqs(table)
+        cache = self._cache(ct)
+        st = self.lib.lacache_project_block(self.handle, ctypes.byref(w), _ptr(self._ids(block_ids)), seqs, len(table),
+                                            ctypes.byref(cache), _ptr(workspace),
+                                            0 if workspace is None else workspace.numel(), _stream(stream))
+        self._check(st, "lacache_project_block")
 
     def block_step_noalloc(self, weights, block_ids, table, ct: CacheTensors, stream=None, lse=True):
         """lacache_block_step_noalloc: the block step on the library's static scratch (no workspace)."""

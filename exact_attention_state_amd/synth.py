@@ -297,3 +297,22 @@ def lm_head_params(d_model: int, vocab: int, family: int = 0) -> dict:
         n = min(8192, vocab - r0)
         w[r0:r0 + n] = g.standard_normal((n, d_model), dtype=np.float32) * np.float32(0.02)
     return {"gamma_f": gamma_f, "w_lm": round_to_bf16(w)}
+
+
+def multilayer_params(d_model: int, n_heads: int, head_dim: int, d_ff: int, n_layers: int, vocab: int,
+                      qkv_std: float = 0.02, family: int = 0) -> dict:
+    """A model of n_layers layers of one shape (bf16 values, float32 arrays):
+    the embedding E [vocab, D] ~ N(0, 1); per layer the attention RMSNorm gain
+    ~ 1 + N(0, 0.1), W_qkv [3 H d_h, D] ~ N(0, qkv_std^2) (rows: Q heads, K
+    heads, V heads), and the rest of the layer as layer_params."""
+    rng = np.random.default_rng([BASE_SEED, 90 + family, d_model, n_heads, n_layers, vocab])
+    p = {"embed": round_to_bf16(rng.standard_normal((vocab, d_model), dtype=np.float32)), "layers": []}
+    for li in range(n_layers):
+        r = np.random.default_rng([BASE_SEED, 90 + family, d_model, n_heads, n_layers, vocab, li])
+        lp = layer_params(d_model, n_heads * head_dim, d_ff, 1000 * (family + 1) + li)
+        lp["gamma_ffn"] = lp.pop("gamma")
+        lp["gamma_attn"] = round_to_bf16(1.0 + r.standard_normal(d_model, dtype=np.float32) * np.float32(0.1))
+        lp["w_qkv"] = round_to_bf16(r.standard_normal((3 * n_heads * head_dim, d_model), dtype=np.float32)
+                                    * np.float32(qkv_std))
+        p["layers"].append(lp)
+    return p

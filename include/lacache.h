@@ -157,7 +157,8 @@ typedef enum {
   LACACHE_OP_PREFILL = 0,
   LACACHE_OP_BLOCK_STEP = 1,
   LACACHE_OP_DUALCACHE_ATTN = 2,
-  LACACHE_OP_REFRESH_BLOCK = 3     /* seqs: the table of the rows to re-project (proj) */
+  LACACHE_OP_REFRESH_BLOCK = 3,    /* seqs: the table of the rows to re-project (proj) */
+  LACACHE_OP_PROJECT_BLOCK = 4
 } lacache_op;
 
 /* Creates a context on the current HIP device: validates the configuration,
@@ -286,6 +287,22 @@ LACACHE_API lacache_status lacache_dualcache_attn(lacache_ctx *ctx, const void *
                                       void *out_block, float *lse_block,
                                       void *workspace, size_t workspace_bytes,
                                       void *stream);
+
+/* Steps a1-a5 alone for the block rows: gathers the rows of w->embed named
+ * by block_ids, writes them to cache->h, and writes the block rows' RoPE'd
+ * q, k, v into the RoPECache, exactly as lacache_block_step does, with no
+ * attention (cache->m, l, o are not read and may be NULL).  For a layer
+ * after the first, w->embed is that layer's input rows (the previous layer's
+ * output, [rows, d_model]) and block_ids the rows' own indices, so the
+ * "embedding" of a token is its hidden row: the block's fresh q, k, v of
+ * that layer, to be attended by lacache_dualcache_attn over the layer's
+ * cached keys (the DualCache inner step of the DualCache page, "Block-wise
+ * Generation"; approximate at layers after the first, where the other rows'
+ * keys are those of the last refresh).  Workspace:
+ * lacache_workspace_size(LACACHE_OP_PROJECT_BLOCK). */
+LACACHE_API lacache_status lacache_project_block(lacache_ctx *ctx, const lacache_weights *w, const int32_t *block_ids,
+                                                 const lacache_seq *seqs, int32_t batch, const lacache_cache *cache,
+                                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Per-group FP8 FFN of the layers after the first (LaCache Section 3.4,

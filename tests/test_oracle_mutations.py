@@ -3,8 +3,9 @@
 Each mutation below replaces one oracle function with a plausibly wrong
 version (a dropped term, a wrong sign, index, base, rounding or operand
 order); with it in place, at least one pin of tests/test_oracle_pins.py,
-tests/test_fp8_oracle_pins.py or tests/test_layer_oracle_pins.py other than
-the regression fixture (which the oracle itself wrote) must fail.  The mistakes
+tests/test_fp8_oracle_pins.py, tests/test_layer_oracle_pins.py or
+tests/test_multilayer_oracle_pins.py other than the regression fixture (which
+the oracle itself wrote) must fail.  The mistakes
 are planted in the oracle on the CPU only; no GPU is used.
 """
 
@@ -15,15 +16,17 @@ import oracle
 import oracle.fp8_ref as q8
 import oracle.lacache_ref as ref
 import oracle.layer_ref as lay
+import oracle.multilayer_ref as mlr
 import test_fp8_oracle_pins as fp8_pins
 import test_layer_oracle_pins as layer_pins
+import test_multilayer_oracle_pins as ml_pins
 import test_oracle_pins as pins
 
 
 def _pin_calls():
     """Every pin as a zero-argument call (parametrized pins expanded)."""
     calls = []
-    for mod, name in sorted([(p, n) for p in (pins, fp8_pins, layer_pins) for n in dir(p)], key=lambda x: x[1]):
+    for mod, name in sorted([(p, n) for p in (pins, fp8_pins, layer_pins, ml_pins) for n in dir(p)], key=lambda x: x[1]):
         fn = getattr(mod, name)
         if not name.startswith("test_") or not callable(fn) or name == "test_oracle_regression_fixture":
             continue
@@ -218,6 +221,29 @@ def _sample_rows_last_max(hidden_rows, gamma_f, w_lm, eps):
     return out
 
 
+def _approx_all_fresh(params, cfg, state, ids, seqs):
+    # recomputes every row at every layer: no stale keys at all
+    full = mlr.forward_full(params, cfg, ids, seqs)
+    rows = np.concatenate([np.arange(o + bs, o + be) for o, _, bs, be in seqs])
+    return full["X"][-1][rows]
+
+
+def _approx_block_rope_from_zero(params, cfg, state, ids, seqs):
+    orig = mlr.layer_qkv
+
+    def qkv(X_rows, lp, cfg_, pos):
+        return orig(X_rows, lp, cfg_, np.arange(len(pos)))
+    mlr.layer_qkv = qkv
+    try:
+        return mlr.__dict__["_orig_approx_step"](params, cfg, state, ids, seqs)
+    finally:
+        mlr.layer_qkv = orig
+
+
+def _schedule_refresh_off_by_one(params, cfg, ids_per_step, seqs, r):
+    return mlr.__dict__["_orig_run_schedule"](params, cfg, ids_per_step, seqs, None if r is None else r + 1)
+
+
 MUTATIONS = {
     "rms_norm drops gamma": ("rms_norm", _rms_no_gamma),
     "rms_norm eps outside the root": ("rms_norm", _rms_eps_outside),
@@ -244,6 +270,9 @@ MUTATIONS = {
     "sampler cut one row late": ("layer:block_rows", _block_rows_shifted),
     "softmax over the wrong axis": ("layer:softmax_rows", _softmax_columns),
     "argmax takes the last of equal maxima": ("layer:sample_rows", _sample_rows_last_max),
+    "approximate step recomputes every row": ("ml:approx_step", _approx_all_fresh),
+    "approximate step ropes the block from position 0": ("ml:approx_step", _approx_block_rope_from_zero),
+    "refresh interval one step late": ("ml:run_schedule", _schedule_refresh_off_by_one),
 }
 
 
@@ -256,6 +285,8 @@ def test_planted_mutation_fails_a_pin(mutation, monkeypatch):
         mod, fname = q8, fname[4:]
     elif fname.startswith("layer:"):
         mod, fname = lay, fname[6:]
+    elif fname.startswith("ml:"):
+        mod, fname = mlr, fname[3:]
     orig = getattr(mod, fname)
     monkeypatch.setitem(mod.__dict__, f"_orig_{fname}", orig)
     monkeypatch.setattr(mod, fname, fn)
