@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--ffn-only", action="store_true", help="only the FP8 FFN measurement (its JSON object)")
     p.add_argument("--no-layer", action="store_true", help="skip the layer-finish and sampler measurement")
     p.add_argument("--layer-only", action="store_true", help="only the layer-finish and sampler measurement")
+    p.add_argument("--no-multilayer", action="store_true", help="skip the approximate deeper-layer reuse measurement")
+    p.add_argument("--multilayer-only", action="store_true", help="only the approximate deeper-layer reuse measurement")
     return p.parse_args()
 
 
@@ -548,6 +550,59 @@ def measure_layer(dev, reps=20, n_sets=2):
     return {"layer0_finish": layer, "sampler": sampler}
 
 
+def measure_multilayer(dev, n_layers=4, vocab=32768, intervals=(None, 10, 5, 2, 1)):
+    """Approximate deeper-layer reuse (exact_attention_state_amd.multilayer) at
+    LLaDA-8B's layer shape (d_model 4096, 32 x 128 heads, d_ff 12288; W_qkv ~
+    N(0, 0.02^2)) with n_layers layers on llada8b's sequence (768 rows, block
+    32): one block of the workload's 20 inner steps with its seeded edits, for
+    each refresh interval r (None: block boundary only; 1: the full recompute
+    every step).  Per r: the relative error of the block rows' final output
+    against the full recompute at every step (mean and max over the steps),
+    and the GPU time of the block (event-bracketed, eager launches)."""
+    import numpy as np
+    import torch
+    from exact_attention_state_amd import synth
+    from exact_attention_state_amd.multilayer import MultiLayer
+    wl = synth.WORKLOADS["llada8b"]
+    D, H, dh, F = wl.d_model, wl.n_heads, wl.head_dim, synth.LLADA_D_FF
+    p = synth.multilayer_params(D, H, dh, F, n_layers, vocab, qkv_std=0.02)
+    table = wl.table()
+    rng = np.random.default_rng([synth.BASE_SEED, 7, 7])
+    ids = rng.integers(0, vocab, wl.total_tokens).astype(np.int32)
+    rows = np.concatenate([np.arange(o + bs, o + be) for o, _, bs, be in table])
+    import dataclasses
+    wl_v = dataclasses.replace(wl, vocab=vocab)                    # edits draw ids from this vocabulary
+    steps = [ids]
+    for k in range(1, wl.steps):
+        ids, _ = synth.step_ids(wl_v, ids, k)
+        steps.append(ids)
+    dsteps = [(torch.from_numpy(x).to(dev), torch.from_numpy(x[rows].copy()).to(dev)) for x in steps]
+    approx = MultiLayer(p, dh, F, table, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps, device=dev)
+    exact = MultiLayer(p, dh, F, table, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps, device=dev, weights_from=approx)
+    del p
+    ref, _ = exact.run_block(dsteps, 1)
+    ref = [x.double() for x in ref]
+    res = {"shape": {"layers": n_layers, "rows": wl.total_tokens, "block": wl.block_size, "d_model": D,
+                     "heads_x_head_dim": H * dh, "d_ff": F, "qkv_std": 0.02, "vocab": vocab},
+           "steps": len(steps), "intervals": {}}
+    for r in intervals:
+        approx.run_block(dsteps[:2], r)                          # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        outs, refreshed = approx.run_block(dsteps, r)
+        e1.record()
+        torch.cuda.synchronize()
+        err = [float(torch.linalg.norm(o.double() - g) / torch.linalg.norm(g)) for o, g in zip(outs, ref)]
+        res["intervals"][str(r)] = {"ms_per_block": e0.elapsed_time(e1), "refreshes": int(sum(refreshed)),
+                                    "rel_err_mean": float(np.mean(err)), "rel_err_max": float(np.max(err)),
+                                    "rel_err_per_step": err}
+        log(f"[bench] approximate reuse, {n_layers} layers, r = {r}: {e0.elapsed_time(e1):.2f} ms per block of "
+            f"{len(steps)} steps ({sum(refreshed)} refreshes), error vs full recompute mean {np.mean(err):.2e} "
+            f"max {np.max(err):.2e}")
+    return res
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -572,6 +627,10 @@ def main():
     if args.layer_only:
         torch.cuda.init()
         print(json.dumps(measure_layer(torch.device("cuda:0"))), flush=True)
+        return
+    if args.multilayer_only:
+        torch.cuda.init()
+        print(json.dumps({"approx_reuse": measure_multilayer(torch.device("cuda:0"))}), flush=True)
         return
     wl = synth.WORKLOADS[args.workload]
     acc = step_accounting(wl)
@@ -761,6 +820,7 @@ def main():
 
     ffn = measure_ffn(dev, ffn_rows) if ffn_rows else None
     layer = None if args.no_layer else measure_layer(dev)
+    approx_reuse = None if args.no_multilayer else measure_multilayer(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -812,6 +872,7 @@ def main():
         "ffn_fp8": ffn,
         "layer0_finish": None if layer is None else layer["layer0_finish"],
         "sampler": None if layer is None else layer["sampler"],
+        "approx_reuse": approx_reuse,
         "cpu_baseline": cpu,
         "host": platform.node(),
         "graph_error": graph_err,
