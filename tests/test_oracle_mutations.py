@@ -3,9 +3,9 @@
 Each mutation below replaces one oracle function with a plausibly wrong
 version (a dropped term, a wrong sign, index, base, rounding or operand
 order); with it in place, at least one pin of tests/test_oracle_pins.py,
-tests/test_fp8_oracle_pins.py, tests/test_layer_oracle_pins.py or
-tests/test_multilayer_oracle_pins.py other than the regression fixture (which
-the oracle itself wrote) must fail.  The mistakes
+tests/test_fp8_oracle_pins.py, tests/test_layer_oracle_pins.py,
+tests/test_multilayer_oracle_pins.py or tests/test_flashdllm_oracle_pins.py
+other than the regression fixture (which the oracle itself wrote) must fail.  The mistakes
 are planted in the oracle on the CPU only; no GPU is used.
 """
 
@@ -17,6 +17,8 @@ import oracle.fp8_ref as q8
 import oracle.lacache_ref as ref
 import oracle.layer_ref as lay
 import oracle.multilayer_ref as mlr
+import oracle.flashdllm_ref as fdr
+import test_flashdllm_oracle_pins as fd_pins
 import test_fp8_oracle_pins as fp8_pins
 import test_layer_oracle_pins as layer_pins
 import test_multilayer_oracle_pins as ml_pins
@@ -26,7 +28,7 @@ import test_oracle_pins as pins
 def _pin_calls():
     """Every pin as a zero-argument call (parametrized pins expanded)."""
     calls = []
-    for mod, name in sorted([(p, n) for p in (pins, fp8_pins, layer_pins, ml_pins) for n in dir(p)], key=lambda x: x[1]):
+    for mod, name in sorted([(p, n) for p in (pins, fp8_pins, layer_pins, ml_pins, fd_pins) for n in dir(p)], key=lambda x: x[1]):
         fn = getattr(mod, name)
         if not name.startswith("test_") or not callable(fn) or name == "test_oracle_regression_fixture":
             continue
@@ -244,6 +246,38 @@ def _schedule_refresh_off_by_one(params, cfg, ids_per_step, seqs, r):
     return mlr.__dict__["_orig_run_schedule"](params, cfg, ids_per_step, seqs, None if r is None else r + 1)
 
 
+def _importance_softmax_over_queries(q_block, k, scale, n_kv_heads=None):
+    q, kk = np.asarray(q_block, np.float64), np.asarray(k, np.float64)
+    imp = np.zeros(kk.shape[0])
+    for h in range(q.shape[1]):
+        s = scale * q[:, h] @ kk[:, h * kk.shape[1] // q.shape[1]].T
+        e = np.exp(s - s.max(axis=0, keepdims=True))
+        imp += (e / e.sum(axis=0, keepdims=True)).sum(axis=0)
+    return imp
+
+
+def _tracking_ties_to_higher_row(imp, exclude, budget):
+    imp = np.asarray(imp, np.float64)
+    ex = set(int(x) for x in exclude)
+    cand = sorted((j for j in range(len(imp)) if j not in ex), key=lambda j: (-imp[j], -j))
+    return np.array(sorted(cand[:budget]), dtype=np.int64)
+
+
+def _views_not_isolated(view, pos, n_ctx):
+    vis = fdr.__dict__["_orig_verify_visible"](view, pos, n_ctx)
+    vis[:, n_ctx:] = True
+    return vis
+
+
+def _accept_non_strict(draft_tok, mask_tok, mask_conf, gamma):
+    n = 0
+    for d, m, c in zip(draft_tok, mask_tok, mask_conf):
+        if int(d) != int(m) or not float(c) >= gamma:
+            break
+        n += 1
+    return n
+
+
 MUTATIONS = {
     "rms_norm drops gamma": ("rms_norm", _rms_no_gamma),
     "rms_norm eps outside the root": ("rms_norm", _rms_eps_outside),
@@ -273,6 +307,10 @@ MUTATIONS = {
     "approximate step recomputes every row": ("ml:approx_step", _approx_all_fresh),
     "approximate step ropes the block from position 0": ("ml:approx_step", _approx_block_rope_from_zero),
     "refresh interval one step late": ("ml:run_schedule", _schedule_refresh_off_by_one),
+    "importance normalised over the queries": ("fd:importance", _importance_softmax_over_queries),
+    "tracking ties go to the higher row": ("fd:select_tracking", _tracking_ties_to_higher_row),
+    "verify views see each other": ("fd:verify_visible", _views_not_isolated),
+    "acceptance threshold not strict": ("fd:verify_accept", _accept_non_strict),
 }
 
 
@@ -287,6 +325,8 @@ def test_planted_mutation_fails_a_pin(mutation, monkeypatch):
         mod, fname = lay, fname[6:]
     elif fname.startswith("ml:"):
         mod, fname = mlr, fname[3:]
+    elif fname.startswith("fd:"):
+        mod, fname = fdr, fname[3:]
     orig = getattr(mod, fname)
     monkeypatch.setitem(mod.__dict__, f"_orig_{fname}", orig)
     monkeypatch.setattr(mod, fname, fn)
