@@ -62,6 +62,7 @@ def parse():
     p.add_argument("--layer-only", action="store_true", help="only the layer-finish and sampler measurement")
     p.add_argument("--no-multilayer", action="store_true", help="skip the approximate deeper-layer reuse measurement")
     p.add_argument("--multilayer-only", action="store_true", help="only the approximate deeper-layer reuse measurement")
+    p.add_argument("--no-flashdllm", action="store_true", help="skip the selective update / verify measurement")
     return p.parse_args()
 
 
@@ -603,6 +604,64 @@ def measure_multilayer(dev, n_layers=4, vocab=32768, intervals=(None, 10, 5, 2, 
     return res
 
 
+def measure_flashdllm(dev, reps=50, budget=32):
+    """The selective cache update and two-view verify on llada8b after a
+    block step: lacache_track_select (importance of the 768 rows for the 32
+    block queries, then the 32-row tracking set) and lacache_verify_attn with a
+    verify query of the tracking set, a 32-token draft view and a 32-token mask
+    view (96 tokens) over the cached rows.  Median microseconds per call over
+    `reps` calls, and each call's algorithmic bytes (the sample's K rows for
+    the importance; K and V rows for the verify attention) against 8 TB/s."""
+    import numpy as np
+    import torch
+    from exact_attention_state_amd import synth
+    from exact_attention_state_amd.workload import DeviceWorkload
+    wl = synth.WORKLOADS["llada8b"]
+    dw = DeviceWorkload(wl, device=dev)
+    dw.prefill()
+    dw.block_step(dw.next_block_ids())
+    torch.cuda.synchronize()
+    (off, n, bs, be), = dw.table
+    H, Hk, d = wl.n_heads, wl.n_kv_heads, wl.head_dim
+    imp = torch.zeros(dw.n_rows, dtype=torch.float32, device=dev)
+    trk = torch.empty(1, budget, dtype=torch.int32, device=dev)
+    ws = dw.ctx.track_workspace(dw.n_rows, dev)
+    rng = np.random.default_rng(5)
+    S = be - bs
+    others = np.setdiff1d(np.arange(n), np.arange(bs, be))
+    pos = np.concatenate([np.sort(rng.choice(others, budget, replace=False)), np.arange(bs, be), np.arange(bs, be)])
+    view = np.concatenate([np.zeros(budget), np.ones(S), 2 * np.ones(S)]).astype(np.int32)
+    V = len(pos)
+    qv, kv, vv = (torch.randn(V, hh, d, device=dev, dtype=torch.float16) for hh in (H, Hk, Hk))
+    pos_d, view_d = torch.from_numpy(pos.astype(np.int32)).to(dev), torch.from_numpy(view).to(dev)
+    out = torch.empty(V, H, d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(V, H, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) * 1e3 for a, b in ev)[reps // 2]
+
+    t_trk = timed(lambda: dw.ctx.track_select(dw.ct, dw.table, budget, imp, trk, workspace=ws))
+    t_ver = timed(lambda: dw.ctx.verify_attn(qv, kv, vv, view_d, pos_d, [0, V], dw.ct, dw.table, out, lse))
+    kv_row = Hk * d * 2
+    res = {"budget": budget, "verify_tokens": V,
+           "track_select": {"us_per_call": t_trk, "algorithmic_bytes": n * kv_row + S * H * d * 2,
+                            "hbm_frac": (n * kv_row + S * H * d * 2) / (t_trk * 1e-6) / 1e9 / HBM_PEAK_GBS},
+           "verify_attn": {"us_per_call": t_ver, "algorithmic_bytes": 2 * n * kv_row + V * (H + 2 * Hk) * d * 2,
+                           "hbm_frac": (2 * n * kv_row + V * (H + 2 * Hk) * d * 2) / (t_ver * 1e-6) / 1e9 / HBM_PEAK_GBS}}
+    log(f"[bench] selective update: track_select {t_trk:.1f} us; verify attention ({V} tokens) {t_ver:.1f} us")
+    assert dw.ctx.read_device_status() == 0
+    return res
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -630,7 +689,8 @@ def main():
         return
     if args.multilayer_only:
         torch.cuda.init()
-        print(json.dumps({"approx_reuse": measure_multilayer(torch.device("cuda:0"))}), flush=True)
+        print(json.dumps({"approx_reuse": measure_multilayer(torch.device("cuda:0")),
+                          "selective_verify": measure_flashdllm(torch.device("cuda:0"))}), flush=True)
         return
     wl = synth.WORKLOADS[args.workload]
     acc = step_accounting(wl)
@@ -821,6 +881,7 @@ def main():
     ffn = measure_ffn(dev, ffn_rows) if ffn_rows else None
     layer = None if args.no_layer else measure_layer(dev)
     approx_reuse = None if args.no_multilayer else measure_multilayer(dev)
+    sel_verify = None if args.no_flashdllm else measure_flashdllm(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -873,6 +934,7 @@ def main():
         "layer0_finish": None if layer is None else layer["layer0_finish"],
         "sampler": None if layer is None else layer["sampler"],
         "approx_reuse": approx_reuse,
+        "selective_verify": sel_verify,
         "cpu_baseline": cpu,
         "host": platform.node(),
         "graph_error": graph_err,

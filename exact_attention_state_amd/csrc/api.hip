@@ -458,6 +458,7 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   if (e == hipSuccess) e = lc::setup_gemm_attributes();
   if (e == hipSuccess) e = lc::setup_fp8_attributes();
   if (e == hipSuccess) e = lc::setup_layer_attributes();
+  if (e == hipSuccess) e = lc::setup_flashdllm_attributes();
   if (e != hipSuccess) {
     if (ctx->rope) (void)hipFree(ctx->rope);
     if (ctx->flags) (void)hipFree(ctx->flags);
@@ -1443,6 +1444,160 @@ lacache_status lacache_sampler_cut(lacache_ctx *ctx, const void *hidden, int64_t
     return lc::launch_softmax_argmax(sm, s, ev);
   });
   if (e != hipSuccess) return hip_fail(ctx, "sampler softmax launch", e);
+  return LACACHE_OK;
+}
+
+namespace {
+bool flashdllm_capable(const lacache_ctx *ctx) {
+  return ctx->cfg.dtype == LACACHE_BF16 && (ctx->cfg.head_dim == 64 || ctx->cfg.head_dim == 128);
+}
+const char *kFlashNeeds = "the selective update and verify need bf16 (fp16 RoPECache) and head_dim 64 or 128";
+int max_seq_len_of(const lacache_seq *seqs, int32_t batch) {
+  int m = 0;
+  for (int i = 0; i < batch; ++i) m = std::max(m, seqs[i].seq_len);
+  return m;
+}
+// Host prefix sums over samples (verify tokens or search positions): non-decreasing, from >= 0.
+lacache_status check_prefix(lacache_ctx *ctx, const int32_t *start, int32_t batch, int max_per_sample, const char *what) {
+  if (!start) return fail(ctx, LACACHE_ERR_INVALID_ARG, "%s is NULL", what);
+  if (start[0] < 0) return fail(ctx, LACACHE_ERR_INVALID_ARG, "%s[0] < 0", what);
+  for (int i = 0; i < batch; ++i) {
+    const int n = start[i + 1] - start[i];
+    if (n < 0) return fail(ctx, LACACHE_ERR_INVALID_ARG, "%s decreases at sample %d", what, i);
+    if (max_per_sample > 0 && n > max_per_sample)
+      return fail(ctx, LACACHE_ERR_UNSUPPORTED, "%s: %d entries for sample %d (at most %d)", what, n, i, max_per_sample);
+  }
+  return LACACHE_OK;
+}
+}  // namespace
+
+lacache_status lacache_track_workspace_size(const lacache_ctx *ctx, int64_t n_rows, size_t *bytes) {
+  if (!ctx || !bytes || n_rows < 1) return LACACHE_ERR_INVALID_ARG;
+  *bytes = align256((size_t)ctx->cfg.n_heads * n_rows * sizeof(float));
+  return LACACHE_OK;
+}
+
+lacache_status lacache_track_select(lacache_ctx *ctx, const lacache_cache *cache, const float *lse,
+                                    const lacache_seq *seqs, int32_t batch, int32_t budget, float *importance,
+                                    int32_t *tracked, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if (!flashdllm_capable(ctx)) return fail(ctx, LACACHE_ERR_UNSUPPORTED, "%s", kFlashNeeds);
+  if ((st = check_cache(ctx, cache, false)) != LACACHE_OK) return st;
+  if ((st = check_table(ctx, seqs, batch, cache->n_rows)) != LACACHE_OK) return st;
+  if (budget < 1 || budget > 64) return fail(ctx, LACACHE_ERR_UNSUPPORTED, "budget %d (1 .. 64 supported)", budget);
+  if (max_seq_len_of(seqs, batch) > lc::kTrackMaxKeys)
+    return fail(ctx, LACACHE_ERR_UNSUPPORTED, "sequences of more than %d rows", lc::kTrackMaxKeys);
+  if (!lse || !importance || !tracked) return fail(ctx, LACACHE_ERR_INVALID_ARG, "lse, importance or tracked is NULL");
+  const size_t need = (size_t)ctx->cfg.n_heads * cache->n_rows * sizeof(float);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(ctx, LACACHE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes,
+                workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  lc::TrackArgs ta;
+  ta.q = cache->q;
+  ta.lse = lse;
+  ta.k = cache->k;
+  ta.partial = static_cast<float *>(workspace);
+  ta.importance = importance;
+  ta.tracked = tracked;
+  ta.n_rows = cache->n_rows;
+  ta.H = ctx->cfg.n_heads;
+  ta.Hkv = ctx->cfg.n_kv_heads;
+  ta.budget = budget;
+  ta.scale_log2 = scale_log2(ctx);
+  for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
+    const int ns = std::min(kMaxInline, batch - s0);
+    lc::SeqArgs sa = slice_args(seqs, s0, ns);
+    for (int i = 0; i < ns; ++i) sa.pre[1][i + 1] = sa.pre[1][i] + (sa.len[i] + 63) / 64;
+    ta.sample_base = s0;
+    hipError_t e = timed(ctx, LACACHE_KERNEL_TRACK_IMPORTANCE, s, [&](const lc::LaunchEvents &ev) {
+      return lc::launch_importance(ctx->cfg.head_dim, sa, ta, s, ev);
+    });
+    if (e != hipSuccess) return hip_fail(ctx, "importance launch", e);
+    e = timed(ctx, LACACHE_KERNEL_TRACK_SELECT, s, [&](const lc::LaunchEvents &ev) {
+      return lc::launch_track_select(sa, ta, max_seq_len_of(seqs + s0, ns), s, ev);
+    });
+    if (e != hipSuccess) return hip_fail(ctx, "tracking selection launch", e);
+  }
+  return LACACHE_OK;
+}
+
+lacache_status lacache_verify_attn(lacache_ctx *ctx, const void *q_ver, const void *k_ver, const void *v_ver,
+                                   const int32_t *view, const int32_t *pos, const int32_t *ver_start,
+                                   const lacache_cache *cache, const lacache_seq *seqs, int32_t batch, void *out,
+                                   float *lse, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if (!flashdllm_capable(ctx)) return fail(ctx, LACACHE_ERR_UNSUPPORTED, "%s", kFlashNeeds);
+  if ((st = check_cache(ctx, cache, false)) != LACACHE_OK) return st;
+  if ((st = check_table(ctx, seqs, batch, cache->n_rows, INT32_MAX)) != LACACHE_OK) return st;
+  if (max_seq_len_of(seqs, batch) > lc::kVerifyMaxKeys)
+    return fail(ctx, LACACHE_ERR_UNSUPPORTED, "sequences of more than %d rows", lc::kVerifyMaxKeys);
+  if ((st = check_prefix(ctx, ver_start, batch, 0, "ver_start")) != LACACHE_OK) return st;
+  const void *ptrs[6] = {q_ver, k_ver, v_ver, view, pos, out};
+  for (const void *p : ptrs)
+    if (!p || !aligned16(p)) return fail(ctx, LACACHE_ERR_INVALID_ARG, "a pointer is NULL or not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  lc::VerifyArgs va;
+  va.q = q_ver;
+  va.k_ver = k_ver;
+  va.v_ver = v_ver;
+  va.view = view;
+  va.pos = pos;
+  va.k = cache->k;
+  va.v = cache->v;
+  va.out = out;
+  va.lse = lse;
+  va.H = ctx->cfg.n_heads;
+  va.Hkv = ctx->cfg.n_kv_heads;
+  va.scale_log2 = scale_log2(ctx);
+  for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
+    const int ns = std::min(kMaxInline, batch - s0);
+    lc::SeqArgs sa = slice_args(seqs, s0, ns);
+    for (int i = 0; i <= ns; ++i) sa.pre[0][i] = ver_start[s0 + i];
+    for (int i = 0; i < ns; ++i) sa.pre[1][i + 1] = sa.pre[1][i] + (ver_start[s0 + i + 1] - ver_start[s0 + i] + 63) / 64;
+    hipError_t e = timed(ctx, LACACHE_KERNEL_VERIFY_ATTN, s, [&](const lc::LaunchEvents &ev) {
+      return lc::launch_verify_attn(ctx->cfg.head_dim, sa, va, s, ev);
+    });
+    if (e != hipSuccess) return hip_fail(ctx, "verify attention launch", e);
+  }
+  return LACACHE_OK;
+}
+
+lacache_status lacache_verify_accept(lacache_ctx *ctx, const int32_t *draft, const int32_t *mask_tok,
+                                     const float *mask_conf, const int32_t *pos, const int32_t *search_start,
+                                     const lacache_seq *seqs, int32_t batch, float gamma, int32_t *ids,
+                                     int32_t *n_accepted, void *stream) {
+  if (!ctx) return LACACHE_ERR_INVALID_ARG;
+  lacache_status st;
+  if ((st = check_device(ctx)) != LACACHE_OK) return st;
+  if ((st = check_table(ctx, seqs, batch, -1, INT32_MAX)) != LACACHE_OK) return st;
+  if ((st = check_prefix(ctx, search_start, batch, 64, "search_start")) != LACACHE_OK) return st;
+  const void *ptrs[6] = {draft, mask_tok, mask_conf, pos, ids, n_accepted};
+  for (const void *p : ptrs)
+    if (!p) return fail(ctx, LACACHE_ERR_INVALID_ARG, "a pointer is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  lc::AcceptArgs aa;
+  aa.draft = draft;
+  aa.mask_tok = mask_tok;
+  aa.mask_conf = mask_conf;
+  aa.pos = pos;
+  aa.ids = ids;
+  aa.flags = ctx->flags;
+  aa.gamma = gamma;
+  for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
+    const int ns = std::min(kMaxInline, batch - s0);
+    lc::SeqArgs sa = slice_args(seqs, s0, ns);
+    for (int i = 0; i <= ns; ++i) sa.pre[0][i] = search_start[s0 + i];
+    aa.n_accepted = n_accepted + s0;
+    hipError_t e = timed(ctx, LACACHE_KERNEL_VERIFY_ACCEPT, s, [&](const lc::LaunchEvents &ev) {
+      return lc::launch_verify_accept(sa, aa, s, ev);
+    });
+    if (e != hipSuccess) return hip_fail(ctx, "verify acceptance launch", e);
+  }
   return LACACHE_OK;
 }
 

@@ -218,6 +218,47 @@ int softmax_chunks(int V);
 hipError_t launch_softmax_argmax(const SoftmaxArgs &a, hipStream_t s, const LaunchEvents &ev);
 hipError_t setup_layer_attributes();
 
+// Selective cache update and two-view verify (flashdllm.hip); fp16 RoPECache.
+constexpr int kTrackMaxKeys = 16384;     // rows per sample the tracking selection holds in LDS
+constexpr int kVerifyMaxKeys = 32768;    // rows per sample the verify attention's carried-position bitmap covers
+struct TrackArgs {
+  const void *q;           // RoPECache q [n_rows, H, dh] (the block rows' fresh queries)
+  const float *lse;        // [n_rows, H] the block rows' log-sum-exp (natural log)
+  const void *k;           // RoPECache k [n_rows, Hkv, dh]
+  float *partial;          // [H, n_rows] per-head importance (workspace)
+  float *importance;       // [n_rows] importance of every row of the table's samples
+  int *tracked;            // [batch, budget] selected rows within their sample, in row order; -1 pads
+  int64_t n_rows;
+  int H, Hkv, budget, sample_base;
+  float scale_log2;
+};
+hipError_t launch_importance(int dh, const SeqArgs &sa, const TrackArgs &a, hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_track_select(const SeqArgs &sa, const TrackArgs &a, int max_len, hipStream_t s,
+                               const LaunchEvents &ev);
+struct VerifyArgs {
+  const void *q;           // [V, H, dh] verify queries (fp16, RoPE'd at their positions); sample b: rows pre[0][b] ..
+  const void *k_ver, *v_ver;  // [V, Hkv, dh] their own keys and values
+  const int *view;         // [V] 0 tracking, 1 draft view, 2 mask view
+  const int *pos;          // [V] position within the sample each verify token carries
+  const void *k, *v;       // RoPECache [n_rows, Hkv, dh]: the context
+  void *out;               // [V, H, dh] bf16
+  float *lse;              // [V, H] natural log, or null
+  int H, Hkv;
+  float scale_log2;
+};
+hipError_t launch_verify_attn(int dh, const SeqArgs &sa, const VerifyArgs &a, hipStream_t s, const LaunchEvents &ev);
+struct AcceptArgs {
+  const int *draft, *mask_tok;  // [S] argmax tokens of the two views at the search positions
+  const float *mask_conf;  // [S] the mask view's confidence
+  const int *pos;          // [S] search positions within the sample, increasing
+  int *ids;                // [n_rows] token ids; accepted draft tokens are written at off + pos
+  int *n_accepted;         // [batch]
+  unsigned *flags;
+  float gamma;
+};
+hipError_t launch_verify_accept(const SeqArgs &sa, const AcceptArgs &a, hipStream_t s, const LaunchEvents &ev);
+hipError_t setup_flashdllm_attributes();
+
 // Work decomposition shared by the planner and the kernels.
 constexpr int kRowsA = 32;     // block rows per type-A item
 constexpr int kRowsB = 64;     // invariant rows per type-B item

@@ -22,6 +22,7 @@ F32, BF16 = 0, 1
 OP_PREFILL, OP_BLOCK_STEP, OP_DUALCACHE_ATTN, OP_REFRESH_BLOCK, OP_PROJECT_BLOCK = 0, 1, 2, 3, 4
 DEVFLAG_BAD_TOKEN_ID = 1
 DEVFLAG_CACHE_RANGE = 2
+DEVFLAG_SEARCH_ORDER = 4
 
 EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "lacache_prefill_cache",
             "lacache_block_step", "lacache_refresh_block", "lacache_dualcache_attn", "lacache_read_device_status",
@@ -29,14 +30,17 @@ EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "laca
             "lacache_packed_weight_size", "lacache_pack_qkv_weight", "lacache_block_step_noalloc",
             "lacache_ffn_weight_bytes", "lacache_ffn_pack_weights", "lacache_ffn_workspace_size", "lacache_ffn_fp8",
             "lacache_layer_finish_workspace_size", "lacache_layer_finish", "lacache_sampler_workspace_size",
-            "lacache_sampler_cut", "lacache_project_block")
+            "lacache_sampler_cut", "lacache_project_block", "lacache_track_workspace_size",
+            "lacache_track_select", "lacache_verify_attn", "lacache_verify_accept")
 (KERNEL_QKV, KERNEL_BLOCK_ROWS, KERNEL_INVARIANT_ROWS, KERNEL_MERGE, KERNEL_REFRESH_ATTN, KERNEL_QKV_PREP,
  KERNEL_QKV_GEMM, KERNEL_ATTN, KERNEL_FFN_NORM, KERNEL_FFN_GATE_UP, KERNEL_FFN_DOWN, KERNEL_LAYER_OPROJ,
  KERNEL_LAYER_NORM, KERNEL_LAYER_GATE_UP, KERNEL_LAYER_DOWN, KERNEL_SAMPLER_NORM, KERNEL_SAMPLER_LMHEAD,
- KERNEL_SAMPLER_SOFTMAX) = range(18)
+ KERNEL_SAMPLER_SOFTMAX, KERNEL_TRACK_IMPORTANCE, KERNEL_TRACK_SELECT, KERNEL_VERIFY_ATTN,
+ KERNEL_VERIFY_ACCEPT) = range(22)
 KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn", "qkv_prep", "qkv_gemm", "attn",
                 "ffn_norm", "ffn_gate_up", "ffn_down", "layer_oproj", "layer_norm", "layer_gate_up", "layer_down",
-                "sampler_norm", "sampler_lmhead", "sampler_softmax")
+                "sampler_norm", "sampler_lmhead", "sampler_softmax", "track_importance", "track_select",
+                "verify_attn", "verify_accept")
 
 
 class Config(ctypes.Structure):
@@ -113,6 +117,12 @@ def load_library(path: str = LIB_PATH):
         "lacache_ffn_fp8": (st, [P, I32, ctypes.POINTER(FfnWeights), P, P, I64, P, P, P, SZ, P]),
         "lacache_project_block": (st, [P, ctypes.POINTER(Weights), P, ctypes.POINTER(Seq), I32,
                                        ctypes.POINTER(Cache), P, SZ, P]),
+        "lacache_track_workspace_size": (st, [P, I64, ctypes.POINTER(SZ)]),
+        "lacache_track_select": (st, [P, ctypes.POINTER(Cache), P, ctypes.POINTER(Seq), I32, I32, P, P, P, SZ, P]),
+        "lacache_verify_attn": (st, [P, P, P, P, P, P, ctypes.POINTER(I32), ctypes.POINTER(Cache), ctypes.POINTER(Seq),
+                                     I32, P, P, P]),
+        "lacache_verify_accept": (st, [P, P, P, P, P, ctypes.POINTER(I32), ctypes.POINTER(Seq), I32, ctypes.c_float,
+                                       P, P, P]),
         "lacache_layer_finish_workspace_size": (st, [P, I32, I64, I32, ctypes.POINTER(SZ)]),
         "lacache_layer_finish": (st, [P, I32, ctypes.POINTER(LayerWeights), P, P, I64, P, P, P, SZ, P]),
         "lacache_sampler_workspace_size": (st, [P, I32, ctypes.POINTER(Seq), I32, ctypes.POINTER(SZ)]),
@@ -428,6 +438,57 @@ class Context:
                                           ws.numel(), _stream(stream))
         self._check(st, "lacache_sampler_cut")
         return ws
+
+    # ------------------------------------------------------------------
+    # Selective cache update and two-view verify
+    # ------------------------------------------------------------------
+    def track_workspace(self, n_rows, device="cuda"):
+        n = ctypes.c_size_t()
+        self._check(self.lib.lacache_track_workspace_size(self.handle, n_rows, ctypes.byref(n)),
+                    "lacache_track_workspace_size")
+        return torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+
+    def track_select(self, ct: CacheTensors, table, budget, importance, tracked, workspace=None, stream=None):
+        """Importance of every row (importance [n_rows] fp32) for the block queries in ct.q with the LSE in
+        ct.lse, and the tracking set (tracked [batch, budget] int32, positions within the sample, -1 pads)."""
+        if importance.dtype != torch.float32 or tracked.dtype != torch.int32:
+            raise ValueError("importance must be fp32 and tracked int32")
+        if importance.numel() < ct.n_rows or tracked.numel() < len(table) * budget:
+            raise ValueError("importance or tracked is too small")
+        ws = workspace if workspace is not None else self.track_workspace(ct.n_rows, importance.device)
+        cache = self._cache(ct)
+        st = self.lib.lacache_track_select(self.handle, ctypes.byref(cache), _ptr(ct.lse), _seqs(table), len(table),
+                                          budget, _ptr(importance), _ptr(tracked), _ptr(ws), ws.numel(),
+                                          _stream(stream))
+        self._check(st, "lacache_track_select")
+
+    def verify_attn(self, q_ver, k_ver, v_ver, view, pos, ver_start, ct: CacheTensors, table, out, lse=None,
+                    stream=None):
+        """Two-view verify attention; ver_start: host list [batch + 1] of the samples' first verify tokens."""
+        for name, t in (("q_ver", q_ver), ("k_ver", k_ver), ("v_ver", v_ver)):
+            if t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous fp16 CUDA tensor")
+        if view.dtype != torch.int32 or pos.dtype != torch.int32 or out.dtype != torch.bfloat16:
+            raise ValueError("view and pos must be int32, out bf16")
+        starts = (ctypes.c_int32 * (len(table) + 1))(*[int(x) for x in ver_start])
+        cache = self._cache(ct)
+        st = self.lib.lacache_verify_attn(self.handle, _ptr(q_ver), _ptr(k_ver), _ptr(v_ver), _ptr(view), _ptr(pos),
+                                         starts, ctypes.byref(cache), _seqs(table), len(table), _ptr(out), _ptr(lse),
+                                         _stream(stream))
+        self._check(st, "lacache_verify_attn")
+
+    def verify_accept(self, draft, mask_tok, mask_conf, pos, search_start, table, gamma, ids, n_accepted,
+                      stream=None):
+        """Sequential acceptance; search_start: host list [batch + 1]; updates ids in place."""
+        for name, t in (("draft", draft), ("mask_tok", mask_tok), ("pos", pos), ("ids", ids),
+                        ("n_accepted", n_accepted)):
+            if t.dtype != torch.int32 or not t.is_cuda:
+                raise ValueError(f"{name} must be an int32 CUDA tensor")
+        starts = (ctypes.c_int32 * (len(table) + 1))(*[int(x) for x in search_start])
+        st = self.lib.lacache_verify_accept(self.handle, _ptr(draft), _ptr(mask_tok), _ptr(mask_conf), _ptr(pos),
+                                           starts, _seqs(table), len(table), float(gamma), _ptr(ids),
+                                           _ptr(n_accepted), _stream(stream))
+        self._check(st, "lacache_verify_accept")
 
     def profile(self, enable: bool):
         """Bracket every launch with HIP events (diagnostics)."""

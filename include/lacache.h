@@ -89,6 +89,8 @@ typedef enum { LACACHE_F32 = 0, LACACHE_BF16 = 1 } lacache_dtype;
 /* Device status flags (lacache_read_device_status). */
 #define LACACHE_DEVFLAG_BAD_TOKEN_ID 1u
 #define LACACHE_DEVFLAG_CACHE_RANGE 2u   /* a q/k/v value exceeded the fp16 range */
+#define LACACHE_DEVFLAG_SEARCH_ORDER 4u  /* lacache_verify_accept: search positions not increasing
+                                            or outside the sample (nothing accepted there) */
 
 /* First-layer shape (Section 3.3.2).  Supported: head_dim 64 or 128,
  * d_model a multiple of 256 up to 8192, n_heads a multiple of n_kv_heads,
@@ -438,6 +440,63 @@ LACACHE_API lacache_status lacache_sampler_cut(lacache_ctx *ctx, const void *hid
                                                float *probs, void *workspace, size_t workspace_bytes,
                                                void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Flash-dLLM's selective cache update and two-view verify (the Flash-dLLM
+ * article: the third element of "Flash-Cache: Fusing Projection, RoPE, and
+ * Cache Writes into One Kernel", and "Flash-Verify: Making the Diffusion
+ * Model Its Own Verifier").  bf16 contexts (fp16 RoPECache), head_dim 64 or
+ * 128.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes of lacache_track_select for buffers of n_rows rows. */
+LACACHE_API lacache_status lacache_track_workspace_size(const lacache_ctx *ctx, int64_t n_rows, size_t *bytes);
+
+/* Attention importance and the tracking set.  For each sample b of the
+ * table and each of its rows j: importance[seq_offset + j] = sum over heads h
+ * and the block's queries i of exp(scale q_ih . k_jh - lse_ih), the softmax
+ * weight row j receives from the current block (cache->q and cache->k: the
+ * RoPECache after the step; lse [n_rows, n_heads]: the block rows' LSE as
+ * lacache_block_step writes it).  tracked[b budget + r], r < budget: the
+ * budget rows outside the block (positions within the sample) of largest
+ * importance, the lower position on ties, in increasing position; -1 where
+ * fewer rows are eligible.  budget in [1, 64]; sequences of at most 16384
+ * rows.  Workspace: lacache_track_workspace_size(cache->n_rows). */
+LACACHE_API lacache_status lacache_track_select(lacache_ctx *ctx, const lacache_cache *cache, const float *lse,
+                                                const lacache_seq *seqs, int32_t batch, int32_t budget,
+                                                float *importance, int32_t *tracked, void *workspace,
+                                                size_t workspace_bytes, void *stream);
+
+/* Two-view verify attention.  Sample b's verify tokens are rows
+ * ver_start[b] .. ver_start[b+1]-1 (ver_start: host, non-decreasing) of
+ * q_ver, k_ver, v_ver ([*, n_heads / n_kv_heads, head_dim] fp16, RoPE'd at
+ * their positions: the projection of the verify query), with view[t] (0
+ * tracking, 1 draft view, 2 mask view) and pos[t] (the position within the
+ * sample it carries).  Each verify query attends over the sample's cached
+ * rows (cache->k, cache->v) except the positions its sample's verify tokens
+ * carry, and over the verify tokens' own keys of view 0 or of its own view.
+ * out [*, n_heads, head_dim] bf16 and lse [*, n_heads] (natural log, or NULL)
+ * at the verify tokens' rows.  Sequences of at most 32768 rows. */
+LACACHE_API lacache_status lacache_verify_attn(lacache_ctx *ctx, const void *q_ver, const void *k_ver,
+                                               const void *v_ver, const int32_t *view, const int32_t *pos,
+                                               const int32_t *ver_start, const lacache_cache *cache,
+                                               const lacache_seq *seqs, int32_t batch, void *out, float *lse,
+                                               void *stream);
+
+/* Verify acceptance.  Sample b's search positions are entries
+ * search_start[b] .. search_start[b+1]-1 (host, non-decreasing; at most 64
+ * per sample) of pos (increasing positions within the sample), draft and
+ * mask_tok (the argmax tokens of the draft and mask views) and mask_conf (the
+ * mask view's confidence).  n_accepted[b] = the length of the longest prefix
+ * whose draft and mask tokens agree with mask_conf > gamma; the accepted
+ * draft tokens are written to ids[seq_offset + pos] (ids: the flat token ids
+ * of the table's rows).  Positions not increasing or outside the sample set
+ * LACACHE_DEVFLAG_SEARCH_ORDER and accept nothing in that sample. */
+LACACHE_API lacache_status lacache_verify_accept(lacache_ctx *ctx, const int32_t *draft, const int32_t *mask_tok,
+                                                 const float *mask_conf, const int32_t *pos,
+                                                 const int32_t *search_start, const lacache_seq *seqs,
+                                                 int32_t batch, float gamma, int32_t *ids, int32_t *n_accepted,
+                                                 void *stream);
+
 /* Bytes of the packed projection weight for this context: 0 where the
  * configuration has no many-token projection (fp32, or d_model not a
  * multiple of 512). */
@@ -487,7 +546,11 @@ typedef enum {
   LACACHE_KERNEL_SAMPLER_NORM = 15,  /* sampler: final norm of the block rows       */
   LACACHE_KERNEL_SAMPLER_LMHEAD = 16, /* sampler: lm-head GEMM (fp32 logits)        */
   LACACHE_KERNEL_SAMPLER_SOFTMAX = 17, /* sampler: float softmax and argmax         */
-  LACACHE_KERNEL_COUNT = 18
+  LACACHE_KERNEL_TRACK_IMPORTANCE = 18, /* selective update: attention importance   */
+  LACACHE_KERNEL_TRACK_SELECT = 19,  /* selective update: the tracking set          */
+  LACACHE_KERNEL_VERIFY_ATTN = 20,   /* two-view verify attention                   */
+  LACACHE_KERNEL_VERIFY_ACCEPT = 21, /* verify acceptance                           */
+  LACACHE_KERNEL_COUNT = 22
 } lacache_kernel;
 
 LACACHE_API lacache_status lacache_profile_enable(lacache_ctx *ctx, int enable);
