@@ -651,13 +651,27 @@ def measure_flashdllm(dev, reps=50, budget=32):
 
     t_trk = timed(lambda: dw.ctx.track_select(dw.ct, dw.table, budget, imp, trk, workspace=ws))
     t_ver = timed(lambda: dw.ctx.verify_attn(qv, kv, vv, view_d, pos_d, [0, V], dw.ct, dw.table, out, lse))
+    # Kernel time alone (events stamped by the dispatches; the call times above include the host's launch path).
+    dw.ctx.profile(True)
+    dw.ctx.profile_read()
+    for _ in range(reps):
+        dw.ctx.track_select(dw.ct, dw.table, budget, imp, trk, workspace=ws)
+        dw.ctx.verify_attn(qv, kv, vv, view_d, pos_d, [0, V], dw.ct, dw.table, out, lse)
+    torch.cuda.synchronize()
+    prof = dw.ctx.profile_read()
+    dw.ctx.profile(False)
+    kus = {k: prof[k][0] * 1e3 / max(prof[k][1], 1) for k in ("track_importance", "track_select", "verify_attn")}
     kv_row = Hk * d * 2
+    b_trk, b_ver = n * kv_row + S * H * d * 2, 2 * n * kv_row + V * (H + 2 * Hk) * d * 2
+    k_trk = kus["track_importance"] + kus["track_select"]
     res = {"budget": budget, "verify_tokens": V,
-           "track_select": {"us_per_call": t_trk, "algorithmic_bytes": n * kv_row + S * H * d * 2,
-                            "hbm_frac": (n * kv_row + S * H * d * 2) / (t_trk * 1e-6) / 1e9 / HBM_PEAK_GBS},
-           "verify_attn": {"us_per_call": t_ver, "algorithmic_bytes": 2 * n * kv_row + V * (H + 2 * Hk) * d * 2,
-                           "hbm_frac": (2 * n * kv_row + V * (H + 2 * Hk) * d * 2) / (t_ver * 1e-6) / 1e9 / HBM_PEAK_GBS}}
-    log(f"[bench] selective update: track_select {t_trk:.1f} us; verify attention ({V} tokens) {t_ver:.1f} us")
+           "track_select": {"us_per_call": t_trk, "kernel_us": {k: kus[k] for k in ("track_importance", "track_select")},
+                            "algorithmic_bytes": b_trk, "hbm_frac_kernels": b_trk / (k_trk * 1e-6) / 1e9 / HBM_PEAK_GBS},
+           "verify_attn": {"us_per_call": t_ver, "kernel_us": kus["verify_attn"], "algorithmic_bytes": b_ver,
+                           "hbm_frac_kernel": b_ver / (kus["verify_attn"] * 1e-6) / 1e9 / HBM_PEAK_GBS}}
+    log(f"[bench] selective update: track_select {t_trk:.1f} us per call (kernels: importance "
+        f"{kus['track_importance']:.1f} us, selection {kus['track_select']:.1f} us); verify attention ({V} tokens) "
+        f"{t_ver:.1f} us per call ({kus['verify_attn']:.1f} us kernel)")
     assert dw.ctx.read_device_status() == 0
     return res
 

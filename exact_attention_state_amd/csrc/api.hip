@@ -1558,7 +1558,7 @@ lacache_status lacache_verify_attn(lacache_ctx *ctx, const void *q_ver, const vo
     const int ns = std::min(kMaxInline, batch - s0);
     lc::SeqArgs sa = slice_args(seqs, s0, ns);
     for (int i = 0; i <= ns; ++i) sa.pre[0][i] = ver_start[s0 + i];
-    for (int i = 0; i < ns; ++i) sa.pre[1][i + 1] = sa.pre[1][i] + (ver_start[s0 + i + 1] - ver_start[s0 + i] + 63) / 64;
+    for (int i = 0; i < ns; ++i) sa.pre[1][i + 1] = sa.pre[1][i] + (ver_start[s0 + i + 1] - ver_start[s0 + i] + 15) / 16;
     hipError_t e = timed(ctx, LACACHE_KERNEL_VERIFY_ATTN, s, [&](const lc::LaunchEvents &ev) {
       return lc::launch_verify_attn(ctx->cfg.head_dim, sa, va, s, ev);
     });

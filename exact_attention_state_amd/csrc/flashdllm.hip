@@ -6,15 +6,16 @@
 //   lse_ih) over the current block's queries i of the sample (lse: the block
 //   rows' log-sum-exp from their attention), i.e. the softmax weight key row j
 //   receives.  One wave per 16 keys and head: MFMA 16x16x32 f16 of the key
-//   rows against the query rows, per-head partial sums (no atomics; the heads
-//   are added in order by the selection kernel).
+//   rows against the query rows, per-head partial sums [rows][heads] (no
+//   atomics; the heads are added in order by the selection kernel).
 // * Tracking set: per sample, the `budget` rows outside the block of largest
 //   importance (the lower row on ties), in row order.
 // * Verify attention: verify queries (tracking, draft view, mask view) over
 //   the sample's cached rows other than the positions they carry, then their
 //   own keys: a key of view 0 (tracking) is seen by every query, a key of view
 //   1 or 2 only by queries of the same view.  Flash attention per 16 queries
-//   and head, 32 keys per step, fp32 online softmax.
+//   and head, 32 keys per step, fp32 online softmax, the key tiles split over
+//   4 waves and merged.
 // * Acceptance: per sample, the longest prefix of the search positions whose
 //   draft and mask-view tokens agree with mask-view confidence above gamma;
 //   the accepted draft tokens are written into the ids.
@@ -82,75 +83,104 @@ __global__ __launch_bounds__(256) void importance_kernel(const SeqArgs sa, const
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int key = key0 + 4 * g + v;
-      if (key < N) a.partial[(size_t)h * a.n_rows + off + key] = imp[v];
+      if (key < N) a.partial[(size_t)(off + key) * a.H + h] = imp[v];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Tracking set: one workgroup per sample (N <= kTrackMaxKeys).
+// Tracking set: one workgroup per sample (N <= kTrackMaxKeys).  Every row
+// gets a 64-bit key that orders block rows last, then larger importance
+// first, then the lower row; a bitonic sort in LDS orders the keys and the
+// first `budget` name the tracking set, which one wave puts in row order.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void better_hi(float &v, int &i, float v2, int i2) {   // larger value, then lower index
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
-}
-
 __global__ __launch_bounds__(256) void track_select_kernel(const SeqArgs sa, const TrackArgs a) {
   extern __shared__ __align__(16) char smem[];
-  float *val = reinterpret_cast<float *>(smem);                   // [N]
-  __shared__ float s_v[4];
-  __shared__ int s_i[4];
-  __shared__ int s_sel[64];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  unsigned long long *key = reinterpret_cast<unsigned long long *>(smem);   // [NP]
+  const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int N = sa.len[b], off = sa.off[b], bs = sa.bs[b], be = sa.be[b];
-  for (int j = tid; j < N; j += 256) {
-    float v = 0.f;
-    for (int h = 0; h < a.H; ++h) v += a.partial[(size_t)h * a.n_rows + off + j];
-    a.importance[off + j] = v;
-    val[j] = (j >= bs && j < be) ? -INFINITY : v;
+  int NP = 1;
+  while (NP < N) NP <<= 1;
+  for (int j = tid; j < NP; j += 256) {
+    unsigned long long k = ~0ull;                                // padding: after every row
+    if (j < N) {
+      // The row's heads are contiguous: all loaded at once (up to 64 heads, a
+      // multiple of 4), then added in head order.
+      const float *pr = a.partial + (size_t)(off + j) * a.H;
+      float v = 0.f;
+      if ((a.H & 3) == 0 && a.H <= 64) {
+        float4 x[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (4 * c < a.H) x[c] = *reinterpret_cast<const float4 *>(pr + 4 * c);
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (4 * c < a.H) v = (((v + x[c].x) + x[c].y) + x[c].z) + x[c].w;
+      } else {
+        for (int h = 0; h < a.H; ++h) v += pr[h];
+      }
+      a.importance[off + j] = v;
+      // Bit 63: a block row (last); bits 62..31: the complement of the
+      // importance's bits (importance >= 0 orders like its bits, so larger
+      // first); bits 30..0: the row.
+      const bool excl = j >= bs && j < be;
+      const uint32_t desc = ~__float_as_uint(fmaxf(v, 0.f));
+      k = ((unsigned long long)excl << 63) | ((unsigned long long)desc << 31) | (uint32_t)j;
+    }
+    key[j] = k;
   }
   __syncthreads();
-  for (int r = 0; r < a.budget; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int j = tid; j < N; j += 256) better_hi(bv, bi, val[j], j);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) better_hi(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
-    if (lane == 0) {
-      s_v[w] = bv;
-      s_i[w] = bi;
+  // Pair i of a stage is (lo, lo + stride), lo = 2 i - i % stride; thread t
+  // takes pairs t, t + 256, ...  At strides up to 64 the 64 pairs of a wave lie
+  // in 128 elements no other wave touches, so the wave's own ordering suffices
+  // there; a workgroup barrier separates the stages at larger strides.
+  for (int size = 2; size <= NP; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < NP / 2; i += 256) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const unsigned long long x = key[lo], y = key[hi];
+        if ((x > y) == up) {
+          key[lo] = y;
+          key[hi] = x;
+        }
+      }
+      const int next = stride > 1 ? stride >> 1 : size;            // the next stage's stride
+      if (stride > 64 || (next > 64 && 2 * size <= NP)) __syncthreads();
+      else wave_lds_sync();
     }
-    __syncthreads();
-    if (tid == 0) {
-      float v = s_v[0];
-      int i = s_i[0];
-      for (int k = 1; k < 4; ++k) better_hi(v, i, s_v[k], s_i[k]);
-      const bool ok = v > -INFINITY;
-      s_sel[r] = ok ? i : 0x7fffffff;
-      if (ok) val[i] = -INFINITY;
+  __syncthreads();
+  // The first `budget` keys, put in row order (block rows and padding: -1, last).
+  if (tid < 64) {
+    int me = 0x7fffffff;
+    if (tid < a.budget && tid < N) {
+      const unsigned long long k = key[tid];
+      if (!(k >> 63)) me = (int)(uint32_t)(k & 0x7fffffffu);
     }
-    __syncthreads();
-  }
-  // Row order: the selection ranked by row (pads, 0x7fffffff, last, written as -1).
-  if (tid < a.budget) {
-    const int me = s_sel[tid];
     int rank = 0;
-    for (int j = 0; j < a.budget; ++j) rank += (s_sel[j] < me) || (s_sel[j] == me && j < tid);
-    a.tracked[(size_t)(a.sample_base + b) * a.budget + rank] = me == 0x7fffffff ? -1 : me;
+    for (int j = 0; j < a.budget; ++j) {
+      const int o = __shfl(me, j);
+      rank += (o < me) || (o == me && j < tid);
+    }
+    if (tid < a.budget) a.tracked[(size_t)(a.sample_base + b) * a.budget + rank] = me == 0x7fffffff ? -1 : me;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Verify attention: grid (query-tile items of 64 verify queries, heads).
+// Verify attention: one workgroup of 4 waves per (16 verify queries, head);
+// grid (query-tile items, heads).  Keys in tiles of 32 (the sample's context
+// rows, then the verify tokens' own), wave w taking tiles w, w + 4, ..., the
+// next one loaded while the current one is used; the 4 waves' states
+// (max, normaliser, unnormalised O) are merged in LDS at the end.
 // ---------------------------------------------------------------------------
 template <int DH>
 __global__ __launch_bounds__(256) void verify_attn_kernel(const SeqArgs sa, const VerifyArgs a) {
   __shared__ uint32_t s_carried[kVerifyMaxKeys / 32];
   __shared__ __align__(16) f16_t s_p[4][16 * 32];                // per wave: P [16 queries][32 keys]
-  __shared__ __align__(16) f16_t s_vt[4][DH * 32];               // per wave: V^T [DH features][32 keys]
+  constexpr int VS = DH + 8;                                     // staged V row (halves): conflict-free 16-byte writes
+  __shared__ __align__(16) f16_t s_vt[4][32 * VS];               // per wave: V [32 keys][DH (+8)]
+  __shared__ float s_m[4][16], s_l[4][16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int item = blockIdx.x, h = blockIdx.y;
   const int b = find_sample(sa.pre[1], sa.n, item);
@@ -165,8 +195,9 @@ __global__ __launch_bounds__(256) void verify_attn_kernel(const SeqArgs sa, cons
     if (p >= 0 && p < N) atomicOr(&s_carried[p >> 5], 1u << (p & 31));
   }
   __syncthreads();
-  const int qt0 = (item - sa.pre[1][b]) * 64 + w * 16;           // the wave's first query (within the sample)
-  if (qt0 >= Q) return;                                          // whole wave (no barrier follows)
+  f16_t *P = s_p[w];
+  f16_t *VT = s_vt[w];
+  const int qt0 = (item - sa.pre[1][b]) * 16;                    // the wave's first query (within the sample)
   const f16_t *qv = static_cast<const f16_t *>(a.q);
   const f16_t *kc = static_cast<const f16_t *>(a.k), *vc = static_cast<const f16_t *>(a.v);
   const f16_t *kv = static_cast<const f16_t *>(a.k_ver), *vv = static_cast<const f16_t *>(a.v_ver);
@@ -187,23 +218,47 @@ __global__ __launch_bounds__(256) void verify_attn_kernel(const SeqArgs sa, cons
   }
 #pragma unroll
   for (int f = 0; f < DH / 16; ++f) o[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f16_t *P = s_p[w];
-  f16_t *VT = s_vt[w];
-  const int nkt = (N + 31) / 32 + (Q + 31) / 32;                 // context tiles, then the verify keys
-  for (int t = 0; t < nkt; ++t) {
-    const bool ctx = t < (N + 31) / 32;
-    const int j0 = ctx ? t * 32 : (t - (N + 31) / 32) * 32;
-    const int lim = ctx ? N : Q;
-    // Scores of the wave's 16 queries against keys j0 .. j0 + 31 (two 16-key halves).
+  const int nctx = (N + 31) / 32, nkt = nctx + (Q + 31) / 32;   // context tiles, then the verify keys
+  // Tile t's K operands (key l % 16 of each 16-key half) and V pieces (piece
+  // c * 64 + l: key e / (DH / 8), features 8 (e % (DH / 8)) ..).
+  h8_t kf[2][DH / 32], vp[DH / 16];
+  auto load = [&](int t) {
+    const bool ctx = t < nctx;
+    const int j0 = (ctx ? t : t - nctx) * 32, lim = ctx ? N : Q;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int j = min(j0 + 16 * half + r16, lim - 1);
+      const f16_t *kp = ctx ? kc + ((size_t)(off + j) * a.Hkv + kvh) * DH : kv + ((size_t)(v0 + j) * a.Hkv + kvh) * DH;
+#pragma unroll
+      for (int ks = 0; ks < DH / 32; ++ks) kf[half][ks] = ld_h8(kp + ks * 32 + g * 8);
+    }
+#pragma unroll
+    for (int c = 0; c < DH / 16; ++c) {
+      const int e = c * 64 + lane, key = e / (DH / 8), f0 = 8 * (e % (DH / 8));
+      const int j = min(j0 + key, lim - 1);
+      const f16_t *vpp = ctx ? vc + ((size_t)(off + j) * a.Hkv + kvh) * DH : vv + ((size_t)(v0 + j) * a.Hkv + kvh) * DH;
+      vp[c] = ld_h8(vpp + f0);
+    }
+  };
+  if (w < nkt) load(w);
+  for (int t = w; t < nkt; t += 4) {
+    const bool ctx = t < nctx;
+    const int j0 = (ctx ? t : t - nctx) * 32, lim = ctx ? N : Q;
+    // Scores of the 16 queries against keys j0 .. j0 + 31 (two 16-key halves).
     f32x4_t s[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int j = min(j0 + 16 * half + r16, lim - 1);           // B operand: key l % 16
-      const f16_t *kp = ctx ? kc + ((size_t)(off + j) * a.Hkv + kvh) * DH : kv + ((size_t)(v0 + j) * a.Hkv + kvh) * DH;
       s[half] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < DH / 32; ++ks) s[half] = mfma_h(qf[ks], ld_h8(kp + ks * 32 + g * 8), s[half]);
+      for (int ks = 0; ks < DH / 32; ++ks) s[half] = mfma_h(qf[ks], kf[half][ks], s[half]);
     }
+    // V of the tile into LDS, then the next tile's loads go out.
+#pragma unroll
+    for (int c = 0; c < DH / 16; ++c) {
+      const int e = c * 64 + lane, key = e / (DH / 8), f0 = 8 * (e % (DH / 8));
+      *reinterpret_cast<h8_t *>(VT + key * VS + f0) = vp[c];
+    }
+    if (t + 4 < nkt) load(t + 4);
     // Visibility of key column l % 16 (+16) for the lane's 4 query rows.
     float tmax[4];
 #pragma unroll
@@ -237,38 +292,51 @@ __global__ __launch_bounds__(256) void verify_attn_kernel(const SeqArgs sa, cons
       }
       l[v] = l[v] * alpha[v] + sum16(ps);
     }
-    // V^T of the 32 keys: lane l loads 8 features of key (l / 2 .. ) and writes them transposed.
-#pragma unroll
-    for (int c = 0; c < DH / 16; ++c) {
-      const int e = c * 64 + lane;                                // piece e: key e / (DH / 8), features 8 (e % (DH / 8)) ..
-      const int key = e / (DH / 8), f0 = 8 * (e % (DH / 8));
-      const int j = min(j0 + key, lim - 1);
-      const f16_t *vp = ctx ? vc + ((size_t)(off + j) * a.Hkv + kvh) * DH : vv + ((size_t)(v0 + j) * a.Hkv + kvh) * DH;
-      const h8_t x = ld_h8(vp + f0);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) VT[(f0 + q) * 32 + key] = x[q];
-    }
     wave_lds_sync();
-    // O = O alpha + P V: A = P rows (query l % 16, keys 8 (l / 16) ..), B = V^T rows (feature l % 16).
+    // O = O alpha + P V: A = P rows (query l % 16, keys 8 (l / 16) ..), B =
+    // column 16 f + l % 16 of V over the same 8 keys.
     const h8_t pa = *reinterpret_cast<const h8_t *>(P + r16 * 32 + 8 * g);
 #pragma unroll
     for (int f = 0; f < DH / 16; ++f) {
+      h8_t vb;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) vb[kk] = VT[(8 * g + kk) * VS + 16 * f + r16];
 #pragma unroll
       for (int v = 0; v < 4; ++v) o[f][v] *= alpha[v];
-      o[f] = mfma_h(pa, *reinterpret_cast<const h8_t *>(VT + (16 * f + r16) * 32 + 8 * g), o[f]);
+      o[f] = mfma_h(pa, vb, o[f]);
     }
     wave_lds_sync();
   }
-  // Rows 4 g + v of the tile, feature 16 f + l % 16.
+  // Merge of the 4 waves' states (the V areas reused for the unnormalised O).
+  __syncthreads();
+  float *so = reinterpret_cast<float *>(&s_vt[0][0]);            // [4 waves][16 rows][DH]
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int qi = qt0 + 4 * g + v;
+  for (int f = 0; f < DH / 16; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) so[(w * 16 + 4 * g + v) * DH + 16 * f + r16] = o[f][v];
+  if (r16 == 0)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      s_m[w][4 * g + v] = m[v];
+      s_l[w][4 * g + v] = l[v];
+    }
+  __syncthreads();
+  if (w != 0) return;
+  for (int e = lane; e < 16 * DH; e += 64) {
+    const int row = e / DH, qi = qt0 + row;
     if (qi >= Q) continue;
-    const float inv = 1.0f / l[v];
-    bf16_t *out = static_cast<bf16_t *>(a.out) + ((size_t)(v0 + qi) * a.H + h) * DH;
+    float M = s_m[0][row];
 #pragma unroll
-    for (int f = 0; f < DH / 16; ++f) out[16 * f + r16] = f2bf(o[f][v] * inv);
-    if (a.lse && r16 == 0) a.lse[(size_t)(v0 + qi) * a.H + h] = (m[v] + __log2f(l[v])) * kLn2;
+    for (int k = 1; k < 4; ++k) M = fmaxf(M, s_m[k][row]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float c = s_m[k][row] == -INFINITY ? 0.f : fast_exp2(s_m[k][row] - M);
+      num += c * so[(k * 16 + row) * DH + (e % DH)];
+      den += c * s_l[k][row];
+    }
+    static_cast<bf16_t *>(a.out)[((size_t)(v0 + qi) * a.H + h) * DH + (e % DH)] = f2bf(num / den);
+    if (a.lse && e % DH == 0) a.lse[(size_t)(v0 + qi) * a.H + h] = (M + __log2f(den)) * kLn2;
   }
 }
 
@@ -314,7 +382,9 @@ hipError_t launch_track_select(const SeqArgs &sa, const TrackArgs &a, int max_le
                                const LaunchEvents &ev) {
   if (sa.n <= 0) return hipSuccess;
   if (max_len > kTrackMaxKeys || a.budget > 64 || a.budget < 1) return hipErrorInvalidValue;
-  lc_launch<track_select_kernel>(dim3(sa.n), dim3(256), (unsigned)(max_len * sizeof(float)), s, ev, sa, a);
+  int np = 1;
+  while (np < max_len) np <<= 1;
+  lc_launch<track_select_kernel>(dim3(sa.n), dim3(256), (unsigned)(np * sizeof(unsigned long long)), s, ev, sa, a);
   return hipGetLastError();
 }
 
@@ -336,7 +406,8 @@ hipError_t launch_verify_accept(const SeqArgs &sa, const AcceptArgs &a, hipStrea
 
 hipError_t setup_flashdllm_attributes() {
   return hipFuncSetAttribute(reinterpret_cast<const void *>(track_select_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kTrackMaxKeys * (int)sizeof(float));
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             kTrackMaxKeys * (int)sizeof(unsigned long long));
 }
 
 }  // namespace lc

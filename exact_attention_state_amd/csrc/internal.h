@@ -225,7 +225,7 @@ struct TrackArgs {
   const void *q;           // RoPECache q [n_rows, H, dh] (the block rows' fresh queries)
   const float *lse;        // [n_rows, H] the block rows' log-sum-exp (natural log)
   const void *k;           // RoPECache k [n_rows, Hkv, dh]
-  float *partial;          // [H, n_rows] per-head importance (workspace)
+  float *partial;          // [n_rows, H] per-head importance (workspace)
   float *importance;       // [n_rows] importance of every row of the table's samples
   int *tracked;            // [batch, budget] selected rows within their sample, in row order; -1 pads
   int64_t n_rows;
