@@ -529,7 +529,20 @@ def measure_layer(dev, reps=20, n_sets=2):
              "algorithmic_bytes": {k: a["bytes"] for k, a in acc.items()}}
     log(f"[bench] layer finish, {T} rows: {us:.1f} us per call ({layer['bf16_mfma_frac']:.3f} of the bf16 MFMA peak); "
         + ", ".join(f"{k} {v['us_avg']:.1f} us" for k, v in layer["kernels"].items()))
-    del sets, ws, r
+    # The same layer on the block's rows only (the deeper layers' approximate
+    # step): HBM-bound on the weights, the GEMMs split their contraction.
+    Mb = wl.block_size
+    wsb = ctx.layer_workspace(F, Mb, True, dev)
+    ub, pb = timed_calls(lambda i: ctx.layer_finish(F, sets[i % n_sets], hd[:Mb], od[:Mb], out[:Mb], r_out=r[:Mb],
+                                                    workspace=wsb, stream=stream))
+    accb = layer_accounting(Mb, D, HD, F)
+    bytes_b = sum(a["bytes"] for a in accb.values())
+    layer_block = {"rows": Mb, "us_per_call": ub, "hbm_frac": bytes_b / (ub * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                   "kernels": _kernel_fracs(accb, pb), "algorithmic_bytes": {k: a["bytes"] for k, a in accb.items()}}
+    log(f"[bench] layer finish, {Mb} block rows: {ub:.1f} us per call ({layer_block['hbm_frac']:.3f} of HBM peak); "
+        + ", ".join(f"{k} {v['us_avg']:.1f} us" for k, v in layer_block["kernels"].items()))
+    layer["block_rows"] = layer_block
+    del sets, ws, wsb, r
     lm = synth.lm_head_params(D, V, 0)
     gd, wd = bf(lm["gamma_f"]), bf(lm["w_lm"])
     del lm

@@ -1195,20 +1195,27 @@ const char *kLayerNeeds = "the layer finish needs bf16, d_model in {512, 1024, 2
                           "of 128 and n_heads * head_dim a multiple of 64";
 struct LayerWs {
   void *r, *x, *y;
+  float *part;
 };
-// r [n, D] (when the caller keeps none), x [n, D], y [n, F], all bf16.
+// r [n, D] (when the caller keeps none), x [n, D], y [n, F], all bf16, then
+// the split-contraction partials of the three GEMMs (one at a time; none for
+// more than 64 rows or where every CU already has an output tile).
 size_t layer_ws_layout(const lacache_ctx *ctx, int32_t d_ff, int64_t n, bool own_r, void *base, LayerWs *out) {
-  const size_t D = ctx->cfg.d_model;
-  const size_t sizes[3] = {own_r ? align256((size_t)n * D * 2) : 0, align256((size_t)n * D * 2),
-                           align256((size_t)n * d_ff * 2)};
+  const size_t D = ctx->cfg.d_model, HD = (size_t)ctx->cfg.n_heads * ctx->cfg.head_dim;
+  const int M = n > (int64_t)1 << 24 ? 0 : (int)n;
+  const size_t part = std::max({lc::bf16_gemm_part_bytes(M, (int)D, (int)HD, lc::kGemmOutBf16),
+                                lc::bf16_gemm_part_bytes(M, d_ff, (int)D, lc::kGemmOutSwiglu),
+                                lc::bf16_gemm_part_bytes(M, (int)D, d_ff, lc::kGemmOutBf16)});
+  const size_t sizes[4] = {own_r ? align256((size_t)n * D * 2) : 0, align256((size_t)n * D * 2),
+                           align256((size_t)n * d_ff * 2), align256(part)};
   char *p = static_cast<char *>(base);
   size_t off = 0;
-  void *ptrs[3];
-  for (int i = 0; i < 3; ++i) {
-    ptrs[i] = p ? p + off : nullptr;
+  void *ptrs[4];
+  for (int i = 0; i < 4; ++i) {
+    ptrs[i] = p && sizes[i] ? p + off : nullptr;
     off += sizes[i];
   }
-  if (out) *out = LayerWs{ptrs[0], ptrs[1], ptrs[2]};
+  if (out) *out = LayerWs{ptrs[0], ptrs[1], ptrs[2], static_cast<float *>(ptrs[3])};
   return off;
 }
 }  // namespace
@@ -1261,6 +1268,7 @@ lacache_status lacache_layer_finish(lacache_ctx *ctx, int32_t d_ff, const lacach
   g.M = M;
   g.N = D;
   g.K = HD;
+  g.part = ws.part;
   hipError_t e = timed(ctx, LACACHE_KERNEL_LAYER_OPROJ, s, [&](const lc::LaunchEvents &ev) {
     return lc::launch_bf16_gemm(g, lc::kGemmOutBf16, ctx->layer_tile, s, ev);
   });
@@ -1289,6 +1297,7 @@ lacache_status lacache_layer_finish(lacache_ctx *ctx, int32_t d_ff, const lacach
   g.M = M;
   g.N = d_ff;
   g.K = D;
+  g.part = ws.part;
   e = timed(ctx, LACACHE_KERNEL_LAYER_GATE_UP, s, [&](const lc::LaunchEvents &ev) {
     return lc::launch_bf16_gemm(g, lc::kGemmOutSwiglu, ctx->layer_tile == 2 ? 3 : ctx->layer_tile, s, ev);
   });
@@ -1306,6 +1315,7 @@ lacache_status lacache_layer_finish(lacache_ctx *ctx, int32_t d_ff, const lacach
   g.M = M;
   g.N = D;
   g.K = d_ff;
+  g.part = ws.part;
   e = timed(ctx, LACACHE_KERNEL_LAYER_DOWN, s, [&](const lc::LaunchEvents &ev) {
     return lc::launch_bf16_gemm(g, lc::kGemmOutBf16, ctx->layer_tile, s, ev);
   });

@@ -190,10 +190,21 @@ struct Bf16GemmArgs {
   void *out;               // [M, N] bf16 or fp32 (SwiGLU: [M, N] bf16 with N the features), leading dimension ldo
   int M, N, K;
   int lda, ldb, ldr, ldo;
+  // Split contraction (set by the launcher): `splits` workgroups share each
+  // output tile, split s summing contraction steps [s KG / splits, (s+1) KG /
+  // splits) of the KG 64-wide steps into part[s][M][ldp] (fp32, the tiles'
+  // columns in the kernel's own order); a second kernel adds the splits in
+  // order and applies the epilogue.
+  float *part;
+  int splits, ldp;
 };
 enum { kGemmOutBf16 = 0, kGemmOutF32 = 1, kGemmOutSwiglu = 2 };
 // tile: 0 automatic, 1 256 x 256, 2 128 x 128, 3 64 x 256 (rows x columns of the output)
 hipError_t launch_bf16_gemm(const Bf16GemmArgs &a, int out_kind, int tile, hipStream_t s, const LaunchEvents &ev);
+// Bytes of split-contraction partials launch_bf16_gemm may use for this
+// shape (0: it never splits); a.part must then hold that many bytes, or be
+// null to forbid splitting.
+size_t bf16_gemm_part_bytes(int M, int N, int K, int out_kind);
 struct RowNormArgs {
   const bf16_t *src;       // rows, leading dimension lds (elements)
   const bf16_t *gamma;     // [D]

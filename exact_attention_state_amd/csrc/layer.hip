@@ -21,6 +21,8 @@
 // the swizzle from the source side: lane l of a copy fetches the chunk that
 // belongs in its fixed LDS slot.
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace lc {
@@ -51,16 +53,20 @@ __global__ __launch_bounds__(512) void bf16_gemm_kernel(const Bf16GemmArgs a) {
   // Output tiles: SwiGLU tiles cover TN / 2 features (their gate and up rows).
   const int NX = EPI == kLayerEpiSwiglu ? a.N / (TN / 2) : (a.N + TN - 1) / TN;
   const int MY = (a.M + TM - 1) / TM, ntiles = NX * MY;
+  const int S = a.splits > 1 ? a.splits : 1, nunits = ntiles * S;
   // Workgroup wg runs on die wg % 8; each die takes a contiguous run of the
-  // tile sequence, which walks groups of kGM row tiles column by column.
-  const int per_die = (ntiles + 7) / 8, wg = blockIdx.x;
-  const int u = (wg & 7) * per_die + (wg >> 3);
-  if (u >= ntiles) return;                                     // whole workgroup
+  // unit sequence (unit = tile x split; a tile's splits adjacent), which
+  // walks groups of kGM row tiles column by column.
+  const int per_die = (nunits + 7) / 8, wg = blockIdx.x;
+  const int uu = (wg & 7) * per_die + (wg >> 3);
+  if (uu >= nunits) return;                                    // whole workgroup
+  const int u = uu / S, split = uu % S;
   constexpr int kGM = 8;
   const int grp = u / (kGM * NX), within = u % (kGM * NX);
   const int gm = min(kGM, MY - grp * kGM);
   const int m0 = (grp * kGM + within % gm) * TM, nt = within / gm;
-  const int KG = a.K / 64;
+  const int KGA = a.K / 64;
+  const int kg0 = (int)((long)split * KGA / S), KG = (int)((long)(split + 1) * KGA / S) - kg0;
   const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_address(smem));
 
   // Copy c of a stage fills rows 8c .. 8c + 7 of the stage's [TM + TN] rows
@@ -93,7 +99,7 @@ __global__ __launch_bounds__(512) void bf16_gemm_kernel(const Bf16GemmArgs a) {
       const int lrow = lr0 + (lane >> 3);                      // stage row this lane fills
       const int grow = min(row0 + (lane >> 3), R - 1);
       const uint32_t voff = (uint32_t)(grow - srow) * (uint32_t)ld * 2u + (swz_slot(lrow, lane & 7) << 4);
-      const char *sb = reinterpret_cast<const char *>(base) + ((size_t)srow * ld + (size_t)g * 64) * 2;
+      const char *sb = reinterpret_cast<const char *>(base) + ((size_t)srow * ld + (size_t)(kg0 + g) * 64) * 2;
       dma16_s(sb, voff, st + c * 1024);
     }
   };
@@ -151,6 +157,32 @@ __global__ __launch_bounds__(512) void bf16_gemm_kernel(const Bf16GemmArgs a) {
   // Results leave through this wave's LDS area, one 16-row fragment row
   // block at a time, as row-wise 16-byte pieces.  A fragment's lane l holds
   // rows 4 (l / 16) + v, column l % 16.
+  if (S > 1) {
+    // Split partial: the wave's 16 WCB columns of the tile (fragment j of
+    // wave wn at tile column 16 (wn WCB + j)), raw fp32.
+    constexpr int COLS = 16 * T::WCB, STRIDE = COLS + 4, CPL = COLS / 4;
+    float *ws = reinterpret_cast<float *>(smem) + w * 16 * STRIDE;
+    const int rr = lane >> 2, c0 = (lane & 3) * CPL;
+    float *dst = a.part + (size_t)split * a.M * a.ldp + (size_t)nt * TN + wn * COLS + c0;
+#pragma unroll
+    for (int i = 0; i < T::WRB; ++i) {
+#pragma unroll
+      for (int j = 0; j < T::WCB; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ws[(4 * q4 + v) * STRIDE + 16 * j + r16] = acc[i][j][v];
+      wave_lds_sync();
+      const int m = m0 + (wm * T::WRB + i) * 16 + rr;
+      if (m < a.M) {
+        const float *src = ws + rr * STRIDE + c0;
+#pragma unroll
+        for (int p = 0; p < CPL / 4; ++p)
+          *reinterpret_cast<float4 *>(dst + (size_t)m * a.ldp + 4 * p) =
+              make_float4(src[4 * p], src[4 * p + 1], src[4 * p + 2], src[4 * p + 3]);
+      }
+      wave_lds_sync();
+    }
+    return;
+  }
   if constexpr (EPI == kLayerEpiSwiglu) {
     constexpr int H = T::WCB / 2, FC = 16 * H, STRIDE = FC + 4, PPR = FC / 8;   // features per wave, pieces per row
     float *ws = reinterpret_cast<float *>(smem) + w * 16 * STRIDE;
@@ -227,6 +259,69 @@ __global__ __launch_bounds__(512) void bf16_gemm_kernel(const Bf16GemmArgs a) {
       wave_lds_sync();
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Sum of the split partials, in split order, and the epilogue: one thread per
+// 8 consecutive outputs of a row.  Partial column of output n: n itself, or,
+// for SwiGLU tiles of TN B rows (gate rows then up rows) whose waves hold
+// HW = WCB / 2 gate and HW up fragments each, feature f = nt (TN / 2) + fi
+// sits at tile column 16 (wn WCB + j) + fi % 16 with fi / 16 = wn HW + j
+// (gate) and at 16 HW more (up).
+// ---------------------------------------------------------------------------
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const Bf16GemmArgs a, int TN, int HW) {
+  const int per_row = a.N / 8;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)a.M * per_row) return;
+  const int m = (int)(idx / per_row), n = (int)(idx % per_row) * 8;
+  const size_t sstride = (size_t)a.M * a.ldp;
+  auto sum8 = [&](int col, float *y) {
+    const float *p = a.part + (size_t)m * a.ldp + col;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = 0.f;
+    for (int sp = 0; sp < a.splits; ++sp, p += sstride) {
+      const float4 u0 = *reinterpret_cast<const float4 *>(p), u1 = *reinterpret_cast<const float4 *>(p + 4);
+      y[0] += u0.x; y[1] += u0.y; y[2] += u0.z; y[3] += u0.w;
+      y[4] += u1.x; y[5] += u1.y; y[6] += u1.z; y[7] += u1.w;
+    }
+  };
+  float y[8];
+  if constexpr (EPI == kLayerEpiSwiglu) {
+    const int half = TN / 2, nt = n / half, fi = n % half, cb = fi / 16;
+    const int col = nt * TN + 16 * (2 * HW * (cb / HW) + cb % HW) + fi % 16;
+    float up[8];
+    sum8(col, y);
+    sum8(col + 16 * HW, up);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float gt = bf2f(f2bf(y[e])), u = bf2f(f2bf(up[e]));
+      y[e] = gt / (1.0f + __expf(-gt)) * u;
+    }
+  } else {
+    sum8(n, y);
+    if constexpr (EPI == kLayerEpiF32) {
+      float *o = static_cast<float *>(a.out) + (size_t)m * a.ldo + n;
+      *reinterpret_cast<float4 *>(o) = make_float4(y[0], y[1], y[2], y[3]);
+      *reinterpret_cast<float4 *>(o + 4) = make_float4(y[4], y[5], y[6], y[7]);
+      return;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = bf2f(f2bf(y[e]));       // the linear's bf16 output
+    if (a.res) {
+      const uint4 ru = *reinterpret_cast<const uint4 *>(a.res + (size_t)m * a.ldr + n);
+      const uint32_t rw[4] = {ru.x, ru.y, ru.z, ru.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        y[2 * q] += __uint_as_float(rw[q] << 16);
+        y[2 * q + 1] += __uint_as_float(rw[q] & 0xffff0000u);
+      }
+    }
+  }
+  uint32_t ow[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ow[q] = (uint32_t)f2bf(y[2 * q]) | ((uint32_t)f2bf(y[2 * q + 1]) << 16);
+  *reinterpret_cast<uint4 *>(static_cast<bf16_t *>(a.out) + (size_t)m * a.ldo + n) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -386,11 +481,35 @@ namespace {
 template <int TM, int TN, int NST> constexpr int bf16_gemm_smem() { return NST * BT<TM, TN>::STAGE; }
 inline unsigned grid8(long tiles) { return (unsigned)((tiles + 7) / 8 * 8); }
 
+// Splits of a skinny launch: enough tiles x splits to give every CU a
+// workgroup, with at least kMinSplitSteps contraction steps per split.
+constexpr int kMinSplitSteps = 4;
+int skinny_splits(long tiles, int K) {
+  const long cus = device_cus();
+  if (tiles >= cus) return 1;
+  const long s = std::min<long>((cus + tiles - 1) / tiles, (K / 64) / kMinSplitSteps);
+  return s > 1 ? (int)s : 1;
+}
+template <int TN, int EPI> long skinny_nx(int N) { return EPI == kLayerEpiSwiglu ? N / (TN / 2) : (N + TN - 1) / TN; }
+
 template <int TM, int TN, int NST, int EPI>
-hipError_t go(const Bf16GemmArgs &a, hipStream_t s, const LaunchEvents &ev) {
-  const long NX = EPI == kLayerEpiSwiglu ? a.N / (TN / 2) : (a.N + TN - 1) / TN;
+hipError_t go(const Bf16GemmArgs &a0, hipStream_t s, const LaunchEvents &ev, bool may_split) {
+  Bf16GemmArgs a = a0;
+  const long NX = skinny_nx<TN, EPI>(a.N);
   const long tiles = NX * ((a.M + TM - 1) / TM);
-  lc_launch<bf16_gemm_kernel<TM, TN, NST, EPI>>(dim3(grid8(tiles)), dim3(512), bf16_gemm_smem<TM, TN, NST>(), s, ev, a);
+  a.splits = may_split && a.part ? skinny_splits(tiles, a.K) : 1;
+  a.ldp = (int)(NX * TN);
+  if (a.splits == 1) {
+    lc_launch<bf16_gemm_kernel<TM, TN, NST, EPI>>(dim3(grid8(tiles)), dim3(512), bf16_gemm_smem<TM, TN, NST>(), s, ev, a);
+    return hipGetLastError();
+  }
+  // The two launches share one event pair: the first stamps the start, the last the end.
+  const LaunchEvents first{ev.start, nullptr}, last{nullptr, ev.stop};
+  lc_launch<bf16_gemm_kernel<TM, TN, NST, EPI>>(dim3(grid8(tiles * a.splits)), dim3(512),
+                                                bf16_gemm_smem<TM, TN, NST>(), s, first, a);
+  const long threads = (long)a.M * (a.N / 8);
+  lc_launch<splitk_reduce_kernel<EPI>>(dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, last, a, TN,
+                                       BT<TM, TN>::WCB / 2);
   return hipGetLastError();
 }
 
@@ -403,15 +522,22 @@ template <int EPI> hipError_t dispatch(const Bf16GemmArgs &a, int tile, hipStrea
     else tile = EPI == kLayerEpiSwiglu ? 3 : 2;                            // 128 x 128 (SwiGLU: 64 x 256)
   }
   switch (tile) {
-    case 1: return go<256, 256, 2, EPI>(a, s, ev);
+    case 1: return go<256, 256, 2, EPI>(a, s, ev, false);
     case 2:
       if constexpr (EPI == kLayerEpiSwiglu) return hipErrorInvalidValue;
-      else return go<128, 128, 4, EPI>(a, s, ev);
-    case 3: return go<64, 256, 3, EPI>(a, s, ev);
+      else return go<128, 128, 4, EPI>(a, s, ev, false);
+    case 3: return go<64, 256, 3, EPI>(a, s, ev, a.M <= 64);
     default: return hipErrorInvalidValue;
   }
 }
 }  // namespace
+
+size_t bf16_gemm_part_bytes(int M, int N, int K, int out_kind) {
+  if (M <= 0 || M > 64 || K % 64) return 0;
+  const long NX = out_kind == kGemmOutSwiglu ? skinny_nx<256, kLayerEpiSwiglu>(N) : skinny_nx<256, kLayerEpiBf16>(N);
+  const int sp = skinny_splits(NX, K);
+  return sp > 1 ? (size_t)sp * M * NX * 256 * sizeof(float) : 0;
+}
 
 hipError_t launch_bf16_gemm(const Bf16GemmArgs &a, int epi, int tile, hipStream_t s, const LaunchEvents &ev) {
   if (a.M <= 0) return hipSuccess;

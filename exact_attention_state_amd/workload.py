@@ -13,7 +13,8 @@ from . import lacache, synth
 
 def to_device_array(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     """float32 array (exactly representable in `dtype`) -> device tensor of that dtype."""
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    t = torch.from_numpy(a if a.flags.writeable else a.copy())
     if dtype == "bf16":
         t = t.to(torch.bfloat16)          # exact: values are bf16-representable
     return t.to(device)
