@@ -722,7 +722,7 @@ namespace {
 // rows) that the dispatcher can spread evenly.  Measured on the batched16,
 // long4 and varlen32 workloads against fixed segment lengths of 128..2432.
 constexpr int64_t kStreamItems = 2048;
-int stream_segment_rows(const lc::SeqArgs &sa, int H, lc::DType dt) {
+int stream_segment_rows(const lc::SeqArgs &sa, int H, lc::DType dt, bool *equal_out = nullptr) {
   if (dt != lc::kBF16) return 0;
   int64_t tiles = 0, rows = 0;
   int nu0 = -1;
@@ -738,6 +738,7 @@ int stream_segment_rows(const lc::SeqArgs &sa, int H, lc::DType dt) {
       else if (nU != nu0) equal = false;
     }
   }
+  if (equal_out) *equal_out = equal;
   if (tiles * H <= kStreamItems || nu0 <= 0) return 0;
   if (!equal) return 128;
   const int64_t target = std::max<int64_t>(16, rows * H / (4 * (int64_t)lc::device_cus()));
@@ -796,7 +797,8 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     const int ns = std::min(kMaxInline, batch - s0);
     lc::SeqArgs sa = slice_args(seqs, s0, ns);
     plan_block_rows(split, sa);
-    const int seg_rows = stream_segment_rows(sa, H, dt);
+    bool equal_lengths = false;
+    const int seg_rows = stream_segment_rows(sa, H, dt, &equal_lengths);
     for (int i = 0; i < ns; ++i) {
       const int nU = sa.len[i] - (sa.be[i] - sa.bs[i]);
       sa.pre[2][i + 1] = sa.pre[2][i] + (seg_rows ? (nU + seg_rows - 1) / seg_rows : (nU + lc::kRowsB - 1) / lc::kRowsB);
@@ -873,7 +875,7 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
         if (e != hipSuccess) return hip_fail(ctx, "block-step merge launch", e);
       }
       e = timed(ctx, LACACHE_KERNEL_INVARIANT_ROWS, s, [&](const lc::LaunchEvents &ev) {
-        return lc::launch_invariant_stream(dt, dh, sa, aa, sa.pre[2][ns] * H, s, ev);
+        return lc::launch_invariant_stream(dt, dh, sa, aa, equal_lengths ? 4 : 2, s, ev);
       });
     } else {
       const int Mmerge = aa.direct ? 0 : M;

@@ -737,7 +737,14 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
 // ---------------------------------------------------------------------------
 // Type B, streaming (16-bit caches, blocks of at most 32 * NKS keys): one
 // wave per item (sample, head, segment of a.seg_rows invariant rows), taken
-// in groups of 16 rows.  The load unit only reaches full rate when
+// in groups of 16 rows.  NW waves per workgroup, each on its own item with
+// its own LDS; die d (workgroups d, d + 8, ...) takes the d-th eighth of the
+// segments, every head of a segment on consecutive waves, so the rows' (m,
+// l) reads and LSE writes (all heads of a row share their lines) and a
+// sample's block keys stay within one die's L2.  Four waves per workgroup
+// (one workgroup per CU by LDS) spread equal segments evenly over the CUs;
+// two keep more waves per CU for the many short segments of unequal
+// batches (measured on long4 and varlen32).  The load unit only reaches full rate when
 // consecutive lanes move consecutive 16-byte pieces, which the MFMA layouts
 // (lane = row) never do; so every global access of the loop is row-wise:
 // the queries, FACache rows and (m, l) of a group arrive by global -> LDS
@@ -759,6 +766,7 @@ template <int DH, int NKS> struct StreamLds {
   static constexpr int BYTES = OUT + TILE + 64;
   static constexpr int COPIES = CPT + 1;                      // copy instructions per group
   static constexpr int LOADS = CPT;                           // FACache row loads per group (row-wise, to registers)
+  static_assert(4 * BYTES <= 160 * 1024, "four waves' LDS must fit a CU");
 };
 
 // V of up to MAXC keys into a VTile (16-bit) by one wave, with dma16.
@@ -775,14 +783,19 @@ __device__ __forceinline__ void vtile_stage_wave(uint32_t lds, const f16_t *vbas
   }
 }
 
-template <typename TO, int DH, int NKS>
-__global__ __launch_bounds__(64) void invariant_stream_kernel(const SeqArgs sa, const AttnArgs a) {
+template <typename TO, int DH, int NKS, int NW>
+__global__ __launch_bounds__(64 * NW) void invariant_stream_kernel(const SeqArgs sa, const AttnArgs a) {
   using T = f16_t;
   using L = StreamLds<DH, NKS>;
   constexpr int NDB = DH / 16, BMAX = 32 * NKS;
-  extern __shared__ __align__(16) char smem[];
-  const int lane = threadIdx.x, g = lane >> 4, r16 = lane & 15;
-  const int item = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  extern __shared__ __align__(16) char smem_all[];
+  char *const smem = smem_all + (threadIdx.x >> 6) * L::BYTES;
+  const int nit = sa.pre[2][sa.n];
+  const int die = blockIdx.x & 7, j = (blockIdx.x >> 3) * NW + (threadIdx.x >> 6);
+  const int lo = (int)((long)die * nit / 8), hi = (int)((long)(die + 1) * nit / 8);
+  const int item = lo + j / a.H, h = j % a.H;
+  if (item >= hi) return;                                     // whole wave; no barriers below
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   const int b = find_sample(sa.pre[2], sa.n, item);
   const int seg = item - sa.pre[2][b];
   const int bs = sa.bs[b], B = sa.be[b] - bs, nU = sa.len[b] - B;
@@ -1582,22 +1595,29 @@ hipError_t launch_attn_ab(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a
 }
 
 
-hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
+hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int waves,
                                    hipStream_t s, const LaunchEvents &ev) {
-  if (n_blocks <= 0) return hipSuccess;
+  const int nit = sa.pre[2][sa.n];
+  if (nit <= 0) return hipSuccess;
   int bmax = 0;
   for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
   if (bmax > kStreamMaxBlock) return hipErrorInvalidValue;
-  if (dt != kBF16) return hipErrorInvalidValue;
-#define LC_STR(DH, NK) \
-  lc_launch<invariant_stream_kernel<bf16_t, DH, NK>>(dim3(n_blocks), dim3(64), StreamLds<DH, NK>::BYTES, s, ev, sa, a)
+  if (dt != kBF16 || (waves != 2 && waves != 4)) return hipErrorInvalidValue;
+  // Eight dies, each with at most ceil(nit / 8) segments x H waves.
+  const unsigned grid = 8u * (unsigned)(((nit + 7) / 8 * a.H + waves - 1) / waves);
+#define LC_STR(DH, NK, NW)                                                                                       \
+  lc_launch<invariant_stream_kernel<bf16_t, DH, NK, NW>>(dim3(grid), dim3(64 * NW), NW * StreamLds<DH, NK>::BYTES, s, \
+                                                         ev, sa, a)
+#define LC_STR_W(DH, NK) \
+  if (waves == 4) LC_STR(DH, NK, 4); else LC_STR(DH, NK, 2)
   if (dh == 128) {
-    if (bmax <= 32) LC_STR(128, 1);
-    else LC_STR(128, 2);
+    if (bmax <= 32) LC_STR_W(128, 1);
+    else LC_STR_W(128, 2);
   } else {
-    if (bmax <= 32) LC_STR(64, 1);
-    else LC_STR(64, 2);
+    if (bmax <= 32) LC_STR_W(64, 1);
+    else LC_STR_W(64, 2);
   }
+#undef LC_STR_W
 #undef LC_STR
   return hipGetLastError();
 }
@@ -1691,6 +1711,14 @@ hipError_t setup_kernel_attributes() {
   LC_ATTR((block_rows_stream_kernel<bf16_t, 64, 4>), (StreamA<64, 4>::BYTES));
   LC_ATTR((block_rows_stream_kernel<bf16_t, 128, 2>), (StreamA<128, 2>::BYTES));
   LC_ATTR((block_rows_stream_kernel<bf16_t, 64, 2>), (StreamA<64, 2>::BYTES));
+#define LC_ATTR_IS(DH, NK)                                                        \
+  LC_ATTR((invariant_stream_kernel<bf16_t, DH, NK, 2>), (2 * StreamLds<DH, NK>::BYTES)); \
+  LC_ATTR((invariant_stream_kernel<bf16_t, DH, NK, 4>), (4 * StreamLds<DH, NK>::BYTES));
+  LC_ATTR_IS(128, 1)
+  LC_ATTR_IS(128, 2)
+  LC_ATTR_IS(64, 1)
+  LC_ATTR_IS(64, 2)
+#undef LC_ATTR_IS
 #undef LC_ATTR
   return e;
 }
