@@ -718,11 +718,12 @@ namespace {
 // nothing is left to overlap and the separate merge launch only adds.
 // The launch lasts as long as its busiest CU, so the segments balance the
 // work: equal batches split every (sample, head) into equal segments, about
-// four per CU in all; batches of unequal lengths take short segments (128
+// four per CU in all; batches of unequal lengths take short segments (192
 // rows) that the dispatcher can spread evenly.  Measured on the batched16,
-// long4 and varlen32 workloads against fixed segment lengths of 128..2432.
+// long4 and varlen32 workloads against fixed segment lengths of 128..2432
+// (and, with four waves per workgroup, 128..384 on varlen32).
 constexpr int64_t kStreamItems = 2048;
-int stream_segment_rows(const lc::SeqArgs &sa, int H, lc::DType dt, bool *equal_out = nullptr) {
+int stream_segment_rows(const lc::SeqArgs &sa, int H, lc::DType dt) {
   if (dt != lc::kBF16) return 0;
   int64_t tiles = 0, rows = 0;
   int nu0 = -1;
@@ -738,9 +739,8 @@ int stream_segment_rows(const lc::SeqArgs &sa, int H, lc::DType dt, bool *equal_
       else if (nU != nu0) equal = false;
     }
   }
-  if (equal_out) *equal_out = equal;
   if (tiles * H <= kStreamItems || nu0 <= 0) return 0;
-  if (!equal) return 128;
+  if (!equal) return 192;
   const int64_t target = std::max<int64_t>(16, rows * H / (4 * (int64_t)lc::device_cus()));
   const int nseg = std::max<int64_t>(1, (nu0 + target - 1) / target);
   return ((nu0 + nseg - 1) / nseg + 15) / 16 * 16;
@@ -797,8 +797,7 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     const int ns = std::min(kMaxInline, batch - s0);
     lc::SeqArgs sa = slice_args(seqs, s0, ns);
     plan_block_rows(split, sa);
-    bool equal_lengths = false;
-    const int seg_rows = stream_segment_rows(sa, H, dt, &equal_lengths);
+    const int seg_rows = stream_segment_rows(sa, H, dt);
     for (int i = 0; i < ns; ++i) {
       const int nU = sa.len[i] - (sa.be[i] - sa.bs[i]);
       sa.pre[2][i + 1] = sa.pre[2][i] + (seg_rows ? (nU + seg_rows - 1) / seg_rows : (nU + lc::kRowsB - 1) / lc::kRowsB);
@@ -875,7 +874,7 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
         if (e != hipSuccess) return hip_fail(ctx, "block-step merge launch", e);
       }
       e = timed(ctx, LACACHE_KERNEL_INVARIANT_ROWS, s, [&](const lc::LaunchEvents &ev) {
-        return lc::launch_invariant_stream(dt, dh, sa, aa, equal_lengths ? 4 : 2, s, ev);
+        return lc::launch_invariant_stream(dt, dh, sa, aa, s, ev);
       });
     } else {
       const int Mmerge = aa.direct ? 0 : M;

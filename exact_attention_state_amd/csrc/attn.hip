@@ -742,9 +742,10 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
 // segments, every head of a segment on consecutive waves, so the rows' (m,
 // l) reads and LSE writes (all heads of a row share their lines) and a
 // sample's block keys stay within one die's L2.  Four waves per workgroup
-// (one workgroup per CU by LDS) spread equal segments evenly over the CUs;
-// two keep more waves per CU for the many short segments of unequal
-// batches (measured on long4 and varlen32).  The load unit only reaches full rate when
+// (one workgroup per CU by LDS) spread the segments evenly over the CUs
+// (single-wave workgroups left some CUs with six waves and others with two:
+// long4 101 -> 89.5 us, batched16 46.5 -> 40.1 us, varlen32 210 -> 194 us
+// with 192-row segments).  The load unit only reaches full rate when
 // consecutive lanes move consecutive 16-byte pieces, which the MFMA layouts
 // (lane = row) never do; so every global access of the loop is row-wise:
 // the queries, FACache rows and (m, l) of a group arrive by global -> LDS
@@ -1595,21 +1596,21 @@ hipError_t launch_attn_ab(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a
 }
 
 
-hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int waves,
-                                   hipStream_t s, const LaunchEvents &ev) {
+hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, hipStream_t s,
+                                   const LaunchEvents &ev) {
+  constexpr int waves = 4;
   const int nit = sa.pre[2][sa.n];
   if (nit <= 0) return hipSuccess;
   int bmax = 0;
   for (int i = 0; i < sa.n; ++i) bmax = bmax > sa.be[i] - sa.bs[i] ? bmax : sa.be[i] - sa.bs[i];
   if (bmax > kStreamMaxBlock) return hipErrorInvalidValue;
-  if (dt != kBF16 || (waves != 2 && waves != 4)) return hipErrorInvalidValue;
+  if (dt != kBF16) return hipErrorInvalidValue;
   // Eight dies, each with at most ceil(nit / 8) segments x H waves.
   const unsigned grid = 8u * (unsigned)(((nit + 7) / 8 * a.H + waves - 1) / waves);
 #define LC_STR(DH, NK, NW)                                                                                       \
   lc_launch<invariant_stream_kernel<bf16_t, DH, NK, NW>>(dim3(grid), dim3(64 * NW), NW * StreamLds<DH, NK>::BYTES, s, \
                                                          ev, sa, a)
-#define LC_STR_W(DH, NK) \
-  if (waves == 4) LC_STR(DH, NK, 4); else LC_STR(DH, NK, 2)
+#define LC_STR_W(DH, NK) LC_STR(DH, NK, waves)
   if (dh == 128) {
     if (bmax <= 32) LC_STR_W(128, 1);
     else LC_STR_W(128, 2);
@@ -1711,8 +1712,7 @@ hipError_t setup_kernel_attributes() {
   LC_ATTR((block_rows_stream_kernel<bf16_t, 64, 4>), (StreamA<64, 4>::BYTES));
   LC_ATTR((block_rows_stream_kernel<bf16_t, 128, 2>), (StreamA<128, 2>::BYTES));
   LC_ATTR((block_rows_stream_kernel<bf16_t, 64, 2>), (StreamA<64, 2>::BYTES));
-#define LC_ATTR_IS(DH, NK)                                                        \
-  LC_ATTR((invariant_stream_kernel<bf16_t, DH, NK, 2>), (2 * StreamLds<DH, NK>::BYTES)); \
+#define LC_ATTR_IS(DH, NK) \
   LC_ATTR((invariant_stream_kernel<bf16_t, DH, NK, 4>), (4 * StreamLds<DH, NK>::BYTES));
   LC_ATTR_IS(128, 1)
   LC_ATTR_IS(128, 2)

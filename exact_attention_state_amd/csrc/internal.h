@@ -140,9 +140,8 @@ int attn_ab_capacity(DType dt, int dh, const SeqArgs &sa);
 hipError_t launch_attn_ab(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int nA, int nB, hipStream_t s,
                           const LaunchEvents &ev);
 constexpr int kStreamMaxBlock = 64;   // largest block the streaming type-B kernel serves
-// waves: items (one wave each) per workgroup, 2 or 4.
-hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int waves,
-                                   hipStream_t s, const LaunchEvents &ev);
+hipError_t launch_invariant_stream(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, hipStream_t s,
+                                   const LaunchEvents &ev);
 hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                                hipStream_t s, const LaunchEvents &ev);
 // Streaming refresh (bf16 parameters, 16-bit caches): items of 64 * mb rows

@@ -173,8 +173,8 @@ def test_streaming_kernels_head128_every_row(case, monkeypatch, capfd):
     (64-row tile, head) invariant items in equal segments (the 32-key
     streaming invariant-row kernel, four waves per workgroup).  b64_ragged:
     28 samples of 628..828 tokens, blocks of 64: 448 block-row workgroups
-    (2-stage ring, two per CU) and 128-row segments of the 64-key streaming
-    invariant-row kernel (two waves per workgroup)."""
+    (2-stage ring, two per CU) and 192-row segments of the 64-key streaming
+    invariant-row kernel."""
     monkeypatch.setenv("LACACHE_LOG", "1")
     if case == "b32_equal":
         prompts, block, gen = (568,) * 32, 32, 64
@@ -186,9 +186,9 @@ def test_streaming_kernels_head128_every_row(case, monkeypatch, capfd):
     dw = _run_full(wl, 1)
     names = _launched(capfd)
     _say(f"[parity] {wl.name} launched {sorted(names)}")
-    nst, nks, nw = (4, 1, 4) if case == "b32_equal" else (2, 2, 2)
+    nst, nks = (4, 1) if case == "b32_equal" else (2, 2)
     _expect(names, rf"lc::block_rows_stream_kernel<unsigned short, 128, {nst}>",
-            rf"lc::invariant_stream_kernel<unsigned short, 128, {nks}, {nw}>")
+            rf"lc::invariant_stream_kernel<unsigned short, 128, {nks}, 4>")
 
 
 # ---------------------------------------------------------------------------
