@@ -30,7 +30,8 @@ struct lacache_ctx {
   int refresh_rows;        // streaming refresh item rows fixed by LACACHE_REFRESH_ROWS (64 or 128), else 0
   void *scratch;           // device address of this device's static scratch (lacache_block_step_noalloc)
   int fp8_tile;            // down-projection FP8 GEMM tile fixed by LACACHE_FP8_TILE (1: 256, 2: 128), else 0
-  int layer_tile;          // bf16 layer GEMM tile fixed by LACACHE_LAYER_TILE (1: 256, 2: 128, 3: 64 x 256), else 0
+  int layer_tile;          // bf16 layer GEMM tile fixed by LACACHE_LAYER_TILE (1: 256, 2: 128, 3: 64 x 256,
+                           // 4: 128 x 128 with four waves), else 0
   std::string last_error;
   // Diagnostics: event pairs stamped by each launch while profiling is on.
   bool profiling = false;
@@ -433,6 +434,7 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
     if (!std::strcmp(env, "256")) ctx->layer_tile = 1;
     else if (!std::strcmp(env, "128")) ctx->layer_tile = 2;
     else if (!std::strcmp(env, "64")) ctx->layer_tile = 3;
+    else if (!std::strcmp(env, "128w4")) ctx->layer_tile = 4;
   }
   if (const char *env = std::getenv("LACACHE_GEMM_TILE")) {
     if (!std::strcmp(env, "whole")) ctx->gemm_tile = lc::kGemmTileWhole;

@@ -199,7 +199,7 @@ struct Bf16GemmArgs {
   int splits, ldp;
 };
 enum { kGemmOutBf16 = 0, kGemmOutF32 = 1, kGemmOutSwiglu = 2 };
-// tile: 0 automatic, 1 256 x 256, 2 128 x 128, 3 64 x 256 (rows x columns of the output)
+// tile: 0 automatic, 1 256 x 256, 2 128 x 128, 3 64 x 256, 4 128 x 128 with four waves (rows x columns of the output)
 hipError_t launch_bf16_gemm(const Bf16GemmArgs &a, int out_kind, int tile, hipStream_t s, const LaunchEvents &ev);
 // Bytes of split-contraction partials launch_bf16_gemm may use for this
 // shape (0: it never splits); a.part must then hold that many bytes, or be

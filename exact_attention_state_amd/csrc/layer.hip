@@ -30,13 +30,16 @@ namespace lc {
 // ---------------------------------------------------------------------------
 // bf16 GEMM
 // ---------------------------------------------------------------------------
-template <int TM, int TN> struct BT {
-  static constexpr int WM = TM >= 128 ? 2 : 1, WN = 8 / WM;      // wave grid
+// NW waves per workgroup: 8 (wave tiles TM/2 x TN/4, or TM x TN/8 below 128
+// rows) or 4 (TM/2 x TN/2: a 128 x 128 tile gives 64 x 64 per wave, half the
+// LDS fragment reads per MFMA of eight 64 x 32 waves).
+template <int TM, int TN, int NW = 8> struct BT {
+  static constexpr int WM = TM >= 128 ? 2 : 1, WN = NW / WM;     // wave grid
   static constexpr int WRB = TM / WM / 16, WCB = TN / WN / 16;   // 16 x 16 fragments per wave
   static constexpr int CB = TN / 16;
   static constexpr int STAGE = (TM + TN) * 128;                  // one 64-wide contraction step
-  static constexpr int COPIES = (TM + TN) / 64;                  // 1 KB copies (8 rows) per wave per stage
-  static_assert(COPIES * 64 == TM + TN, "copies must tile the stage");
+  static constexpr int COPIES = (TM + TN) / (8 * NW);            // 1 KB copies (8 rows) per wave per stage
+  static_assert(COPIES * 8 * NW == TM + TN, "copies must tile the stage");
   static_assert(WRB >= 1 && WCB >= 2 && WCB % 2 == 0, "wave tile");
 };
 
@@ -44,9 +47,9 @@ enum { kLayerEpiBf16 = 0, kLayerEpiF32 = 1, kLayerEpiSwiglu = 2 };
 
 __device__ __forceinline__ uint32_t swz_slot(int row, int chunk) { return (uint32_t)(chunk ^ ((row >> 1) & 7)); }
 
-template <int TM, int TN, int NST, int EPI>
-__global__ __launch_bounds__(512) void bf16_gemm_kernel(const Bf16GemmArgs a) {
-  using T = BT<TM, TN>;
+template <int TM, int TN, int NST, int EPI, int NW = 8>
+__global__ __launch_bounds__(64 * NW) void bf16_gemm_kernel(const Bf16GemmArgs a) {
+  using T = BT<TM, TN, NW>;
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w % T::WM, wn = w / T::WM;
@@ -492,7 +495,7 @@ int skinny_splits(long tiles, int K) {
 }
 template <int TN, int EPI> long skinny_nx(int N) { return EPI == kLayerEpiSwiglu ? N / (TN / 2) : (N + TN - 1) / TN; }
 
-template <int TM, int TN, int NST, int EPI>
+template <int TM, int TN, int NST, int EPI, int NW = 8>
 hipError_t go(const Bf16GemmArgs &a0, hipStream_t s, const LaunchEvents &ev, bool may_split) {
   Bf16GemmArgs a = a0;
   const long NX = skinny_nx<TN, EPI>(a.N);
@@ -500,16 +503,17 @@ hipError_t go(const Bf16GemmArgs &a0, hipStream_t s, const LaunchEvents &ev, boo
   a.splits = may_split && a.part ? skinny_splits(tiles, a.K) : 1;
   a.ldp = (int)(NX * TN);
   if (a.splits == 1) {
-    lc_launch<bf16_gemm_kernel<TM, TN, NST, EPI>>(dim3(grid8(tiles)), dim3(512), bf16_gemm_smem<TM, TN, NST>(), s, ev, a);
+    lc_launch<bf16_gemm_kernel<TM, TN, NST, EPI, NW>>(dim3(grid8(tiles)), dim3(64 * NW), bf16_gemm_smem<TM, TN, NST>(), s,
+                                                      ev, a);
     return hipGetLastError();
   }
   // The two launches share one event pair: the first stamps the start, the last the end.
   const LaunchEvents first{ev.start, nullptr}, last{nullptr, ev.stop};
-  lc_launch<bf16_gemm_kernel<TM, TN, NST, EPI>>(dim3(grid8(tiles * a.splits)), dim3(512),
-                                                bf16_gemm_smem<TM, TN, NST>(), s, first, a);
+  lc_launch<bf16_gemm_kernel<TM, TN, NST, EPI, NW>>(dim3(grid8(tiles * a.splits)), dim3(64 * NW),
+                                                    bf16_gemm_smem<TM, TN, NST>(), s, first, a);
   const long threads = (long)a.M * (a.N / 8);
   lc_launch<splitk_reduce_kernel<EPI>>(dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, last, a, TN,
-                                       BT<TM, TN>::WCB / 2);
+                                       BT<TM, TN, NW>::WCB / 2);
   return hipGetLastError();
 }
 
@@ -517,8 +521,11 @@ template <int EPI> hipError_t dispatch(const Bf16GemmArgs &a, int tile, hipStrea
   const long cus = device_cus();
   const long n256 = EPI == kLayerEpiSwiglu ? a.N / 128 : (a.N + 255) / 256;
   if (tile == 0) {
+    const long t256 = n256 * ((a.M + 255) / 256);
     if (a.M <= 64) tile = 3;                                               // skinny: 64 x 256
-    else if (n256 * ((a.M + 255) / 256) >= cus) tile = 1;                  // 256 x 256
+    else if (EPI == kLayerEpiSwiglu && t256 >= cus && t256 < 4 * cus && 4 * t256 < 3 * ((t256 + cus - 1) / cus) * cus)
+      tile = 4;            // 256 x 256 SwiGLU tiles would leave a short last round (768 rows: 237 -> 215 us)
+    else if (t256 >= cus) tile = 1;                                        // 256 x 256
     else tile = EPI == kLayerEpiSwiglu ? 3 : 2;                            // 128 x 128 (SwiGLU: 64 x 256)
   }
   switch (tile) {
@@ -527,6 +534,7 @@ template <int EPI> hipError_t dispatch(const Bf16GemmArgs &a, int tile, hipStrea
       if constexpr (EPI == kLayerEpiSwiglu) return hipErrorInvalidValue;
       else return go<128, 128, 4, EPI>(a, s, ev, false);
     case 3: return go<64, 256, 3, EPI>(a, s, ev, a.M <= 64);
+    case 4: return go<128, 128, 2, EPI, 4>(a, s, ev, false);
     default: return hipErrorInvalidValue;
   }
 }
@@ -592,6 +600,12 @@ hipError_t setup_layer_attributes() {
   LC_BGA(128, 128, 4, kLayerEpiBf16) LC_BGA(128, 128, 4, kLayerEpiF32)
   LC_BGA(64, 256, 3, kLayerEpiBf16) LC_BGA(64, 256, 3, kLayerEpiF32) LC_BGA(64, 256, 3, kLayerEpiSwiglu)
 #undef LC_BGA
+#define LC_BGA4(NST, EPI)                                                                                     \
+  if (e == hipSuccess)                                                                                        \
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(bf16_gemm_kernel<128, 128, NST, EPI, 4>),          \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bf16_gemm_smem<128, 128, NST>());
+  LC_BGA4(2, kLayerEpiBf16) LC_BGA4(2, kLayerEpiF32) LC_BGA4(2, kLayerEpiSwiglu)
+#undef LC_BGA4
   return e;
 }
 

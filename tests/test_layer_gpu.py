@@ -138,7 +138,8 @@ def _run_layer(D, H, F, T, seed, tile=None, monkeypatch=None):
 # LLaDA-8B's layer shape at a block of 32 rows (16 splits of W_o and down).
 @pytest.mark.parametrize("D,H,F,T,tile", [(512, 4, 384, 77, None), (1024, 8, 512, 300, None),
                                            (512, 4, 384, 513, "256"), (512, 4, 256, 200, "128"),
-                                           (512, 4, 256, 130, "64"), (512, 4, 384, 1, None),
+                                           (512, 4, 256, 130, "64"), (512, 4, 256, 200, "128w4"),
+                                           (512, 4, 384, 1, None),
                                            (1024, 8, 512, 17, None), (1024, 8, 768, 61, None),
                                            (1024, 8, 512, 64, None), (4096, 32, 12288, 32, None)])
 def test_layer_finish_every_row(D, H, F, T, tile, monkeypatch):
