@@ -51,7 +51,11 @@ def _one_call(wl, what):
     dw.ctx.block_step_noalloc(dw.weights, blk, dw.table, ct2)
     torch.cuda.synchronize()
     for k in ("h", "q", "k", "v", "out", "lse", "m", "l", "o"):
-        assert torch.equal(getattr(dw.ct, k), getattr(ct2, k)), f"{what}: {k} differs from lacache_block_step"
+        # bitwise: the FACache entries of block rows are never written and may
+        # hold any bits, NaN patterns included (which torch.equal calls unequal)
+        a, b = getattr(dw.ct, k), getattr(ct2, k)
+        bits = torch.int16 if a.element_size() == 2 else torch.int32
+        assert torch.equal(a.view(bits), b.view(bits)), f"{what}: {k} differs from lacache_block_step"
     ref = oracle.full_recompute(dw.params, cfg_of(wl), dw.ids_host, dw.table)
     rows = np.concatenate([np.arange(off, off + n) for (off, n, _, _) in dw.table])
     st = check_output(host(ct2.out)[rows], ref["out"][rows], wl.dtype, f"{what} out")
