@@ -20,6 +20,16 @@ Two commands, each reading the CSV files a rocprofv3 run writes with
     runs (KiB per dispatch), each scaled by the factor that makes the same
     counter read N bytes for a plain copy kernel of N bytes (the ``copyBuffer``
     dispatches of the copy runs, median).
+
+  python -m exact_attention_state_amd.profsum step-traffic --workload W --fetch ... --write ... \\
+      --copy-fetch ... --copy-write ... --copy-bytes N [--command CMD ...] > profiles/traffic_W_step.json
+
+    The same, per kernel class of the block step as bench.py names them
+    (qkv, qkv_prep, qkv_gemm, attn, merge, block_rows, invariant_rows), over
+    the dispatches of each class's most frequent grid size (the step's
+    launches; the refresh's differ in shape), with the sha256 of the class's
+    sources and its algorithmic bytes from bench.py, which reads this record
+    for its roofline's traffic while the sources are unchanged.
 """
 
 from __future__ import annotations
@@ -112,6 +122,62 @@ def traffic(fetch, write, copy_fetch, copy_write, copy_bytes, only=None, min_gri
     return res
 
 
+# Kernel classes of the block step (bench.py's names), by substring of the
+# kernel name; the first match wins.
+STEP_CLASSES = (("qkv_prep", ("qkv_prep_kernel",)), ("qkv_gemm", ("qkv_gemm", "qkv_skinny")),
+                ("qkv", ("qkv_fused_kernel",)), ("attn", ("attn_ab_kernel",)), ("merge", ("merge_kernel",)),
+                ("block_rows", ("block_rows_stream_kernel", "block_rows_kernel")),
+                ("invariant_rows", ("invariant_stream_kernel", "invariant_rows_kernel")))
+
+
+def step_class(name: str):
+    for cls, subs in STEP_CLASSES:
+        if any(x in name for x in subs):
+            return cls
+    return None
+
+
+def step_traffic(workload, fetch, write, copy_fetch, copy_write, copy_bytes) -> dict:
+    import os
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    from exact_attention_state_amd import synth
+    ff, wf = copy_factor(copy_fetch, copy_bytes), copy_factor(copy_write, copy_bytes)
+    acc = bench.step_accounting(synth.WORKLOADS[workload])["kernels"]
+
+    def per_class(path):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            cls = step_class(r["Kernel_Name"])
+            if cls:
+                grid = int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0)
+                out.setdefault(cls, {}).setdefault(grid, []).append(float(r["Counter_Value"]))
+        return out
+
+    f, w = per_class(fetch), per_class(write)
+    res = {"workload": workload,
+           "what": f"HBM traffic per launch of the block-step kernels ({workload} workload, cold-cache protocol with "
+                   "rotating sets); per kernel class the dispatches of its most frequent grid size (the step's); "
+                   "median over those dispatches",
+           "calibration": {"copy_kernel": f"__amd_rocclr_copyBuffer, {copy_bytes} bytes read and written "
+                                          "(bench.py --copy-calibration)",
+                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+                           "note": "bytes = counter (KiB) x 1024 x factor; the factor is what the same counter "
+                                   "reads for the copy"},
+           "kernels": {}}
+    for cls in sorted(set(f) & set(w)):
+        grid = max(f[cls], key=lambda g: len(f[cls][g]))
+        fk, wk = statistics.median(f[cls][grid]), statistics.median(w[cls].get(grid, [0.0]))
+        e = {"source_sha256": bench.kernel_source_hash(cls), "launches": len(f[cls][grid]), "grid_size": grid,
+             "fetch_size_kib": round(fk, 1), "write_size_kib": round(wk, 1),
+             "hbm_fetch_bytes": round(fk * 1024 * ff), "hbm_write_bytes": round(wk * 1024 * wf)}
+        e["hbm_bytes_per_launch"] = e["hbm_fetch_bytes"] + e["hbm_write_bytes"]
+        if cls in acc:
+            e["algorithmic_bytes"] = acc[cls]["bytes"]
+        res["kernels"][cls] = e
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -130,9 +196,20 @@ def main(argv=None):
     c.add_argument("--min-grid", type=int)
     c.add_argument("--max-grid", type=int)
     c.add_argument("--command", action="append", default=[], help="a command of the runs (recorded)")
+    st = sub.add_parser("step-traffic")
+    st.add_argument("--workload", required=True)
+    for a_ in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
+        st.add_argument(a_, required=True)
+    st.add_argument("--copy-bytes", type=int, required=True)
+    st.add_argument("--command", action="append", default=[], help="a command of the runs (recorded)")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         sys.stdout.write(trace_markdown(a.csv, a.title, a.command, a.only, a.min_grid, a.max_grid))
+    elif a.cmd == "step-traffic":
+        res = step_traffic(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes)
+        res["commands"] = a.command
+        json.dump(res, sys.stdout, indent=1)
+        sys.stdout.write("\n")
     else:
         res = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, a.only, a.min_grid, a.max_grid)
         res["commands"] = a.command

@@ -41,3 +41,28 @@ def test_traffic_is_scaled_by_the_copy_calibration(tmp_path):
     k = r["kernels"]["k"]
     assert k["fetch_bytes_median"] == 20 * 1024 * 2 and k["write_bytes_median"] == 4 * 1024 and k["dispatches"] == 3
     json.dumps(r)
+
+
+def test_step_traffic_takes_the_step_grid_and_bench_hashes(tmp_path):
+    import bench
+    head = "Kernel_Name,Grid_Size,Counter_Value\n"
+    cf = _write(tmp_path / "cf.csv", head + '"__amd_rocclr_copyBuffer",64,1024\n')
+    cw = _write(tmp_path / "cw.csv", head + '"__amd_rocclr_copyBuffer",64,2048\n')
+    # three step launches of the skinny projection (grid 131072) and one refresh-shaped launch
+    rows = ['"void lc::qkv_skinny_fused_kernel<128, 2, 8>(lc::QkvArgs)",131072,100',
+            '"void lc::qkv_skinny_fused_kernel<128, 2, 8>(lc::QkvArgs)",131072,300',
+            '"void lc::qkv_skinny_fused_kernel<128, 2, 8>(lc::QkvArgs)",131072,200',
+            '"void lc::qkv_skinny_fused_kernel<128, 2, 8>(lc::QkvArgs)",4096,9999',
+            '"void lc::attn_ab_kernel<half, unsigned short, 128, 32>(lc::SeqArgs, lc::AttnArgs, int)",122880,50']
+    f = _write(tmp_path / "f.csv", head + "\n".join(rows) + "\n")
+    w = _write(tmp_path / "w.csv", head + "\n".join(r.rsplit(",", 1)[0] + ",8" for r in rows) + "\n")
+    r = profsum.step_traffic("llada8b", f, w, cf, cw, copy_bytes=2 * 1024 * 1024)
+    q = r["kernels"]["qkv_gemm"]
+    assert q["grid_size"] == 131072 and q["launches"] == 3 and q["fetch_size_kib"] == 200.0
+    assert q["hbm_fetch_bytes"] == 200 * 1024 * 2 and q["hbm_write_bytes"] == 8 * 1024
+    assert q["hbm_bytes_per_launch"] == q["hbm_fetch_bytes"] + q["hbm_write_bytes"]
+    assert q["source_sha256"] == bench.kernel_source_hash("qkv_gemm")
+    assert q["algorithmic_bytes"] == bench.step_accounting(__import__("exact_attention_state_amd.synth").synth.WORKLOADS["llada8b"])["kernels"]["qkv_gemm"]["bytes"]
+    assert set(r["kernels"]) == {"qkv_gemm", "attn"}
+    assert profsum.step_class("lc::merge_kernel<half, unsigned short, 128>") == "merge"
+    assert profsum.step_class("lc::qkv_prep_kernel<8>") == "qkv_prep"
