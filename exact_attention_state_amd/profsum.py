@@ -26,10 +26,11 @@ Two commands, each reading the CSV files a rocprofv3 run writes with
 
     The same, per kernel class of the block step as bench.py names them
     (qkv, qkv_prep, qkv_gemm, attn, merge, block_rows, invariant_rows), over
-    the dispatches of each class's most frequent grid size (the step's
-    launches; the refresh's differ in shape), with the sha256 of the class's
-    sources and its algorithmic bytes from bench.py, which reads this record
-    for its roofline's traffic while the sources are unchanged.
+    the dispatches of each class's step grid size (the grid launched about as
+    often as the attention, which runs in steps only; the refresh's launches
+    differ in shape), with the sha256 of the class's sources and its
+    algorithmic bytes from bench.py, which reads this record for its
+    roofline's traffic while the sources are unchanged.
 """
 
 from __future__ import annotations
@@ -155,10 +156,21 @@ def step_traffic(workload, fetch, write, copy_fetch, copy_write, copy_bytes) -> 
         return out
 
     f, w = per_class(fetch), per_class(write)
+    # Step launches: the attention classes run in steps only; a projection
+    # class's step grid is the one launched about as often (the refresh's
+    # launches differ in shape and count; a class launched far less often
+    # than the steps belongs to the refresh alone and is left out).
+    n_step = max((max(len(v) for v in f[c].values()) for c in ("attn", "block_rows", "invariant_rows") if c in f),
+                 default=0)
+
+    def step_grid(cls):
+        cands = [(abs(len(v) - n_step), g) for g, v in f[cls].items() if len(v) >= 0.9 * n_step]
+        return min(cands)[1] if cands else None
+
     res = {"workload": workload,
            "what": f"HBM traffic per launch of the block-step kernels ({workload} workload, cold-cache protocol with "
-                   "rotating sets); per kernel class the dispatches of its most frequent grid size (the step's); "
-                   "median over those dispatches",
+                   "rotating sets); per kernel class the dispatches of its step grid size (launched about as often "
+                   "as the step's attention); median over those dispatches",
            "calibration": {"copy_kernel": f"__amd_rocclr_copyBuffer, {copy_bytes} bytes read and written "
                                           "(bench.py --copy-calibration)",
                            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
@@ -166,7 +178,9 @@ def step_traffic(workload, fetch, write, copy_fetch, copy_write, copy_bytes) -> 
                                    "reads for the copy"},
            "kernels": {}}
     for cls in sorted(set(f) & set(w)):
-        grid = max(f[cls], key=lambda g: len(f[cls][g]))
+        grid = step_grid(cls)
+        if grid is None:
+            continue
         fk, wk = statistics.median(f[cls][grid]), statistics.median(w[cls].get(grid, [0.0]))
         e = {"source_sha256": bench.kernel_source_hash(cls), "launches": len(f[cls][grid]), "grid_size": grid,
              "fetch_size_kib": round(fk, 1), "write_size_kib": round(wk, 1),

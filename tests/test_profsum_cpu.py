@@ -48,12 +48,13 @@ def test_step_traffic_takes_the_step_grid_and_bench_hashes(tmp_path):
     head = "Kernel_Name,Grid_Size,Counter_Value\n"
     cf = _write(tmp_path / "cf.csv", head + '"__amd_rocclr_copyBuffer",64,1024\n')
     cw = _write(tmp_path / "cw.csv", head + '"__amd_rocclr_copyBuffer",64,2048\n')
-    # three step launches of the skinny projection (grid 131072) and one refresh-shaped launch
-    rows = ['"void lc::qkv_skinny_fused_kernel<128, 2, 8>(lc::QkvArgs)",131072,100',
-            '"void lc::qkv_skinny_fused_kernel<128, 2, 8>(lc::QkvArgs)",131072,300',
-            '"void lc::qkv_skinny_fused_kernel<128, 2, 8>(lc::QkvArgs)",131072,200',
-            '"void lc::qkv_skinny_fused_kernel<128, 2, 8>(lc::QkvArgs)",4096,9999',
-            '"void lc::attn_ab_kernel<half, unsigned short, 128, 32>(lc::SeqArgs, lc::AttnArgs, int)",122880,50']
+    # three step launches of the skinny projection (grid 131072), refresh-shaped
+    # launches (more of them, another grid) and three attention launches; a
+    # prep kernel launched once (the refresh's) is left out
+    sk = '"void lc::qkv_skinny_fused_kernel<128, 2, 8>(lc::QkvArgs)"'
+    at = '"void lc::attn_ab_kernel<half, unsigned short, 128, 32>(lc::SeqArgs, lc::AttnArgs, int)"'
+    rows = [f"{sk},131072,100", f"{sk},131072,300", f"{sk},131072,200"] + [f"{sk},4096,9999"] * 5 + \
+           [f"{at},122880,50"] * 3 + ['"void lc::qkv_prep_kernel<8>(lc::PrepArgs)",49152,77']
     f = _write(tmp_path / "f.csv", head + "\n".join(rows) + "\n")
     w = _write(tmp_path / "w.csv", head + "\n".join(r.rsplit(",", 1)[0] + ",8" for r in rows) + "\n")
     r = profsum.step_traffic("llada8b", f, w, cf, cw, copy_bytes=2 * 1024 * 1024)
