@@ -89,81 +89,158 @@ __global__ __launch_bounds__(256) void importance_kernel(const SeqArgs sa, const
 }
 
 // ---------------------------------------------------------------------------
-// Tracking set: one workgroup per sample (N <= kTrackMaxKeys).  Every row
-// gets a 64-bit key that orders block rows last, then larger importance
-// first, then the lower row; a bitonic sort in LDS orders the keys and the
-// first `budget` name the tracking set, which one wave puts in row order.
+// Tracking set: one workgroup per sample (N <= kTrackMaxKeys).  Each row's
+// importance is the sum of its heads' partials (in head order); rows outside
+// the block are ranked by d = ~bits(max(importance, 0)), which orders larger
+// importance first (the bits of a non-negative float order like its value).
+// A radix select finds T, the K-th smallest d over those rows (K = budget,
+// or fewer rows), in three passes over 11, 11 and 10 bits: each pass counts
+// the rows that match the bits found so far into buckets of the next bits
+// (LDS atomics) and picks the bucket where the count crosses what remains.
+// Rows with d < T are all in the set; of the rows with d = T, the lowest
+// rows fill it (a pass in row order, only when they are more than needed).
+// One wave then writes the set in row order (-1 where fewer than budget).
 // ---------------------------------------------------------------------------
+constexpr int kSelBuckets = 2048;
+
+// Exclusive prefix over the 256 threads of v; the total in *total.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s_w, uint32_t *total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_w[w] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    before += k < w ? s_w[k] : 0u;
+    all += s_w[k];
+  }
+  __syncthreads();                                            // s_w is reused by the next scan
+  *total = all;
+  return before + x - v;
+}
+
 __global__ __launch_bounds__(256) void track_select_kernel(const SeqArgs sa, const TrackArgs a) {
   extern __shared__ __align__(16) char smem[];
-  unsigned long long *key = reinterpret_cast<unsigned long long *>(smem);   // [NP]
-  const int tid = threadIdx.x;
+  uint32_t *s_d = reinterpret_cast<uint32_t *>(smem);          // [N] d of every row
+  __shared__ uint32_t s_hist[kSelBuckets];
+  __shared__ uint32_t s_w[4];
+  __shared__ uint32_t s_pick[2];                               // bucket, rows before it
+  __shared__ uint32_t s_n, s_eq;
+  __shared__ int s_sel[64];
+  const int tid = threadIdx.x, lane = tid & 63;
   const int b = blockIdx.x;
   const int N = sa.len[b], off = sa.off[b], bs = sa.bs[b], be = sa.be[b];
-  int NP = 1;
-  while (NP < N) NP <<= 1;
-  for (int j = tid; j < NP; j += 256) {
-    unsigned long long k = ~0ull;                                // padding: after every row
-    if (j < N) {
-      // The row's heads are contiguous: all loaded at once (up to 64 heads, a
-      // multiple of 4), then added in head order.
-      const float *pr = a.partial + (size_t)(off + j) * a.H;
-      float v = 0.f;
-      if ((a.H & 3) == 0 && a.H <= 64) {
-        float4 x[16];
+  const int K = min(a.budget, N - (be - bs));                  // rows the set holds
+  for (int j = tid; j < N; j += 256) {
+    // The row's heads are contiguous: all loaded at once (up to 64 heads, a
+    // multiple of 4), then added in head order.
+    const float *pr = a.partial + (size_t)(off + j) * a.H;
+    float v = 0.f;
+    if ((a.H & 3) == 0 && a.H <= 64) {
+      float4 x[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-          if (4 * c < a.H) x[c] = *reinterpret_cast<const float4 *>(pr + 4 * c);
+      for (int c = 0; c < 16; ++c)
+        if (4 * c < a.H) x[c] = *reinterpret_cast<const float4 *>(pr + 4 * c);
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-          if (4 * c < a.H) v = (((v + x[c].x) + x[c].y) + x[c].z) + x[c].w;
-      } else {
-        for (int h = 0; h < a.H; ++h) v += pr[h];
-      }
-      a.importance[off + j] = v;
-      // Bit 63: a block row (last); bits 62..31: the complement of the
-      // importance's bits (importance >= 0 orders like its bits, so larger
-      // first); bits 30..0: the row.
-      const bool excl = j >= bs && j < be;
-      const uint32_t desc = ~__float_as_uint(fmaxf(v, 0.f));
-      k = ((unsigned long long)excl << 63) | ((unsigned long long)desc << 31) | (uint32_t)j;
+      for (int c = 0; c < 16; ++c)
+        if (4 * c < a.H) v = (((v + x[c].x) + x[c].y) + x[c].z) + x[c].w;
+    } else {
+      for (int h = 0; h < a.H; ++h) v += pr[h];
     }
-    key[j] = k;
+    a.importance[off + j] = v;
+    s_d[j] = ~__float_as_uint(fmaxf(v, 0.f));
   }
-  __syncthreads();
-  // Pair i of a stage is (lo, lo + stride), lo = 2 i - i % stride; thread t
-  // takes pairs t, t + 256, ...  At strides up to 64 the 64 pairs of a wave lie
-  // in 128 elements no other wave touches, so the wave's own ordering suffices
-  // there; a workgroup barrier separates the stages at larger strides.
-  for (int size = 2; size <= NP; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < NP / 2; i += 256) {
-        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const unsigned long long x = key[lo], y = key[hi];
-        if ((x > y) == up) {
-          key[lo] = y;
-          key[hi] = x;
+  uint32_t prefix = 0, mask = 0, need = (uint32_t)max(K, 0);
+  if (K > 0) {
+    // Three passes: bits 31..21, 20..10, 9..0 of d.
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t nb = pass == 2 ? 1024u : 2048u;
+      for (int k = tid; k < kSelBuckets; k += 256) s_hist[k] = 0u;
+      __syncthreads();                                         // also publishes s_d (first pass)
+      for (int j = tid; j < N; j += 256) {
+        if (j >= bs && j < be) continue;
+        const uint32_t d = s_d[j];
+        if ((d & mask) == prefix) atomicAdd(&s_hist[(d >> sh) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      // Thread t owns buckets 8t .. 8t + 7; the bucket where the ascending
+      // count reaches `need` is found by the thread whose range holds it.
+      uint32_t c[8], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        c[q] = s_hist[8 * tid + q];
+        sum += c[q];
+      }
+      uint32_t total;
+      uint32_t before = block_exclusive_scan(sum, s_w, &total);
+      if (before < need && need <= before + sum) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (need <= before + c[q]) {
+            s_pick[0] = 8 * tid + q;
+            s_pick[1] = before;
+            break;
+          }
+          before += c[q];
         }
       }
-      const int next = stride > 1 ? stride >> 1 : size;            // the next stage's stride
-      if (stride > 64 || (next > 64 && 2 * size <= NP)) __syncthreads();
-      else wave_lds_sync();
+      __syncthreads();
+      prefix |= s_pick[0] << sh;
+      mask |= (nb - 1) << sh;
+      need -= s_pick[1];
+      __syncthreads();                                         // s_pick is rewritten by the next pass
     }
-  __syncthreads();
-  // The first `budget` keys, put in row order (block rows and padding: -1, last).
+    // prefix = T; `need` rows with d = T complete the set.
+    if (tid == 0) {
+      s_n = 0u;
+      s_eq = 0u;
+    }
+    __syncthreads();
+    for (int j = tid; j < N; j += 256) {
+      if (j >= bs && j < be) continue;
+      const uint32_t d = s_d[j];
+      if (d < prefix) s_sel[atomicAdd(&s_n, 1u)] = j;
+      else if (d == prefix) atomicAdd(&s_eq, 1u);
+    }
+    __syncthreads();
+    const uint32_t n_less = s_n, n_eq = s_eq;
+    if (n_eq == need) {                                        // every tie is in the set
+      for (int j = tid; j < N; j += 256)
+        if (!(j >= bs && j < be) && s_d[j] == prefix) s_sel[atomicAdd(&s_n, 1u)] = j;
+    } else {
+      // The lowest `need` rows with d = T: 256 rows at a time in row order.
+      uint32_t taken = 0;
+      for (int j0 = 0; j0 < N && taken < need; j0 += 256) {
+        const int j = j0 + tid;
+        const uint32_t f = j < N && !(j >= bs && j < be) && s_d[j] == prefix ? 1u : 0u;
+        uint32_t cnt;
+        const uint32_t pos = block_exclusive_scan(f, s_w, &cnt);
+        if (f && taken + pos < need) s_sel[n_less + taken + pos] = j;
+        taken += cnt;
+      }
+    }
+    __syncthreads();
+  }
+  // The set in row order (-1 where fewer rows than budget).
   if (tid < 64) {
-    int me = 0x7fffffff;
-    if (tid < a.budget && tid < N) {
-      const unsigned long long k = key[tid];
-      if (!(k >> 63)) me = (int)(uint32_t)(k & 0x7fffffffu);
-    }
+    const int me = tid < K ? s_sel[tid] : 0x7fffffff;
     int rank = 0;
-    for (int j = 0; j < a.budget; ++j) {
-      const int o = __shfl(me, j);
-      rank += (o < me) || (o == me && j < tid);
+    for (int q = 0; q < K; ++q) {
+      const int o = __shfl(me, q);
+      rank += o < me;
     }
-    if (tid < a.budget) a.tracked[(size_t)(a.sample_base + b) * a.budget + rank] = me == 0x7fffffff ? -1 : me;
+    if (tid < a.budget) {
+      const size_t base = (size_t)(a.sample_base + b) * a.budget;
+      if (tid < K) a.tracked[base + rank] = me;
+      else a.tracked[base + tid] = -1;
+    }
   }
 }
 
@@ -382,9 +459,7 @@ hipError_t launch_track_select(const SeqArgs &sa, const TrackArgs &a, int max_le
                                const LaunchEvents &ev) {
   if (sa.n <= 0) return hipSuccess;
   if (max_len > kTrackMaxKeys || a.budget > 64 || a.budget < 1) return hipErrorInvalidValue;
-  int np = 1;
-  while (np < max_len) np <<= 1;
-  lc_launch<track_select_kernel>(dim3(sa.n), dim3(256), (unsigned)(np * sizeof(unsigned long long)), s, ev, sa, a);
+  lc_launch<track_select_kernel>(dim3(sa.n), dim3(256), (unsigned)(max_len * sizeof(uint32_t)), s, ev, sa, a);
   return hipGetLastError();
 }
 
@@ -406,8 +481,7 @@ hipError_t launch_verify_accept(const SeqArgs &sa, const AcceptArgs &a, hipStrea
 
 hipError_t setup_flashdllm_attributes() {
   return hipFuncSetAttribute(reinterpret_cast<const void *>(track_select_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             kTrackMaxKeys * (int)sizeof(unsigned long long));
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kTrackMaxKeys * (int)sizeof(uint32_t));
 }
 
 }  // namespace lc

@@ -77,6 +77,34 @@ def test_track_select_matches_oracle(wi):
     assert same >= 0.9 * budget * len(dw.table)
 
 
+def test_track_select_breaks_ties_by_row():
+    """40 rows outside the block get one and the same key, aligned with the
+    block queries: their importance values are bitwise equal and dominate, so
+    the 32 slots are decided by the tie rule (the lower rows)."""
+    wl = synth.WORKLOADS["llada8b"]
+    dw = _stepped(wl)
+    off, n, bs, be = dw.table[0]
+    H, Hk = wl.n_heads, wl.n_kv_heads
+    qm = dw.ct.q[off + bs:off + be].float().mean(0)                       # [H, d]
+    kd = (qm.view(Hk, H // Hk, -1).mean(1) * 12.0).to(dw.ct.k.dtype)     # [Hk, d]
+    rng = np.random.default_rng(77)
+    rows = np.sort(rng.choice(np.setdiff1d(np.arange(n), np.arange(bs, be)), size=40, replace=False))
+    dw.ct.k[torch.from_numpy(off + rows).cuda()] = kd
+    torch.cuda.synchronize()
+    budget = 32
+    imp = torch.zeros(dw.n_rows, dtype=torch.float32, device="cuda")
+    trk = torch.empty(len(dw.table), budget, dtype=torch.int32, device="cuda")
+    dw.ctx.track_select(dw.ct, dw.table, budget, imp, trk)
+    torch.cuda.synchronize()
+    got = imp.cpu().numpy().astype(np.float64)[off:off + n]
+    assert np.all(got[rows] == got[rows[0]]), "identical keys must get identical importance"
+    assert got[rows[0]] > np.max(np.delete(got, np.concatenate([rows, np.arange(bs, be)])))
+    want = FD.select_tracking(got, np.arange(bs, be), budget)
+    np.testing.assert_array_equal(trk.cpu().numpy()[0], want)
+    np.testing.assert_array_equal(want, rows[:budget])
+    _say(f"  40 tied rows: the set is their 32 lowest rows")
+
+
 @pytest.mark.parametrize("wi", [0, 1])
 def test_verify_attention_matches_oracle(wi):
     wl = _workloads()[wi]
