@@ -245,19 +245,23 @@ __global__ __launch_bounds__(256) void track_select_kernel(const SeqArgs sa, con
 }
 
 // ---------------------------------------------------------------------------
-// Verify attention: one workgroup of 4 waves per (16 verify queries, head);
+// Verify attention: one workgroup of NW waves per (16 verify queries, head);
 // grid (query-tile items, heads).  Keys in tiles of 32 (the sample's context
-// rows, then the verify tokens' own), wave w taking tiles w, w + 4, ..., the
-// next one loaded while the current one is used; the 4 waves' states
-// (max, normaliser, unnormalised O) are merged in LDS at the end.
+// rows, then the verify tokens' own), wave w taking tiles w, w + NW, ..., the
+// next one loaded while the current one is used; the waves' states (max,
+// normaliser, unnormalised O) are merged in LDS at the end by every thread.
+// Eight waves (each with three or four of llada8b's 27 tiles): 23.3 us,
+// against 28.5 us with four and 40.7 us with sixteen (LDS for one
+// workgroup per CU).
 // ---------------------------------------------------------------------------
-template <int DH>
-__global__ __launch_bounds__(256) void verify_attn_kernel(const SeqArgs sa, const VerifyArgs a) {
+template <int DH, int NW>
+__global__ __launch_bounds__(64 * NW) void verify_attn_kernel(const SeqArgs sa, const VerifyArgs a) {
   __shared__ uint32_t s_carried[kVerifyMaxKeys / 32];
-  __shared__ __align__(16) f16_t s_p[4][16 * 32];                // per wave: P [16 queries][32 keys]
+  __shared__ __align__(16) f16_t s_p[NW][16 * 32];               // per wave: P [16 queries][32 keys]
   constexpr int VS = DH + 8;                                     // staged V row (halves): conflict-free 16-byte writes
-  __shared__ __align__(16) f16_t s_vt[4][32 * VS];               // per wave: V [32 keys][DH (+8)]
-  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ __align__(16) f16_t s_vt[NW][32 * VS];              // per wave: V [32 keys][DH (+8)]
+  static_assert(sizeof(f16_t) * 32 * VS >= sizeof(float) * 16 * DH, "a wave's V area holds its O for the merge");
+  __shared__ float s_m[NW][16], s_l[NW][16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int item = blockIdx.x, h = blockIdx.y;
   const int b = find_sample(sa.pre[1], sa.n, item);
@@ -265,9 +269,9 @@ __global__ __launch_bounds__(256) void verify_attn_kernel(const SeqArgs sa, cons
   const int v0 = sa.pre[0][b], Q = sa.pre[0][b + 1] - v0;        // this sample's verify tokens
   const int kvh = h * a.Hkv / a.H, r16 = lane & 15, g = lane >> 4;
   // Positions the verify tokens carry are not context.
-  for (int j = tid; j < (N + 31) / 32; j += 256) s_carried[j] = 0u;
+  for (int j = tid; j < (N + 31) / 32; j += 64 * NW) s_carried[j] = 0u;
   __syncthreads();
-  for (int j = tid; j < Q; j += 256) {
+  for (int j = tid; j < Q; j += 64 * NW) {
     const int p = a.pos[v0 + j];
     if (p >= 0 && p < N) atomicOr(&s_carried[p >> 5], 1u << (p & 31));
   }
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(256) void verify_attn_kernel(const SeqArgs sa, cons
     }
   };
   if (w < nkt) load(w);
-  for (int t = w; t < nkt; t += 4) {
+  for (int t = w; t < nkt; t += NW) {
     const bool ctx = t < nctx;
     const int j0 = (ctx ? t : t - nctx) * 32, lim = ctx ? N : Q;
     // Scores of the 16 queries against keys j0 .. j0 + 31 (two 16-key halves).
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(256) void verify_attn_kernel(const SeqArgs sa, cons
       const int e = c * 64 + lane, key = e / (DH / 8), f0 = 8 * (e % (DH / 8));
       *reinterpret_cast<h8_t *>(VT + key * VS + f0) = vp[c];
     }
-    if (t + 4 < nkt) load(t + 4);
+    if (t + NW < nkt) load(t + NW);
     // Visibility of key column l % 16 (+16) for the lane's 4 query rows.
     float tmax[4];
 #pragma unroll
@@ -384,9 +388,9 @@ __global__ __launch_bounds__(256) void verify_attn_kernel(const SeqArgs sa, cons
     }
     wave_lds_sync();
   }
-  // Merge of the 4 waves' states (the V areas reused for the unnormalised O).
+  // Merge of the NW waves' states (the V areas reused for the unnormalised O).
   __syncthreads();
-  float *so = reinterpret_cast<float *>(&s_vt[0][0]);            // [4 waves][16 rows][DH]
+  float *so = reinterpret_cast<float *>(&s_vt[0][0]);            // [NW waves][16 rows][DH]
 #pragma unroll
   for (int f = 0; f < DH / 16; ++f)
 #pragma unroll
@@ -398,16 +402,15 @@ __global__ __launch_bounds__(256) void verify_attn_kernel(const SeqArgs sa, cons
       s_l[w][4 * g + v] = l[v];
     }
   __syncthreads();
-  if (w != 0) return;
-  for (int e = lane; e < 16 * DH; e += 64) {
+  for (int e = tid; e < 16 * DH; e += 64 * NW) {
     const int row = e / DH, qi = qt0 + row;
     if (qi >= Q) continue;
     float M = s_m[0][row];
 #pragma unroll
-    for (int k = 1; k < 4; ++k) M = fmaxf(M, s_m[k][row]);
+    for (int k = 1; k < NW; ++k) M = fmaxf(M, s_m[k][row]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NW; ++k) {
       const float c = s_m[k][row] == -INFINITY ? 0.f : fast_exp2(s_m[k][row] - M);
       num += c * so[(k * 16 + row) * DH + (e % DH)];
       den += c * s_l[k][row];
@@ -467,8 +470,9 @@ hipError_t launch_verify_attn(int dh, const SeqArgs &sa, const VerifyArgs &a, hi
   const int items = sa.pre[1][sa.n];
   if (items <= 0) return hipSuccess;
   const dim3 grid(items, a.H);
-  if (dh == 128) lc_launch<verify_attn_kernel<128>>(grid, dim3(256), 0, s, ev, sa, a);
-  else if (dh == 64) lc_launch<verify_attn_kernel<64>>(grid, dim3(256), 0, s, ev, sa, a);
+  constexpr int nw = 8;
+  if (dh == 128) lc_launch<verify_attn_kernel<128, nw>>(grid, dim3(64 * nw), 0, s, ev, sa, a);
+  else if (dh == 64) lc_launch<verify_attn_kernel<64, nw>>(grid, dim3(64 * nw), 0, s, ev, sa, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
