@@ -1370,18 +1370,38 @@ __global__ __launch_bounds__(256) void refresh_stream_kernel(const SeqArgs sa, c
     nk = min(S::TK, seg_end - k0);
   };
   // Tile tt into stage tt % NST: wave w does copies q = w, w+4, .. of the
-  // tile's K then V rows (keys past the tile repeat its last key).
+  // tile's K then V rows (keys past the tile repeat its last key).  The
+  // tile's first key sets a scalar base; a full tile's per-lane byte offsets
+  // are the same for every tile and computed once.
+  constexpr int NJ = S::CPW / 2;
+  uint32_t koff[NJ], voff[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = (j * 4 + w) * S::RPC + rr;
+    koff[j] = (uint32_t)(c * kvstride + ((slot ^ kslot(c, S::PPR)) << 3)) * 2u;
+    voff[j] = (uint32_t)(c * kvstride + ((slot ^ (c & 3)) << 3)) * 2u;
+  }
   auto issue = [&](int tt) {
     int k0, nk;
     tile_keys(tt, k0, nk);
-    const uint32_t st = lbase + (tt % S::NST) * S::STAGE;
+    const uint32_t st = lbase + (uint32_t)(tt % S::NST) * S::STAGE;
+    const T *bk = kb + (size_t)k0 * kvstride, *bv = vb + (size_t)k0 * kvstride;
+    if (nk == S::TK) {
 #pragma unroll
-    for (int j = 0; j < S::CPW / 2; ++j) {
-      const int q = j * 4 + w;
-      const int c = q * S::RPC + rr;
-      const size_t key = (size_t)(k0 + min(c, nk - 1)) * kvstride;
-      dma16(kb + key + ((slot ^ kslot(c, S::PPR)) << 3), st + q * 1024);
-      dma16(vb + key + ((slot ^ (c & 3)) << 3), st + S::KT + q * 1024);
+      for (int j = 0; j < NJ; ++j) {
+        const int q = j * 4 + w;
+        dma16_s(bk, koff[j], st + q * 1024);
+        dma16_s(bv, voff[j], st + S::KT + q * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int q = j * 4 + w;
+        const int c = q * S::RPC + rr;
+        const uint32_t key = (uint32_t)(min(c, nk - 1) * kvstride);
+        dma16_s(bk, (key + ((slot ^ kslot(c, S::PPR)) << 3)) * 2u, st + q * 1024);
+        dma16_s(bv, (key + ((slot ^ (c & 3)) << 3)) * 2u, st + S::KT + q * 1024);
+      }
     }
   };
 
@@ -1411,8 +1431,11 @@ __global__ __launch_bounds__(256) void refresh_stream_kernel(const SeqArgs sa, c
 
   AttnState<MB, DH> st;
   state_init_empty(st);
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const char *stg = smem + (tt % S::NST) * S::STAGE;
+  // One tile (stage STG = tt % NST, a compile-time constant: the loop below
+  // is unrolled by NST, so the stage's LDS offsets fold into the reads).
+  auto one_tile = [&](const int tt, auto STGC) {
+    constexpr int STG = decltype(STGC)::value;
+    const char *stg = smem + STG * S::STAGE;
     int k0, nk;
     tile_keys(tt, k0, nk);
     // S^T = K Q^T over the tile's 64 keys (both halves before the softmax:
@@ -1466,6 +1489,11 @@ __global__ __launch_bounds__(256) void refresh_stream_kernel(const SeqArgs sa, c
       lds_barrier();
       if (tt + S::NST < ntiles) issue(tt + S::NST);
     }
+  };
+  static_assert(S::NST == 2, "the tile loop is unrolled by two stages");
+  for (int tt = 0; tt < ntiles; tt += 2) {
+    one_tile(tt, std::integral_constant<int, 0>{});
+    if (tt + 1 < ntiles) one_tile(tt + 1, std::integral_constant<int, 1>{});
   }
 
 #pragma unroll
