@@ -1007,17 +1007,37 @@ __global__ __launch_bounds__(256) void block_rows_stream_kernel(const SeqArgs sa
   const int rr = lane / S::PPR, slot = lane % S::PPR;             // row-wise lane: row rr (+ RPC q), slot
 
   // Tile tt into stage tt % NST: wave w does copies q = w, w+4, .. of the
-  // tile's K then V rows (keys past the chunk repeat its last key).
-  auto issue = [&](int tt) {
-    const uint32_t st = lbase + S::QB + (tt % S::NST) * S::STAGE;
-    const int k0 = tt * S::TK;
+  // tile's K then V rows (keys past the chunk repeat its last key).  The
+  // tile's first key sets a scalar base; a full tile's per-lane byte offsets
+  // are the same for every tile and computed once.
+  constexpr int NJ = S::CPW / 2;
+  uint32_t koff[NJ], voff[NJ];
 #pragma unroll
-    for (int j = 0; j < S::CPW / 2; ++j) {
-      const int q = j * 4 + w;
-      const int c = q * S::RPC + rr;
-      const size_t key = (size_t)min(k0 + c, nkeys - 1) * kvstride;
-      dma16(kbase + key + ((slot ^ kslot(c, S::PPR)) << 3), st + q * 1024);
-      dma16(vbase + key + ((slot ^ (c & 3)) << 3), st + S::KT + q * 1024);
+  for (int j = 0; j < NJ; ++j) {
+    const int c = (j * 4 + w) * S::RPC + rr;
+    koff[j] = (uint32_t)(c * kvstride + ((slot ^ kslot(c, S::PPR)) << 3)) * 2u;
+    voff[j] = (uint32_t)(c * kvstride + ((slot ^ (c & 3)) << 3)) * 2u;
+  }
+  auto issue = [&](int tt) {
+    const uint32_t st = lbase + S::QB + (uint32_t)(tt % S::NST) * S::STAGE;
+    const int k0 = tt * S::TK;
+    const T *bk = kbase + (size_t)k0 * kvstride, *bv = vbase + (size_t)k0 * kvstride;
+    if (k0 + S::TK <= nkeys) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int q = j * 4 + w;
+        dma16_s(bk, koff[j], st + q * 1024);
+        dma16_s(bv, voff[j], st + S::KT + q * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int q = j * 4 + w;
+        const int c = q * S::RPC + rr;
+        const uint32_t key = (uint32_t)(min(c, nkeys - 1 - k0) * kvstride);
+        dma16_s(bk, (key + ((slot ^ kslot(c, S::PPR)) << 3)) * 2u, st + q * 1024);
+        dma16_s(bv, (key + ((slot ^ (c & 3)) << 3)) * 2u, st + S::KT + q * 1024);
+      }
     }
   };
   // The 32 query rows (QTile), rows past the block repeat its last row.
