@@ -683,7 +683,6 @@ lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache_weights *w,
                 workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lc::DType dt = dtype_of(ctx);
-  const int dh = ctx->cfg.head_dim, H = ctx->cfg.n_heads;
 
   for (int s0 = 0; s0 < batch; s0 += kMaxInline) {
     const int ns = std::min(kMaxInline, batch - s0);

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void track_select_kernel(const SeqArgs sa, con
   __shared__ uint32_t s_pick[2];                               // bucket, rows before it
   __shared__ uint32_t s_n, s_eq;
   __shared__ int s_sel[64];
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int N = sa.len[b], off = sa.off[b], bs = sa.bs[b], be = sa.be[b];
   const int K = min(a.budget, N - (be - bs));                  // rows the set holds
