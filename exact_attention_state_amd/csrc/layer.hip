@@ -496,14 +496,30 @@ int skinny_splits(long tiles, int K) {
   const long s = std::min<long>(cus / tiles, (K / 64) / kMinSplitSteps);
   return s > 1 ? (int)s : 1;
 }
+// Splits of a launch of 128 x 128 tiles that leaves compute units idle and
+// contracts over many steps (the down projection at 768 rows: 192 tiles of
+// 192 steps): up to four of at least kLongSplitSteps steps each, run with
+// two-stage rings so that two workgroups share a CU.  Measured at LLaDA-8B's
+// layer on 768 rows: down 176 -> 138 us (three splits 151 us; four with the
+// four-stage ring 160 us); W_o, 64 steps, stays whole (63 us either way).
+constexpr int kLongSplitSteps = 48;
+int long_splits(long tiles, int K) {
+  if (tiles >= device_cus()) return 1;
+  const int s = std::min(4, (K / 64) / kLongSplitSteps);
+  return s > 1 ? s : 1;
+}
 template <int TN, int EPI> long skinny_nx(int N) { return EPI == kLayerEpiSwiglu ? N / (TN / 2) : (N + TN - 1) / TN; }
 
+enum { kSplitNone = 0, kSplitSkinny = 1, kSplitLong = 2 };
 template <int TM, int TN, int NST, int EPI, int NW = 8>
-hipError_t go(const Bf16GemmArgs &a0, hipStream_t s, const LaunchEvents &ev, bool may_split) {
+hipError_t go(const Bf16GemmArgs &a0, hipStream_t s, const LaunchEvents &ev, int rule) {
   Bf16GemmArgs a = a0;
   const long NX = skinny_nx<TN, EPI>(a.N);
   const long tiles = NX * ((a.M + TM - 1) / TM);
-  a.splits = may_split && a.part ? skinny_splits(tiles, a.K) : 1;
+  a.splits = !a.part                ? 1
+             : rule == kSplitSkinny ? skinny_splits(tiles, a.K)
+             : rule == kSplitLong   ? long_splits(tiles, a.K)
+                                    : 1;
   a.ldp = (int)(NX * TN);
   if (a.splits == 1) {
     lc_launch<bf16_gemm_kernel<TM, TN, NST, EPI, NW>>(dim3(grid8(tiles)), dim3(64 * NW), bf16_gemm_smem<TM, TN, NST>(), s,
@@ -532,22 +548,36 @@ template <int EPI> hipError_t dispatch(const Bf16GemmArgs &a, int tile, hipStrea
     else tile = EPI == kLayerEpiSwiglu ? 3 : 2;                            // 128 x 128 (SwiGLU: 64 x 256)
   }
   switch (tile) {
-    case 1: return go<256, 256, 2, EPI>(a, s, ev, false);
+    case 1: return go<256, 256, 2, EPI>(a, s, ev, kSplitNone);
     case 2:
-      if constexpr (EPI == kLayerEpiSwiglu) return hipErrorInvalidValue;
-      else return go<128, 128, 4, EPI>(a, s, ev, false);
-    case 3: return go<64, 256, 3, EPI>(a, s, ev, a.M <= 64);
-    case 4: return go<128, 128, 2, EPI, 4>(a, s, ev, false);
+      if constexpr (EPI == kLayerEpiSwiglu) {
+        return hipErrorInvalidValue;
+      } else {
+        const long t128 = (long)((a.N + 127) / 128) * ((a.M + 127) / 128);
+        if (a.part && long_splits(t128, a.K) > 1) return go<128, 128, 2, EPI>(a, s, ev, kSplitLong);
+        return go<128, 128, 4, EPI>(a, s, ev, kSplitNone);
+      }
+    case 3: return go<64, 256, 3, EPI>(a, s, ev, a.M <= 64 ? kSplitSkinny : kSplitNone);
+    case 4: return go<128, 128, 2, EPI, 4>(a, s, ev, kSplitNone);
     default: return hipErrorInvalidValue;
   }
 }
 }  // namespace
 
 size_t bf16_gemm_part_bytes(int M, int N, int K, int out_kind) {
-  if (M <= 0 || M > 64 || K % 64) return 0;
-  const long NX = out_kind == kGemmOutSwiglu ? skinny_nx<256, kLayerEpiSwiglu>(N) : skinny_nx<256, kLayerEpiBf16>(N);
-  const int sp = skinny_splits(NX, K);
-  return sp > 1 ? (size_t)sp * M * NX * 256 * sizeof(float) : 0;
+  if (M <= 0 || K % 64) return 0;
+  size_t bytes = 0;
+  if (M <= 64) {                                               // 64 x 256 tiles
+    const long NX = out_kind == kGemmOutSwiglu ? skinny_nx<256, kLayerEpiSwiglu>(N) : skinny_nx<256, kLayerEpiBf16>(N);
+    const int sp = skinny_splits(NX, K);
+    if (sp > 1) bytes = (size_t)sp * M * NX * 256 * sizeof(float);
+  }
+  if (out_kind != kGemmOutSwiglu) {                            // 128 x 128 tiles (any row count)
+    const long NX = (N + 127) / 128;
+    const int sp = long_splits(NX * ((M + 127) / 128), K);
+    if (sp > 1) bytes = std::max(bytes, (size_t)sp * M * NX * 128 * sizeof(float));
+  }
+  return bytes;
 }
 
 hipError_t launch_bf16_gemm(const Bf16GemmArgs &a, int epi, int tile, hipStream_t s, const LaunchEvents &ev) {
@@ -601,6 +631,7 @@ hipError_t setup_layer_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, bf16_gemm_smem<TM, TN, NST>());
   LC_BGA(256, 256, 2, kLayerEpiBf16) LC_BGA(256, 256, 2, kLayerEpiF32) LC_BGA(256, 256, 2, kLayerEpiSwiglu)
   LC_BGA(128, 128, 4, kLayerEpiBf16) LC_BGA(128, 128, 4, kLayerEpiF32)
+  LC_BGA(128, 128, 2, kLayerEpiBf16) LC_BGA(128, 128, 2, kLayerEpiF32)
   LC_BGA(64, 256, 3, kLayerEpiBf16) LC_BGA(64, 256, 3, kLayerEpiF32) LC_BGA(64, 256, 3, kLayerEpiSwiglu)
 #undef LC_BGA
 #define LC_BGA4(NST, EPI)                                                                                     \

@@ -136,7 +136,12 @@ def _run_layer(D, H, F, T, seed, tile=None, monkeypatch=None):
 # Up to 64 rows with few output tiles the GEMMs split their contraction
 # (partials reduced in a second kernel): 1, 17, 32, 61 and 64 rows, and
 # LLaDA-8B's layer shape at a block of 32 rows (16 splits of W_o and down).
+# More rows with few 128 x 128 tiles and a long contraction split the down
+# projection too: d_ff 6144 (two splits) and 12288 (four), at 300 and 200
+# rows, and at 40 rows with the 128 x 128 tiles forced.
 @pytest.mark.parametrize("D,H,F,T,tile", [(512, 4, 384, 77, None), (1024, 8, 512, 300, None),
+                                           (512, 4, 6144, 300, None), (512, 4, 12288, 200, None),
+                                           (1024, 8, 12288, 40, "128"),
                                            (512, 4, 384, 513, "256"), (512, 4, 256, 200, "128"),
                                            (512, 4, 256, 130, "64"), (512, 4, 256, 200, "128w4"),
                                            (512, 4, 384, 1, None),
