@@ -1048,18 +1048,21 @@ bool ffn_capable(const lacache_ctx *ctx, int32_t d_ff) {
 int64_t ffn_rows_padded(int64_t n) { return (n + 255) / 256 * 256; }
 struct FfnWs {
   void *xq, *yq, *r;
-  float *sx, *sy;
+  float *sx, *sy, *part;
 };
 // Workspace of one FFN call: x codes [M_pad, D], their scales, y codes
-// [M_pad, F], their scales, and the residual r when the caller keeps none.
+// [M_pad, F], their scales, the residual r when the caller keeps none, and
+// the down projection's split partials when it splits.
 size_t ffn_ws_layout(const lacache_ctx *ctx, int32_t d_ff, int64_t n_rows, bool own_r, void *base, FfnWs *out) {
   const size_t D = ctx->cfg.d_model, F = d_ff, Mp = (size_t)ffn_rows_padded(n_rows);
-  const size_t sizes[5] = {align256(Mp * D), align256(D / 128 * Mp * 4), align256(Mp * F), align256(F / 128 * Mp * 4),
-                           own_r ? align256((size_t)n_rows * D * 2) : 0};
+  const int M = n_rows > (int64_t)1 << 24 ? 0 : (int)n_rows;
+  const size_t sizes[6] = {align256(Mp * D), align256(D / 128 * Mp * 4), align256(Mp * F), align256(F / 128 * Mp * 4),
+                           own_r ? align256((size_t)n_rows * D * 2) : 0,
+                           align256(lc::fp8_part_bytes(M, (int)Mp, (int)D, (int)F, ctx->fp8_tile))};
   char *p = static_cast<char *>(base);
   size_t off = 0;
-  void *ptrs[5];
-  for (int i = 0; i < 5; ++i) {
+  void *ptrs[6];
+  for (int i = 0; i < 6; ++i) {
     ptrs[i] = p ? p + off : nullptr;
     off += sizes[i];
   }
@@ -1069,6 +1072,7 @@ size_t ffn_ws_layout(const lacache_ctx *ctx, int32_t d_ff, int64_t n_rows, bool 
     out->yq = ptrs[2];
     out->sy = static_cast<float *>(ptrs[3]);
     out->r = ptrs[4];
+    out->part = sizes[5] ? static_cast<float *>(ptrs[5]) : nullptr;
   }
   return off;
 }
@@ -1182,6 +1186,7 @@ lacache_status lacache_ffn_fp8(lacache_ctx *ctx, int32_t d_ff, const lacache_ffn
   gd.K = d_ff;
   gd.res = na.r;
   gd.out = out;
+  gd.part = ws.part;
   e = timed(ctx, LACACHE_KERNEL_FFN_DOWN, s, [&](const lc::LaunchEvents &ev) { return lc::launch_fp8_gemm_resid(gd, ctx->fp8_tile, s, ev); });
   if (e != hipSuccess) return hip_fail(ctx, "FFN down launch", e);
   return LACACHE_OK;

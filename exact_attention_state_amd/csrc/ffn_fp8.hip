@@ -235,31 +235,36 @@ __global__ __launch_bounds__(512) void fp8_gemm_kernel(const Fp8GemmArgs a) {
   // column tile.  The ~32 workgroups a die runs at once then share 4 weight
   // tiles and 8 activation tiles through its L2.
   const int NX = a.N / TN, MY = a.M_pad / TM, ntiles = NX * MY;
-  const int per_die = (ntiles + 7) / 8;
+  // Units: tile x split of the contraction (a tile's splits adjacent).
+  const int S = EPI == kEpiResid && a.splits > 1 ? a.splits : 1, nunits = ntiles * S;
+  const int per_die = (nunits + 7) / 8;
   const int wg = blockIdx.x;
-  const int u = (wg & 7) * per_die + (wg >> 3);
-  if (u >= ntiles) return;                                     // whole workgroup: no barrier is skipped by part of it
+  const int uu = (wg & 7) * per_die + (wg >> 3);
+  if (uu >= nunits) return;                                    // whole workgroup: no barrier is skipped by part of it
+  const int u = uu / S, split = uu % S;
   constexpr int kGM = 8;
   const int grp = u / (kGM * NX), within = u % (kGM * NX);
   const int gm = min(kGM, MY - grp * kGM);                     // row tiles in this (last, maybe partial) group
   const int m0 = (grp * kGM + within % gm) * TM, n0 = (within / gm) * TN;
-  const int KG = a.K / 128, NB = a.N / 128;
+  const int KGA = a.K / 128, NB = a.N / 128;
+  const int kg0 = (int)((long)split * KGA / S), KG = (int)((long)(split + 1) * KGA / S) - kg0;   // this split's groups
   const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_address(smem));
-  const char *Ab = static_cast<const char *>(a.A) + (size_t)(m0 >> 8) * KG * kF8Tile + ((m0 & 255) >> 4) * kF8Frag;
-  const char *Bb = static_cast<const char *>(a.B) + (size_t)(n0 >> 8) * KG * kF8Tile + ((n0 & 255) >> 4) * kF8Frag;
+  const char *Ab = static_cast<const char *>(a.A) + (size_t)(m0 >> 8) * KGA * kF8Tile + ((m0 & 255) >> 4) * kF8Frag;
+  const char *Bb = static_cast<const char *>(a.B) + (size_t)(n0 >> 8) * KGA * kF8Tile + ((n0 & 255) >> 4) * kF8Frag;
   const int my_copies = L::COPIES + (w < L::SA_COPIES ? 1 : 0) + (w == 7 ? 1 : 0);
 
   auto issue = [&](int g) {
     const uint32_t st = lbase + (g % NST) * L::STAGE;
-    const char *ag = Ab + (size_t)g * kF8Tile, *bg = Bb + (size_t)g * kF8Tile;
+    const int gg = kg0 + g;                                    // absolute group
+    const char *ag = Ab + (size_t)gg * kF8Tile, *bg = Bb + (size_t)gg * kF8Tile;
 #pragma unroll
     for (int j = 0; j < L::COPIES; ++j) {
       const int c = w * L::COPIES + j;
       const char *src = c < 2 * L::RB ? ag + c * 1024 : bg + (c - 2 * L::RB) * 1024;
       dma16_s(src, lane_bytes(lane, 4), st + c * 1024);
     }
-    if (w < L::SA_COPIES) dma4_s(a.sa + (size_t)g * a.M_pad + m0 + w * 64, lane_bytes(lane, 2), st + L::A_BYTES + L::B_BYTES + w * 256);
-    if (w == 7) dma4_s(a.sw + (size_t)g * NB + n0 / 128, lane_bytes(min(lane, TN / 128 - 1), 2), st + L::A_BYTES + L::B_BYTES + L::SA_BYTES);
+    if (w < L::SA_COPIES) dma4_s(a.sa + (size_t)gg * a.M_pad + m0 + w * 64, lane_bytes(lane, 2), st + L::A_BYTES + L::B_BYTES + w * 256);
+    if (w == 7) dma4_s(a.sw + (size_t)gg * NB + n0 / 128, lane_bytes(min(lane, TN / 128 - 1), 2), st + L::A_BYTES + L::B_BYTES + L::SA_BYTES);
   };
   // The wave's column blocks within the tile.
   auto cb_of = [&](int j) {
@@ -386,6 +391,28 @@ __global__ __launch_bounds__(512) void fp8_gemm_kernel(const Fp8GemmArgs a) {
     float *ws = reinterpret_cast<float *>(smem) + w * 16 * STRIDE;
     const int rr = lane >> 2, c0 = (lane & 3) * CPL;
     const int ncol = n0 + wn * COLS + c0;
+    if (S > 1) {
+      // Split partial: this split's fp32 sums, row-wise, for the reduction.
+#pragma unroll
+      for (int i = 0; i < L::WRB; ++i) {
+#pragma unroll
+        for (int j = 0; j < L::WCB; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) ws[(4 * (lane >> 4) + v) * STRIDE + 16 * j + (lane & 15)] = acc[i][j][v];
+        wave_lds_sync();
+        const int m = m0 + (wm * L::WRB + i) * 16 + rr;
+        if (m < a.M) {
+          float *dst = a.part + ((size_t)split * a.M + m) * a.N + ncol;
+#pragma unroll
+          for (int p = 0; p < CPL / 4; ++p)
+            *reinterpret_cast<float4 *>(dst + 4 * p) =
+                make_float4(ws[rr * STRIDE + c0 + 4 * p], ws[rr * STRIDE + c0 + 4 * p + 1],
+                            ws[rr * STRIDE + c0 + 4 * p + 2], ws[rr * STRIDE + c0 + 4 * p + 3]);
+        }
+        wave_lds_sync();
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < L::WRB; ++i) {
 #pragma unroll
@@ -464,10 +491,60 @@ __global__ __launch_bounds__(512) void fp8_gemm_kernel(const Fp8GemmArgs a) {
   }
 }
 
+// out = bf16(res + the sum of the split partials, in split order): one
+// thread per 8 consecutive outputs of a row.
+__global__ __launch_bounds__(256) void fp8_splitk_reduce_kernel(const Fp8GemmArgs a) {
+  const int per_row = a.N / 8;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)a.M * per_row) return;
+  const int m = (int)(idx / per_row), n = (int)(idx % per_row) * 8;
+  const float *p = a.part + (size_t)m * a.N + n;
+  const size_t sstride = (size_t)a.M * a.N;
+  float y[8] = {};
+  for (int sp = 0; sp < a.splits; ++sp, p += sstride) {
+    const float4 u0 = *reinterpret_cast<const float4 *>(p), u1 = *reinterpret_cast<const float4 *>(p + 4);
+    y[0] += u0.x; y[1] += u0.y; y[2] += u0.z; y[3] += u0.w;
+    y[4] += u1.x; y[5] += u1.y; y[6] += u1.z; y[7] += u1.w;
+  }
+  const uint4 ru = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.res) + (size_t)m * a.N + n);
+  const uint32_t rw[4] = {ru.x, ru.y, ru.z, ru.w};
+  uint32_t ow[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float y0 = y[2 * q] + __uint_as_float(rw[q] << 16), y1 = y[2 * q + 1] + __uint_as_float(rw[q] & 0xffff0000u);
+    ow[q] = (uint32_t)f2bf(y0) | ((uint32_t)f2bf(y1) << 16);
+  }
+  *reinterpret_cast<uint4 *>(static_cast<bf16_t *>(a.out) + (size_t)m * a.N + n) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 size_t fp8_packed_bytes(int N, int K) { return (size_t)((N + 255) / 256) * (K / 128) * kF8Tile; }
+
+namespace {
+// Splits of a down projection on 128 x 128 tiles that leaves compute units
+// idle and contracts over many 128-wide groups (768 rows of LLaDA-8B's FFN:
+// 192 tiles, 96 groups): two halves of at least kF8SplitGroups groups, run
+// with two-stage rings so that two workgroups share a CU.  Measured there:
+// 82 us whole, 73 us in two, 75 us in four, 87 us in six (the fp32
+// partials' traffic grows with the count).
+constexpr int kF8SplitGroups = 24;
+int fp8_splits(int N, int M_pad, int K) {
+  const long tiles = (long)(N / 128) * (M_pad / 128);
+  if (tiles >= device_cus()) return 1;
+  return (K / 128) / kF8SplitGroups >= 2 ? 2 : 1;
+}
+bool fp8_resid_big(int N, int M_pad, int tile) {
+  return tile == 1 || (tile == 0 && (long)(N / 256) * (M_pad / 256) >= device_cus());
+}
+}  // namespace
+
+size_t fp8_part_bytes(int M, int M_pad, int N, int K, int tile) {
+  if (M <= 0 || N % 256 || K % 128 || M_pad % 256 || fp8_resid_big(N, M_pad, tile)) return 0;
+  const int sp = fp8_splits(N, M_pad, K);
+  return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
+}
 
 hipError_t launch_fp8_pack_weight(const void *W, int N, int K, int mode, void *Wp, float *sw, int Np, hipStream_t s) {
   if (N % 128 || K % 128 || N <= 0 || K <= 0) return hipErrorInvalidValue;
@@ -507,13 +584,26 @@ hipError_t launch_fp8_gemm_resid(const Fp8GemmArgs &a, int tile, hipStream_t s, 
   if (a.M_pad <= 0) return hipSuccess;
   if (a.N % 256 || a.K % 128 || a.M_pad % 256) return hipErrorInvalidValue;
   // 256 x 256 tiles when they give every compute unit a workgroup, else 128 x 128.
-  const bool big = tile == 1 || (tile == 0 && (a.N / 256) * (a.M_pad / 256) >= device_cus());
-  if (big)
+  Fp8GemmArgs b = a;
+  b.splits = 1;
+  if (fp8_resid_big(a.N, a.M_pad, tile)) {
     lc_launch<fp8_gemm_kernel<256, 256, 2, kEpiResid>>(dim3(fp8_grid(a.N / 256 * (a.M_pad / 256))), dim3(512),
-                                                       fp8_gemm_smem<256, 256, 2>(), s, ev, a);
-  else
-    lc_launch<fp8_gemm_kernel<128, 128, 4, kEpiResid>>(dim3(fp8_grid(a.N / 128 * (a.M_pad / 128))), dim3(512),
-                                                       fp8_gemm_smem<128, 128, 4>(), s, ev, a);
+                                                       fp8_gemm_smem<256, 256, 2>(), s, ev, b);
+    return hipGetLastError();
+  }
+  const int tiles = a.N / 128 * (a.M_pad / 128);
+  if (a.part) b.splits = fp8_splits(a.N, a.M_pad, a.K);
+  if (b.splits == 1) {
+    lc_launch<fp8_gemm_kernel<128, 128, 4, kEpiResid>>(dim3(fp8_grid(tiles)), dim3(512), fp8_gemm_smem<128, 128, 4>(), s,
+                                                       ev, b);
+    return hipGetLastError();
+  }
+  // The two launches share one event pair: the first stamps the start, the last the end.
+  const LaunchEvents first{ev.start, nullptr}, last{nullptr, ev.stop};
+  lc_launch<fp8_gemm_kernel<128, 128, 2, kEpiResid>>(dim3(fp8_grid((long)tiles * b.splits)), dim3(512),
+                                                     fp8_gemm_smem<128, 128, 2>(), s, first, b);
+  const long threads = (long)a.M * (a.N / 8);
+  lc_launch<fp8_splitk_reduce_kernel>(dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, last, b);
   return hipGetLastError();
 }
 
@@ -526,6 +616,9 @@ hipError_t setup_fp8_attributes() {
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(fp8_gemm_kernel<128, 128, 4, kEpiResid>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, fp8_gemm_smem<128, 128, 4>());
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(fp8_gemm_kernel<128, 128, 2, kEpiResid>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, fp8_gemm_smem<128, 128, 2>());
   return e;
 }
 

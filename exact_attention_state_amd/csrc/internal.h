@@ -172,13 +172,18 @@ struct Fp8GemmArgs {
   float *sy;               //   [N/256][M_pad]
   const void *res;         // residual epilogue: out = bf16(res + A W^T), [M, N] bf16
   void *out;
+  float *part;             // residual epilogue, split contraction: fp32 partials [splits][M][N] (workspace), or null
+  int splits;              // set by the launcher
 };
 size_t fp8_packed_bytes(int N, int K);                     // bytes of a packed FP8 operand of N rows
 hipError_t launch_fp8_pack_weight(const void *W, int N, int K, int mode, void *Wp, float *sw, int Np, hipStream_t s);
 hipError_t launch_fp8_addnorm_quant(const Fp8NormArgs &a, hipStream_t s, const LaunchEvents &ev);
 hipError_t launch_fp8_gemm_swiglu(const Fp8GemmArgs &a, hipStream_t s, const LaunchEvents &ev);
-// tile: 0 automatic, 1 = 256 x 256, 2 = 128 x 128
+// tile: 0 automatic, 1 = 256 x 256, 2 = 128 x 128.  With a.part set, a
+// launch of 128 x 128 tiles that leaves CUs idle and contracts over many
+// groups is split (fp8_part_bytes bytes of partials).
 hipError_t launch_fp8_gemm_resid(const Fp8GemmArgs &a, int tile, hipStream_t s, const LaunchEvents &ev);
+size_t fp8_part_bytes(int M, int M_pad, int N, int K, int tile);
 hipError_t setup_fp8_attributes();
 
 // The rest of layer 0 and the sampler cut (layer.hip).

@@ -137,7 +137,9 @@ def _gemm_bound(qa, sa, qw, sw):
     return (GEMM_REL + KG * 2.0 ** -23) * absprod
 
 
-@pytest.mark.parametrize("D,F,T", [(512, 384, 77), (1024, 768, 300), (512, 1024, 513)])
+# (512, 6144, 301): the down projection's 16 tiles of 128 x 128 contract over
+# 48 groups and split in two (partials summed by a second kernel).
+@pytest.mark.parametrize("D,F,T", [(512, 384, 77), (1024, 768, 300), (512, 1024, 513), (512, 6144, 301)])
 def test_ffn_fp8_every_stage(D, F, T, monkeypatch):
     _say(f"[ffn] D {D} F {F} T {T}")
     if T == 300:
