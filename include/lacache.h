@@ -407,12 +407,15 @@ LACACHE_API lacache_status lacache_layer_finish_workspace_size(const lacache_ctx
 
 /* Enqueues the rest of the layer for n_rows rows: out (and r_out unless
  * NULL).  The diagnostic environment variable LACACHE_LAYER_TILE ("256",
- * "128" or "64"), read by lacache_create, fixes the output tile of the bf16
- * GEMMs here and in lacache_sampler_cut (256 x 256, 128 x 128 or 64 x 256;
- * the SwiGLU GEMM takes 64 x 256 for "128") instead of the choice by launch
- * size.  Workspace after the call (each part at a multiple of 256 bytes, in
- * this order): r [n_rows, d_model] when r_out is NULL; x [n_rows, d_model];
- * y [n_rows, d_ff]. */
+ * "128", "64" or "128w4"), read by lacache_create, fixes the output tile of
+ * the bf16 GEMMs here and in lacache_sampler_cut (256 x 256, 128 x 128,
+ * 64 x 256, or 128 x 128 with four waves; the SwiGLU GEMM takes 64 x 256 for
+ * "128") instead of the choice by launch size.  GEMMs whose tiles leave
+ * compute units idle split their contraction (at most 64 rows on 64 x 256
+ * tiles; a long contraction on 128 x 128 tiles) and sum fp32 partials in
+ * the workspace.  Workspace after the call (each part at a multiple of 256
+ * bytes, in this order): r [n_rows, d_model] when r_out is NULL; x [n_rows,
+ * d_model]; y [n_rows, d_ff]. */
 LACACHE_API lacache_status lacache_layer_finish(lacache_ctx *ctx, int32_t d_ff, const lacache_layer_weights *w,
                                                 const void *h, const void *attn_out, int64_t n_rows, void *r_out,
                                                 void *out, void *workspace, size_t workspace_bytes, void *stream);
