@@ -1783,16 +1783,24 @@ hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnAr
 // consumer waits for has been started and finishes without waiting; the
 // poll is bounded anyway (a timeout sets a status bit and the workgroup
 // carries on; a dispatcher that did not deal round robin would show as
-// timeouts, the counters of a head then living in two L2s).  The last consumer of a head resets its counters, so the
-// next launch starts from zero without a memset.
+// timeouts, the counters of a head then living in two L2s).  The last
+// consumer of a head resets its counters, so the next launch starts from
+// zero without a memset.
 //
 // A consumer workgroup is two items of attn_ab_kernel side by side, one per
 // 256 threads with its own LDS: two type-A items (chunks 2c and 2c + 1 of one
 // (sample, 32-row group, head); both run the same number of tile iterations)
 // or two type-B items (consecutive 64-row tiles of one (sample, head)); an
-// odd last item pairs with an inactive half.  Every item runs the code it
-// runs in attn_ab_kernel (the compiler may contract a multiply and an add
-// differently in the two kernels, so outputs can differ in the last bit).
+// odd last item pairs with an inactive half.  The loads that do not need the
+// fresh q/k/v go out before the poll.  Every item runs the code it runs in
+// attn_ab_kernel (the compiler may contract a multiply and an add differently
+// in the two kernels, so outputs can differ in the last bit).
+//
+// Measured slower than the separate launches (llada8b: 37.5-38.3 us against
+// 24.0 + 11.8 us): a projection workgroup holds 213 VGPRs, one allocation
+// serves every role of a kernel, so consumers only start as producers retire
+// and then run the same chain of memory round trips as in their own launch.
+// Off by default; LACACHE_FUSED_STEP=1 at context creation selects it.
 // ---------------------------------------------------------------------------
 template <int NPW>
 __global__ __launch_bounds__(512) void step_fused_kernel(const SeqArgs sa, const PrepArgs p, const GemmArgs g,
