@@ -68,9 +68,8 @@ def parse():
 
 KERNEL_SOURCES = {
     "qkv": ["exact_attention_state_amd/csrc/qkv.hip"],
-    "qkv_prep": ["exact_attention_state_amd/csrc/gemm.hip", "exact_attention_state_amd/csrc/skinny.h"],
-    "qkv_gemm": ["exact_attention_state_amd/csrc/gemm.hip", "exact_attention_state_amd/csrc/skinny.h"],
-    "step_fused": ["exact_attention_state_amd/csrc/attn.hip", "exact_attention_state_amd/csrc/skinny.h"],
+    "qkv_prep": ["exact_attention_state_amd/csrc/gemm.hip"],
+    "qkv_gemm": ["exact_attention_state_amd/csrc/gemm.hip"],
     "block_rows": ["exact_attention_state_amd/csrc/attn.hip"],
     "invariant_rows": ["exact_attention_state_amd/csrc/attn.hip"],
     "attn": ["exact_attention_state_amd/csrc/attn.hip"],
@@ -137,14 +136,6 @@ def attention_summary(acc, kern):
     block rows' partials where it runs) as one unit: algorithmic bytes over the
     summed average durations of its launches, against the HBM peak."""
     names = [k for k in ("attn", "block_rows", "invariant_rows", "merge") if k in kern]
-    if "step_fused" in kern:
-        # The projection and the attention share one launch: the unit is the
-        # whole step (that launch and the merge), all its algorithmic bytes.
-        names = [k for k in ("step_fused", "merge") if k in kern]
-        us = sum(kern[k]["us_avg"] for k in names)
-        nbytes = acc["kernels"]["step_fused"]["bytes"]
-        return {"kernels": names, "us": us, "algorithmic_bytes": nbytes, "includes_projection": True,
-                "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS if us else None}
     us = sum(kern[k]["us_avg"] for k in names)
     nbytes = acc["kernels"]["attn"]["bytes"]
     return {"kernels": names, "us": us, "algorithmic_bytes": nbytes,
@@ -203,10 +194,6 @@ def step_accounting(wl):
         # gathers the embedding rows, writes the EmbedCache rows and Q/K/V
         # (bound by the weight's HBM stream).
         kern["qkv_gemm"] = dict(bytes=F * D * 2 + 2 * M * D * s + D * s + M * F * c, flops=2 * M * F * D)
-        # Small steps (at most 32 tokens, d_h 128, one KV head per head, H a
-        # multiple of 8) run that projection and the attention in one launch.
-        kern["step_fused"] = dict(bytes=kern["qkv_gemm"]["bytes"] + kern["attn"]["bytes"],
-                                  flops=kern["qkv_gemm"]["flops"] + kern["attn"]["flops"])
     elif wl.dtype == "bf16" and D % 512 == 0 and M >= 128:
         # Prep (embedding rows in, EmbedCache rows and the fp16 activations
         # out), then the GEMM over the packed fp16 weight (activations in,

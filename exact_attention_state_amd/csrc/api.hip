@@ -25,8 +25,6 @@ struct lacache_ctx {
   int device;
   float2 *rope;
   unsigned *flags;
-  int *sync;               // fused small block step: per-head hand-off counters (32 ints per head, zero between steps)
-  bool fused_step;         // fused small block step (LACACHE_FUSED_STEP=1 at creation; measured slower, off)
   int split_keys;          // keys per type-A chunk if fixed by LACACHE_SPLIT_KEYS, else 0 (per call)
   int gemm_tile;           // packed GEMM tile fixed by LACACHE_GEMM_TILE (lc::GemmTile), else automatic
   int refresh_rows;        // streaming refresh item rows fixed by LACACHE_REFRESH_ROWS (64 or 128), else 0
@@ -411,9 +409,6 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   ctx->cfg = c;
   ctx->rope = nullptr;
   ctx->flags = nullptr;
-  ctx->sync = nullptr;
-  ctx->fused_step = false;
-  if (const char *env = std::getenv("LACACHE_FUSED_STEP")) ctx->fused_step = std::strcmp(env, "1") == 0;
   ctx->split_keys = 0;
   if (const char *env = std::getenv("LACACHE_SPLIT_KEYS")) {
     const int v = std::atoi(env);
@@ -459,8 +454,6 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   if (e == hipSuccess) e = hipMemcpy(ctx->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMalloc(&ctx->flags, 256);
   if (e == hipSuccess) e = hipMemset(ctx->flags, 0, 256);
-  if (e == hipSuccess) e = hipMalloc(&ctx->sync, (size_t)c.n_heads * 32 * sizeof(int));
-  if (e == hipSuccess) e = hipMemset(ctx->sync, 0, (size_t)c.n_heads * 32 * sizeof(int));
   ctx->scratch = nullptr;
   if (e == hipSuccess) e = static_scratch_address(ctx->device, &ctx->scratch);
   if (e == hipSuccess) e = lc::setup_kernel_attributes();
@@ -471,7 +464,6 @@ lacache_status lacache_create(const lacache_config *cfg, lacache_ctx **out) {
   if (e != hipSuccess) {
     if (ctx->rope) (void)hipFree(ctx->rope);
     if (ctx->flags) (void)hipFree(ctx->flags);
-    if (ctx->sync) (void)hipFree(ctx->sync);
     delete ctx;
     return LACACHE_ERR_HIP;
   }
@@ -487,7 +479,6 @@ lacache_status lacache_destroy(lacache_ctx *ctx) {
   (void)hipDeviceSynchronize();
   (void)hipFree(ctx->rope);
   (void)hipFree(ctx->flags);
-  (void)hipFree(ctx->sync);
   for (auto &mk : ctx->marks) {
     (void)hipEventDestroy(mk.start);
     (void)hipEventDestroy(mk.stop);
@@ -533,9 +524,11 @@ lacache_status lacache_workspace_size(const lacache_ctx *cctx, int32_t op, const
 
 namespace {
 
-// Arguments of the prep and GEMM kernels for tokens [row0, row0 + M) of a slice.
-void qkv_gemm_args(const lacache_ctx *ctx, const lacache_weights *w, const lacache_cache *c, const int32_t *ids,
-                   int mode, int row0, int ids_base, int M, const GemmWs &gw, lc::PrepArgs &pa, lc::GemmArgs &ga) {
+// One prep + GEMM pass over tokens [row0, row0 + M) of a slice.
+hipError_t run_qkv_gemm(lacache_ctx *ctx, const lacache_weights *w, const lacache_cache *c, const int32_t *ids,
+                        const lc::SeqArgs &sa, int mode, int row0, int ids_base, int M, const GemmWs &gw,
+                        hipStream_t s) {
+  lc::PrepArgs pa;
   std::memset(&pa, 0, sizeof(pa));
   pa.ids = ids;
   pa.E = w->embed;
@@ -555,6 +548,12 @@ void qkv_gemm_args(const lacache_ctx *ctx, const lacache_weights *w, const lacac
   pa.D = ctx->cfg.d_model;
   pa.dh = ctx->cfg.head_dim;
   pa.eps = ctx->cfg.rms_eps;
+  const bool fused = w->w_qkv_packed && lc::skinny_fused_supported(M, ctx->cfg.d_model, ctx->cfg.vocab);
+  if (!fused) {
+    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV_PREP, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv_prep(sa, pa, s, ev); });
+    if (e != hipSuccess) return e;
+  }
+  lc::GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
   ga.A = gw.A;
   ga.W = w->w_qkv;
@@ -570,20 +569,6 @@ void qkv_gemm_args(const lacache_ctx *ctx, const lacache_weights *w, const lacac
   ga.F = features(ctx);
   ga.H = ctx->cfg.n_heads;
   ga.Hkv = ctx->cfg.n_kv_heads;
-}
-
-// One prep + GEMM pass over tokens [row0, row0 + M) of a slice.
-hipError_t run_qkv_gemm(lacache_ctx *ctx, const lacache_weights *w, const lacache_cache *c, const int32_t *ids,
-                        const lc::SeqArgs &sa, int mode, int row0, int ids_base, int M, const GemmWs &gw,
-                        hipStream_t s) {
-  lc::PrepArgs pa;
-  lc::GemmArgs ga;
-  qkv_gemm_args(ctx, w, c, ids, mode, row0, ids_base, M, gw, pa, ga);
-  const bool fused = w->w_qkv_packed && lc::skinny_fused_supported(M, ctx->cfg.d_model, ctx->cfg.vocab);
-  if (!fused) {
-    hipError_t e = timed(ctx, LACACHE_KERNEL_QKV_PREP, s, [&](const lc::LaunchEvents &ev) { return lc::launch_qkv_prep(sa, pa, s, ev); });
-    if (e != hipSuccess) return e;
-  }
   if (fused)
     return timed(ctx, LACACHE_KERNEL_QKV_GEMM, s, [&](const lc::LaunchEvents &ev) {
       return lc::launch_qkv_skinny_fused(ctx->cfg.head_dim, sa, pa, ga, s, ev);
@@ -835,16 +820,9 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
       }
     }
     const int M = sa.pre[0][ns];
-    // Small launches with the packed weight: the projection and the attention
-    // in one launch (launch_step_fused), then the merge.
-    const bool fused = combined && ctx->fused_step && gemm && w->w_qkv_packed &&
-                       lc::step_fused_supported(dt, dh, H, ctx->cfg.n_kv_heads, M, ctx->cfg.d_model, ctx->cfg.vocab);
 
-    hipError_t e = hipSuccess;
-    if (!fused) {
-      e = project_block_rows(ctx, w, cache, block_ids, sa, row_base, gemm, gemm_ws, s);
-      if (e != hipSuccess) return hip_fail(ctx, "block-step qkv launch", e);
-    }
+    hipError_t e = project_block_rows(ctx, w, cache, block_ids, sa, row_base, gemm, gemm_ws, s);
+    if (e != hipSuccess) return hip_fail(ctx, "block-step qkv launch", e);
 
     lc::AttnArgs aa;
     std::memset(&aa, 0, sizeof(aa));
@@ -871,26 +849,10 @@ lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w, co
     if (combined) {
       // Small launches: the block rows' partials and the invariant rows in one
       // launch (their latencies overlap), then the merge.
-      if (fused) {
-        lc::PrepArgs pa;
-        lc::GemmArgs ga;
-        qkv_gemm_args(ctx, w, cache, block_ids, 0, 0, row_base, M, GemmWs{nullptr, nullptr, nullptr}, pa, ga);
-        lc::FusedStepArgs fa;
-        std::memset(&fa, 0, sizeof(fa));
-        fa.sync = ctx->sync;
-        fa.flags = ctx->flags;
-        fa.spin_limit = 1 << 18;                   // normal waits take tens of polls
-        lc::step_fused_plan(sa, split_s, fa, H);
-        e = timed(ctx, LACACHE_KERNEL_STEP_FUSED, s, [&](const lc::LaunchEvents &ev) {
-          return lc::launch_step_fused(sa, pa, ga, aa, fa, s, ev);
-        });
-        if (e != hipSuccess) return hip_fail(ctx, "fused block-step launch", e);
-      } else {
-        e = timed(ctx, LACACHE_KERNEL_ATTN, s, [&](const lc::LaunchEvents &ev) {
-          return lc::launch_attn_ab(dt, dh, sa, aa, sa.pre[1][ns] * H, sa.pre[2][ns] * H, s, ev);
-        });
-        if (e != hipSuccess) return hip_fail(ctx, "block-step attention launch", e);
-      }
+      e = timed(ctx, LACACHE_KERNEL_ATTN, s, [&](const lc::LaunchEvents &ev) {
+        return lc::launch_attn_ab(dt, dh, sa, aa, sa.pre[1][ns] * H, sa.pre[2][ns] * H, s, ev);
+      });
+      if (e != hipSuccess) return hip_fail(ctx, "block-step attention launch", e);
       e = timed(ctx, LACACHE_KERNEL_MERGE, s, [&](const lc::LaunchEvents &ev) { return lc::launch_merge(dt, dh, sa, aa, M, s, ev); });
       if (e != hipSuccess) return hip_fail(ctx, "block-step merge launch", e);
       row_base += M;

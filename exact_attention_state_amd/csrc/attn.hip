@@ -40,7 +40,6 @@
 #include <type_traits>
 
 #include "internal.h"
-#include "skinny.h"
 
 namespace lc {
 
@@ -513,22 +512,10 @@ template <int DH> constexpr size_t merge_a_bytes() {
 }
 
 
-// Hook between an item's loads that do not depend on the block's fresh
-// q/k/v and those that do (the fused block step waits there for the
-// projection); it must meet every workgroup barrier the same way.
-struct NoWait {
-  __device__ void operator()() const {}
-};
-
-// tid: thread index among the item's 256 (four waves).  ntl >= 0 runs that
-// many tile iterations (at least the item's own; the extra ones only meet
-// the barriers), so two items can share one workgroup's barriers; an
-// inactive item loads and stores nothing.
-template <typename T, typename TO, int DH, typename Wait = NoWait>
-__device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int item, int h, char *smem, int tid,
-                                   int ntl = -1, bool active = true, const Wait &wait = Wait()) {
+template <typename T, typename TO, int DH>
+__device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int item, int h, char *smem) {
   constexpr int MB = 2, NDB = DH / 16, DPW = NDB / 4;
-  const int lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
 
   const int b = find_sample(sa.pre[1], sa.n, item);
@@ -549,19 +536,7 @@ __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int ite
   T *qbuf = reinterpret_cast<T *>(smem);
   T *vbuf = qbuf + kRowsA * DH;
   T *kbuf = vbuf + VTile<T, DH, kTileA>::kBytes / sizeof(T);
-  const T *kbase0 = static_cast<const T *>(a.k) + ((size_t)(sa.off[b] + key0)) * kvstride + hk * DH;
-  const T *vbase0 = static_cast<const T *>(a.v) + ((size_t)(sa.off[b] + key0)) * kvstride + hk * DH;
-  const int ntiles = active ? (nkeys + kTileA - 1) / kTileA : 0;
-  // With a wait hook, the first tile goes out before the wait when none of
-  // its keys is a block key.
-  constexpr bool kHook = !std::is_same<Wait, NoWait>::value;
-  const bool pre = kHook && kLdsK && ntiles > 0 && (key0 + min(kTileA, nkeys) <= sa.bs[b] || key0 >= sa.be[b]);
-  if (pre) {
-    if constexpr (kLdsK) ktile_stage<T, DH, kTileA, 256>(kbuf, kbase0, kvstride, min(kTileA, nkeys), tid);
-    vtile_stage<T, DH, kTileA, 256>(vbuf, vbase0, kvstride, min(kTileA, nkeys), tid);
-  }
-  wait();
-  if (active) {
+  {
     const int qrow0 = a.qmode == 0 ? sa.off[b] + sa.bs[b] : a.row_base + sa.pre[0][b];
 #pragma unroll
     for (int it = 0; it < kRowsA * QT::PPR / 256; ++it) {
@@ -577,22 +552,19 @@ __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int ite
 
   AttnState<MB, DH> st;
   state_init_empty(st);
-  const int nloop = ntl >= 0 ? ntl : ntiles;
-  for (int it = 0; it < nloop; ++it) {
-    const int t0 = it * kTileA;
-    const bool has = it < ntiles;
-    const int nk = has ? min(kTileA, nkeys - t0) : 0;
+  const T *kbase0 = static_cast<const T *>(a.k) + ((size_t)(sa.off[b] + key0)) * kvstride + hk * DH;
+  const T *vbase0 = static_cast<const T *>(a.v) + ((size_t)(sa.off[b] + key0)) * kvstride + hk * DH;
+  for (int t0 = 0; t0 < nkeys; t0 += kTileA) {
+    const int nk = min(kTileA, nkeys - t0);
     const int c0 = 32 * w;
     const int nv = max(0, min(32, nk - c0));
     // A step past the tile's end reads the tile's first keys (and is skipped).
     KStep<T, DH> kf;
     if constexpr (!kLdsK)
-      if (has) load_k_step<T, DH>(kf, kbase0 + (size_t)(t0 + (nv > 0 ? c0 : 0)) * kvstride, kvstride, max(nv, 1), lane);
-    if (it > 0) lds_barrier();                 // the previous tile's K and V reads are done
-    if (has && !(pre && it == 0)) {
-      if constexpr (kLdsK) ktile_stage<T, DH, kTileA, 256>(kbuf, kbase0 + (size_t)t0 * kvstride, kvstride, nk, tid);
-      vtile_stage<T, DH, kTileA, 256>(vbuf, vbase0 + (size_t)t0 * kvstride, kvstride, nk, tid);
-    }
+      load_k_step<T, DH>(kf, kbase0 + (size_t)(t0 + (nv > 0 ? c0 : 0)) * kvstride, kvstride, max(nv, 1), lane);
+    if (t0 > 0) lds_barrier();                 // the previous tile's K and V reads are done
+    if constexpr (kLdsK) ktile_stage<T, DH, kTileA, 256>(kbuf, kbase0 + (size_t)t0 * kvstride, kvstride, nk, tid);
+    vtile_stage<T, DH, kTileA, 256>(vbuf, vbase0 + (size_t)t0 * kvstride, kvstride, nk, tid);
     vtile_wait();
     lds_barrier();
     if constexpr (kLdsK) load_k_step_lds<T, DH>(kf, kbuf, nv > 0 ? c0 : 0, lane);
@@ -661,9 +633,9 @@ __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int ite
 #pragma unroll
       for (int ws = 0; ws < 4; ++ws)
         if (ws != w) acc += s_o[((db * 3 + (ws < w ? ws : ws - 1)) * MB + mb) * 64 + lane] * e[ws];
-      if (active && r < B) st4(part_o + prow * DH + OMap<DH>::feat(g, db, 0), acc * inv);
+      if (r < B) st4(part_o + prow * DH + OMap<DH>::feat(g, db, 0), acc * inv);
     }
-    if (active && r < B && w == 0 && g == 0) a.part_ml[prow] = make_float2(mx, L);
+    if (r < B && w == 0 && g == 0) a.part_ml[prow] = make_float2(mx, L);
   }
 }
 
@@ -672,18 +644,10 @@ __device__ void block_rows_partial(const SeqArgs &sa, const AttnArgs &a, int ite
 // FACache, stream the block's keys.  All global loads (queries, FACache,
 // first key step, V) are issued before the first wait.
 // ---------------------------------------------------------------------------
-// tid: thread index among the item's 256.  An inactive item only meets the
-// one workgroup barrier (so two items can share a workgroup).
-template <typename T, typename TO, int DH, int BMAX, int MB, typename Wait = NoWait>
-__device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, int h, char *smem, int tid,
-                               bool active = true, const Wait &wait = Wait()) {
+template <typename T, typename TO, int DH, int BMAX, int MB>
+__device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, int h, char *smem) {
   constexpr int NDB = DH / 16;
-  const int lane = tid & 63, w = tid >> 6;
-  if (!active) {
-    wait();
-    lds_barrier();
-    return;
-  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
 
   const int b = find_sample(sa.pre[2], sa.n, item);
@@ -720,7 +684,6 @@ __device__ void invariant_rows(const SeqArgs &sa, const AttnArgs &a, int item, i
     lc[mb] = a.l_c[crow[mb]];
     load_row<T, DH>(oc[mb], static_cast<const T *>(a.o_c) + crow[mb] * DH, g);
   }
-  wait();
   const T *kbase = static_cast<const T *>(a.k) + (size_t)(off + bs) * kvstride + hk * DH;
   // 16-bit caches: the block's K is staged row-wise in LDS once per
   // workgroup (one copy instead of one fragment load per wave).
@@ -1198,7 +1161,7 @@ __global__ __launch_bounds__(256) void block_rows_stream_kernel(const SeqArgs sa
 template <typename T, typename TO, int DH>
 __global__ __launch_bounds__(256) void block_rows_kernel(const SeqArgs sa, const AttnArgs a) {
   extern __shared__ __align__(16) char smem[];
-  block_rows_partial<T, TO, DH>(sa, a, blockIdx.x / a.H, blockIdx.x % a.H, smem, threadIdx.x);
+  block_rows_partial<T, TO, DH>(sa, a, blockIdx.x / a.H, blockIdx.x % a.H, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1276,11 +1239,11 @@ template <typename T, typename TO, int DH, int BMAX>
 __global__ __launch_bounds__(256) void attn_ab_kernel(const SeqArgs sa, const AttnArgs a, int nA) {
   extern __shared__ __align__(16) char smem[];
   if ((int)blockIdx.x < nA) {
-    block_rows_partial<T, TO, DH>(sa, a, blockIdx.x / a.H, blockIdx.x % a.H, smem, threadIdx.x);
+    block_rows_partial<T, TO, DH>(sa, a, blockIdx.x / a.H, blockIdx.x % a.H, smem);
     return;
   }
   const int j = blockIdx.x - nA;
-  invariant_rows<T, TO, DH, BMAX, 1>(sa, a, j / a.H, j % a.H, smem, threadIdx.x);
+  invariant_rows<T, TO, DH, BMAX, 1>(sa, a, j / a.H, j % a.H, smem);
 }
 
 // DualCache: the merge alone, 4 (row, head) pairs per workgroup.
@@ -1302,7 +1265,7 @@ __global__ __launch_bounds__(256) void invariant_rows_kernel(const SeqArgs sa, c
     return;
   }
   const int j = blockIdx.x - nmw;
-  invariant_rows<T, TO, DH, BMAX, 1>(sa, a, j / a.H, j % a.H, smem, threadIdx.x);
+  invariant_rows<T, TO, DH, BMAX, 1>(sa, a, j / a.H, j % a.H, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1757,202 +1720,6 @@ hipError_t launch_refresh_attn(DType dt, int dh, const SeqArgs &sa, const AttnAr
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Fused block step for small launches (at most 32 block tokens, d_h = 128,
-// one KV head per query head, 16-bit caches): the skinny projection and the
-// attention of attn_ab_kernel in ONE launch, so the attention's workgroups
-// take the chip as the projection's retire instead of after a launch
-// boundary.  The merge of the block rows' partials follows as its own launch.
-//
-// Workgroups are dealt to the 8 dies round robin (from whichever die the
-// launch starts on), so workgroups i and i + 8 share a die; each reads its
-// die from the XCC_ID register.  Head h lives on die h mod 8: its 8
-// projection workgroups (among the first nprod, 3 of the head's 24
-// fragments of q | k | v each) and its attention workgroups share that
-// die's L2, which is where the hand-off happens:
-//   producer: cache stores, wait until the L2 has them, workgroup barrier,
-//             one atomic add to the head's counter (performed in the L2);
-//   consumer: one thread polls the counter with atomic compare-and-swaps
-//             that never match (also performed in the L2) until all 8
-//             producers counted, sleeping between polls,
-//             then the workgroup barrier releases its waves, whose loads
-//             miss in L1 (nothing of the block's q/k/v was loaded on this CU
-//             before its producers finished) and read the L2.
-// Producers have lower indices than every consumer of their die and the
-// dispatcher starts a die's workgroups in index order, so every producer a
-// consumer waits for has been started and finishes without waiting; the
-// poll is bounded anyway (a timeout sets a status bit and the workgroup
-// carries on; a dispatcher that did not deal round robin would show as
-// timeouts, the counters of a head then living in two L2s).  The last
-// consumer of a head resets its counters, so the next launch starts from
-// zero without a memset.
-//
-// A consumer workgroup is two items of attn_ab_kernel side by side, one per
-// 256 threads with its own LDS: two type-A items (chunks 2c and 2c + 1 of one
-// (sample, 32-row group, head); both run the same number of tile iterations)
-// or two type-B items (consecutive 64-row tiles of one (sample, head)); an
-// odd last item pairs with an inactive half.  The loads that do not need the
-// fresh q/k/v go out before the poll.  Every item runs the code it runs in
-// attn_ab_kernel (the compiler may contract a multiply and an add differently
-// in the two kernels, so outputs can differ in the last bit).
-//
-// Measured slower than the separate launches (llada8b: 37.5-38.3 us against
-// 24.0 + 11.8 us): a projection workgroup holds 213 VGPRs, one allocation
-// serves every role of a kernel, so consumers only start as producers retire
-// and then run the same chain of memory round trips as in their own launch.
-// Off by default; LACACHE_FUSED_STEP=1 at context creation selects it.
-// ---------------------------------------------------------------------------
-template <int NPW>
-__global__ __launch_bounds__(512) void step_fused_kernel(const SeqArgs sa, const PrepArgs p, const GemmArgs g,
-                                                         const AttnArgs a, const FusedStepArgs f) {
-  extern __shared__ __align__(16) char smem[];
-  constexpr int DH = 128, BM = 32;
-  // The die this workgroup runs on: XCC_ID (hardware register 20, bits 3:0).
-  // Workgroups i and i + 8 share a die (the dispatcher deals them round
-  // robin, starting from any die), so i >> 3 numbers a die's workgroups.
-  const int i = blockIdx.x, die = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;
-  const int hpd = a.H / 8;                                      // heads per die
-  if (i < f.nprod) {
-    const int j = i >> 3, part = j & 7, h = die + 8 * (j >> 3);
-    int cb[3];
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int fl = 3 * part + q;                              // fragment of the head's q | k | v
-      cb[q] = (fl >> 3) * (a.H * (DH / 16)) + h * (DH / 16) + (fl & 7);
-    }
-    skinny_project<DH, 2, NPW, false>(sa, p, g, smem, i, f.nprod, cb[0], cb[1], cb[2]);
-    __builtin_amdgcn_s_waitcnt(0);                              // this wave's stores are in the L2
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(f.sync + h * 32, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return;
-  }
-  // Consumer j of this die: type-A pairs (all heads of the die), then type-B pairs.
-  const int j = (i - f.nprod) >> 3;
-  const bool typeA = j < f.npa * hpd;
-  const int jj = typeA ? j : j - f.npa * hpd;
-  const int pr = jj / hpd, h = die + 8 * (jj % hpd);
-  int item0 = 0, item1 = 0;
-  bool act1 = false;
-  {
-    int base = 0;
-    for (int b = 0; b < sa.n; ++b) {
-      if (typeA) {
-        const int B = sa.be[b] - sa.bs[b];
-        const int nrg = (B + kRowsA - 1) / kRowsA, nch = (sa.len[b] + a.split_keys - 1) / a.split_keys;
-        const int np = nrg * ((nch + 1) >> 1);
-        if (pr < base + np) {
-          const int loc = pr - base, rg = loc % nrg, cp = loc / nrg;
-          item0 = sa.pre[1][b] + (2 * cp) * nrg + rg;
-          act1 = 2 * cp + 1 < nch;
-          item1 = act1 ? item0 + nrg : item0;
-          break;
-        }
-        base += np;
-      } else {
-        const int nb = sa.pre[2][b + 1] - sa.pre[2][b];
-        const int np = (nb + 1) >> 1;
-        if (pr < base + np) {
-          item0 = sa.pre[2][b] + 2 * (pr - base);
-          act1 = item0 + 1 < sa.pre[2][b + 1];
-          item1 = act1 ? item0 + 1 : item0;
-          break;
-        }
-        base += np;
-      }
-    }
-  }
-  int *cnt = f.sync + h * 32;
-  // Between the items' independent loads (queries and FACache rows of the
-  // invariant rows, the first key tile of a chunk without block keys) and
-  // their first read of the block's fresh data: one thread polls, then the
-  // workgroup barrier (the loads already issued stay in flight; the
-  // compiler moves no memory access across it).
-  auto wait = [&]() {
-    if (threadIdx.x == 0) {
-      int spins = 0;
-      // A compare-and-swap that never matches (counts are >= 0) reads the
-      // counter in the L2; an add of 0 would be compiled to a plain load.
-      int expected = -1;
-      while ((__hip_atomic_compare_exchange_strong(cnt, &expected, -1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_WORKGROUP),
-              expected) < 8) {
-        expected = -1;
-        if (++spins > f.spin_limit) {
-          atomicOr(f.flags, 8u);                                // LACACHE_DEVFLAG_STEP_HANDOFF
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
-      }
-    }
-    asm volatile("" : : : "memory");
-    lds_barrier();
-    asm volatile("" : : : "memory");
-  };
-  const int half = threadIdx.x >> 8, tid = threadIdx.x & 255;
-  char *hs = smem + half * f.half_bytes;
-  const int item = half ? item1 : item0;
-  const bool active = half == 0 || act1;
-  if (typeA)
-    block_rows_partial<f16_t, bf16_t, DH>(sa, a, item, h, hs, tid, f.ntl, active, wait);
-  else
-    invariant_rows<f16_t, bf16_t, DH, BM, 1>(sa, a, item, h, hs, tid, active, wait);
-  if (threadIdx.x == 0) {
-    const int done = __hip_atomic_fetch_add(cnt + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (done == f.npa + f.npb - 1) {                            // every consumer of the head has passed its poll
-      __hip_atomic_exchange(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_exchange(cnt + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-  }
-}
-
-constexpr size_t fused_half_bytes() { return (attn_ab_smem<f16_t, 128, 32>() + 255) / 256 * 256; }
-constexpr size_t fused_step_smem() {
-  return 2 * fused_half_bytes() > (size_t)skinny_fused_smem<2, 16>() ? 2 * fused_half_bytes()
-                                                                       : (size_t)skinny_fused_smem<2, 16>();
-}
-static_assert(fused_step_smem() <= 160 * 1024, "two attention items per workgroup must fit a CU's LDS");
-
-bool step_fused_supported(DType dt, int dh, int H, int Hkv, int M, int D, int vocab) {
-  return dt == kBF16 && dh == 128 && H == Hkv && H % 8 == 0 && M >= 1 && M <= 32 && skinny_fused_supported(M, D, vocab);
-}
-
-void step_fused_plan(const SeqArgs &sa, int split_keys, FusedStepArgs &f, int H) {
-  int npa = 0, npb = 0, ntl = 0;
-  for (int b = 0; b < sa.n; ++b) {
-    const int B = sa.be[b] - sa.bs[b];
-    const int nrg = (B + kRowsA - 1) / kRowsA, nch = (sa.len[b] + split_keys - 1) / split_keys;
-    npa += nrg * ((nch + 1) / 2);
-    npb += (sa.pre[2][b + 1] - sa.pre[2][b] + 1) / 2;
-    const int longest = sa.len[b] < split_keys ? sa.len[b] : split_keys;
-    const int nt = (longest + kTileA - 1) / kTileA;
-    ntl = ntl > nt ? ntl : nt;
-  }
-  f.nprod = 8 * H;
-  f.npa = npa;
-  f.npb = npb;
-  f.ntl = ntl;
-  f.half_bytes = (int)fused_half_bytes();
-}
-
-hipError_t launch_step_fused(const SeqArgs &sa, const PrepArgs &p, const GemmArgs &g, const AttnArgs &a,
-                             const FusedStepArgs &f, hipStream_t s, const LaunchEvents &ev) {
-  if (!step_fused_supported(kBF16, 128, a.H, a.Hkv, g.M, g.D, p.vocab) || !g.Wp || g.M != p.M || g.D != p.D ||
-      f.nprod != 8 * a.H || g.F != 3 * a.H * 128 || !f.sync)
-    return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(f.nprod + a.H * (f.npa + f.npb)));
-  const size_t smem = fused_step_smem();
-#define LC_FS(NPWV) lc_launch<step_fused_kernel<NPWV>>(grid, dim3(512), (unsigned)smem, s, ev, sa, p, g, a, f)
-  switch (g.D / 512) {
-    case 1: LC_FS(1); break;
-    case 2: LC_FS(2); break;
-    case 4: LC_FS(4); break;
-    case 8: LC_FS(8); break;
-    default: LC_FS(16); break;
-  }
-#undef LC_FS
-  return hipGetLastError();
-}
-
 hipError_t setup_kernel_attributes() {
   hipError_t e = hipSuccess;
 #define LC_ATTR(K, BYTES)                                                                        \
@@ -1977,11 +1744,6 @@ hipError_t setup_kernel_attributes() {
   LC_ATTR_INV(64)
   LC_ATTR_INV(128)
 #undef LC_ATTR_INV
-  LC_ATTR((step_fused_kernel<1>), fused_step_smem());
-  LC_ATTR((step_fused_kernel<2>), fused_step_smem());
-  LC_ATTR((step_fused_kernel<4>), fused_step_smem());
-  LC_ATTR((step_fused_kernel<8>), fused_step_smem());
-  LC_ATTR((step_fused_kernel<16>), fused_step_smem());
   LC_ATTR((block_rows_kernel<f16_t, bf16_t, 128>), (block_rows_smem<f16_t, 128>()));
   LC_ATTR((block_rows_kernel<f16_t, bf16_t, 64>), (block_rows_smem<f16_t, 64>()));
   LC_ATTR((block_rows_kernel<float, float, 128>), (block_rows_smem<float, 128>()));

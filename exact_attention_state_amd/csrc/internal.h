@@ -85,18 +85,6 @@ struct AttnArgs {
   float scale_log2;        // sm_scale * log2(e)
 };
 
-// Fused small block step (launch_step_fused): per-launch plan and the
-// per-head hand-off counters.
-struct FusedStepArgs {
-  int *sync;               // per head h: ints [32 h] (producers done) and [32 h + 1] (consumers done); zero between launches
-  unsigned *flags;         // device status word (8: a poll timed out)
-  int nprod;               // projection workgroups: 8 per head
-  int npa, npb;            // consumer workgroups per head: type-A pairs, type-B pairs
-  int ntl;                 // tile iterations of every type-A item
-  int half_bytes;          // LDS of one item
-  int spin_limit;          // polls before a consumer gives up
-};
-
 // Optional timing events attached to a launch: when set, the kernel is
 // dispatched with hipExtLaunchKernelGGL, which stamps the events with the
 // dispatch's own start and end times.
@@ -140,13 +128,6 @@ bool skinny_supported(int M, int D);      // the packed-weight projection for <=
 int prep_rows(int M, int D, bool packed); // rows the prep kernel writes (zero rows past M included)
 hipError_t launch_pack_qkv_weight(const void *W, void *Wp, int D, int F, int dh, hipStream_t s);
 hipError_t setup_gemm_attributes();
-// Fused small block step: projection and attention (attn_ab_kernel's items)
-// in one launch; the merge follows.  step_fused_plan fills nprod, npa, npb,
-// ntl and half_bytes from the slice's plan (pre[1], pre[2], split_keys).
-bool step_fused_supported(DType dt, int dh, int H, int Hkv, int M, int D, int vocab);
-void step_fused_plan(const SeqArgs &sa, int split_keys, FusedStepArgs &f, int H);
-hipError_t launch_step_fused(const SeqArgs &sa, const PrepArgs &p, const GemmArgs &g, const AttnArgs &a,
-                             const FusedStepArgs &f, hipStream_t s, const LaunchEvents &ev);
 int device_cus();                         // compute units of the current device (cached; 256 if unknown)
 hipError_t launch_block_rows(DType dt, int dh, const SeqArgs &sa, const AttnArgs &a, int n_blocks,
                              hipStream_t s, const LaunchEvents &ev);

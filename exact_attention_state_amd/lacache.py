@@ -23,7 +23,6 @@ OP_PREFILL, OP_BLOCK_STEP, OP_DUALCACHE_ATTN, OP_REFRESH_BLOCK, OP_PROJECT_BLOCK
 DEVFLAG_BAD_TOKEN_ID = 1
 DEVFLAG_CACHE_RANGE = 2
 DEVFLAG_SEARCH_ORDER = 4
-DEVFLAG_STEP_HANDOFF = 8
 
 EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "lacache_prefill_cache",
             "lacache_block_step", "lacache_refresh_block", "lacache_dualcache_attn", "lacache_read_device_status",
@@ -41,7 +40,7 @@ EXPORTED = ("lacache_create", "lacache_destroy", "lacache_workspace_size", "laca
 KERNEL_NAMES = ("qkv", "block_rows", "invariant_rows", "merge", "refresh_attn", "qkv_prep", "qkv_gemm", "attn",
                 "ffn_norm", "ffn_gate_up", "ffn_down", "layer_oproj", "layer_norm", "layer_gate_up", "layer_down",
                 "sampler_norm", "sampler_lmhead", "sampler_softmax", "track_importance", "track_select",
-                "verify_attn", "verify_accept", "step_fused")
+                "verify_attn", "verify_accept")
 
 
 class Config(ctypes.Structure):

@@ -127,7 +127,6 @@ def traffic(fetch, write, copy_fetch, copy_write, copy_bytes, only=None, min_gri
 # kernel name; the first match wins.
 STEP_CLASSES = (("qkv_prep", ("qkv_prep_kernel",)), ("qkv_gemm", ("qkv_gemm", "qkv_skinny")),
                 ("qkv", ("qkv_fused_kernel",)), ("attn", ("attn_ab_kernel",)), ("merge", ("merge_kernel",)),
-                ("step_fused", ("step_fused_kernel",)),
                 ("block_rows", ("block_rows_stream_kernel", "block_rows_kernel")),
                 ("invariant_rows", ("invariant_stream_kernel", "invariant_rows_kernel")))
 

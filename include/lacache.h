@@ -91,8 +91,6 @@ typedef enum { LACACHE_F32 = 0, LACACHE_BF16 = 1 } lacache_dtype;
 #define LACACHE_DEVFLAG_CACHE_RANGE 2u   /* a q/k/v value exceeded the fp16 range */
 #define LACACHE_DEVFLAG_SEARCH_ORDER 4u  /* lacache_verify_accept: search positions not increasing
                                             or outside the sample (nothing accepted there) */
-#define LACACHE_DEVFLAG_STEP_HANDOFF 8u  /* fused block step: an attention workgroup stopped waiting
-                                            for its head's projection (results not valid) */
 
 /* First-layer shape (Section 3.3.2).  Supported: head_dim 64 or 128,
  * d_model a multiple of 256 up to 8192, n_heads a multiple of n_kv_heads,
@@ -223,16 +221,7 @@ LACACHE_API lacache_status lacache_prefill_cache(lacache_ctx *ctx, const lacache
  * NULL) for every row of every sample.  Reads, never writes, the FACache.
  * The result equals a full recompute of layer 0 on the new ids, up to
  * rounding, provided the caches were filled by lacache_prefill_cache for the
- * same block table and only block ids changed since.
- * Diagnostics: with LACACHE_FUSED_STEP=1 in the environment at
- * lacache_create, small bf16 steps (at most 32 block tokens, head_dim 128,
- * n_kv_heads == n_heads a multiple of 8, the packed weight) run the
- * projection and the attention as one launch whose workgroups hand each
- * head's fresh q/k/v over through per-head counters owned by the context
- * (zero between steps); block steps that overlap on that context (other
- * streams or threads) then race and must be serialised by the caller.  Same
- * arithmetic: q/k/v bitwise equal, outputs equal up to the last bit.  It is
- * off by default: measured slower than the separate launches. */
+ * same block table and only block ids changed since. */
 LACACHE_API lacache_status lacache_block_step(lacache_ctx *ctx, const lacache_weights *w,
                                   const int32_t *block_ids, const lacache_seq *seqs,
                                   int32_t batch, const lacache_cache *cache,
@@ -564,9 +553,7 @@ typedef enum {
   LACACHE_KERNEL_TRACK_SELECT = 19,  /* selective update: the tracking set          */
   LACACHE_KERNEL_VERIFY_ATTN = 20,   /* two-view verify attention                   */
   LACACHE_KERNEL_VERIFY_ACCEPT = 21, /* verify acceptance                           */
-  LACACHE_KERNEL_STEP_FUSED = 22,    /* small block steps: projection and attention
-                                        in one launch (the merge follows)          */
-  LACACHE_KERNEL_COUNT = 23
+  LACACHE_KERNEL_COUNT = 22
 } lacache_kernel;
 
 LACACHE_API lacache_status lacache_profile_enable(lacache_ctx *ctx, int enable);
